@@ -1,0 +1,44 @@
+"""CPU oracle for the fine-grained (block-scaled) FP8 linear layer.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product package imports this
+code; only the tests, the smoke check and the CPU-baseline leg of the
+benchmark may call it.  It shares no code, tables or constants with the HIP
+path: the E4M3 codec here is written from the format's bit definition with
+integer arithmetic, the quantizers follow the per-block / per-group
+definition element by element, and the GEMM dequantizes to fp64 and calls a
+plain fp64 matrix product.
+
+What is computed, and where it comes from:
+
+* Weights: one scale per 2D block of 128x128, 8-bit codes
+  ("Fine-grained FP8" page of the transformers docs, introduction: weights
+  are reduced to 8 bits per 2D block, ``weight_block_size=(128, 128)``).
+* Activations: one scale per token per group of input channels, the group
+  matching the weight block along the input channel (128 by default)
+  (same page, introduction), computed at run time
+  (same page, "DeepGEMM fast path": ``activation_scheme="dynamic"``).
+* Scales are fp32 (same page, "UE8M0 scale format": ``float32`` is the
+  default scale type that UE8M0 checkpoints replace).
+* The linear layer's result is that of dequantize-then-matmul
+  ("BFL (fp8r / nvfp4)" page of the diffusers docs, "Kernels": the
+  device-independent path dequantizes the weights and runs a plain linear).
+* The 8-bit format is OCP FP8 E4M3FN (bias 7, largest finite 448, NaN at
+  S.1111.111, no infinities); encoding rounds to nearest, ties to even, and
+  saturates at +-448; the scale of a block or group is fl32(amax / 448) and
+  is the dequantization multiplier.  These are this library's readings of
+  what the pages leave open.
+
+Modules: :mod:`oracle.e4m3` (codec), :mod:`oracle.quant` (quantizers),
+:mod:`oracle.gemm` (block-scaled and grouped GEMM, linear layer).
+"""
+from .e4m3 import E4M3_MAX, decode, encode, fl32_div
+from .quant import act_quant_group, weight_block_quant, quant_element_map
+from .gemm import (bf16_rne_bits, block_gemm, dequant_act, dequant_weight,
+                   grouped_block_gemm, linear, tolerance_report)
+
+__all__ = [
+    "E4M3_MAX", "decode", "encode", "fl32_div",
+    "act_quant_group", "weight_block_quant", "quant_element_map",
+    "bf16_rne_bits", "block_gemm", "dequant_act", "dequant_weight",
+    "grouped_block_gemm", "linear", "tolerance_report",
+]

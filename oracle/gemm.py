@@ -1,0 +1,117 @@
+"""Block-scaled GEMM, grouped GEMM and the linear layer (test oracle).
+
+Test infrastructure: see the package docstring for who may import this.
+
+The linear layer's result is defined as dequantize-then-matmul ("BFL (fp8r /
+nvfp4)" page of the diffusers docs, "Kernels": the portable path turns the
+weights back into the compute type and runs a plain linear), applied to the
+quantized weights *and* the dynamically quantized activations of the
+"Fine-grained FP8" page (introduction):
+
+    A[m, k] = dec(x_q[m, k]) * x_s[m, k // 128]
+    B[n, k] = dec(W_q[n, k]) * W_s[n // 128, k // 128]
+    y_hat   = A @ B^T                    (fp64; every A and B entry is exact)
+    y       = bf16_RNE(y_hat)
+
+This is the same number as applying the per-block scale pair inside the
+K loop, sum_kb x_s[m,kb] W_s[nb,kb] sum_{k in kb} dec(x_q) dec(W_q), up to
+the order of the fp64 additions.  The grouped (mixture-of-experts) variant
+applies the GEMM to each expert's contiguous row range with that expert's
+weights ("Fine-grained FP8" page, "UE8M0 scale format": expert matmuls may
+run through grouped back-ends that take fp32 scales).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .e4m3 import decode
+from .quant import GROUP, act_quant_group
+
+REL_FROB_TOL = 2e-3
+ELEM_REL_TOL = 1e-2
+ELEM_FLOOR = 1e-3  # of the row's RMS: guards near-zero outputs from cancellation
+
+
+def dequant_act(x_q, x_s) -> np.ndarray:
+    """[M,K] codes and [M,K/128] scales -> fp64 [M,K]."""
+    M, K = x_q.shape
+    v = decode(x_q).reshape(M, K // GROUP, GROUP)
+    return (v * np.asarray(x_s, np.float64)[:, :, None]).reshape(M, K)
+
+
+def dequant_weight(w_q, w_s) -> np.ndarray:
+    """[N,K] codes and [ceil(N/128),K/128] scales -> fp64 [N,K]."""
+    N, K = w_q.shape
+    s = np.repeat(np.repeat(np.asarray(w_s, np.float64), GROUP, axis=0)[:N], GROUP, axis=1)
+    return decode(w_q) * s
+
+
+def block_gemm(x_q, x_s, w_q, w_s) -> np.ndarray:
+    """Unrounded fp64 y_hat[M,N] = dequant(x) @ dequant(W)^T."""
+    return dequant_act(x_q, x_s) @ dequant_weight(w_q, w_s).T
+
+
+def grouped_block_gemm(x_q, x_s, w_q, w_s, offsets) -> np.ndarray:
+    """Expert e multiplies rows [off[e], off[e+1]) by W[e].  Rows outside
+    [off[0], off[E]) are NaN (the GPU leaves them unwritten)."""
+    E, N, K = w_q.shape
+    total = x_q.shape[0]
+    y = np.full((total, N), np.nan)
+    for e in range(E):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 > r0:
+            y[r0:r1] = block_gemm(x_q[r0:r1], x_s[r0:r1], w_q[e], w_s[e])
+    return y
+
+
+def linear(x_bits, w_q, w_s):
+    """Dynamic activation quantization followed by the block-scaled GEMM."""
+    x_q, x_s = act_quant_group(x_bits)
+    return block_gemm(x_q, x_s, w_q, w_s)
+
+
+def bf16_rne_bits(y) -> np.ndarray:
+    """fp64 -> bf16 bit patterns, one rounding (nearest, ties to even),
+    subnormals kept, overflow to infinity."""
+    y = np.asarray(y, dtype=np.float64)
+    a = np.abs(y)
+    _, e = np.frexp(a)                       # a = f * 2^e, f in [0.5, 1)
+    qexp = np.maximum(e - 1, -126) - 7       # bf16 quantum of a's binade
+    q = np.ldexp(np.rint(np.ldexp(a, -qexp)), qexp)
+    with np.errstate(over="ignore"):
+        r = np.copysign(q, y).astype(np.float32)
+    return (r.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def bf16_bits_to_f64(b) -> np.ndarray:
+    return (np.asarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def tolerance_report(y_bf16_bits, y_hat, rel_frob_tol=REL_FROB_TOL,
+                     elem_rel_tol=ELEM_REL_TOL) -> dict:
+    """Compare a bf16 result with the unrounded fp64 oracle.
+
+    rel_frob = ||y - y_hat||_F / ||y_hat||_F   (must be <= 2e-3)
+    element:   |y - y_hat| <= 1e-2 * max(|y_hat|, 1e-3 * rms(y_hat row))
+    Also reports how many elements equal bf16_RNE(y_hat) bit for bit.
+    """
+    y = bf16_bits_to_f64(y_bf16_bits)
+    yh = np.asarray(y_hat, np.float64)
+    diff = y - yh
+    nrm = np.linalg.norm(yh)
+    rel_frob = float(np.linalg.norm(diff) / nrm) if nrm > 0 else float(np.linalg.norm(diff))
+    if yh.ndim == 2 and yh.shape[1] > 0:
+        rms = np.sqrt(np.mean(yh * yh, axis=1, keepdims=True))
+    else:
+        rms = np.sqrt(np.mean(yh * yh)) if yh.size else 0.0
+    denom = np.maximum(np.abs(yh), ELEM_FLOOR * rms)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        rel = np.where(denom > 0, np.abs(diff) / denom, np.where(diff == 0, 0.0, np.inf))
+    max_rel = float(rel.max()) if rel.size else 0.0
+    exact = float(np.mean(np.asarray(y_bf16_bits) == bf16_rne_bits(yh))) if yh.size else 1.0
+    return {
+        "rel_frob": rel_frob,
+        "max_elem_rel": max_rel,
+        "bitwise_equal_frac": exact,
+        "ok": bool(rel_frob <= rel_frob_tol and max_rel <= elem_rel_tol),
+    }

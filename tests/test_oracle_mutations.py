@@ -1,0 +1,77 @@
+"""Plant plausible mistakes in the oracle (on the CPU, by monkeypatching)
+and check that at least one pin fails for each: the pins are strong enough
+to catch a wrong scale constant, a wrong rounding rule, a dropped sign, a
+transposed operand, a wrong scale index and a dropped K block."""
+import numpy as np
+import pytest
+
+import oracle_pins as P
+from oracle import e4m3 as oe
+from oracle import gemm as og
+from oracle import quant as oq
+
+
+def _fails(pins):
+    failed = []
+    for pin in pins:
+        try:
+            pin()
+        except AssertionError:
+            return [pin.__name__]
+        except Exception as e:  # a crash also counts as caught
+            return [pin.__name__ + ":" + type(e).__name__]
+    return failed
+
+
+def _encode_ties_away(t):
+    t = np.asarray(t, np.float32).astype(np.float64)
+    a = np.minimum(np.abs(t), 448.0)
+    e = np.floor(np.log2(np.maximum(a, 1e-300)))
+    q = np.exp2(np.maximum(e, -6) - 3)
+    v = np.floor(a / q + 0.5) * q
+    return _orig_encode(np.copysign(v, t).astype(np.float32))
+
+
+_orig_encode = oe.encode
+
+
+def _quant_map_reciprocal(x_f32, amax_f32):
+    x = np.asarray(x_f32, np.float32); amax = np.asarray(amax_f32, np.float32)
+    s = (amax / np.float32(448)).astype(np.float32)
+    r = np.where(s == 0, np.float32(1), np.float32(1) / np.where(s == 0, 1, s)).astype(np.float32)
+    return oe.encode((x * r).astype(np.float32)), s
+
+
+MUTANTS = {
+    "scale_uses_240": lambda mp: mp.setattr(oq, "_F32_448", np.float32(240.0)),
+    "encode_ties_away": lambda mp: mp.setattr(oq, "encode", _encode_ties_away),
+    "divide_by_reciprocal": lambda mp: mp.setattr(oq, "quant_element_map", _quant_map_reciprocal),
+    "decode_bias_8": lambda mp: mp.setattr(oe, "decode", lambda c: _orig_decode(c) / 2.0),
+    "gemm_transposed_weight_scale": lambda mp: mp.setattr(
+        og, "dequant_weight", lambda q, s: _orig_dw(q, s.T.copy() if s.shape[0] == s.shape[1] else s[::-1].copy())),
+    "gemm_drops_last_kblock": lambda mp: mp.setattr(
+        og, "dequant_act", lambda q, s: _orig_da(q, np.concatenate([s[:, :-1], 0 * s[:, -1:]], 1))),
+    "bf16_truncates": lambda mp: mp.setattr(
+        og, "bf16_rne_bits", lambda y: (np.asarray(y, np.float64).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)),
+    "grouped_off_by_one": lambda mp: mp.setattr(
+        og, "grouped_block_gemm", _grouped_shift),
+    "weight_amax_full_block_rows": lambda mp: mp.setattr(oq, "GROUP", 64),
+}
+
+_orig_decode = oe.decode
+_orig_dw = og.dequant_weight
+_orig_da = og.dequant_act
+_orig_grouped = og.grouped_block_gemm
+
+
+def _grouped_shift(x_q, x_s, w_q, w_s, offsets):
+    off = np.asarray(offsets).copy()
+    off[1:-1] = np.maximum(off[1:-1] - 1, 0)
+    return _orig_grouped(x_q, x_s, w_q, w_s, off)
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    MUTANTS[name](monkeypatch)
+    failed = _fails(P.ALL_PINS)
+    assert failed, f"planted mistake {name} passed every pin"
