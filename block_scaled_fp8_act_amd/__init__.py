@@ -1,0 +1,227 @@
+"""Python binding of libfp8blk: block-scaled ("fine-grained") FP8 linear
+layers on AMD MI355X (gfx950).
+
+Argument marshalling only.  Every step of the computation runs in the HIP
+kernels of libfp8blk.so; torch provides device memory and the current
+stream.  There is no fallback: if the library is missing or the device is
+not a gfx950, calls raise.
+
+Low-level entry points carry the C names and take torch tensors for every
+buffer (inputs and preallocated outputs):
+
+    fp8_weight_block_quant(w, w_q, w_scale)
+    fp8_act_quant_group(x, x_q, x_scale)
+    fp8_block_gemm(x_q, x_scale, w_q, w_scale, y)
+    fp8_grouped_block_gemm(x_q, x_scale, w_q, w_scale, offsets, y)
+
+Convenience wrappers allocate the outputs:
+
+    weight_block_quant(w) -> (w_q uint8 [N,K], w_scale fp32 [ceil(N/128), K/128])
+    act_quant_group(x)    -> (x_q uint8 [M,K], x_scale fp32 [M, K/128])
+    block_gemm(x_q, x_scale, w_q, w_scale) -> y bf16 [M,N]
+    grouped_block_gemm(x_q, x_scale, w_q, w_scale, offsets) -> y bf16 [sum M_e, N]
+    linear(x, w_q, w_scale) -> y bf16 [M,N]   (dynamic act quant, then GEMM)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "Fp8BlkError", "BLOCK", "lib_path", "load_library", "status_string",
+    "fp8_weight_block_quant", "fp8_act_quant_group", "fp8_block_gemm",
+    "fp8_grouped_block_gemm", "weight_block_quant", "act_quant_group", "block_gemm",
+    "grouped_block_gemm", "linear",
+]
+
+BLOCK = 128
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "lib", "libfp8blk.so")
+_lib = None
+
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DEVICE, ERR_LAUNCH = range(6)
+
+
+class Fp8BlkError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+class Fp8BlkValueError(Fp8BlkError, ValueError):
+    pass
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libfp8blk.so (built in-tree by block_scaled_fp8_act_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"libfp8blk.so not found at {_LIB_PATH}; build it with "
+            "`python -m block_scaled_fp8_act_amd.build` (no CPU fallback exists)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    sigs = {
+        "fp8_weight_block_quant": [vp, i64, i64, vp, vp, vp],
+        "fp8_act_quant_group": [vp, i64, i64, vp, vp, vp],
+        "fp8_block_gemm": [vp, vp, vp, vp, i64, i64, i64, vp, vp],
+        "fp8_grouped_block_gemm": [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp, vp],
+    }
+    for name, args in sigs.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    lib.fp8blk_status_string.argtypes = [ctypes.c_int]
+    lib.fp8blk_status_string.restype = ctypes.c_char_p
+    lib.fp8blk_abi_version.argtypes = []
+    lib.fp8blk_abi_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().fp8blk_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str):
+    if status == OK:
+        return
+    msg = f"{what}: {status_string(status)}"
+    if status in (ERR_SHAPE, ERR_DEVICE):
+        raise Fp8BlkValueError(status, msg)
+    raise Fp8BlkError(status, msg)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtypes, ndim: int | None = None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} must have dtype in {dtypes}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device (cuda/hip) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got {t.dim()}")
+
+
+_CODES = (torch.uint8, torch.float8_e4m3fn)
+
+
+def _shape_eq(t, shape, name):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+# --------------------------------------------------------------------------
+# low-level entry points (same names as the C ABI)
+
+def fp8_weight_block_quant(w, w_q, w_scale):
+    _need(w, "w", (torch.bfloat16,), 2)
+    N, K = w.shape
+    _need(w_q, "w_q", _CODES); _need(w_scale, "w_scale", (torch.float32,))
+    _shape_eq(w_q, (N, K), "w_q")
+    if K % BLOCK == 0:
+        _shape_eq(w_scale, (-(-N // BLOCK), K // BLOCK), "w_scale")
+    _check(load_library().fp8_weight_block_quant(_ptr(w), N, K, _ptr(w_q), _ptr(w_scale), _stream()),
+           "fp8_weight_block_quant")
+
+
+def fp8_act_quant_group(x, x_q, x_scale):
+    _need(x, "x", (torch.bfloat16,), 2)
+    M, K = x.shape
+    _need(x_q, "x_q", _CODES); _need(x_scale, "x_scale", (torch.float32,))
+    _shape_eq(x_q, (M, K), "x_q")
+    if K % BLOCK == 0:
+        _shape_eq(x_scale, (M, K // BLOCK), "x_scale")
+    _check(load_library().fp8_act_quant_group(_ptr(x), M, K, _ptr(x_q), _ptr(x_scale), _stream()),
+           "fp8_act_quant_group")
+
+
+def fp8_block_gemm(x_q, x_scale, w_q, w_scale, y):
+    _need(x_q, "x_q", _CODES, 2); _need(w_q, "w_q", _CODES, 2)
+    _need(x_scale, "x_scale", (torch.float32,), 2); _need(w_scale, "w_scale", (torch.float32,), 2)
+    _need(y, "y", (torch.bfloat16,), 2)
+    M, K = x_q.shape
+    N = w_q.shape[0]
+    if w_q.shape[1] != K:
+        raise ValueError("x_q and w_q disagree on K")
+    if K % BLOCK == 0:
+        _shape_eq(x_scale, (M, K // BLOCK), "x_scale")
+        _shape_eq(w_scale, (-(-N // BLOCK), K // BLOCK), "w_scale")
+    _shape_eq(y, (M, N), "y")
+    _check(load_library().fp8_block_gemm(_ptr(x_q), _ptr(x_scale), _ptr(w_q), _ptr(w_scale),
+                                         M, N, K, _ptr(y), _stream()), "fp8_block_gemm")
+
+
+def fp8_grouped_block_gemm(x_q, x_scale, w_q, w_scale, offsets, y):
+    _need(x_q, "x_q", _CODES, 2); _need(w_q, "w_q", _CODES, 3)
+    _need(x_scale, "x_scale", (torch.float32,), 2); _need(w_scale, "w_scale", (torch.float32,), 3)
+    _need(offsets, "offsets", (torch.int32,), 1); _need(y, "y", (torch.bfloat16,), 2)
+    total, K = x_q.shape
+    E, N, K2 = w_q.shape
+    if K2 != K:
+        raise ValueError("x_q and w_q disagree on K")
+    if offsets.numel() != E + 1:
+        raise ValueError("offsets must have E+1 entries")
+    if K % BLOCK == 0:
+        _shape_eq(x_scale, (total, K // BLOCK), "x_scale")
+        _shape_eq(w_scale, (E, -(-N // BLOCK), K // BLOCK), "w_scale")
+    _shape_eq(y, (total, N), "y")
+    _check(load_library().fp8_grouped_block_gemm(
+        _ptr(x_q), _ptr(x_scale), _ptr(w_q), _ptr(w_scale), _ptr(offsets), E, total, N, K,
+        _ptr(y), _stream()), "fp8_grouped_block_gemm")
+
+
+# --------------------------------------------------------------------------
+# convenience wrappers (allocate outputs with torch.empty)
+
+def weight_block_quant(w):
+    N, K = w.shape
+    w_q = torch.empty((N, K), dtype=torch.uint8, device=w.device)
+    w_s = torch.empty((-(-N // BLOCK), max(K // BLOCK, 0)), dtype=torch.float32, device=w.device)
+    fp8_weight_block_quant(w, w_q, w_s)
+    return w_q, w_s
+
+
+def act_quant_group(x):
+    M, K = x.shape
+    x_q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    x_s = torch.empty((M, max(K // BLOCK, 0)), dtype=torch.float32, device=x.device)
+    fp8_act_quant_group(x, x_q, x_s)
+    return x_q, x_s
+
+
+def block_gemm(x_q, x_scale, w_q, w_scale):
+    y = torch.empty((x_q.shape[0], w_q.shape[0]), dtype=torch.bfloat16, device=x_q.device)
+    fp8_block_gemm(x_q, x_scale, w_q, w_scale, y)
+    return y
+
+
+def grouped_block_gemm(x_q, x_scale, w_q, w_scale, offsets):
+    y = torch.empty((x_q.shape[0], w_q.shape[1]), dtype=torch.bfloat16, device=x_q.device)
+    fp8_grouped_block_gemm(x_q, x_scale, w_q, w_scale, offsets, y)
+    return y
+
+
+def linear(x, w_q, w_scale):
+    """The FP8 linear layer: dynamic per-token-group quantization of x, then
+    the block-scaled GEMM, back to back on the current stream."""
+    x_q, x_s = act_quant_group(x)
+    return block_gemm(x_q, x_s, w_q, w_scale)

@@ -1,0 +1,131 @@
+// C ABI of fp8blk: argument validation (before any HIP runtime call), the
+// gfx950 device check, and dispatch to the kernels.  Declared in fp8blk.h.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+
+#include "../../include/fp8blk.h"
+#include "fp8blk_launch.h"
+
+namespace {
+
+constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1;
+constexpr int64_t kMaxK = int64_t(1) << 24;
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+constexpr int kMaxDevices = 64;
+
+// 0 = unknown, 1 = gfx950, 2 = other / unusable
+std::atomic<int> g_arch_state[kMaxDevices];
+
+bool misaligned(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+fp8blk_status check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return FP8BLK_ERR_DEVICE;
+  }
+  int st = g_arch_state[dev].load(std::memory_order_acquire);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return FP8BLK_ERR_DEVICE;
+    }
+    st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_arch_state[dev].store(st, std::memory_order_release);
+  }
+  return st == 1 ? FP8BLK_OK : FP8BLK_ERR_DEVICE;
+}
+
+fp8blk_status launched(hipError_t e) { return e == hipSuccess ? FP8BLK_OK : FP8BLK_ERR_LAUNCH; }
+
+// Shape rules shared by the entry points: rows in [0, 2^31), K a positive
+// multiple of 128 up to 2^24, element counts up to 2^40.
+bool bad_rows(int64_t r) { return r < 0 || r > kMaxRows; }
+bool bad_k(int64_t K) { return K <= 0 || K > kMaxK || (K % FP8BLK_BLOCK) != 0; }
+bool too_big(int64_t rows, int64_t K) { return rows > 0 && rows > kMaxElems / K; }
+
+}  // namespace
+
+extern "C" {
+
+const char *fp8blk_status_string(int s) {
+  switch (s) {
+    case FP8BLK_OK: return "FP8BLK_OK";
+    case FP8BLK_ERR_NULL: return "FP8BLK_ERR_NULL: a required pointer is NULL";
+    case FP8BLK_ERR_SHAPE: return "FP8BLK_ERR_SHAPE: bad size (negative, K not a positive multiple of 128, or over the limits)";
+    case FP8BLK_ERR_ALIGN: return "FP8BLK_ERR_ALIGN: a base pointer is not 16-byte aligned";
+    case FP8BLK_ERR_DEVICE: return "FP8BLK_ERR_DEVICE: no usable device, or the current device is not gfx950";
+    case FP8BLK_ERR_LAUNCH: return "FP8BLK_ERR_LAUNCH: kernel launch failed";
+    default: return "FP8BLK_ERR_UNKNOWN";
+  }
+}
+
+int fp8blk_abi_version(void) { return FP8BLK_ABI_VERSION; }
+
+fp8blk_status fp8_weight_block_quant(const void *w_bf16, int64_t N, int64_t K, void *w_q,
+                                     float *w_scale, void *stream) {
+  if (N > 0 && (!w_bf16 || !w_q || !w_scale)) return FP8BLK_ERR_NULL;
+  if (bad_rows(N) || bad_k(K) || too_big(N, K)) return FP8BLK_ERR_SHAPE;
+  if (N > 0 && (misaligned(w_bf16) || misaligned(w_q) || misaligned(w_scale)))
+    return FP8BLK_ERR_ALIGN;
+  if (fp8blk_status d = check_device()) return d;
+  if (N == 0) return FP8BLK_OK;
+  return launched(fp8blk::launch_weight_quant(w_bf16, N, K, w_q, w_scale,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+fp8blk_status fp8_act_quant_group(const void *x_bf16, int64_t M, int64_t K, void *x_q,
+                                  float *x_scale, void *stream) {
+  if (M > 0 && (!x_bf16 || !x_q || !x_scale)) return FP8BLK_ERR_NULL;
+  if (bad_rows(M) || bad_k(K) || too_big(M, K)) return FP8BLK_ERR_SHAPE;
+  if (M > 0 && (misaligned(x_bf16) || misaligned(x_q) || misaligned(x_scale)))
+    return FP8BLK_ERR_ALIGN;
+  if (fp8blk_status d = check_device()) return d;
+  if (M == 0) return FP8BLK_OK;
+  return launched(fp8blk::launch_act_quant(x_bf16, M, K, x_q, x_scale,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+fp8blk_status fp8_block_gemm(const void *x_q, const float *x_scale, const void *w_q,
+                             const float *w_scale, int64_t M, int64_t N, int64_t K, void *y_bf16,
+                             void *stream) {
+  const bool work = M > 0 && N > 0;
+  if (work && (!x_q || !x_scale || !w_q || !w_scale || !y_bf16)) return FP8BLK_ERR_NULL;
+  if (bad_rows(M) || bad_rows(N) || bad_k(K) || too_big(M, K) || too_big(N, K) ||
+      too_big(M, N))
+    return FP8BLK_ERR_SHAPE;
+  if (work && ((M + 127) / 128) * ((N + 127) / 128) > kMaxRows) return FP8BLK_ERR_SHAPE;
+  if (work && (misaligned(x_q) || misaligned(x_scale) || misaligned(w_q) ||
+               misaligned(w_scale) || misaligned(y_bf16)))
+    return FP8BLK_ERR_ALIGN;
+  if (fp8blk_status d = check_device()) return d;
+  if (!work) return FP8BLK_OK;
+  return launched(fp8blk::launch_block_gemm(x_q, x_scale, w_q, w_scale, M, N, K, y_bf16,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+fp8blk_status fp8_grouped_block_gemm(const void *x_q, const float *x_scale, const void *w_q,
+                                     const float *w_scale, const int32_t *expert_offsets,
+                                     int32_t E, int64_t total_M, int64_t N, int64_t K,
+                                     void *y_bf16, void *stream) {
+  const bool work = E > 0 && total_M > 0 && N > 0;
+  if (work && (!x_q || !x_scale || !w_q || !w_scale || !expert_offsets || !y_bf16))
+    return FP8BLK_ERR_NULL;
+  if (E < 0 || bad_rows(total_M) || bad_rows(N) || bad_k(K) || too_big(total_M, K) ||
+      too_big(total_M, N) || (E > 0 && too_big(int64_t(E) * N, K)) || too_big(int64_t(E), N))
+    return FP8BLK_ERR_SHAPE;
+  if (work && ((total_M + 127) / 128 + E) * ((N + 127) / 128) > kMaxRows) return FP8BLK_ERR_SHAPE;
+  if (work && (misaligned(x_q) || misaligned(x_scale) || misaligned(w_q) ||
+               misaligned(w_scale) || misaligned(y_bf16)))
+    return FP8BLK_ERR_ALIGN;
+  if (fp8blk_status d = check_device()) return d;
+  if (!work) return FP8BLK_OK;
+  return launched(fp8blk::launch_grouped_gemm(x_q, x_scale, w_q, w_scale, expert_offsets, E,
+                                              total_M, N, K, y_bf16,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,95 @@
+// Device helpers shared by the fp8blk kernels (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8blk {
+
+constexpr int kBlock = 128;  // weight block edge and activation group width
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// bf16 halves of a packed dword -> fp32 (exact widening).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// DPP lane permutes inside a row of 16 lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Max over the 16 lanes of a DPP row (values are >= 0); every lane gets it.
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_f<0x124>(v));  // row_ror:4
+  v = fmaxf(v, dpp_f<0x128>(v));  // row_ror:8
+  return v;
+}
+
+// Quantization parameters of one block or group.
+//   s  = fl32(amax / 448)           (IEEE division, denormals kept)
+//   sp = s * 2^k, y = fl32(1 / sp)  with k > 0 only for tiny s (< 2^-64),
+//        so that sp, y and the residual below stay far from underflow.
+// The quotient fl32(x / s) is then x' * y corrected once with an exact FMA
+// residual (Markstein's correction with a correctly rounded reciprocal),
+// x' = x * 2^k.  For every bf16 x with |x| <= amax this equals the IEEE
+// quotient wherever the quotient can round to a nonzero E4M3 code, and
+// gives the same signed-zero code elsewhere (checked over all
+// 1,065,402,238 (x, amax) bf16 pairs).  An all-zero set gets s = 0 and
+// sp = y = 1, which maps +-0 to +-0.
+struct QParams {
+  float s, sp, y;
+  int k;
+};
+
+__device__ __forceinline__ QParams make_qparams(float amax) {
+  QParams p;
+  p.s = amax / 448.0f;
+  p.k = 0;
+  if (p.s == 0.0f) {
+    p.sp = 1.0f;
+    p.y = 1.0f;
+  } else {
+    if (p.s < 0x1p-64f) {
+      int e;
+      (void)frexpf(p.s, &e);
+      p.k = 1 - e;
+    }
+    p.sp = ldexpf(p.s, p.k);
+    p.y = 1.0f / p.sp;
+  }
+  return p;
+}
+
+// fl32(x / s) for x' = x * 2^k already formed.
+__device__ __forceinline__ float quotient(float xp, float sp, float y) {
+  const float q0 = xp * y;
+  const float nr = fmaf(q0, sp, -xp);  // exact: q0*sp - x'
+  return fmaf(-nr, y, q0);
+}
+
+// Saturate to the E4M3 range before the hardware conversion (which rounds
+// to nearest even in the OCP E4M3FN format on gfx950).
+__device__ __forceinline__ float sat448(float t) {
+  return __builtin_amdgcn_fmed3f(t, -448.0f, 448.0f);
+}
+
+// Four fp32 -> four E4M3 codes packed little-endian into one dword.
+__device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(a), sat448(b), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(c), sat448(d), w, true);
+  return (uint32_t)w;
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+}  // namespace fp8blk

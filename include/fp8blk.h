@@ -1,0 +1,140 @@
+/*
+ * fp8blk -- block-scaled ("fine-grained") FP8 linear layer for AMD MI355X (gfx950).
+ *
+ * What the library computes
+ * -------------------------
+ * Weights are stored as 8-bit floats with one fp32 scale per 2D block of
+ * 128x128, and activations are quantized at run time with one fp32 scale per
+ * token and per group of 128 input channels, the group matching the weight
+ * block along the input channel ("Fine-grained FP8" page of the transformers
+ * docs, introduction; run-time activation scales are the "dynamic"
+ * activation scheme of its "DeepGEMM fast path" section; fp32 is the default
+ * scale type, per its "UE8M0 scale format" section).  The linear layer's
+ * value is that of dequantize-then-matmul ("BFL (fp8r / nvfp4)" page of the
+ * diffusers docs, "Kernels").
+ *
+ * The readings this library fixes where the pages are silent:
+ *   - the 8-bit format is OCP FP8 E4M3FN (bias 7, max 448, no infinities);
+ *   - scale s = fl32(amax / 448) over the block or group (s is the
+ *     dequantization multiplier: x ~= dec(q) * s);
+ *   - code q = E4M3(fl32(x / s)): the IEEE fp32 quotient is rounded first,
+ *     then rounded to nearest-even E4M3 and saturated to +-448;
+ *   - an all-zero block or group gets s = 0 and signed-zero codes;
+ *   - y[m,n] = bf16_RNE( sum_kb x_s[m,kb] * w_s[n/128,kb] *
+ *                        sum_{k in block kb} dec(x_q[m,k]) * dec(w_q[n,k]) ),
+ *     with fp32 accumulation; the 128-long inner sums run on fp8 matrix
+ *     cores and the scale pair is applied once per K block.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *   - All tensor pointers are DEVICE pointers; the caller owns every buffer.
+ *     The library never allocates, frees or keeps a pointer; it is stateless
+ *     apart from a per-device architecture check that is cached.
+ *   - Layouts are dense row-major: x [M,K], W [N,K] (the nn.Linear layout,
+ *     K contiguous), x_s [M, K/128], w_s [ceil(N/128), K/128], y [M,N].
+ *     bf16 tensors are raw 16-bit patterns; E4M3 codes are bytes.
+ *   - K must be a positive multiple of 128.  N and M may be any size >= 0;
+ *     a last weight block row with fewer than 128 rows covers only the rows
+ *     that exist.  M == 0 or N == 0 (or E == 0) is a no-op returning OK.
+ *   - Every tensor base pointer must be 16-byte aligned (expert_offsets:
+ *     4-byte aligned, as an int32 array).
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *     stream).  Inputs must stay valid until the stream reaches the launch.
+ *     Outputs must not alias inputs.
+ *   - Arguments are validated before any HIP runtime call, in the order
+ *     null pointers, shapes, alignment; then the current device must be a
+ *     gfx950, else FP8BLK_ERR_DEVICE.  A failed launch returns
+ *     FP8BLK_ERR_LAUNCH.  Faults inside a kernel surface as HIP errors at
+ *     the caller's next synchronisation.
+ *   - Non-finite inputs (NaN, Inf) are outside the contract: results are
+ *     unspecified, but the kernels stay in bounds.
+ *   - Size limits: M, N <= 2^31 - 1 and K <= 2^24 per call.
+ */
+#ifndef FP8BLK_H
+#define FP8BLK_H
+
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define FP8BLK_API __attribute__((visibility("default")))
+#else
+#define FP8BLK_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FP8BLK_OK = 0,
+    FP8BLK_ERR_NULL = 1,    /* a required pointer is NULL                    */
+    FP8BLK_ERR_SHAPE = 2,   /* negative size, K % 128 != 0, size over limit  */
+    FP8BLK_ERR_ALIGN = 3,   /* a base pointer is not 16-byte aligned         */
+    FP8BLK_ERR_DEVICE = 4,  /* no device, or the current device is not gfx950 */
+    FP8BLK_ERR_LAUNCH = 5   /* the kernel launch failed                      */
+} fp8blk_status;
+
+#define FP8BLK_BLOCK 128
+#define FP8BLK_ABI_VERSION 1
+
+/* Weight quantization, one fp32 scale per 128x128 block.
+ * "Fine-grained FP8" page, introduction: weights are brought to 8 bits per
+ * 2D block, weight_block_size = (128, 128).  Done once, when weights load.
+ *   w_bf16  [N,K] bf16 in
+ *   w_q     [N,K] E4M3 codes out
+ *   w_scale [ceil(N/128), K/128] fp32 out; block (nb,kb) covers rows
+ *           [128nb, min(N,128nb+128)) and columns [128kb, 128kb+128). */
+FP8BLK_API fp8blk_status fp8_weight_block_quant(const void *w_bf16, int64_t N, int64_t K,
+                                                void *w_q, float *w_scale, void *stream);
+
+/* Dynamic activation quantization, one fp32 scale per token per 128 input
+ * channels.  "Fine-grained FP8" page, introduction (per token, per group,
+ * the group matching the weights' input-channel block, 128 by default) and
+ * "DeepGEMM fast path" (activation_scheme = "dynamic": scales are computed
+ * on every call).
+ *   x_bf16  [M,K] bf16 in
+ *   x_q     [M,K] E4M3 codes out
+ *   x_scale [M, K/128] fp32 out; group (m,g) covers columns [128g, 128g+128). */
+FP8BLK_API fp8blk_status fp8_act_quant_group(const void *x_bf16, int64_t M, int64_t K,
+                                             void *x_q, float *x_scale, void *stream);
+
+/* Block-scaled FP8 GEMM, y = x * W^T in bf16.  "Fine-grained FP8" page,
+ * "DeepGEMM fast path": the FP8 linear layer with (128,128) weight blocks
+ * and dynamic activation groups; value as dequantize-then-matmul ("BFL"
+ * page, "Kernels").  The scale pair x_scale[m,kb] * w_scale[n/128,kb] is
+ * applied to each 128-long partial sum inside the K loop.
+ *   x_q [M,K], x_scale [M,K/128], w_q [N,K], w_scale [ceil(N/128),K/128] in
+ *   y_bf16 [M,N] out (bf16, round to nearest even). */
+FP8BLK_API fp8blk_status fp8_block_gemm(const void *x_q, const float *x_scale,
+                                        const void *w_q, const float *w_scale,
+                                        int64_t M, int64_t N, int64_t K,
+                                        void *y_bf16, void *stream);
+
+/* Grouped block-scaled FP8 GEMM for mixture-of-experts layers: expert e
+ * multiplies rows [off[e], off[e+1]) of x by its own W[e].  "Fine-grained
+ * FP8" page, "UE8M0 scale format": expert matmuls run through grouped
+ * back-ends that take fp32 scales directly; "DeepGEMM fast path" names the
+ * expert back-ends.
+ *   x_q [total_M,K], x_scale [total_M,K/128]
+ *   w_q [E,N,K], w_scale [E, ceil(N/128), K/128]
+ *   expert_offsets: DEVICE int32 [E+1], non-decreasing, off[0] = 0,
+ *       off[E] <= total_M.  Trusted (read on the device, no host sync);
+ *       row ranges are clamped to [0, total_M).
+ *   y_bf16 [total_M,N] out; rows that belong to no expert are not written. */
+FP8BLK_API fp8blk_status fp8_grouped_block_gemm(const void *x_q, const float *x_scale,
+                                                const void *w_q, const float *w_scale,
+                                                const int32_t *expert_offsets, int32_t E,
+                                                int64_t total_M, int64_t N, int64_t K,
+                                                void *y_bf16, void *stream);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+FP8BLK_API const char *fp8blk_status_string(int status);
+
+/* FP8BLK_ABI_VERSION of the built library. */
+FP8BLK_API int fp8blk_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8BLK_H */

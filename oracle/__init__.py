@@ -34,11 +34,13 @@ Modules: :mod:`oracle.e4m3` (codec), :mod:`oracle.quant` (quantizers),
 from .e4m3 import E4M3_MAX, decode, encode, fl32_div
 from .quant import act_quant_group, weight_block_quant, quant_element_map
 from .gemm import (bf16_rne_bits, block_gemm, dequant_act, dequant_weight,
-                   grouped_block_gemm, linear, tolerance_report)
+                   grouped_block_gemm, grouped_term_magnitude, linear, term_magnitude,
+                   tolerance_report)
 
 __all__ = [
     "E4M3_MAX", "decode", "encode", "fl32_div",
     "act_quant_group", "weight_block_quant", "quant_element_map",
     "bf16_rne_bits", "block_gemm", "dequant_act", "dequant_weight",
-    "grouped_block_gemm", "linear", "tolerance_report",
+    "grouped_block_gemm", "grouped_term_magnitude", "linear", "term_magnitude",
+    "tolerance_report",
 ]

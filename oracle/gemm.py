@@ -29,7 +29,11 @@ from .quant import GROUP, act_quant_group
 
 REL_FROB_TOL = 2e-3
 ELEM_REL_TOL = 1e-2
-ELEM_FLOOR = 1e-3  # of the row's RMS: guards near-zero outputs from cancellation
+# Per-element relative error is measured against max(|y_hat|, ELEM_FLOOR * S)
+# with S[m,n] = sum_k |A[m,k]| |B[n,k]|, the magnitude of the terms summed
+# into y_hat[m,n].  ELEM_FLOOR = 2^-9 is bf16's unit roundoff: an output that
+# cancels below 2^-9 of its own terms has lost more bits than bf16 carries.
+ELEM_FLOOR = 2.0 ** -9
 
 
 def dequant_act(x_q, x_s) -> np.ndarray:
@@ -49,6 +53,22 @@ def dequant_weight(w_q, w_s) -> np.ndarray:
 def block_gemm(x_q, x_s, w_q, w_s) -> np.ndarray:
     """Unrounded fp64 y_hat[M,N] = dequant(x) @ dequant(W)^T."""
     return dequant_act(x_q, x_s) @ dequant_weight(w_q, w_s).T
+
+
+def term_magnitude(x_q, x_s, w_q, w_s) -> np.ndarray:
+    """S[m,n] = sum_k |A[m,k]| * |B[n,k]| (fp64), the scale of the rounding
+    error of any evaluation order of the dot product y_hat[m,n]."""
+    return np.abs(dequant_act(x_q, x_s)) @ np.abs(dequant_weight(w_q, w_s)).T
+
+
+def grouped_term_magnitude(x_q, x_s, w_q, w_s, offsets) -> np.ndarray:
+    E, N, K = w_q.shape
+    S = np.full((x_q.shape[0], N), np.nan)
+    for e in range(E):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 > r0:
+            S[r0:r1] = term_magnitude(x_q[r0:r1], x_s[r0:r1], w_q[e], w_s[e])
+    return S
 
 
 def grouped_block_gemm(x_q, x_s, w_q, w_s, offsets) -> np.ndarray:
@@ -87,31 +107,31 @@ def bf16_bits_to_f64(b) -> np.ndarray:
     return (np.asarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
-def tolerance_report(y_bf16_bits, y_hat, rel_frob_tol=REL_FROB_TOL,
+def tolerance_report(y_bf16_bits, y_hat, magnitude, rel_frob_tol=REL_FROB_TOL,
                      elem_rel_tol=ELEM_REL_TOL) -> dict:
     """Compare a bf16 result with the unrounded fp64 oracle.
 
-    rel_frob = ||y - y_hat||_F / ||y_hat||_F   (must be <= 2e-3)
-    element:   |y - y_hat| <= 1e-2 * max(|y_hat|, 1e-3 * rms(y_hat row))
-    Also reports how many elements equal bf16_RNE(y_hat) bit for bit.
+    rel_frob = ||y - y_hat||_F / ||y_hat||_F                 (must be <= 2e-3)
+    element:   |y - y_hat| <= 1e-2 * max(|y_hat|, 2^-9 * S)  (S = term_magnitude)
+    Also reports how many elements equal bf16_RNE(y_hat) bit for bit, and
+    the largest |y - y_hat| / S.
     """
     y = bf16_bits_to_f64(y_bf16_bits)
     yh = np.asarray(y_hat, np.float64)
+    S = np.asarray(magnitude, np.float64)
     diff = y - yh
     nrm = np.linalg.norm(yh)
     rel_frob = float(np.linalg.norm(diff) / nrm) if nrm > 0 else float(np.linalg.norm(diff))
-    if yh.ndim == 2 and yh.shape[1] > 0:
-        rms = np.sqrt(np.mean(yh * yh, axis=1, keepdims=True))
-    else:
-        rms = np.sqrt(np.mean(yh * yh)) if yh.size else 0.0
-    denom = np.maximum(np.abs(yh), ELEM_FLOOR * rms)
+    denom = np.maximum(np.abs(yh), ELEM_FLOOR * S)
     with np.errstate(divide="ignore", invalid="ignore"):
         rel = np.where(denom > 0, np.abs(diff) / denom, np.where(diff == 0, 0.0, np.inf))
+        err_s = np.where(S > 0, np.abs(diff) / S, np.where(diff == 0, 0.0, np.inf))
     max_rel = float(rel.max()) if rel.size else 0.0
     exact = float(np.mean(np.asarray(y_bf16_bits) == bf16_rne_bits(yh))) if yh.size else 1.0
     return {
         "rel_frob": rel_frob,
         "max_elem_rel": max_rel,
+        "max_err_over_S": float(err_s.max()) if err_s.size else 0.0,
         "bitwise_equal_frac": exact,
         "ok": bool(rel_frob <= rel_frob_tol and max_rel <= elem_rel_tol),
     }

@@ -180,3 +180,52 @@ def random_offsets(seed: int, experts: int, sizes=None, max_rows: int = 64):
     off = np.zeros(len(sizes) + 1, dtype=np.int32)
     off[1:] = np.cumsum(sizes)
     return off
+
+
+# ----------------------------------------------------------------------------
+# The exhaustive (x, amax) domain of the element map on bf16 inputs.
+#
+# For every positive finite bf16 amax a (bit patterns 0x0001..0x7F7F) the
+# values are all bf16 x with |x| <= a: bit patterns 0..a and 0x8000..0x8000+a,
+# 2(a+1) values, 1,065,402,238 pairs in all.  Each set (an activation group
+# of 128, or a weight block of 128x128) holds a itself first, then up to
+# 127 (or 16383) of the values, padded with +0, so its amax is exactly a.
+# The amax range is cut into chunks of roughly equal element counts.
+
+EXH_AMAX_LO, EXH_AMAX_HI = 0x0001, 0x7F7F
+
+
+def exhaustive_chunk_bounds(nchunks: int):
+    a = np.arange(EXH_AMAX_LO, EXH_AMAX_HI + 1, dtype=np.int64)
+    cum = np.cumsum(2 * (a + 1))
+    targets = cum[-1] * np.arange(1, nchunks) / nchunks
+    cuts = np.searchsorted(cum, targets) + EXH_AMAX_LO
+    bounds = [EXH_AMAX_LO, *[int(c) for c in cuts], EXH_AMAX_HI + 1]
+    return [(bounds[i], bounds[i + 1]) for i in range(nchunks)]
+
+
+def _exhaustive_sets(a_lo: int, a_hi: int, set_size: int) -> np.ndarray:
+    per = set_size - 1
+    out = []
+    for a in range(a_lo, a_hi):
+        vals = np.concatenate([np.arange(0, a + 1, dtype=np.uint16),
+                               np.arange(0x8000, 0x8000 + a + 1, dtype=np.uint16)])
+        n = -(-vals.size // per)
+        s = np.zeros((n, set_size), dtype=np.uint16)
+        s[:, 0] = a
+        flat = s[:, 1:].reshape(-1)
+        flat[: vals.size] = vals
+        s[:, 1:] = flat.reshape(n, per)
+        out.append(s)
+    return np.concatenate(out) if out else np.zeros((0, set_size), np.uint16)
+
+
+def exhaustive_act_chunk(a_lo: int, a_hi: int) -> np.ndarray:
+    """[G, 128] bf16 bits: one activation group per row (K = 128)."""
+    return _exhaustive_sets(a_lo, a_hi, 128)
+
+
+def exhaustive_weight_chunk(a_lo: int, a_hi: int) -> np.ndarray:
+    """[128*B, 128] bf16 bits: B weight blocks of 128x128 stacked by rows."""
+    s = _exhaustive_sets(a_lo, a_hi, 128 * 128)
+    return s.reshape(-1, 128)

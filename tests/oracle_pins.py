@@ -468,14 +468,26 @@ def pin_tolerance_report(seed=47):
     xq, xs = oq.act_quant_group(x)
     wq, ws = oq.weight_block_quant(w)
     y = og.block_gemm(xq, xs, wq, ws)
-    rep = og.tolerance_report(og.bf16_rne_bits(y), y)
+    S = og.term_magnitude(xq, xs, wq, ws)
+    # S bounds |y| and equals it when every term has the same sign
+    assert np.all(S >= np.abs(y) * (1 - 1e-12))
+    one = np.full((1, 128), 0x38, np.uint8)
+    assert og.term_magnitude(one, np.ones((1, 1), np.float32), one, np.ones((1, 1), np.float32))[0, 0] == 128
+    rep = og.tolerance_report(og.bf16_rne_bits(y), y, S)
     assert rep["ok"] and rep["bitwise_equal_frac"] == 1.0 and rep["rel_frob"] < 2e-3
     # dropping one K block must fail
     xs_drop = xs.copy(); xs_drop[:, 1] = 0
-    assert not og.tolerance_report(og.bf16_rne_bits(og.block_gemm(xq, xs_drop, wq, ws)), y)["ok"]
-    # a sign flip in one output must fail
-    yb = og.bf16_rne_bits(y); yb[3, 7] ^= 0x8000
-    assert not og.tolerance_report(yb, y)["ok"]
+    assert not og.tolerance_report(og.bf16_rne_bits(og.block_gemm(xq, xs_drop, wq, ws)), y, S)["ok"]
+    # a sign flip of the largest output must fail
+    yb = og.bf16_rne_bits(y)
+    i, j = np.unravel_index(np.argmax(np.abs(y)), y.shape)
+    yb[i, j] ^= 0x8000
+    assert not og.tolerance_report(yb, y, S)["ok"]
+    # an error of 2% on one output well above the floor must fail
+    yb = og.bf16_rne_bits(y)
+    i, j = np.unravel_index(np.argmax(np.abs(y) / S), y.shape)
+    yb[i, j] = og.bf16_rne_bits(np.array([y[i, j] * 1.03]))[0]
+    assert not og.tolerance_report(yb, y, S)["ok"]
 
 
 ALL_PINS = [

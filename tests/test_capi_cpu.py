@@ -1,0 +1,138 @@
+"""The C-ABI library without a GPU: it loads, exports every entry point the
+header declares, and rejects bad arguments with the documented status codes
+before touching the HIP runtime.  No compute call is made."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8blk.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from block_scaled_fp8_act_amd import build
+    import block_scaled_fp8_act_amd as fb
+    if not os.path.exists(fb.lib_path()):
+        build.build()
+    return fb.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*FP8BLK_API\s+(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_entry_points():
+    names = declared_functions()
+    for n in ("fp8_weight_block_quant", "fp8_act_quant_group", "fp8_block_gemm",
+              "fp8_grouped_block_gemm", "fp8blk_status_string", "fp8blk_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_internal_symbols_hidden(lib):
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", lib._name], capture_output=True, text=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert exported == set(declared_functions()), exported
+
+
+def test_status_strings(lib):
+    import block_scaled_fp8_act_amd as fb
+    for code in range(6):
+        assert fb.status_string(code).startswith("FP8BLK_")
+    assert fb.status_string(99) == "FP8BLK_ERR_UNKNOWN"
+    assert lib.fp8blk_abi_version() == 1
+
+
+A = 0x10000          # fake, 16-byte aligned addresses: never dereferenced
+B = 0x20000
+C = 0x30000
+D = 0x40000
+E_ = 0x50000
+MIS = 0x10008        # 8-byte aligned only
+NULL = None
+
+
+def call(lib, name, *args):
+    return getattr(lib, name)(*args)
+
+
+@pytest.mark.parametrize("args,want", [
+    ((NULL, 4, 128, B, C, NULL), 1),            # null input
+    ((A, 4, 128, NULL, C, NULL), 1),            # null codes
+    ((A, 4, 128, B, NULL, NULL), 1),            # null scales
+    ((A, -1, 128, B, C, NULL), 2),              # negative rows
+    ((A, 4, 0, B, C, NULL), 2),                 # K = 0
+    ((A, 4, 100, B, C, NULL), 2),               # K % 128 != 0
+    ((A, 4, 1 << 25, B, C, NULL), 2),           # K over the limit
+    ((A, 1 << 31, 128, B, C, NULL), 2),         # rows over the limit
+    ((MIS, 4, 128, B, C, NULL), 3),             # misaligned input
+    ((A, 4, 128, MIS, C, NULL), 3),             # misaligned output
+])
+@pytest.mark.parametrize("name", ["fp8_act_quant_group", "fp8_weight_block_quant"])
+def test_quant_validation(lib, name, args, want):
+    assert call(lib, name, *args) == want
+
+
+@pytest.mark.parametrize("args,want", [
+    ((NULL, B, C, D, 4, 256, 128, E_, NULL), 1),
+    ((A, NULL, C, D, 4, 256, 128, E_, NULL), 1),
+    ((A, B, C, D, 4, 256, 128, NULL, NULL), 1),
+    ((A, B, C, D, -4, 256, 128, E_, NULL), 2),
+    ((A, B, C, D, 4, -1, 128, E_, NULL), 2),
+    ((A, B, C, D, 4, 256, 192, E_, NULL), 2),
+    ((A, B, C, D, 4, 256, 128, MIS, NULL), 3),
+    ((A, MIS, C, D, 4, 256, 128, E_, NULL), 3),
+])
+def test_gemm_validation(lib, args, want):
+    assert call(lib, "fp8_block_gemm", *args) == want
+
+
+@pytest.mark.parametrize("args,want", [
+    ((NULL, B, C, D, A, 4, 64, 256, 128, E_, NULL), 1),
+    ((A, B, C, D, NULL, 4, 64, 256, 128, E_, NULL), 1),
+    ((A, B, C, D, A, -1, 64, 256, 128, E_, NULL), 2),
+    ((A, B, C, D, A, 4, 64, 256, 130, E_, NULL), 2),
+    ((A, B, C, D, A, 4, -64, 256, 128, E_, NULL), 2),
+    ((A, B, C, MIS, A, 4, 64, 256, 128, E_, NULL), 3),
+])
+def test_grouped_validation(lib, args, want):
+    assert call(lib, "fp8_grouped_block_gemm", *args) == want
+
+
+def test_valid_arguments_without_gpu_report_device(lib):
+    """With valid arguments the next check is the device: in a container
+    with no GPU it must answer FP8BLK_ERR_DEVICE, never crash."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert call(lib, "fp8_act_quant_group", A, 4, 128, B, C, NULL) == 4
+    assert call(lib, "fp8_block_gemm", A, B, C, D, 4, 256, 128, E_, NULL) == 4
+
+
+def test_empty_work_is_validated_then_ok_or_device(lib):
+    """M == 0 skips the pointer checks but still checks shape and device."""
+    import torch
+    want = 0 if torch.cuda.is_available() else 4
+    assert call(lib, "fp8_act_quant_group", NULL, 0, 128, NULL, NULL, NULL) == want
+    assert call(lib, "fp8_act_quant_group", NULL, 0, 100, NULL, NULL, NULL) == 2
+    assert call(lib, "fp8_block_gemm", NULL, NULL, NULL, NULL, 0, 16, 128, NULL, NULL) == want
+
+
+def test_binding_raises_without_device():
+    import torch
+    import block_scaled_fp8_act_amd as fb
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    x = torch.zeros(4, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fb.act_quant_group(x)  # CPU tensor: refused, no fallback

@@ -1,0 +1,235 @@
+"""GPU parity of the block-scaled GEMM, the grouped GEMM and the linear
+layer against the CPU oracle (fp64 dequantize-then-matmul).
+
+Tolerance (from the library's acceptance rule): relative Frobenius error
+<= 2e-3 and per-element |y - y_hat| <= 1e-2 * max(|y_hat|, 2^-9 * S) with
+S = sum_k |A||B| the magnitude of the summed terms, against the unrounded
+fp64 y_hat.  Exact pins (integer operands with
+power-of-two scales; unit codes with distinct power-of-two scales) must be
+bit-exact against bf16_RNE of the exact value."""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_fp8_act_amd as fb
+import synth
+from oracle import e4m3 as oe
+from oracle import gemm as og
+from oracle import quant as oq
+from gpu_helpers import bf16_to_host, dev, host, say, to_dev, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_gemm(xq, xs, wq, ws):
+    y = fb.block_gemm(to_dev(xq), to_dev(xs), to_dev(wq), to_dev(ws))
+    torch.cuda.synchronize()
+    return bf16_to_host(y)
+
+
+def check_tol(y_bits, y_hat, S, what):
+    rep = og.tolerance_report(y_bits, y_hat, S)
+    say(what, {k: (round(v, 6) if isinstance(v, float) else v) for k, v in rep.items()})
+    assert rep["ok"], (what, rep)
+    return rep
+
+
+def quantized_operands(x_bits, w_bits):
+    xq, xs = oq.act_quant_group(x_bits)
+    wq, ws = oq.weight_block_quant(w_bits)
+    return xq, xs, wq, ws
+
+
+# ----------------------------------------------------------------------------
+# exact pins
+
+@pytest.mark.parametrize("M,N,K", [(16, 16, 128), (64, 192, 1024), (130, 576, 4096), (1, 300, 512)])
+def test_gemm_exact_integer_operands(M, N, K):
+    """|codes| <= 8 integers, scales in {1/2, 1, 2}: every partial sum and
+    every promotion is exact in fp32, so y must equal bf16_RNE(exact)."""
+    rng = np.random.default_rng(M + N + K)
+    xi = rng.integers(-8, 9, (M, K)); wi = rng.integers(-8, 9, (N, K))
+    xq = oe.encode(xi.astype(np.float32)); wq = oe.encode(wi.astype(np.float32))
+    KB, NB = K // 128, -(-N // 128)
+    xs = np.exp2(rng.integers(-1, 2, (M, KB))).astype(np.float32)
+    ws = np.exp2(rng.integers(0, 2, (NB, KB))).astype(np.float32)
+    y = gpu_gemm(xq, xs, wq, ws)
+    exact = og.block_gemm(xq, xs, wq, ws)          # exact in fp64 here
+    want = og.bf16_rne_bits(exact)
+    bad = np.argwhere(y != want)
+    assert bad.size == 0, f"{len(bad)} outputs differ, first {bad[:3].tolist()}"
+
+
+@pytest.mark.parametrize("M,N,K", [(8, 256, 1536), (33, 200, 1280)])
+def test_gemm_scale_indexing(M, N, K):
+    """All codes 1.0; x_s[m,kb] = 2^((kb+m) % KB), w_s[nb,kb] = 2^(KB*((kb+nb)%2)):
+    each output is 128 * a sum of distinct powers of two, exact in fp32,
+    so a wrong or transposed scale index changes its bits."""
+    KB, NB = K // 128, -(-N // 128)
+    xq = np.full((M, K), 0x38, np.uint8); wq = np.full((N, K), 0x38, np.uint8)
+    xs = np.array([[2.0 ** ((kb + m) % KB) for kb in range(KB)] for m in range(M)], np.float32)
+    ws = np.array([[2.0 ** (KB * ((kb + nb) % 2) - 20) for kb in range(KB)] for nb in range(NB)],
+                  np.float32)
+    y = gpu_gemm(xq, xs, wq, ws)
+    want = og.bf16_rne_bits(og.block_gemm(xq, xs, wq, ws))
+    assert np.array_equal(y, want)
+
+
+# ----------------------------------------------------------------------------
+# tolerance parity
+
+def test_gemm_tiny():
+    x, w = synth.tiny_inputs()
+    xq, xs, wq, ws = quantized_operands(x, w)
+    check_tol(gpu_gemm(xq, xs, wq, ws), og.block_gemm(xq, xs, wq, ws),
+              og.term_magnitude(xq, xs, wq, ws), "tiny")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 128, 128), (15, 100, 256), (17, 576, 384),
+                                   (130, 300, 1024), (257, 1000, 512), (16, 4096, 4096),
+                                   (200, 129, 7168), (129, 257, 128)])
+def test_gemm_ragged(M, N, K):
+    x = synth.dsv3_activations(M + 11 * K, M, K, N)
+    w = synth.normal_bf16(N + 13 * K, (N, K), 0.02)
+    xq, xs, wq, ws = quantized_operands(x, w)
+    check_tol(gpu_gemm(xq, xs, wq, ws), og.block_gemm(xq, xs, wq, ws),
+              og.term_magnitude(xq, xs, wq, ws), f"ragged {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("shape_index", range(4))
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_gemm_llama_decode(shape_index, M):
+    x, w = synth.llama_inputs(shape_index, M, config=2)
+    xq, xs, wq, ws = quantized_operands(x, w)
+    check_tol(gpu_gemm(xq, xs, wq, ws), og.block_gemm(xq, xs, wq, ws),
+              og.term_magnitude(xq, xs, wq, ws), f"llama decode {synth.LLAMA_SHAPES[shape_index][0]} M={M}")
+
+
+def _sampled_rows_check(x, w, rows, what):
+    """Full GEMM on the GPU, oracle on sampled rows (outputs of one row
+    depend on that row of x only)."""
+    xd = to_dev_bf16(x)
+    xq, xs = fb.act_quant_group(xd)
+    wq, ws = oq.weight_block_quant(w)
+    y = fb.block_gemm(xq, xs, to_dev(wq), to_dev(ws))
+    torch.cuda.synchronize()
+    y = bf16_to_host(y)
+    xq_h, xs_h = host(xq), host(xs)
+    want = og.block_gemm(xq_h[rows], xs_h[rows], wq, ws)
+    return check_tol(y[rows], want, og.term_magnitude(xq_h[rows], xs_h[rows], wq, ws), what)
+
+
+@pytest.mark.parametrize("shape_index", range(4))
+def test_gemm_llama_prefill_sampled(shape_index):
+    x, w = synth.llama_inputs(shape_index, 4096, config=3)
+    rows = np.concatenate([[0, 4095], np.random.default_rng(shape_index).choice(4096, 62, replace=False)])
+    _sampled_rows_check(x, w, np.sort(rows), f"llama prefill {synth.LLAMA_SHAPES[shape_index][0]}")
+
+
+@pytest.mark.parametrize("shape_index", range(6))
+@pytest.mark.parametrize("M", [512, 8192])
+def test_gemm_dsv3_sampled(shape_index, M):
+    x, w = synth.dsv3_inputs(shape_index, M)
+    rows = np.concatenate([[0, M - 1], np.random.default_rng(M + shape_index).choice(M, 30, replace=False)])
+    _sampled_rows_check(x, w, np.sort(rows), f"dsv3 {synth.DSV3_SHAPES[shape_index][0]} M={M}")
+
+
+def test_linear_matches_oracle_linear():
+    x, w = synth.llama_inputs(1, 64, config=3)
+    wq, ws = oq.weight_block_quant(w)
+    y = fb.linear(to_dev_bf16(x), to_dev(wq), to_dev(ws))
+    torch.cuda.synchronize()
+    xq, xs = oq.act_quant_group(x)
+    check_tol(bf16_to_host(y), og.linear(x, wq, ws), og.term_magnitude(xq, xs, wq, ws), "linear")
+
+
+def test_gemm_empty_and_errors():
+    d = dev()
+    xq = torch.zeros((0, 256), dtype=torch.uint8, device=d)
+    xs = torch.zeros((0, 2), dtype=torch.float32, device=d)
+    wq = torch.zeros((64, 256), dtype=torch.uint8, device=d)
+    ws = torch.zeros((1, 2), dtype=torch.float32, device=d)
+    assert fb.block_gemm(xq, xs, wq, ws).shape == (0, 64)
+    with pytest.raises(TypeError):
+        fb.block_gemm(xq.float(), xs, wq, ws)
+
+
+# ----------------------------------------------------------------------------
+# grouped GEMM
+
+def _grouped_case(sizes, N, K, seed):
+    E = len(sizes)
+    off = synth.random_offsets(0, E, sizes=sizes)
+    total = int(off[-1])
+    x = synth.dsv3_activations(seed, total, K, seed + 1)
+    w = synth.normal_bf16(seed + 2, (E, N, K), 0.01)
+    xq, xs = oq.act_quant_group(x)
+    NB = -(-N // 128)
+    wq = np.empty((E, N, K), np.uint8); ws = np.empty((E, NB, K // 128), np.float32)
+    for e in range(E):
+        wq[e], ws[e] = oq.weight_block_quant(w[e])
+    return xq, xs, wq, ws, off
+
+
+@pytest.mark.parametrize("sizes,N,K", [
+    ([0, 1, 15, 16, 17, 0, 130, 3], 256, 512),
+    ([5], 576, 384),
+    ([0, 0, 0, 40], 128, 128),
+    ([129, 255, 1, 0, 64], 300, 1024),
+])
+def test_grouped_matches_oracle_and_per_expert_gemm(sizes, N, K):
+    xq, xs, wq, ws, off = _grouped_case(sizes, N, K, sum(sizes) + N)
+    total = int(off[-1])
+    y = fb.grouped_block_gemm(to_dev(xq), to_dev(xs), to_dev(wq), to_dev(ws), to_dev(off))
+    torch.cuda.synchronize()
+    y = bf16_to_host(y)
+    check_tol(y, og.grouped_block_gemm(xq, xs, wq, ws, off),
+              og.grouped_term_magnitude(xq, xs, wq, ws, off), f"grouped {sizes}")
+    for e in range(len(sizes)):
+        r0, r1 = int(off[e]), int(off[e + 1])
+        if r1 > r0:
+            ye = gpu_gemm(xq[r0:r1], xs[r0:r1], wq[e], ws[e])
+            assert np.array_equal(y[r0:r1], ye), f"expert {e} differs from the plain GEMM"
+
+
+def test_grouped_rows_outside_experts_untouched():
+    xq, xs, wq, ws, off = _grouped_case([3, 4], 128, 256, 77)
+    total = int(off[-1]) + 5                            # 5 trailing rows of no expert
+    xq = np.concatenate([xq, np.zeros((5, 256), np.uint8)])
+    xs = np.concatenate([xs, np.ones((5, 2), np.float32)])
+    y = torch.full((total, 128), 7.0, dtype=torch.bfloat16, device=dev())
+    fb.fp8_grouped_block_gemm(to_dev(xq), to_dev(xs), to_dev(wq), to_dev(ws), to_dev(off), y)
+    torch.cuda.synchronize()
+    yh = y.float().cpu().numpy()
+    assert np.all(yh[-5:] == 7.0)
+
+
+@pytest.mark.parametrize("which", [0, 1])
+def test_grouped_moe_sampled(which):
+    """DeepSeek-V3 MoE share (32 experts, ragged Zipf loads) on the GPU; the
+    oracle checks 3 rows of every expert."""
+    x, w, off = synth.moe_inputs(which)
+    E, N, K = w.shape
+    say("moe", which, x.shape, w.shape, "sizes", np.diff(off).min(), np.diff(off).max())
+    xd = to_dev_bf16(x)
+    xq, xs = fb.act_quant_group(xd)
+    wq = torch.empty((E, N, K), dtype=torch.uint8, device=dev())
+    ws = torch.empty((E, -(-N // 128), K // 128), dtype=torch.float32, device=dev())
+    for e in range(E):
+        fb.fp8_weight_block_quant(to_dev_bf16(w[e]), wq[e], ws[e])
+    y = fb.grouped_block_gemm(xq, xs, wq, ws, to_dev(off))
+    torch.cuda.synchronize()
+    y = bf16_to_host(y)
+    xq_h, xs_h, wq_h, ws_h = host(xq), host(xs), host(wq), host(ws)
+    rng = np.random.default_rng(which)
+    rows, want, mag = [], [], []
+    for e in range(E):
+        r0, r1 = int(off[e]), int(off[e + 1])
+        pick = np.unique(np.concatenate([[r0, r1 - 1], rng.integers(r0, r1, 1)]))
+        want.append(og.block_gemm(xq_h[pick], xs_h[pick], wq_h[e], ws_h[e]))
+        mag.append(og.term_magnitude(xq_h[pick], xs_h[pick], wq_h[e], ws_h[e]))
+        rows.append(pick)
+    check_tol(y[np.concatenate(rows)], np.concatenate(want), np.concatenate(mag), f"moe {which}")
+    # the GPU weight quantizer agrees with the oracle on one expert
+    q0, s0 = oq.weight_block_quant(w[5])
+    assert np.array_equal(wq_h[5], q0) and np.array_equal(ws_h[5].view(np.uint32), s0.view(np.uint32))
