@@ -145,6 +145,138 @@ __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ A,
     }
 }
 
+// ---------------------------------------------------------------------------
+// Large-tile configuration: 256x256 output tile per workgroup of 8 waves
+// (2 along M x 4 along N, 128x64 per wave), K step 128.  At the dense fp8
+// rate a 256x256 tile needs 32 bytes per clock per CU from L2 (a 128x128
+// tile would need 64), and each wave's 128x64 sub-tile halves the LDS read
+// traffic per MFMA compared with 64x64.  Operand tiles go from global memory
+// straight into LDS (global_load_lds_dwordx4, no VGPR staging), two stages.
+// Per stage: A 256x128 B, B 256x128 B (16-byte chunks XOR-swizzled by row),
+// and the 256 activation scales of the K block.
+namespace big {
+constexpr int TM = 256, TN = 256, TK = 128;
+constexpr int kThreads = 512;
+constexpr int kStageA = TM * TK;            // bytes
+constexpr int kStageB = TN * TK;
+struct Smem {
+  uint8_t a[2][kStageA];
+  uint8_t b[2][kStageB];
+  float as[2][TM];
+};
+}  // namespace big
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ void lds_dma16(const void *g, void *lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void *)lds_base, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_dma4(const void *g, void *lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void *)lds_base, 4, 0, 0);
+}
+
+// One 256x256 output tile (see above).  Rows past rows_a / rows_b are read
+// from the last valid row (never out of bounds); their outputs are not stored.
+__device__ __forceinline__ void gemm_tile_256(const uint8_t *__restrict__ A,
+                                              const float *__restrict__ As, int rows_a,
+                                              const uint8_t *__restrict__ B,
+                                              const float *__restrict__ Bs, int rows_b,
+                                              int64_t K, uint16_t *__restrict__ Y, int64_t ldy,
+                                              big::Smem &sm) {
+  using namespace big;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+  const int KB = (int)(K / TK);
+
+  // Global source rows/chunks for this lane's four A and four B DMA loads:
+  // load i of wave w fills LDS rows [8r, 8r+8), r = 4w + i; lane l writes
+  // bytes [16l, 16l+16) of that 1 KB run = row 8r + l/8, physical chunk l%8,
+  // which holds logical chunk (l%8) ^ (row%8).
+  const int lchunk = (lane & 7) ^ ((lane >> 3) & 7);
+  const uint8_t *pa[4];
+  const uint8_t *pb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 8 * (4 * wave + i) + (lane >> 3);
+    pa[i] = A + (int64_t)min(row, rows_a - 1) * K + lchunk * 16;
+    pb[i] = B + (int64_t)min(row, rows_b - 1) * K + lchunk * 16;
+  }
+  // Activation scales of rows 64w + l (waves 0..3).
+  const float *ps = As + (int64_t)min(64 * (wave & 3) + lane, rows_a - 1) * KB;
+  // Weight-block scale row of this wave's 64 columns (clamped to the last
+  // existing block row of a short tile; such columns are not stored).
+  const float *pws = Bs + (int64_t)min((wn * 64) / 128, (rows_b - 1) / 128) * KB;
+
+  auto issue = [&](int kb, int st) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lds_dma16(pa[i] + (int64_t)kb * TK, sm.a[st] + (4 * wave + i) * 1024);
+      lds_dma16(pb[i] + (int64_t)kb * TK, sm.b[st] + (4 * wave + i) * 1024);
+    }
+    if (wave < 4) lds_dma4(ps + kb, &sm.as[st][64 * wave]);
+  };
+
+  v4f acc[8][4];
+#pragma unroll
+  for (int mi = 0; mi < 8; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+  issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  const int c0 = (lane >> 4) * 2;
+  const int r16 = lane & 15;
+  for (int kb = 0; kb < KB; ++kb) {
+    const int st = kb & 1;
+    if (kb + 1 < KB) issue(kb + 1, st ^ 1);
+    const float wsc = pws[kb];
+    const uint8_t *sa = sm.a[st];
+    const uint8_t *sb = sm.b[st];
+    v8i bfr[4];
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) {
+      const int row = wn * 64 + ni * 16 + r16;
+      bfr[ni] = frag_from(*reinterpret_cast<const uint4 *>(sb + swz(row, c0)),
+                          *reinterpret_cast<const uint4 *>(sb + swz(row, c0 + 1)));
+    }
+#pragma unroll
+    for (int mi = 0; mi < 8; ++mi) {
+      const int row = wm * 128 + mi * 16 + r16;
+      const v8i af = frag_from(*reinterpret_cast<const uint4 *>(sa + swz(row, c0)),
+                               *reinterpret_cast<const uint4 *>(sa + swz(row, c0 + 1)));
+      const float4 s4 =
+          *reinterpret_cast<const float4 *>(&sm.as[st][wm * 128 + mi * 16 + 4 * (lane >> 4)]);
+      const float sc[4] = {s4.x * wsc, s4.y * wsc, s4.z * wsc, s4.w * wsc};
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni) {
+        const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            af, bfr[ni], v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[mi][ni][r] = fmaf(p[r], sc[r], acc[mi][ni][r]);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int mi = 0; mi < 8; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) {
+      const int col = wn * 64 + ni * 16 + r16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = wm * 128 + mi * 16 + 4 * (lane >> 4) + r;
+        if (row < rows_a && col < rows_b)
+          Y[(int64_t)row * ldy + col] = (uint16_t)bf16_rne(acc[mi][ni][r]);
+      }
+    }
+}
+
 // Map a linear workgroup id to (tile_m, tile_n).  Workgroups are dispatched
 // round-robin over the 8 XCDs (each with its own L2); consecutive logical
 // tiles are made to land on one XCD, and logical tiles are ordered in
@@ -173,6 +305,20 @@ __global__ __launch_bounds__(kGemmThreads) void block_gemm_kernel(
   const int64_t KB = K / BK;
   gemm_tile(xq + m0 * K, xs + m0 * KB, (int)min<int64_t>(BM, M - m0), wq + n0 * K,
             ws + (n0 / BN) * KB, (int)min<int64_t>(BN, N - n0), K, y + m0 * N + n0, N, sm);
+}
+
+__global__ __launch_bounds__(big::kThreads) void block_gemm_256_kernel(
+    const uint8_t *__restrict__ xq, const float *__restrict__ xs, const uint8_t *__restrict__ wq,
+    const float *__restrict__ ws, int64_t M, int64_t N, int64_t K, uint16_t *__restrict__ y,
+    int tiles_m, int tiles_n) {
+  __shared__ big::Smem sm;
+  int tm, tn;
+  tile_coords(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, tm, tn);
+  const int64_t m0 = (int64_t)tm * big::TM, n0 = (int64_t)tn * big::TN;
+  const int64_t KB = K / big::TK;
+  gemm_tile_256(xq + m0 * K, xs + m0 * KB, (int)min<int64_t>(big::TM, M - m0), wq + n0 * K,
+                ws + (n0 / 128) * KB, (int)min<int64_t>(big::TN, N - n0), K, y + m0 * N + n0, N,
+                sm);
 }
 
 // Grouped variant.  The logical m-tiles of all experts are numbered
@@ -212,6 +358,15 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_kernel(
 
 hipError_t launch_block_gemm(const void *xq, const float *xs, const void *wq, const float *ws,
                              int64_t M, int64_t N, int64_t K, void *y, hipStream_t stream) {
+  const int64_t big_tiles = ((M + big::TM - 1) / big::TM) * ((N + big::TN - 1) / big::TN);
+  if (big_tiles >= 128) {
+    const int tm = (int)((M + big::TM - 1) / big::TM), tn = (int)((N + big::TN - 1) / big::TN);
+    hipLaunchKernelGGL(block_gemm_256_kernel, dim3((unsigned)(tm * tn)), dim3(big::kThreads), 0,
+                       stream, static_cast<const uint8_t *>(xq), xs,
+                       static_cast<const uint8_t *>(wq), ws, M, N, K, static_cast<uint16_t *>(y),
+                       tm, tn);
+    return hipGetLastError();
+  }
   const int tiles_m = (int)((M + BM - 1) / BM);
   const int tiles_n = (int)((N + BN - 1) / BN);
   hipLaunchKernelGGL(block_gemm_kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(kGemmThreads),

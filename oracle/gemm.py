@@ -31,9 +31,13 @@ REL_FROB_TOL = 2e-3
 ELEM_REL_TOL = 1e-2
 # Per-element relative error is measured against max(|y_hat|, ELEM_FLOOR * S)
 # with S[m,n] = sum_k |A[m,k]| |B[n,k]|, the magnitude of the terms summed
-# into y_hat[m,n].  ELEM_FLOOR = 2^-9 is bf16's unit roundoff: an output that
-# cancels below 2^-9 of its own terms has lost more bits than bf16 carries.
-ELEM_FLOOR = 2.0 ** -9
+# into y_hat[m,n].  fp8 matrix instructions accumulate a 128-term product to
+# about 2^-13 * S (not to fp32's 2^-24; this is what the per-128-block fp32
+# promotion of the method bounds), so an output that cancels below
+# 2^-13 / 1e-2 ~= 2^-6.4 of its own terms can exceed a 1e-2 relative error
+# from that accumulation alone; below 2^-6 * S the check becomes the absolute
+# bound 1e-2 * 2^-6 * S.
+ELEM_FLOOR = 2.0 ** -6
 
 
 def dequant_act(x_q, x_s) -> np.ndarray:
@@ -112,7 +116,7 @@ def tolerance_report(y_bf16_bits, y_hat, magnitude, rel_frob_tol=REL_FROB_TOL,
     """Compare a bf16 result with the unrounded fp64 oracle.
 
     rel_frob = ||y - y_hat||_F / ||y_hat||_F                 (must be <= 2e-3)
-    element:   |y - y_hat| <= 1e-2 * max(|y_hat|, 2^-9 * S)  (S = term_magnitude)
+    element:   |y - y_hat| <= 1e-2 * max(|y_hat|, 2^-6 * S)  (S = term_magnitude)
     Also reports how many elements equal bf16_RNE(y_hat) bit for bit, and
     the largest |y - y_hat| / S.
     """
