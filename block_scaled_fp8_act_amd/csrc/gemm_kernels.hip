@@ -12,27 +12,14 @@
 // block, fp32 result) and the scale pair is applied with one fp32 FMA per
 // output per K block ("promotion" into the fp32 accumulator).
 //
-// Workgroup tile 128x128 (4 waves of 64x64), K step 128, double-buffered
-// LDS staging of the fp8 A and B tiles with a 16-byte-chunk XOR swizzle
-// (chunk c of row r is stored at c ^ (r & 7)) so that the 16 lanes reading
-// the same chunk of 16 consecutive rows spread over the LDS banks.
+// Three configurations: 256x256 and 128x128 LDS-staged tiles for M > 64,
+// and a weight-streaming split-K kernel for M <= 64 (decode).
+#include <algorithm>
+
 #include "fp8blk_device.h"
 #include "fp8blk_launch.h"
 
 namespace fp8blk {
-
-constexpr int BM = 128, BN = 128, BK = 128;
-constexpr int kGemmThreads = 256;
-
-struct GemmSmem {
-  uint8_t a[2][BM * BK];
-  uint8_t b[2][BN * BK];
-  float as[2][BM];
-};
-
-__device__ __forceinline__ int swz(int row, int chunk) {
-  return row * BK + ((chunk ^ (row & 7)) << 4);
-}
 
 __device__ __forceinline__ v8i frag_from(uint4 lo, uint4 hi) {
   v8i r;
@@ -41,130 +28,36 @@ __device__ __forceinline__ v8i frag_from(uint4 lo, uint4 hi) {
   return r;
 }
 
-// One BM x BN output tile.
-//   A  : x_q at row m0 (row stride K bytes); rows_a valid rows (<= BM)
-//   As : x_scale at row m0 (row stride KB floats)
-//   B  : w_q at row n0 (row stride K bytes); rows_b valid rows (<= BN)
-//   Bs : w_scale row n0/128 (KB floats)
-//   Y  : y at (m0, n0), row stride ldy elements
-__device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ A,
-                                          const float *__restrict__ As, int rows_a,
-                                          const uint8_t *__restrict__ B,
-                                          const float *__restrict__ Bs, int rows_b, int64_t K,
-                                          uint16_t *__restrict__ Y, int64_t ldy, GemmSmem &sm) {
-  const int t = threadIdx.x;
-  const int lane = t & 63;
-  const int wave = t >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int KB = (int)(K / BK);
-
-  uint4 ga[4], gb[4];
-  float gs = 0.0f;
-  auto gload = [&](int kb) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int j = t + kGemmThreads * i;
-      const int row = j >> 3, ch = j & 7;
-      const int64_t off = (int64_t)row * K + (int64_t)kb * BK + ch * 16;
-      ga[i] = row < rows_a ? *reinterpret_cast<const uint4 *>(A + off) : make_uint4(0, 0, 0, 0);
-      gb[i] = row < rows_b ? *reinterpret_cast<const uint4 *>(B + off) : make_uint4(0, 0, 0, 0);
-    }
-    gs = (t < rows_a) ? As[(int64_t)t * KB + kb] : 0.0f;
-  };
-  auto swrite = [&](int st) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int j = t + kGemmThreads * i;
-      const int row = j >> 3, ch = j & 7;
-      *reinterpret_cast<uint4 *>(sm.a[st] + swz(row, ch)) = ga[i];
-      *reinterpret_cast<uint4 *>(sm.b[st] + swz(row, ch)) = gb[i];
-    }
-    if (t < BM) sm.as[st][t] = gs;
-  };
-
-  v4f acc[4][4];
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-
-  gload(0);
-  swrite(0);
-  __syncthreads();
-
-  const int c0 = (lane >> 4) * 2;
-  for (int kb = 0; kb < KB; ++kb) {
-    const int st = kb & 1;
-    if (kb + 1 < KB) gload(kb + 1);
-    const float wsc = Bs[kb];
-    v8i af[4], bfr[4];
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-      const int row = wm * 64 + mi * 16 + (lane & 15);
-      af[mi] = frag_from(*reinterpret_cast<const uint4 *>(sm.a[st] + swz(row, c0)),
-                         *reinterpret_cast<const uint4 *>(sm.a[st] + swz(row, c0 + 1)));
-    }
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni) {
-      const int row = wn * 64 + ni * 16 + (lane & 15);
-      bfr[ni] = frag_from(*reinterpret_cast<const uint4 *>(sm.b[st] + swz(row, c0)),
-                          *reinterpret_cast<const uint4 *>(sm.b[st] + swz(row, c0 + 1)));
-    }
-    v4f sc[4];
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-      const float4 s4 =
-          *reinterpret_cast<const float4 *>(&sm.as[st][wm * 64 + mi * 16 + 4 * (lane >> 4)]);
-      sc[mi] = v4f{s4.x * wsc, s4.y * wsc, s4.z * wsc, s4.w * wsc};
-    }
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < 4; ++ni) {
-        const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            af[mi], bfr[ni], v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 0, 0, 0);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[mi][ni][r] = fmaf(p[r], sc[mi][r], acc[mi][ni][r]);
-      }
-    if (kb + 1 < KB) swrite(st ^ 1);
-    __syncthreads();
-  }
-
-  // Epilogue: lane holds rows 4*(lane/16)+r of each 16x16 tile, column lane%16.
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni) {
-      const int col = wn * 64 + ni * 16 + (lane & 15);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = wm * 64 + mi * 16 + 4 * (lane >> 4) + r;
-        if (row < rows_a && col < rows_b)
-          Y[(int64_t)row * ldy + col] = (uint16_t)bf16_rne(acc[mi][ni][r]);
-      }
-    }
-}
-
 // ---------------------------------------------------------------------------
-// Large-tile configuration: 256x256 output tile per workgroup of 8 waves
-// (2 along M x 4 along N, 128x64 per wave), K step 128.  At the dense fp8
-// rate a 256x256 tile needs 32 bytes per clock per CU from L2 (a 128x128
-// tile would need 64), and each wave's 128x64 sub-tile halves the LDS read
-// traffic per MFMA compared with 64x64.  Operand tiles go from global memory
-// straight into LDS (global_load_lds_dwordx4, no VGPR staging), two stages.
-// Per stage: A 256x128 B, B 256x128 B (16-byte chunks XOR-swizzled by row),
-// and the 256 activation scales of the K block.
-namespace big {
-constexpr int TM = 256, TN = 256, TK = 128;
-constexpr int kThreads = 512;
-constexpr int kStageA = TM * TK;            // bytes
-constexpr int kStageB = TN * TK;
-struct Smem {
-  uint8_t a[2][kStageA];
-  uint8_t b[2][kStageB];
-  float as[2][TM];
+// Tiled configurations.  A workgroup of WM x WN waves computes a
+// (WM*FM*16) x (WN*64) output tile; each wave owns FM 16-row fragments by
+// four 16-column fragments (FM*16 x 64 outputs, FM*16 fp32 accumulators per
+// lane), K step 128 = one scale block.
+//   Tile<2,4,8>: 256x256, 8 waves.  At the dense fp8 rate a 256x256 tile
+//     needs 32 bytes per clock per CU from L2 (a 128x128 tile needs 64), and
+//     a 128x64 wave sub-tile halves LDS reads per MFMA against 64x64.
+//   Tile<2,2,4>: 128x128, 4 waves, for grids too small to fill 256 CUs with
+//     256x256 tiles.
+// Operand tiles go from global memory straight into LDS
+// (global_load_lds_dwordx4, no VGPR staging), two stages.  Per stage: A
+// TMx128 B, B TNx128 B (16-byte chunks XOR-swizzled by row) and the TM
+// activation scales of the K block.
+template <int WM, int WN, int FM>
+struct Tile {
+  static constexpr int kWaves = WM * WN;
+  static constexpr int kThreads = kWaves * 64;
+  static constexpr int TM = WM * FM * 16;
+  static constexpr int TN = WN * 64;
+  static constexpr int kDmaA = TM / 8 / kWaves;  // 1 KB DMA loads per wave per stage
+  static constexpr int kDmaB = TN / 8 / kWaves;
+  static_assert(kDmaA * 8 * kWaves == TM && kDmaB * 8 * kWaves == TN, "tile/DMA mismatch");
+  static_assert(TM / 64 <= kWaves, "scale DMA needs TM/64 waves");
+  struct Smem {
+    uint8_t a[2][TM * 128];
+    uint8_t b[2][TN * 128];
+    float as[2][TM];
+  };
 };
-}  // namespace big
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -175,52 +68,77 @@ __device__ __forceinline__ void lds_dma4(const void *g, void *lds_base) {
   __builtin_amdgcn_global_load_lds(g, (lds_void *)lds_base, 4, 0, 0);
 }
 
-// One 256x256 output tile (see above).  Rows past rows_a / rows_b are read
-// from the last valid row (never out of bounds); their outputs are not stored.
-__device__ __forceinline__ void gemm_tile_256(const uint8_t *__restrict__ A,
-                                              const float *__restrict__ As, int rows_a,
-                                              const uint8_t *__restrict__ B,
-                                              const float *__restrict__ Bs, int rows_b,
-                                              int64_t K, uint16_t *__restrict__ Y, int64_t ldy,
-                                              big::Smem &sm) {
-  using namespace big;
+// Chunk swizzle: chunk c of row r is stored at c ^ ((r >> 1) & 7).  The 16
+// lanes of a ds_read_b128 quarter-wave read one logical chunk of 16
+// consecutive rows; rows r and r+1 sit in different 128-byte halves of the
+// 64 four-byte banks and (r >> 1) & 7 spreads each pair over the eight
+// chunk positions, so the 16 lanes hit 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
+}
+
+// One output tile.  A: x_q at the tile's first row (row stride K bytes),
+// rows_a valid rows; As: x_scale at that row (row stride KB floats); B: w_q
+// at the tile's first column's row, rows_b valid rows; Bs: w_scale row of
+// that first column's 128-block; Y: y at the tile origin (row stride ldy).
+// Rows past rows_a / rows_b are read from the last valid row (never out of
+// bounds); their outputs are not stored.
+//
+// The loop over a wave's FM A fragments is software-pipelined: each MFMA of
+// fragment mi is followed by the four promotion FMAs of the same column
+// fragment of mi-1 (whose MFMAs finished long ago), and the LDS reads for
+// fragment mi+1 go out right after the first MFMA; scheduling barriers pin
+// this order so the FMAs fill the MFMA shadow without waiting on a result.
+template <int WM, int WN, int FM>
+__device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ A,
+                                          const float *__restrict__ As, int rows_a,
+                                          const uint8_t *__restrict__ B,
+                                          const float *__restrict__ Bs, int rows_b, int64_t K,
+                                          uint16_t *__restrict__ Y, int64_t ldy,
+                                          typename Tile<WM, WN, FM>::Smem &sm) {
+  using T = Tile<WM, WN, FM>;
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int wm = wave >> 2, wn = wave & 3;
-  const int KB = (int)(K / TK);
+  const int wm = wave / WN, wn = wave % WN;
+  const int KB = (int)(K / 128);
 
-  // Global source rows/chunks for this lane's four A and four B DMA loads:
-  // load i of wave w fills LDS rows [8r, 8r+8), r = 4w + i; lane l writes
-  // bytes [16l, 16l+16) of that 1 KB run = row 8r + l/8, physical chunk l%8,
-  // which holds logical chunk (l%8) ^ (row%8).
-  const int lchunk = (lane & 7) ^ ((lane >> 3) & 7);
-  const uint8_t *pa[4];
-  const uint8_t *pb[4];
+  // DMA load i of a wave fills LDS rows [8r, 8r+8), r = kDma*w + i; lane l
+  // writes bytes [16l, 16l+16) of that 1 KB run = row 8r + l/8, physical
+  // chunk l%8, which holds logical chunk (l%8) ^ ((row >> 1) & 7).
+  const uint8_t *pa[T::kDmaA];
+  const uint8_t *pb[T::kDmaB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 8 * (4 * wave + i) + (lane >> 3);
+  for (int i = 0; i < T::kDmaA; ++i) {
+    const int row = 8 * (T::kDmaA * wave + i) + (lane >> 3);
+    const int lchunk = (lane & 7) ^ ((row >> 1) & 7);
     pa[i] = A + (int64_t)min(row, rows_a - 1) * K + lchunk * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < T::kDmaB; ++i) {
+    const int row = 8 * (T::kDmaB * wave + i) + (lane >> 3);
+    const int lchunk = (lane & 7) ^ ((row >> 1) & 7);
     pb[i] = B + (int64_t)min(row, rows_b - 1) * K + lchunk * 16;
   }
-  // Activation scales of rows 64w + l (waves 0..3).
-  const float *ps = As + (int64_t)min(64 * (wave & 3) + lane, rows_a - 1) * KB;
+  // Activation scales of rows 64w + l (waves w < TM/64).
+  const float *ps = As + (int64_t)min(64 * wave + lane, rows_a - 1) * KB;
   // Weight-block scale row of this wave's 64 columns (clamped to the last
   // existing block row of a short tile; such columns are not stored).
   const float *pws = Bs + (int64_t)min((wn * 64) / 128, (rows_b - 1) / 128) * KB;
 
   auto issue = [&](int kb, int st) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      lds_dma16(pa[i] + (int64_t)kb * TK, sm.a[st] + (4 * wave + i) * 1024);
-      lds_dma16(pb[i] + (int64_t)kb * TK, sm.b[st] + (4 * wave + i) * 1024);
-    }
-    if (wave < 4) lds_dma4(ps + kb, &sm.as[st][64 * wave]);
+    for (int i = 0; i < T::kDmaA; ++i)
+      lds_dma16(pa[i] + (int64_t)kb * 128, sm.a[st] + (T::kDmaA * wave + i) * 1024);
+#pragma unroll
+    for (int i = 0; i < T::kDmaB; ++i)
+      lds_dma16(pb[i] + (int64_t)kb * 128, sm.b[st] + (T::kDmaB * wave + i) * 1024);
+    if (wave < T::TM / 64) lds_dma4(ps + kb, &sm.as[st][64 * wave]);
   };
 
-  v4f acc[8][4];
+  v4f acc[FM][4];
 #pragma unroll
-  for (int mi = 0; mi < 8; ++mi)
+  for (int mi = 0; mi < FM; ++mi)
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
@@ -230,51 +148,200 @@ __device__ __forceinline__ void gemm_tile_256(const uint8_t *__restrict__ A,
 
   const int c0 = (lane >> 4) * 2;
   const int r16 = lane & 15;
+  const int arow0 = wm * FM * 16 + r16;
+  const int brow0 = wn * 64 + r16;
+  const int srow0 = wm * FM * 16 + 4 * (lane >> 4);
   for (int kb = 0; kb < KB; ++kb) {
     const int st = kb & 1;
     if (kb + 1 < KB) issue(kb + 1, st ^ 1);
     const float wsc = pws[kb];
     const uint8_t *sa = sm.a[st];
     const uint8_t *sb = sm.b[st];
+    const float4 *sas = reinterpret_cast<const float4 *>(&sm.as[st][srow0]);
     v8i bfr[4];
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) {
-      const int row = wn * 64 + ni * 16 + r16;
+      const int row = brow0 + ni * 16;
       bfr[ni] = frag_from(*reinterpret_cast<const uint4 *>(sb + swz(row, c0)),
                           *reinterpret_cast<const uint4 *>(sb + swz(row, c0 + 1)));
     }
+    v8i af = frag_from(*reinterpret_cast<const uint4 *>(sa + swz(arow0, c0)),
+                       *reinterpret_cast<const uint4 *>(sa + swz(arow0, c0 + 1)));
+    float4 s4 = sas[0];
+    v8i afn = af;
+    float4 s4n = s4;
+    v4f pp[4];
+    float scp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int mi = 0; mi < 8; ++mi) {
-      const int row = wm * 128 + mi * 16 + r16;
-      const v8i af = frag_from(*reinterpret_cast<const uint4 *>(sa + swz(row, c0)),
-                               *reinterpret_cast<const uint4 *>(sa + swz(row, c0 + 1)));
-      const float4 s4 =
-          *reinterpret_cast<const float4 *>(&sm.as[st][wm * 128 + mi * 16 + 4 * (lane >> 4)]);
-      const float sc[4] = {s4.x * wsc, s4.y * wsc, s4.z * wsc, s4.w * wsc};
+    for (int mi = 0; mi < FM; ++mi) {
+      v4f pc[4];
 #pragma unroll
       for (int ni = 0; ni < 4; ++ni) {
-        const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+        pc[ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
             af, bfr[ni], v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 0, 0, 0);
+        if (ni == 0 && mi + 1 < FM) {
+          const int row = arow0 + (mi + 1) * 16;
+          afn = frag_from(*reinterpret_cast<const uint4 *>(sa + swz(row, c0)),
+                          *reinterpret_cast<const uint4 *>(sa + swz(row, c0 + 1)));
+          s4n = sas[(mi + 1) * 4];
+        }
+        if (mi > 0) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[mi][ni][r] = fmaf(p[r], sc[r], acc[mi][ni][r]);
+          for (int r = 0; r < 4; ++r)
+            acc[mi - 1][ni][r] = fmaf(pp[ni][r], scp[r], acc[mi - 1][ni][r]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
+      scp[0] = s4.x * wsc; scp[1] = s4.y * wsc; scp[2] = s4.z * wsc; scp[3] = s4.w * wsc;
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni) pp[ni] = pc[ni];
+      af = afn;
+      s4 = s4n;
     }
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[FM - 1][ni][r] = fmaf(pp[ni][r], scp[r], acc[FM - 1][ni][r]);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
+  // Epilogue: lane holds rows 4*(lane/16)+r of each 16x16 fragment, column lane%16.
 #pragma unroll
-  for (int mi = 0; mi < 8; ++mi)
+  for (int mi = 0; mi < FM; ++mi)
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) {
       const int col = wn * 64 + ni * 16 + r16;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int row = wm * 128 + mi * 16 + 4 * (lane >> 4) + r;
+        const int row = wm * FM * 16 + mi * 16 + 4 * (lane >> 4) + r;
         if (row < rows_a && col < rows_b)
           Y[(int64_t)row * ldy + col] = (uint16_t)bf16_rne(acc[mi][ni][r]);
       }
     }
+}
+
+// ---------------------------------------------------------------------------
+// Small-M ("decode") configuration, M <= 64: the GEMM is a stream of W from
+// HBM (arithmetic intensity 2..32 flop/byte).  One workgroup owns a slab of
+// 16 output columns; its kDecWaves waves split the K blocks round-robin
+// (wave w takes kb = w, w + S, ...), so the slab's weight rows are read once,
+// straight from global memory into MFMA operand registers (no LDS staging),
+// U blocks per wave at a time so that many loads are in flight.  Each wave
+// keeps 16x16 partial tiles for up to four 16-row fragments of x; the
+// partials are summed through LDS at the end.  Activation codes come from L2
+// (x is small and read by every workgroup); activation scales are staged
+// once in LDS, transposed to [kb][row], while the first weight loads fly.
+constexpr int kDecWaves = 16;
+constexpr int kDecThreads = kDecWaves * 64;
+constexpr int kDecMaxM = 64;
+constexpr int kDecMaxScaleBytes = 32 * 1024;  // x_scale staging limit (KB * MF * 16 * 4)
+
+template <int MF>
+__global__ __launch_bounds__(kDecThreads) void decode_gemm_kernel(
+    const uint8_t *__restrict__ xq, const float *__restrict__ xs, const uint8_t *__restrict__ wq,
+    const float *__restrict__ ws, int M, int64_t N, int64_t K, uint16_t *__restrict__ y) {
+  constexpr int R = MF * 16;                  // staged rows
+  constexpr int U = 4 / MF;                   // K blocks in flight per wave
+  extern __shared__ __align__(16) float dsm[];
+  float *s_as = dsm;                          // [KB][R]
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int KB = (int)(K / 128);
+  v4f *s_part = reinterpret_cast<v4f *>(dsm);   // [waves][MF][64], reuses s_as after the loop
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int rows_b = (int)min<int64_t>(16, N - n0);
+
+  const int r16 = lane & 15;
+  const int kc = (lane >> 4) * 32;  // this lane's 32 K bytes within the block
+  const uint8_t *pb = wq + (n0 + min(r16, rows_b - 1)) * K + kc;
+  const uint8_t *pa[MF];
+#pragma unroll
+  for (int f = 0; f < MF; ++f) pa[f] = xq + (int64_t)min(f * 16 + r16, M - 1) * K + kc;
+  const float *pws = ws + (n0 / 128) * KB;
+  const int nmine = wave < KB ? (KB - wave + kDecWaves - 1) / kDecWaves : 0;
+
+  uint4 bw[U][2];
+  v8i af[U][MF];
+  auto load = [&](int j0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (j0 + u < nmine) {
+        const int64_t ko = (int64_t)(wave + kDecWaves * (j0 + u)) * 128;
+        bw[u][0] = *reinterpret_cast<const uint4 *>(pb + ko);
+        bw[u][1] = *reinterpret_cast<const uint4 *>(pb + ko + 16);
+#pragma unroll
+        for (int f = 0; f < MF; ++f)
+          af[u][f] = frag_from(*reinterpret_cast<const uint4 *>(pa[f] + ko),
+                               *reinterpret_cast<const uint4 *>(pa[f] + ko + 16));
+      }
+    }
+  };
+  load(0);
+
+  for (int i = t; i < KB * R; i += kDecThreads) {
+    const int kb = i / R, m = i % R;
+    s_as[i] = xs[(int64_t)min(m, M - 1) * KB + kb];
+  }
+  __syncthreads();
+
+  v4f acc[MF];
+#pragma unroll
+  for (int f = 0; f < MF; ++f) acc[f] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+  for (int j0 = 0; j0 < nmine; j0 += U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (j0 + u < nmine) {
+        const int kb = wave + kDecWaves * (j0 + u);
+        const float wsc = pws[kb];
+        const v8i bf = frag_from(bw[u][0], bw[u][1]);
+#pragma unroll
+        for (int f = 0; f < MF; ++f) {
+          const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              af[u][f], bf, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 0, 0, 0);
+          const float4 s4 =
+              *reinterpret_cast<const float4 *>(&s_as[kb * R + f * 16 + 4 * (lane >> 4)]);
+          acc[f][0] = fmaf(p[0], s4.x * wsc, acc[f][0]);
+          acc[f][1] = fmaf(p[1], s4.y * wsc, acc[f][1]);
+          acc[f][2] = fmaf(p[2], s4.z * wsc, acc[f][2]);
+          acc[f][3] = fmaf(p[3], s4.w * wsc, acc[f][3]);
+        }
+      }
+    }
+    if (j0 + U < nmine) load(j0 + U);
+  }
+  __syncthreads();  // every wave is done with s_as
+#pragma unroll
+  for (int f = 0; f < MF; ++f) s_part[(wave * MF + f) * 64 + lane] = acc[f];
+  __syncthreads();
+  // wave f (< MF) sums fragment f over the waves and stores it
+  if (wave < MF) {
+    v4f sum = s_part[wave * 64 + lane];
+#pragma unroll
+    for (int w = 1; w < kDecWaves; ++w) {
+      const v4f v = s_part[(w * MF + wave) * 64 + lane];
+      sum[0] += v[0]; sum[1] += v[1]; sum[2] += v[2]; sum[3] += v[3];
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = wave * 16 + 4 * (lane >> 4) + r;
+      if (row < M && r16 < rows_b) y[(int64_t)row * N + n0 + r16] = (uint16_t)bf16_rne(sum[r]);
+    }
+  }
+}
+
+template <int MF>
+static hipError_t launch_decode(const void *xq, const float *xs, const void *wq, const float *ws,
+                                int64_t M, int64_t N, int64_t K, void *y, hipStream_t stream) {
+  const int64_t KB = K / 128;
+  const size_t lds = std::max((size_t)KB * MF * 16 * 4, (size_t)kDecWaves * MF * 64 * 16);
+  hipLaunchKernelGGL(decode_gemm_kernel<MF>, dim3((unsigned)((N + 15) / 16)), dim3(kDecThreads),
+                     lds, stream, static_cast<const uint8_t *>(xq), xs,
+                     static_cast<const uint8_t *>(wq), ws, (int)M, N, K,
+                     static_cast<uint16_t *>(y));
+  return hipGetLastError();
 }
 
 // Map a linear workgroup id to (tile_m, tile_n).  Workgroups are dispatched
@@ -294,43 +361,34 @@ __device__ __forceinline__ void tile_coords(int bid, int total, int tiles_m, int
   tn = in_group / gsz;
 }
 
-__global__ __launch_bounds__(kGemmThreads) void block_gemm_kernel(
+template <int WM, int WN, int FM>
+__global__ __launch_bounds__(WM * WN * 64) void block_gemm_kernel(
     const uint8_t *__restrict__ xq, const float *__restrict__ xs, const uint8_t *__restrict__ wq,
     const float *__restrict__ ws, int64_t M, int64_t N, int64_t K, uint16_t *__restrict__ y,
     int tiles_m, int tiles_n) {
-  __shared__ GemmSmem sm;
+  using T = Tile<WM, WN, FM>;
+  __shared__ typename T::Smem sm;
   int tm, tn;
   tile_coords(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, tm, tn);
-  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-  const int64_t KB = K / BK;
-  gemm_tile(xq + m0 * K, xs + m0 * KB, (int)min<int64_t>(BM, M - m0), wq + n0 * K,
-            ws + (n0 / BN) * KB, (int)min<int64_t>(BN, N - n0), K, y + m0 * N + n0, N, sm);
-}
-
-__global__ __launch_bounds__(big::kThreads) void block_gemm_256_kernel(
-    const uint8_t *__restrict__ xq, const float *__restrict__ xs, const uint8_t *__restrict__ wq,
-    const float *__restrict__ ws, int64_t M, int64_t N, int64_t K, uint16_t *__restrict__ y,
-    int tiles_m, int tiles_n) {
-  __shared__ big::Smem sm;
-  int tm, tn;
-  tile_coords(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, tm, tn);
-  const int64_t m0 = (int64_t)tm * big::TM, n0 = (int64_t)tn * big::TN;
-  const int64_t KB = K / big::TK;
-  gemm_tile_256(xq + m0 * K, xs + m0 * KB, (int)min<int64_t>(big::TM, M - m0), wq + n0 * K,
-                ws + (n0 / 128) * KB, (int)min<int64_t>(big::TN, N - n0), K, y + m0 * N + n0, N,
-                sm);
+  const int64_t m0 = (int64_t)tm * T::TM, n0 = (int64_t)tn * T::TN;
+  const int64_t KB = K / 128;
+  gemm_tile<WM, WN, FM>(xq + m0 * K, xs + m0 * KB, (int)min<int64_t>(T::TM, M - m0), wq + n0 * K,
+                        ws + (n0 / 128) * KB, (int)min<int64_t>(T::TN, N - n0), K, y + m0 * N + n0,
+                        N, sm);
 }
 
 // Grouped variant.  The logical m-tiles of all experts are numbered
-// consecutively (expert e owns ceil(M_e/128) of them); the grid is sized
-// for the upper bound ceil(total_M/128) + E, and workgroups past the real
-// count exit at once.  Offsets are read on the device (no host sync) and
-// clamped to [0, total_M].
-__global__ __launch_bounds__(kGemmThreads) void grouped_gemm_kernel(
+// consecutively (expert e owns ceil(M_e/TM) of them); the grid is sized for
+// the upper bound ceil(total_M/TM) + E, and workgroups past the real count
+// exit at once.  Offsets are read on the device (no host sync) and clamped
+// to [0, total_M].
+template <int WM, int WN, int FM>
+__global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(
     const uint8_t *__restrict__ xq, const float *__restrict__ xs, const uint8_t *__restrict__ wq,
     const float *__restrict__ ws, const int32_t *__restrict__ offsets, int E, int64_t total_M,
     int64_t N, int64_t K, uint16_t *__restrict__ y, int tiles_n) {
-  __shared__ GemmSmem sm;
+  using T = Tile<WM, WN, FM>;
+  __shared__ typename T::Smem sm;
   const int tn = blockIdx.x % tiles_n;
   int mt = blockIdx.x / tiles_n;
   int64_t r0 = 0, r1 = 0;
@@ -339,50 +397,58 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_kernel(
     int64_t a = offsets[e], b = offsets[e + 1];
     a = a < 0 ? 0 : (a > total_M ? total_M : a);
     b = b < a ? a : (b > total_M ? total_M : b);
-    const int cnt = (int)((b - a + BM - 1) / BM);
+    const int cnt = (int)((b - a + T::TM - 1) / T::TM);
     if (mt < cnt) {
-      r0 = a + (int64_t)mt * BM;
+      r0 = a + (int64_t)mt * T::TM;
       r1 = b;
       break;
     }
     mt -= cnt;
   }
   if (e == E) return;
-  const int64_t n0 = (int64_t)tn * BN;
-  const int64_t KB = K / BK;
-  const int64_t NB = (N + BN - 1) / BN;
-  gemm_tile(xq + r0 * K, xs + r0 * KB, (int)min<int64_t>(BM, r1 - r0), wq + (int64_t)e * N * K + n0 * K,
-            ws + ((int64_t)e * NB + n0 / BN) * KB, (int)min<int64_t>(BN, N - n0), K,
-            y + r0 * N + n0, N, sm);
+  const int64_t n0 = (int64_t)tn * T::TN;
+  const int64_t KB = K / 128;
+  const int64_t NB = (N + 127) / 128;
+  gemm_tile<WM, WN, FM>(xq + r0 * K, xs + r0 * KB, (int)min<int64_t>(T::TM, r1 - r0),
+                        wq + (int64_t)e * N * K + n0 * K, ws + ((int64_t)e * NB + n0 / 128) * KB,
+                        (int)min<int64_t>(T::TN, N - n0), K, y + r0 * N + n0, N, sm);
+}
+
+template <int WM, int WN, int FM>
+static hipError_t launch_tiled(const void *xq, const float *xs, const void *wq, const float *ws,
+                               int64_t M, int64_t N, int64_t K, void *y, hipStream_t stream) {
+  using T = Tile<WM, WN, FM>;
+  const int tm = (int)((M + T::TM - 1) / T::TM), tn = (int)((N + T::TN - 1) / T::TN);
+  hipLaunchKernelGGL((block_gemm_kernel<WM, WN, FM>), dim3((unsigned)(tm * tn)), dim3(T::kThreads),
+                     0, stream, static_cast<const uint8_t *>(xq), xs,
+                     static_cast<const uint8_t *>(wq), ws, M, N, K, static_cast<uint16_t *>(y),
+                     tm, tn);
+  return hipGetLastError();
 }
 
 hipError_t launch_block_gemm(const void *xq, const float *xs, const void *wq, const float *ws,
                              int64_t M, int64_t N, int64_t K, void *y, hipStream_t stream) {
-  const int64_t big_tiles = ((M + big::TM - 1) / big::TM) * ((N + big::TN - 1) / big::TN);
-  if (big_tiles >= 128) {
-    const int tm = (int)((M + big::TM - 1) / big::TM), tn = (int)((N + big::TN - 1) / big::TN);
-    hipLaunchKernelGGL(block_gemm_256_kernel, dim3((unsigned)(tm * tn)), dim3(big::kThreads), 0,
-                       stream, static_cast<const uint8_t *>(xq), xs,
-                       static_cast<const uint8_t *>(wq), ws, M, N, K, static_cast<uint16_t *>(y),
-                       tm, tn);
-    return hipGetLastError();
+  if (M <= kDecMaxM) {
+    const int MF = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+    if ((K / 128) * MF * 16 * 4 <= kDecMaxScaleBytes) {
+      if (MF == 1) return launch_decode<1>(xq, xs, wq, ws, M, N, K, y, stream);
+      if (MF == 2) return launch_decode<2>(xq, xs, wq, ws, M, N, K, y, stream);
+      return launch_decode<4>(xq, xs, wq, ws, M, N, K, y, stream);
+    }
   }
-  const int tiles_m = (int)((M + BM - 1) / BM);
-  const int tiles_n = (int)((N + BN - 1) / BN);
-  hipLaunchKernelGGL(block_gemm_kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(kGemmThreads),
-                     0, stream, static_cast<const uint8_t *>(xq), xs,
-                     static_cast<const uint8_t *>(wq), ws, M, N, K, static_cast<uint16_t *>(y),
-                     tiles_m, tiles_n);
-  return hipGetLastError();
+  const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  if (big_tiles >= 192) return launch_tiled<2, 4, 8>(xq, xs, wq, ws, M, N, K, y, stream);
+  return launch_tiled<2, 2, 4>(xq, xs, wq, ws, M, N, K, y, stream);
 }
 
 hipError_t launch_grouped_gemm(const void *xq, const float *xs, const void *wq, const float *ws,
                                const int32_t *offsets, int32_t E, int64_t total_M, int64_t N,
                                int64_t K, void *y, hipStream_t stream) {
-  const int64_t tiles_n = (N + BN - 1) / BN;
-  const int64_t tiles_m = (total_M + BM - 1) / BM + E;
-  hipLaunchKernelGGL(grouped_gemm_kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(kGemmThreads),
-                     0, stream, static_cast<const uint8_t *>(xq), xs,
+  using T = Tile<2, 4, 8>;
+  const int64_t tiles_n = (N + T::TN - 1) / T::TN;
+  const int64_t tiles_m = (total_M + T::TM - 1) / T::TM + E;
+  hipLaunchKernelGGL((grouped_gemm_kernel<2, 4, 8>), dim3((unsigned)(tiles_m * tiles_n)),
+                     dim3(T::kThreads), 0, stream, static_cast<const uint8_t *>(xq), xs,
                      static_cast<const uint8_t *>(wq), ws, offsets, (int)E, total_M, N, K,
                      static_cast<uint16_t *>(y), (int)tiles_n);
   return hipGetLastError();

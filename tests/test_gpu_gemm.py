@@ -87,7 +87,9 @@ def test_gemm_tiny():
 
 @pytest.mark.parametrize("M,N,K", [(1, 128, 128), (15, 100, 256), (17, 576, 384),
                                    (130, 300, 1024), (257, 1000, 512), (16, 4096, 4096),
-                                   (200, 129, 7168), (129, 257, 128)])
+                                   (200, 129, 7168), (129, 257, 128), (33, 4096, 4096),
+                                   (40, 300, 512), (64, 1024, 2048), (65, 256, 256),
+                                   (2, 24576, 1536), (3, 576, 18432), (520, 3000, 1280)])
 def test_gemm_ragged(M, N, K):
     x = synth.dsv3_activations(M + 11 * K, M, K, N)
     w = synth.normal_bf16(N + 13 * K, (N, K), 0.02)
@@ -185,11 +187,18 @@ def test_grouped_matches_oracle_and_per_expert_gemm(sizes, N, K):
     y = bf16_to_host(y)
     check_tol(y, og.grouped_block_gemm(xq, xs, wq, ws, off),
               og.grouped_term_magnitude(xq, xs, wq, ws, off), f"grouped {sizes}")
+    # each expert's rows also agree with the plain GEMM on that expert (the two
+    # may pick different tile configurations, so only to the tolerance)
     for e in range(len(sizes)):
         r0, r1 = int(off[e]), int(off[e + 1])
         if r1 > r0:
             ye = gpu_gemm(xq[r0:r1], xs[r0:r1], wq[e], ws[e])
-            assert np.array_equal(y[r0:r1], ye), f"expert {e} differs from the plain GEMM"
+            check_tol(ye, og.block_gemm(xq[r0:r1], xs[r0:r1], wq[e], ws[e]),
+                      og.term_magnitude(xq[r0:r1], xs[r0:r1], wq[e], ws[e]), f"plain expert {e}")
+            diff = np.abs(og.bf16_bits_to_f64(ye) - og.bf16_bits_to_f64(y[r0:r1]))
+            scale = np.abs(og.bf16_bits_to_f64(ye)) + 2.0 ** -6 * og.term_magnitude(
+                xq[r0:r1], xs[r0:r1], wq[e], ws[e])
+            assert np.all(diff <= 2e-2 * scale), f"expert {e}: grouped and plain GEMM disagree"
 
 
 def test_grouped_rows_outside_experts_untouched():
