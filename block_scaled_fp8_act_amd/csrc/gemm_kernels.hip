@@ -52,10 +52,12 @@ struct Tile {
   static constexpr int kDmaB = TN / 8 / kWaves;
   static_assert(kDmaA * 8 * kWaves == TM && kDmaB * 8 * kWaves == TN, "tile/DMA mismatch");
   static_assert(TM / 64 <= kWaves, "scale DMA needs TM/64 waves");
+  static_assert(TM / 64 < kWaves, "one wave must be free for the weight-scale DMA");
   struct Smem {
     uint8_t a[2][TM * 128];
     uint8_t b[2][TN * 128];
     float as[2][TM];
+    float ws[2][64];  // weight-block scales of the tile's (<= 2) column blocks
   };
 };
 
@@ -68,13 +70,15 @@ __device__ __forceinline__ void lds_dma4(const void *g, void *lds_base) {
   __builtin_amdgcn_global_load_lds(g, (lds_void *)lds_base, 4, 0, 0);
 }
 
-// Chunk swizzle: chunk c of row r is stored at c ^ ((r >> 1) & 7).  The 16
-// lanes of a ds_read_b128 quarter-wave read one logical chunk of 16
-// consecutive rows; rows r and r+1 sit in different 128-byte halves of the
-// 64 four-byte banks and (r >> 1) & 7 spreads each pair over the eight
-// chunk positions, so the 16 lanes hit 16 distinct 16-byte bank groups.
+// Chunk swizzle: chunk c of row r is stored at c ^ f(r) with
+// f(r) = ((r & 3) << 1) | ((r >> 2) & 1), a permutation of r's low three
+// bits.  A fragment read (16 lanes on 16 consecutive rows, one chunk each)
+// then runs at the full LDS rate (~220 B/clk/CU measured on gfx950), where
+// c ^ (r & 7) or c ^ ((r >> 1) & 7) run at half rate and no swizzle at a
+// quarter.
+__device__ __forceinline__ int swz_f(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
 __device__ __forceinline__ int swz(int row, int chunk) {
-  return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
+  return row * 128 + ((chunk ^ swz_f(row)) << 4);
 }
 
 // One output tile.  A: x_q at the tile's first row (row stride K bytes),
@@ -105,35 +109,45 @@ __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ A,
 
   // DMA load i of a wave fills LDS rows [8r, 8r+8), r = kDma*w + i; lane l
   // writes bytes [16l, 16l+16) of that 1 KB run = row 8r + l/8, physical
-  // chunk l%8, which holds logical chunk (l%8) ^ ((row >> 1) & 7).
-  const uint8_t *pa[T::kDmaA];
-  const uint8_t *pb[T::kDmaB];
+  // chunk l%8, which holds logical chunk (l%8) ^ swz_f(row).
+  // 32-bit byte offsets from the tile's base (< 256 * K <= 2^32), so each
+  // DMA address is a uniform base plus one VGPR.
+  uint32_t oa[T::kDmaA];
+  uint32_t ob[T::kDmaB];
 #pragma unroll
   for (int i = 0; i < T::kDmaA; ++i) {
     const int row = 8 * (T::kDmaA * wave + i) + (lane >> 3);
-    const int lchunk = (lane & 7) ^ ((row >> 1) & 7);
-    pa[i] = A + (int64_t)min(row, rows_a - 1) * K + lchunk * 16;
+    const int lchunk = (lane & 7) ^ swz_f(row);
+    oa[i] = (uint32_t)min(row, rows_a - 1) * (uint32_t)K + lchunk * 16;
   }
 #pragma unroll
   for (int i = 0; i < T::kDmaB; ++i) {
     const int row = 8 * (T::kDmaB * wave + i) + (lane >> 3);
-    const int lchunk = (lane & 7) ^ ((row >> 1) & 7);
-    pb[i] = B + (int64_t)min(row, rows_b - 1) * K + lchunk * 16;
+    const int lchunk = (lane & 7) ^ swz_f(row);
+    ob[i] = (uint32_t)min(row, rows_b - 1) * (uint32_t)K + lchunk * 16;
   }
   // Activation scales of rows 64w + l (waves w < TM/64).
   const float *ps = As + (int64_t)min(64 * wave + lane, rows_a - 1) * KB;
-  // Weight-block scale row of this wave's 64 columns (clamped to the last
-  // existing block row of a short tile; such columns are not stored).
-  const float *pws = Bs + (int64_t)min((wn * 64) / 128, (rows_b - 1) / 128) * KB;
+  // Weight-block scales of the tile's column blocks (TN / 128 of them),
+  // DMA'd with the stage by lanes 0..TN/128-1 of wave TM/64 (clamped to the
+  // last existing block row of a short tile; such columns are not stored).
+  // Keeping every per-step load on the vector memory path leaves no scalar
+  // load in flight, so LDS waits can count partially (LDS returns in order).
+  constexpr int kNbTile = T::TN / 128;
+  const float *pws = Bs + (int64_t)min(lane, min(kNbTile, (rows_b + 127) / 128) - 1) * KB;
+  const int wsel = (wn * 64) / 128;  // this wave's column block within the tile
 
   auto issue = [&](int kb, int st) {
+    const uint8_t *ak = A + (int64_t)kb * 128;
+    const uint8_t *bk = B + (int64_t)kb * 128;
 #pragma unroll
     for (int i = 0; i < T::kDmaA; ++i)
-      lds_dma16(pa[i] + (int64_t)kb * 128, sm.a[st] + (T::kDmaA * wave + i) * 1024);
+      lds_dma16(ak + oa[i], sm.a[st] + (T::kDmaA * wave + i) * 1024);
 #pragma unroll
     for (int i = 0; i < T::kDmaB; ++i)
-      lds_dma16(pb[i] + (int64_t)kb * 128, sm.b[st] + (T::kDmaB * wave + i) * 1024);
+      lds_dma16(bk + ob[i], sm.b[st] + (T::kDmaB * wave + i) * 1024);
     if (wave < T::TM / 64) lds_dma4(ps + kb, &sm.as[st][64 * wave]);
+    if (wave == T::TM / 64 && lane < kNbTile) lds_dma4(pws + kb, &sm.ws[st][0]);
   };
 
   v4f acc[FM][4];
@@ -151,23 +165,34 @@ __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ A,
   const int arow0 = wm * FM * 16 + r16;
   const int brow0 = wn * 64 + r16;
   const int srow0 = wm * FM * 16 + 4 * (lane >> 4);
+
+
   for (int kb = 0; kb < KB; ++kb) {
     const int st = kb & 1;
     if (kb + 1 < KB) issue(kb + 1, st ^ 1);
-    const float wsc = pws[kb];
+    const float wsc = sm.ws[st][wsel];
     const uint8_t *sa = sm.a[st];
-    const uint8_t *sb = sm.b[st];
     const float4 *sas = reinterpret_cast<const float4 *>(&sm.as[st][srow0]);
+    // Reads in first-use order (B0, A0, B1, B2, B3, scales), so the first
+    // MFMA waits only for the first four; LDS returns in order.
+    const uint8_t *sb = sm.b[st];
     v8i bfr[4];
+    v8i af;
+    float4 s4;
+    bfr[0] = frag_from(*reinterpret_cast<const uint4 *>(sb + swz(brow0, c0)),
+                       *reinterpret_cast<const uint4 *>(sb + swz(brow0, c0 + 1)));
+    af = frag_from(*reinterpret_cast<const uint4 *>(sa + swz(arow0, c0)),
+                   *reinterpret_cast<const uint4 *>(sa + swz(arow0, c0 + 1)));
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) {
+    for (int ni = 1; ni < 4; ++ni) {
       const int row = brow0 + ni * 16;
       bfr[ni] = frag_from(*reinterpret_cast<const uint4 *>(sb + swz(row, c0)),
                           *reinterpret_cast<const uint4 *>(sb + swz(row, c0 + 1)));
+      __builtin_amdgcn_sched_barrier(0);
     }
-    v8i af = frag_from(*reinterpret_cast<const uint4 *>(sa + swz(arow0, c0)),
-                       *reinterpret_cast<const uint4 *>(sa + swz(arow0, c0 + 1)));
-    float4 s4 = sas[0];
+    s4 = sas[0];
+    __builtin_amdgcn_sched_barrier(0);
     v8i afn = af;
     float4 s4n = s4;
     v4f pp[4];
@@ -198,12 +223,14 @@ __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ A,
       af = afn;
       s4 = s4n;
     }
+    // all MFMAs of this step are issued: publish the next stage, start its
+    // fragment reads, then finish this step's last promotion meanwhile
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[FM - 1][ni][r] = fmaf(pp[ni][r], scp[r], acc[FM - 1][ni][r]);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
   }
 
   // Epilogue: lane holds rows 4*(lane/16)+r of each 16x16 fragment, column lane%16.
