@@ -45,7 +45,36 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rows", action="store_true", help="also time the other hot-path rows")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="end with a plain 512 MiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
+
+
+GEMM_SOURCE = os.path.join(ROOT, "block_scaled_fp8_act_amd", "csrc", "gemm_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "block_gemm_llama_prefill_traffic.md")
+
+
+def source_digest(path):
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per GEMM launch of this workload from the committed rocprofv3
+    --pmc summary (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy kernel),
+    or None when the GEMM source has changed since the counters were taken."""
+    try:
+        fields = {}
+        for line in open(TRAFFIC_FILE):
+            if ":" in line and line.strip().startswith("- "):
+                k, v = line.strip()[2:].split(":", 1)
+                fields[k.strip()] = v.strip().strip("`")
+        if fields.get("gemm_source_sha256_16") != source_digest(GEMM_SOURCE):
+            return None
+        return float(fields["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def gen_inputs(torch, dev, seed):
@@ -190,7 +219,8 @@ def main():
         "roofline": {
             "bound": "mfma", "kernel": "block_gemm_kernel",
             "achieved": round(gemm_tflops, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4), "traffic": None,
+            "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4), "traffic": measured_traffic(),
+            "traffic_unit": "HBM bytes per launch (mean over the 4 projections)",
         },
         "act_quant": {"achieved": round(act_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                       "frac": round(act_gbs / PEAK_HBM_GBS, 4), "bound": "hbm"},
@@ -201,6 +231,14 @@ def main():
         out["rows"] = other_rows(torch, fb, dev, stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
+    if args.calibrate_copy:
+        src = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        t = _time(torch, stream, lambda: dst.copy_(src), iters=10, warm=1)
+        out["copy_512MiB_GBps"] = round(2 * src.numel() / t / 1e9, 1)
     print(json.dumps(out), flush=True)
 
 

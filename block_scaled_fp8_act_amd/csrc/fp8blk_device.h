@@ -72,16 +72,27 @@ __device__ __forceinline__ float quotient(float xp, float sp, float y) {
   return fmaf(-nr, y, q0);
 }
 
-// Saturate to the E4M3 range before the hardware conversion (which rounds
-// to nearest even in the OCP E4M3FN format on gfx950).
-__device__ __forceinline__ float sat448(float t) {
-  return __builtin_amdgcn_fmed3f(t, -448.0f, 448.0f);
+// fl32(amax / 448) for amax >= 2^-100: the product with R = fl32(1/448)
+// corrected once with an exact FMA residual (Markstein's correction with a
+// correctly rounded reciprocal); equal to the IEEE quotient for every bf16
+// amax >= 2^-100 (checked over all of them).  Smaller amax take the IEEE
+// division (make_qparams).
+__device__ __forceinline__ float div448(float amax) {
+  constexpr float R = 0x1.24924ap-9f;  // fl32(1/448)
+  const float q0 = amax * R;
+  const float r = fmaf(-q0, 448.0f, amax);
+  return fmaf(r, R, q0);
 }
 
-// Four fp32 -> four E4M3 codes packed little-endian into one dword.
+// Four fp32 -> four E4M3 codes packed little-endian into one dword, with
+// the hardware conversion (round to nearest even, OCP E4M3FN on gfx950).
+// Without its clamp bit the conversion returns NaN from |t| >= 464 and
+// rounds (448, 464) to 448; the quantizers' quotients never exceed 448.88
+// (|x| <= amax and s = fl32(amax / 448)), so no saturation step is needed:
+// the E4M3 saturation at +-448 is exactly what RNE gives on that range.
 __device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(a), sat448(b), 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(c), sat448(d), w, true);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
   return (uint32_t)w;
 }
 

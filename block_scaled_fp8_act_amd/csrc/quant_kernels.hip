@@ -10,8 +10,8 @@
 // Both kernels are HBM-bound (3 bytes moved per element, plus 4 bytes per
 // set), so the layout is chosen for fully coalesced 16-byte loads and the
 // VALU work per element is kept small: the per-set division and reciprocal
-// are paid once per set, and each element costs one multiply, two FMAs, a
-// clamp and half a packed conversion.
+// are paid once per set, and each element costs one multiply, two FMAs and
+// half a packed conversion.
 #include "fp8blk_device.h"
 #include "fp8blk_launch.h"
 
@@ -22,50 +22,98 @@ namespace fp8blk {
 //
 // The input is viewed as a flat sequence of 128-element groups (row-major
 // [M,K] with K % 128 == 0 makes group g = columns [128*(g % KB), +128) of row
-// g / KB, and its scale lives at x_scale[g]).  A wave handles a "tile" of 16
-// consecutive groups = 4 KB of bf16: load i (0..3) of lane l reads 16 bytes
-// at tile*4096 + i*1024 + l*16, so every load instruction is one contiguous
+// g / KB, and its scale lives at x_scale[g]).  A "tile" is 16 consecutive
+// groups = 4 KB of bf16: load i (0..3) of lane l reads 16 bytes at
+// tile*4096 + i*1024 + l*16, so every load instruction is one contiguous
 // 1 KB run and each group is one DPP row of 16 lanes (8 values per lane).
+// A wave handles two tiles per iteration (eight 16-byte loads in flight per
+// lane).
+//
+// Fast path: when no group of the wave's tiles has 0 < amax < 2^-50 (always, in
+// practice), s comes from div448, the power-of-two rescale is skipped
+// (k = 0) and each element costs one multiply and two FMAs plus half a
+// packed conversion.  Otherwise the wave takes the general element map of
+// make_qparams / quotient.  Both agree with the IEEE definition on every
+// (x, amax) bf16 pair.
 constexpr int kActThreads = 256;
 constexpr int kActWaves = kActThreads / 64;
 constexpr int kGroupsPerTile = 16;
+constexpr int kTilesPerIter = 2;
+constexpr float kTinyAmax = 0x1p-50f;
+
+__device__ __forceinline__ void unpack8(const uint4 &v, float *f) {
+  f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
+  f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+  f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
+  f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+}
+
+__device__ __forceinline__ float absmax8(const float *f) {
+  return fmaxf(fmaxf(fmaxf(fabsf(f[0]), fabsf(f[1])), fmaxf(fabsf(f[2]), fabsf(f[3]))),
+               fmaxf(fmaxf(fabsf(f[4]), fabsf(f[5])), fmaxf(fabsf(f[6]), fabsf(f[7]))));
+}
 
 __global__ __launch_bounds__(kActThreads) void act_quant_kernel(
     const uint4 *__restrict__ x, uint2 *__restrict__ q, float *__restrict__ scale,
     int64_t n_groups) {
+  constexpr int L = 4 * kTilesPerIter;  // loads per lane per iteration
   const int lane = threadIdx.x & 63;
   const int64_t n_tiles = (n_groups + kGroupsPerTile - 1) / kGroupsPerTile;
-  const int64_t stride = (int64_t)gridDim.x * kActWaves;
-  for (int64_t tile = (int64_t)blockIdx.x * kActWaves + (threadIdx.x >> 6); tile < n_tiles;
-       tile += stride) {
-    uint4 v[4];
-    bool ok[4];
+  const int64_t stride = (int64_t)gridDim.x * kActWaves * kTilesPerIter;
+  for (int64_t tile0 = ((int64_t)blockIdx.x * kActWaves + (threadIdx.x >> 6)) * kTilesPerIter;
+       tile0 < n_tiles; tile0 += stride) {
+    uint4 v[L];
+    bool ok[L];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t g = tile * kGroupsPerTile + i * 4 + (lane >> 4);
+    for (int i = 0; i < L; ++i) {
+      const int64_t g = tile0 * kGroupsPerTile + i * 4 + (lane >> 4);
       ok[i] = g < n_groups;
-      v[i] = ok[i] ? x[tile * 256 + i * 64 + lane] : make_uint4(0, 0, 0, 0);
+      v[i] = ok[i] ? x[tile0 * 256 + i * 64 + lane] : make_uint4(0, 0, 0, 0);
     }
+    float amax[L];
+    bool tiny = false;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < L; ++i) {
       float f[8];
-      f[0] = bf16_lo(v[i].x); f[1] = bf16_hi(v[i].x);
-      f[2] = bf16_lo(v[i].y); f[3] = bf16_hi(v[i].y);
-      f[4] = bf16_lo(v[i].z); f[5] = bf16_hi(v[i].z);
-      f[6] = bf16_lo(v[i].w); f[7] = bf16_hi(v[i].w);
-      float m = fmaxf(fmaxf(fabsf(f[0]), fabsf(f[1])), fmaxf(fabsf(f[2]), fabsf(f[3])));
-      m = fmaxf(m, fmaxf(fmaxf(fabsf(f[4]), fabsf(f[5])), fmaxf(fabsf(f[6]), fabsf(f[7]))));
-      const float amax = row16_max(m);
-      const QParams p = make_qparams(amax);
-      float t[8];
+      unpack8(v[i], f);
+      amax[i] = row16_max(absmax8(f));
+      tiny |= ok[i] && amax[i] > 0.0f && amax[i] < kTinyAmax;
+    }
+    if (__builtin_amdgcn_ballot_w64(tiny) == 0) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) t[j] = quotient(ldexpf(f[j], p.k), p.sp, p.y);
-      uint2 out;
-      out.x = pack4_e4m3(t[0], t[1], t[2], t[3]);
-      out.y = pack4_e4m3(t[4], t[5], t[6], t[7]);
-      if (ok[i]) {
-        q[tile * 256 + i * 64 + lane] = out;
-        if ((lane & 15) == 0) scale[tile * kGroupsPerTile + i * 4 + (lane >> 4)] = p.s;
+      for (int i = 0; i < L; ++i) {
+        float f[8];
+        unpack8(v[i], f);
+        const float s = div448(amax[i]);
+        const float sp = s == 0.0f ? 1.0f : s;   // all-zero group: codes are +-0
+        const float y = 1.0f / sp;
+        float t[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) t[j] = quotient(f[j], sp, y);
+        uint2 out;
+        out.x = pack4_e4m3(t[0], t[1], t[2], t[3]);
+        out.y = pack4_e4m3(t[4], t[5], t[6], t[7]);
+        if (ok[i]) {
+          q[tile0 * 256 + i * 64 + lane] = out;
+          if ((lane & 15) == 0) scale[tile0 * kGroupsPerTile + i * 4 + (lane >> 4)] = s;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < L; ++i) {
+        float f[8];
+        unpack8(v[i], f);
+        const QParams p = make_qparams(amax[i]);
+        float t[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) t[j] = quotient(ldexpf(f[j], p.k), p.sp, p.y);
+        uint2 out;
+        out.x = pack4_e4m3(t[0], t[1], t[2], t[3]);
+        out.y = pack4_e4m3(t[4], t[5], t[6], t[7]);
+        if (ok[i]) {
+          q[tile0 * 256 + i * 64 + lane] = out;
+          if ((lane & 15) == 0) scale[tile0 * kGroupsPerTile + i * 4 + (lane >> 4)] = p.s;
+        }
       }
     }
   }
@@ -135,8 +183,9 @@ hipError_t launch_act_quant(const void *x, int64_t M, int64_t K, void *q, float 
                             hipStream_t stream) {
   const int64_t n_groups = M * (K / kBlock);
   const int64_t n_tiles = (n_groups + kGroupsPerTile - 1) / kGroupsPerTile;
-  int64_t blocks = (n_tiles + kActWaves - 1) / kActWaves;
-  const int64_t cap = 256 * 16;  // grid-stride beyond 16 workgroups per CU
+  const int64_t per_block = (int64_t)kActWaves * kTilesPerIter;
+  int64_t blocks = (n_tiles + per_block - 1) / per_block;
+  const int64_t cap = 256 * 8;  // grid-stride beyond 8 workgroups per CU
   if (blocks > cap) blocks = cap;
   hipLaunchKernelGGL(act_quant_kernel, dim3((unsigned)blocks), dim3(kActThreads), 0, stream,
                      static_cast<const uint4 *>(x), static_cast<uint2 *>(q), s, n_groups);
