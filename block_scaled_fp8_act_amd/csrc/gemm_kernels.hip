@@ -173,16 +173,19 @@ __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ A,
     const float wsc = sm.ws[st][wsel];
     const uint8_t *sa = sm.a[st];
     const float4 *sas = reinterpret_cast<const float4 *>(&sm.as[st][srow0]);
-    // Reads in first-use order (B0, A0, B1, B2, B3, scales), so the first
-    // MFMA waits only for the first four; LDS returns in order.
+    // Reads in first-use order (B0, A0, B1, B2, B3, scales, then fragment 1),
+    // so the first MFMA waits only for the first four; LDS returns in order.
+    // A fragments are then fetched two fragments ahead of their MFMAs.
     const uint8_t *sb = sm.b[st];
     v8i bfr[4];
-    v8i af;
-    float4 s4;
+    auto read_a = [&](int mi) {
+      const int row = arow0 + mi * 16;
+      return frag_from(*reinterpret_cast<const uint4 *>(sa + swz(row, c0)),
+                       *reinterpret_cast<const uint4 *>(sa + swz(row, c0 + 1)));
+    };
     bfr[0] = frag_from(*reinterpret_cast<const uint4 *>(sb + swz(brow0, c0)),
                        *reinterpret_cast<const uint4 *>(sb + swz(brow0, c0 + 1)));
-    af = frag_from(*reinterpret_cast<const uint4 *>(sa + swz(arow0, c0)),
-                   *reinterpret_cast<const uint4 *>(sa + swz(arow0, c0 + 1)));
+    v8i af = read_a(0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ni = 1; ni < 4; ++ni) {
@@ -191,10 +194,12 @@ __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ A,
                           *reinterpret_cast<const uint4 *>(sb + swz(row, c0 + 1)));
       __builtin_amdgcn_sched_barrier(0);
     }
-    s4 = sas[0];
+    float4 s4 = sas[0];
+    v8i afn = read_a(1);
+    float4 s4n = sas[4];
     __builtin_amdgcn_sched_barrier(0);
-    v8i afn = af;
-    float4 s4n = s4;
+    v8i afn2 = afn;
+    float4 s4n2 = s4n;
     v4f pp[4];
     float scp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -204,11 +209,9 @@ __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ A,
       for (int ni = 0; ni < 4; ++ni) {
         pc[ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
             af, bfr[ni], v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 0, 0, 0);
-        if (ni == 0 && mi + 1 < FM) {
-          const int row = arow0 + (mi + 1) * 16;
-          afn = frag_from(*reinterpret_cast<const uint4 *>(sa + swz(row, c0)),
-                          *reinterpret_cast<const uint4 *>(sa + swz(row, c0 + 1)));
-          s4n = sas[(mi + 1) * 4];
+        if (ni == 0 && mi + 2 < FM) {
+          afn2 = read_a(mi + 2);
+          s4n2 = sas[(mi + 2) * 4];
         }
         if (mi > 0) {
 #pragma unroll
@@ -222,6 +225,8 @@ __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ A,
       for (int ni = 0; ni < 4; ++ni) pp[ni] = pc[ni];
       af = afn;
       s4 = s4n;
+      afn = afn2;
+      s4n = s4n2;
     }
     // all MFMAs of this step are issued: publish the next stage, start its
     // fragment reads, then finish this step's last promotion meanwhile
