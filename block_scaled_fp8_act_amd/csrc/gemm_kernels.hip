@@ -157,6 +157,11 @@ __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ A,
     for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
   issue(0, 0);
+  // Y (a kernel argument) is first used by the epilogue; consuming it here
+  // makes its scalar load complete before the loop.  With no scalar load in
+  // flight the LDS reads of the loop can be waited on partially (LDS
+  // returns in order; scalar loads may not).
+  asm volatile("" ::"s"(Y));
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -169,8 +174,8 @@ __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ A,
 
   for (int kb = 0; kb < KB; ++kb) {
     const int st = kb & 1;
-    if (kb + 1 < KB) issue(kb + 1, st ^ 1);
     const float wsc = sm.ws[st][wsel];
+    __builtin_amdgcn_sched_barrier(0);
     const uint8_t *sa = sm.a[st];
     const float4 *sas = reinterpret_cast<const float4 *>(&sm.as[st][srow0]);
     // Reads in first-use order (B0, A0, B1, B2, B3, scales, then fragment 1),
@@ -209,15 +214,23 @@ __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ A,
       for (int ni = 0; ni < 4; ++ni) {
         pc[ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
             af, bfr[ni], v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
         if (ni == 0 && mi + 2 < FM) {
           afn2 = read_a(mi + 2);
           s4n2 = sas[(mi + 2) * 4];
+          __builtin_amdgcn_sched_barrier(0);
         }
         if (mi > 0) {
 #pragma unroll
           for (int r = 0; r < 4; ++r)
             acc[mi - 1][ni][r] = fmaf(pp[ni][r], scp[r], acc[mi - 1][ni][r]);
         }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (mi == 0) {
+        // next stage's DMA goes out once this step's first fragment is
+        // running, so the step-start LDS reads can be waited on partially
+        if (kb + 1 < KB) issue(kb + 1, st ^ 1);
         __builtin_amdgcn_sched_barrier(0);
       }
       scp[0] = s4.x * wsc; scp[1] = s4.y * wsc; scp[2] = s4.z * wsc; scp[3] = s4.w * wsc;
