@@ -28,14 +28,21 @@ What is computed, and where it comes from:
   is the dequantization multiplier.  These are this library's readings of
   what the pages leave open.
 
+* Power-of-two scales stored as E8M0 bytes ("UE8M0 scale format" on the
+  same page, ``scale_fmt="ue8m0"``): :mod:`oracle.ue8m0` states the
+  readings (codec, round-up exponent, activations scaled the same way).
+
 Modules: :mod:`oracle.e4m3` (codec), :mod:`oracle.quant` (quantizers),
-:mod:`oracle.gemm` (block-scaled and grouped GEMM, linear layer).
+:mod:`oracle.gemm` (block-scaled and grouped GEMM, linear layer),
+:mod:`oracle.ue8m0` (E8M0 scales: codec, quantizers, GEMM).
 """
 from .e4m3 import E4M3_MAX, decode, encode, fl32_div
 from .quant import act_quant_group, weight_block_quant, quant_element_map
 from .gemm import (bf16_rne_bits, block_gemm, dequant_act, dequant_weight,
                    grouped_block_gemm, grouped_term_magnitude, linear, term_magnitude,
                    tolerance_report)
+from .ue8m0 import (act_quant_group_ue8m0, block_gemm_ue8m0, e8m0_decode, e8m0_exponent,
+                    grouped_block_gemm_ue8m0, weight_block_quant_ue8m0)
 
 __all__ = [
     "E4M3_MAX", "decode", "encode", "fl32_div",
@@ -43,4 +50,6 @@ __all__ = [
     "bf16_rne_bits", "block_gemm", "dequant_act", "dequant_weight",
     "grouped_block_gemm", "grouped_term_magnitude", "linear", "term_magnitude",
     "tolerance_report",
+    "act_quant_group_ue8m0", "block_gemm_ue8m0", "e8m0_decode", "e8m0_exponent",
+    "grouped_block_gemm_ue8m0", "weight_block_quant_ue8m0",
 ]

@@ -18,6 +18,7 @@ import oracle
 from oracle import e4m3 as oe
 from oracle import gemm as og
 from oracle import quant as oq
+from oracle import ue8m0 as ou
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -490,6 +491,158 @@ def pin_tolerance_report(seed=47):
     assert not og.tolerance_report(yb, y, S)["ok"]
 
 
+# ----------------------------------------------------------------------------
+# UE8M0 (power-of-two scale) pins
+
+def pin_e8m0_codec():
+    """Byte b is 2^(b-127) for b in [0, 254], NaN for 0xff (no zero)."""
+    got = ou.e8m0_decode(np.arange(256, dtype=np.uint8))
+    for b in range(255):
+        assert Fraction(float(got[b])) == Fraction(2) ** (b - 127), (b, got[b])
+    assert math.isnan(got[255])
+    assert got[127] == 1.0 and got[0] == 2.0 ** -127 and got[254] == 2.0 ** 127
+
+
+def _e_brute(amax: Fraction) -> int:
+    e = -127
+    while amax > 448 * Fraction(2) ** e:
+        e += 1
+    return e
+
+
+def pin_e8m0_exponent_exhaustive():
+    """Every non-negative finite bf16 amax: e is the smallest integer >= -127
+    with amax <= 448 * 2^e (walked up from -127 in exact rationals)."""
+    bits = np.arange(0, 0x7F80, dtype=np.uint32)
+    amax = (bits << 16).view(np.float32)
+    got = ou.e8m0_exponent(amax)
+    # the brute force walk is quadratic; check the binade edges exhaustively
+    # and every value through a monotone sweep
+    e = -127
+    for i, a in enumerate(amax):
+        fa = f32_value(int(bits[i]) << 16)
+        while fa > 448 * Fraction(2) ** e:
+            e += 1
+        assert got[i] == e, (hex(int(bits[i])), int(got[i]), e)
+        if i % 4096 == 0:
+            assert _e_brute(fa) == e
+    # fp32 amax values at and just around the edges 448 * 2^j: the edge
+    # itself and the value just below it take e = j, the value just above j+1
+    for j in (-126, -100, -3, 0, 1, 60, 119):
+        edge = np.float32(448.0 * 2.0 ** j)
+        above = np.nextafter(edge, np.float32(np.inf))
+        below = np.nextafter(edge, np.float32(0))
+        assert int(ou.e8m0_exponent(edge)) == j
+        assert int(ou.e8m0_exponent(below)) == j
+        assert int(ou.e8m0_exponent(above)) == j + 1
+    assert int(ou.e8m0_exponent(np.float32(448.0 * 2.0 ** -127))) == -127
+    assert int(ou.e8m0_exponent(np.float32(2.0 ** -149))) == -127
+
+
+def pin_ue8m0_hand_groups():
+    for row in read_golden("ue8m0_hand_groups.txt"):
+        amax_s, xs_s, b_s, q_s = [p.strip() for p in row.split("|")]
+        xb = np.array([int(v, 16) for v in xs_s.split()], np.uint16)
+        want_q = [int(v, 16) for v in q_s.split()]
+        row128 = np.zeros((1, 128), np.uint16)
+        row128[0, : len(xb)] = xb
+        q, b = ou.act_quant_group_ue8m0(row128)
+        assert int(b[0, 0]) == int(b_s, 16), (amax_s, hex(int(b[0, 0])), b_s)
+        assert list(q[0, : len(xb)]) == want_q, (amax_s, [hex(c) for c in q[0, : len(xb)]], q_s)
+        blk = np.zeros((130, 128), np.uint16)          # ragged: a 2-row second block row
+        blk[129, : len(xb)] = xb
+        wq, wb = ou.weight_block_quant_ue8m0(blk)
+        assert wb.shape == (2, 1) and int(wb[1, 0]) == int(b_s, 16) and int(wb[0, 0]) == 0
+        assert list(wq[129, : len(xb)]) == want_q
+
+
+def pin_ue8m0_invariants(seed=53):
+    rng = np.random.default_rng(seed)
+    M, K = 32, 512
+    x = (rng.standard_normal((M, K)) * np.exp2(rng.integers(-60, 60, (M, 1)))).astype(np.float32)
+    xb = (x.view(np.uint32) >> 16).astype(np.uint16)
+    xv = (xb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    q, b = ou.act_quant_group_ue8m0(xb)
+    assert q.shape == (M, K) and b.shape == (M, K // 128) and b.dtype == np.uint8
+    assert not np.any((q & 0x7F) == 0x7F), "NaN code produced"
+    s = np.exp2(b.astype(np.float64) - 127)
+    amax = np.abs(xv.reshape(M, K // 128, 128)).max(axis=2)
+    ratio = amax / s
+    assert np.all(ratio <= 448) and np.all((ratio > 224) | (b == 0))
+    # the quotient is exact, so dequantization errs by at most half a quantum
+    t = xv / np.repeat(s, 128, axis=1)
+    at = np.maximum(np.abs(t), 1e-300)
+    ulp = np.exp2(np.maximum(np.floor(np.log2(at)), -6) - 3)
+    deq = oe.decode(q) * np.repeat(s, 128, axis=1)
+    assert np.all(np.abs(xv - deq) <= 0.5 * ulp * np.repeat(s, 128, axis=1))
+    # same codes as the fp32-scale map on the exact quotient
+    assert np.array_equal(q, oe.encode(t.astype(np.float32)))
+    # power-of-two equivariance: the codes stay, the bytes shift by j
+    for j in (-9, 4):
+        xj = (xv * 2.0 ** j).astype(np.float32)
+        qj, bj = ou.act_quant_group_ue8m0((xj.view(np.uint32) >> 16).astype(np.uint16))
+        assert np.array_equal(qj, q) and np.array_equal(bj.astype(int), b.astype(int) + j)
+    # token independence
+    q2, b2 = ou.act_quant_group_ue8m0(xb[7:11])
+    assert np.array_equal(q2, q[7:11]) and np.array_equal(b2, b[7:11])
+    # exact on representable values: x = c * 2^j with amax = 448 * 2^j
+    codes, vals = e4m3_finite_table()
+    pick = rng.choice(len(codes), 127)
+    xr = np.array([448.0] + [math.copysign(float(vals[i]), -1.0 if codes[i] >> 7 else 1.0) for i in pick])
+    for j in (-30, 0, 17):
+        xe = (xr * 2.0 ** j).astype(np.float32)
+        qe, be = ou.act_quant_group_ue8m0((xe.view(np.uint32) >> 16).astype(np.uint16)[None, :])
+        assert int(be[0, 0]) == 127 + j and list(qe[0, 1:]) == [codes[i] for i in pick]
+
+
+def pin_ue8m0_weight_blocks(seed=59):
+    rng = np.random.default_rng(seed)
+    N, K = 300, 384                                      # last block row has 44 rows
+    w = (rng.standard_normal((N, K)) * np.exp2(rng.integers(-8, 8, (N, 1)))).astype(np.float32)
+    wb = (w.view(np.uint32) >> 16).astype(np.uint16)
+    q, b = ou.weight_block_quant_ue8m0(wb)
+    assert q.shape == (N, K) and b.shape == (3, 3)
+    wv = (wb.astype(np.uint32) << 16).view(np.float32)
+    for nb in range(3):
+        for kb in range(3):
+            blk = wv[nb * 128: min(N, nb * 128 + 128), kb * 128: kb * 128 + 128]
+            e = _e_brute(Fraction(float(np.abs(blk).max())))
+            assert int(b[nb, kb]) == e + 127, (nb, kb)
+            want = oe.encode((blk.astype(np.float64) * 2.0 ** -e).astype(np.float32))
+            assert np.array_equal(q[nb * 128: min(N, nb * 128 + 128), kb * 128: kb * 128 + 128], want)
+
+
+def pin_ue8m0_gemm(seed=61):
+    """With power-of-two scales every dequantized entry is a dyadic rational:
+    the exact dot products (rational arithmetic) match the fp64 result."""
+    import synth
+    x = synth.normal_bf16(seed, (3, 256))
+    w = synth.normal_bf16(seed + 1, (130, 256), 0.02)
+    w[128:] = synth.normal_bf16(seed + 2, (2, 256), 0.5)   # block row 1: other exponents
+    xq, xe = ou.act_quant_group_ue8m0(x)
+    wq, we = ou.weight_block_quant_ue8m0(w)
+    y = ou.block_gemm_ue8m0(xq, xe, wq, we)
+    dx = [[Fraction(float(v)) for v in r] for r in oe.decode(xq)]
+    dw = [[Fraction(float(v)) for v in r] for r in oe.decode(wq)]
+    for m in range(3):
+        for n in (0, 1, 77, 127, 128, 129):
+            acc = Fraction(0)
+            for k in range(256):
+                sx = Fraction(2) ** (int(xe[m, k // 128]) - 127)
+                sw = Fraction(2) ** (int(we[n // 128, k // 128]) - 127)
+                acc += dx[m][k] * sx * dw[n][k] * sw
+            assert abs(Fraction(float(y[m, n])) - acc) <= abs(acc) * Fraction(1, 2 ** 50) + Fraction(1, 2 ** 1000), (m, n)
+    S = ou.term_magnitude_ue8m0(xq, xe, wq, we)
+    assert np.all(S >= np.abs(y) * (1 - 1e-12))
+    # grouped: two experts split the rows
+    wq2 = np.stack([wq, wq[::-1].copy()]); we2 = np.stack([we, we[::-1].copy()])
+    off = np.array([0, 1, 3], np.int32)
+    assert np.all(we[0] != we[1])
+    yg = ou.grouped_block_gemm_ue8m0(xq, xe, wq2, we2, off)
+    np.testing.assert_array_equal(yg[0], y[0])
+    np.testing.assert_array_equal(yg[1:], ou.block_gemm_ue8m0(xq[1:], xe[1:], wq2[1], we2[1]))
+
+
 ALL_PINS = [
     pin_format_points, pin_hand_encodings, pin_decode_matches_enumeration,
     pin_encode_roundtrip_and_monotone, pin_encode_brute_force, pin_fl32_div,
@@ -497,4 +650,6 @@ ALL_PINS = [
     pin_group_invariants, pin_roundtrip_bound, pin_weight_blocks, pin_zero_groups,
     pin_gemm_exact_integers, pin_gemm_scale_indexing, pin_gemm_brute_force,
     pin_bf16_rounding, pin_grouped, pin_tolerance_report,
+    pin_e8m0_codec, pin_e8m0_exponent_exhaustive, pin_ue8m0_hand_groups,
+    pin_ue8m0_invariants, pin_ue8m0_weight_blocks, pin_ue8m0_gemm,
 ]

@@ -9,6 +9,7 @@ import oracle_pins as P
 from oracle import e4m3 as oe
 from oracle import gemm as og
 from oracle import quant as oq
+from oracle import ue8m0 as ou
 
 
 def _fails(pins):
@@ -56,9 +57,30 @@ MUTANTS = {
     "grouped_off_by_one": lambda mp: mp.setattr(
         og, "grouped_block_gemm", _grouped_shift),
     "weight_amax_full_block_rows": lambda mp: mp.setattr(oq, "GROUP", 64),
+    "ue8m0_floor_exponent": lambda mp: mp.setattr(ou, "e8m0_exponent", _e8m0_floor),
+    "ue8m0_strict_bound": lambda mp: mp.setattr(ou, "e8m0_exponent", _e8m0_strict),
+    "ue8m0_no_lower_clamp": lambda mp: mp.setattr(ou, "E_MIN", -133),
+    "e8m0_bias_128": lambda mp: mp.setattr(ou, "E8M0_BIAS", 128),
+    "ue8m0_gemm_weight_bytes_reversed": lambda mp: mp.setattr(
+        ou, "block_gemm_ue8m0", lambda xq, xe, wq, we: _orig_bg_ue(xq, xe, wq, we[::-1].copy())),
 }
 
 _orig_decode = oe.decode
+_orig_e8m0_exponent = ou.e8m0_exponent
+_orig_bg_ue = ou.block_gemm_ue8m0
+
+
+def _e8m0_floor(amax):
+    a = np.asarray(amax, np.float32).astype(np.float64)
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(a > 0, a, 1.0) / 448.0))
+    return np.maximum(np.where(a > 0, e, -127), -127).astype(np.int64)
+
+
+def _e8m0_strict(amax):
+    a = np.asarray(amax, np.float32).astype(np.float64)
+    e = _orig_e8m0_exponent(amax)
+    return np.where(a == 448.0 * np.exp2(e.astype(np.float64)), e + 1, e)
 _orig_dw = og.dequant_weight
 _orig_da = og.dequant_act
 _orig_grouped = og.grouped_block_gemm

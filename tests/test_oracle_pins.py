@@ -25,3 +25,15 @@ def test_codec_agrees_with_torch_float8_e4m3fn():
     x = np.clip(x, -448, 448)
     want = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     assert np.array_equal(oe.encode(x), want)
+
+
+def test_e8m0_decode_agrees_with_torch_float8_e8m0fnu():
+    """torch's float8_e8m0fnu (CPU) decodes the same OCP MX scale type."""
+    torch = pytest.importorskip("torch")
+    from oracle import ue8m0 as ou
+    if not hasattr(torch, "float8_e8m0fnu"):
+        pytest.skip("torch lacks float8_e8m0fnu")
+    b = np.arange(256, dtype=np.uint8)
+    d = ou.e8m0_decode(b)
+    t = torch.from_numpy(b.copy()).view(torch.float8_e8m0fnu).double().numpy()
+    assert np.all((d == t) | (np.isnan(d) & np.isnan(t)))
