@@ -14,10 +14,16 @@ buffer (inputs and preallocated outputs):
     fp8_block_gemm(x_q, x_scale, w_q, w_scale, y)
     fp8_grouped_block_gemm(x_q, x_scale, w_q, w_scale, offsets, y)
 
-Convenience wrappers allocate the outputs:
+and their power-of-two-scale twins (scales as E8M0 bytes, uint8 or
+torch.float8_e8m0fnu tensors): fp8_weight_block_quant_ue8m0,
+fp8_act_quant_group_ue8m0, fp8_block_gemm_ue8m0, fp8_grouped_block_gemm_ue8m0.
 
-    weight_block_quant(w) -> (w_q uint8 [N,K], w_scale fp32 [ceil(N/128), K/128])
-    act_quant_group(x)    -> (x_q uint8 [M,K], x_scale fp32 [M, K/128])
+Convenience wrappers allocate the outputs; ``scale_fmt`` is "float" (fp32
+scales) or "ue8m0" (E8M0 bytes), and the GEMMs pick the path from the scale
+tensors' dtype:
+
+    weight_block_quant(w, scale_fmt) -> (w_q uint8 [N,K], w_scale [ceil(N/128), K/128])
+    act_quant_group(x, scale_fmt)    -> (x_q uint8 [M,K], x_scale [M, K/128])
     block_gemm(x_q, x_scale, w_q, w_scale) -> y bf16 [M,N]
     grouped_block_gemm(x_q, x_scale, w_q, w_scale, offsets) -> y bf16 [sum M_e, N]
     linear(x, w_q, w_scale) -> y bf16 [M,N]   (dynamic act quant, then GEMM)
@@ -32,8 +38,9 @@ import torch
 __all__ = [
     "Fp8BlkError", "BLOCK", "lib_path", "load_library", "status_string",
     "fp8_weight_block_quant", "fp8_act_quant_group", "fp8_block_gemm",
-    "fp8_grouped_block_gemm", "weight_block_quant", "act_quant_group", "block_gemm",
-    "grouped_block_gemm", "linear",
+    "fp8_grouped_block_gemm", "fp8_weight_block_quant_ue8m0", "fp8_act_quant_group_ue8m0",
+    "fp8_block_gemm_ue8m0", "fp8_grouped_block_gemm_ue8m0", "weight_block_quant",
+    "act_quant_group", "block_gemm", "grouped_block_gemm", "linear", "SCALE_FMTS",
 ]
 
 BLOCK = 128
@@ -74,6 +81,10 @@ def load_library() -> ctypes.CDLL:
         "fp8_act_quant_group": [vp, i64, i64, vp, vp, vp],
         "fp8_block_gemm": [vp, vp, vp, vp, i64, i64, i64, vp, vp],
         "fp8_grouped_block_gemm": [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp, vp],
+        "fp8_weight_block_quant_ue8m0": [vp, i64, i64, vp, vp, vp],
+        "fp8_act_quant_group_ue8m0": [vp, i64, i64, vp, vp, vp],
+        "fp8_block_gemm_ue8m0": [vp, vp, vp, vp, i64, i64, i64, vp, vp],
+        "fp8_grouped_block_gemm_ue8m0": [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp, vp],
     }
     for name, args in sigs.items():
         fn = getattr(lib, name)
@@ -132,31 +143,36 @@ def _shape_eq(t, shape, name):
 # --------------------------------------------------------------------------
 # low-level entry points (same names as the C ABI)
 
-def fp8_weight_block_quant(w, w_q, w_scale):
+_F32 = (torch.float32,)
+_E8M0 = (torch.uint8,) + ((torch.float8_e8m0fnu,) if hasattr(torch, "float8_e8m0fnu") else ())
+SCALE_FMTS = ("float", "ue8m0")
+
+
+def _weight_quant(cname, sdt, w, w_q, w_scale):
     _need(w, "w", (torch.bfloat16,), 2)
     N, K = w.shape
-    _need(w_q, "w_q", _CODES); _need(w_scale, "w_scale", (torch.float32,))
+    _need(w_q, "w_q", _CODES); _need(w_scale, "w_scale", sdt)
     _shape_eq(w_q, (N, K), "w_q")
     if K % BLOCK == 0:
         _shape_eq(w_scale, (-(-N // BLOCK), K // BLOCK), "w_scale")
-    _check(load_library().fp8_weight_block_quant(_ptr(w), N, K, _ptr(w_q), _ptr(w_scale), _stream()),
-           "fp8_weight_block_quant")
+    _check(getattr(load_library(), cname)(_ptr(w), N, K, _ptr(w_q), _ptr(w_scale), _stream()),
+           cname)
 
 
-def fp8_act_quant_group(x, x_q, x_scale):
+def _act_quant(cname, sdt, x, x_q, x_scale):
     _need(x, "x", (torch.bfloat16,), 2)
     M, K = x.shape
-    _need(x_q, "x_q", _CODES); _need(x_scale, "x_scale", (torch.float32,))
+    _need(x_q, "x_q", _CODES); _need(x_scale, "x_scale", sdt)
     _shape_eq(x_q, (M, K), "x_q")
     if K % BLOCK == 0:
         _shape_eq(x_scale, (M, K // BLOCK), "x_scale")
-    _check(load_library().fp8_act_quant_group(_ptr(x), M, K, _ptr(x_q), _ptr(x_scale), _stream()),
-           "fp8_act_quant_group")
+    _check(getattr(load_library(), cname)(_ptr(x), M, K, _ptr(x_q), _ptr(x_scale), _stream()),
+           cname)
 
 
-def fp8_block_gemm(x_q, x_scale, w_q, w_scale, y):
+def _gemm(cname, sdt, x_q, x_scale, w_q, w_scale, y):
     _need(x_q, "x_q", _CODES, 2); _need(w_q, "w_q", _CODES, 2)
-    _need(x_scale, "x_scale", (torch.float32,), 2); _need(w_scale, "w_scale", (torch.float32,), 2)
+    _need(x_scale, "x_scale", sdt, 2); _need(w_scale, "w_scale", sdt, 2)
     _need(y, "y", (torch.bfloat16,), 2)
     M, K = x_q.shape
     N = w_q.shape[0]
@@ -166,13 +182,13 @@ def fp8_block_gemm(x_q, x_scale, w_q, w_scale, y):
         _shape_eq(x_scale, (M, K // BLOCK), "x_scale")
         _shape_eq(w_scale, (-(-N // BLOCK), K // BLOCK), "w_scale")
     _shape_eq(y, (M, N), "y")
-    _check(load_library().fp8_block_gemm(_ptr(x_q), _ptr(x_scale), _ptr(w_q), _ptr(w_scale),
-                                         M, N, K, _ptr(y), _stream()), "fp8_block_gemm")
+    _check(getattr(load_library(), cname)(_ptr(x_q), _ptr(x_scale), _ptr(w_q), _ptr(w_scale),
+                                          M, N, K, _ptr(y), _stream()), cname)
 
 
-def fp8_grouped_block_gemm(x_q, x_scale, w_q, w_scale, offsets, y):
+def _grouped(cname, sdt, x_q, x_scale, w_q, w_scale, offsets, y):
     _need(x_q, "x_q", _CODES, 2); _need(w_q, "w_q", _CODES, 3)
-    _need(x_scale, "x_scale", (torch.float32,), 2); _need(w_scale, "w_scale", (torch.float32,), 3)
+    _need(x_scale, "x_scale", sdt, 2); _need(w_scale, "w_scale", sdt, 3)
     _need(offsets, "offsets", (torch.int32,), 1); _need(y, "y", (torch.bfloat16,), 2)
     total, K = x_q.shape
     E, N, K2 = w_q.shape
@@ -184,44 +200,89 @@ def fp8_grouped_block_gemm(x_q, x_scale, w_q, w_scale, offsets, y):
         _shape_eq(x_scale, (total, K // BLOCK), "x_scale")
         _shape_eq(w_scale, (E, -(-N // BLOCK), K // BLOCK), "w_scale")
     _shape_eq(y, (total, N), "y")
-    _check(load_library().fp8_grouped_block_gemm(
+    _check(getattr(load_library(), cname)(
         _ptr(x_q), _ptr(x_scale), _ptr(w_q), _ptr(w_scale), _ptr(offsets), E, total, N, K,
-        _ptr(y), _stream()), "fp8_grouped_block_gemm")
+        _ptr(y), _stream()), cname)
+
+
+def fp8_weight_block_quant(w, w_q, w_scale):
+    _weight_quant("fp8_weight_block_quant", _F32, w, w_q, w_scale)
+
+
+def fp8_act_quant_group(x, x_q, x_scale):
+    _act_quant("fp8_act_quant_group", _F32, x, x_q, x_scale)
+
+
+def fp8_block_gemm(x_q, x_scale, w_q, w_scale, y):
+    _gemm("fp8_block_gemm", _F32, x_q, x_scale, w_q, w_scale, y)
+
+
+def fp8_grouped_block_gemm(x_q, x_scale, w_q, w_scale, offsets, y):
+    _grouped("fp8_grouped_block_gemm", _F32, x_q, x_scale, w_q, w_scale, offsets, y)
+
+
+def fp8_weight_block_quant_ue8m0(w, w_q, w_scale):
+    _weight_quant("fp8_weight_block_quant_ue8m0", _E8M0, w, w_q, w_scale)
+
+
+def fp8_act_quant_group_ue8m0(x, x_q, x_scale):
+    _act_quant("fp8_act_quant_group_ue8m0", _E8M0, x, x_q, x_scale)
+
+
+def fp8_block_gemm_ue8m0(x_q, x_scale, w_q, w_scale, y):
+    _gemm("fp8_block_gemm_ue8m0", _E8M0, x_q, x_scale, w_q, w_scale, y)
+
+
+def fp8_grouped_block_gemm_ue8m0(x_q, x_scale, w_q, w_scale, offsets, y):
+    _grouped("fp8_grouped_block_gemm_ue8m0", _E8M0, x_q, x_scale, w_q, w_scale, offsets, y)
 
 
 # --------------------------------------------------------------------------
 # convenience wrappers (allocate outputs with torch.empty)
 
-def weight_block_quant(w):
+def _scale_dtype(scale_fmt):
+    if scale_fmt not in SCALE_FMTS:
+        raise ValueError(f"scale_fmt must be one of {SCALE_FMTS}, got {scale_fmt!r}")
+    return torch.float32 if scale_fmt == "float" else torch.uint8
+
+
+def _is_e8m0(t):
+    return t.dtype in _E8M0
+
+
+def weight_block_quant(w, scale_fmt="float"):
     N, K = w.shape
     w_q = torch.empty((N, K), dtype=torch.uint8, device=w.device)
-    w_s = torch.empty((-(-N // BLOCK), max(K // BLOCK, 0)), dtype=torch.float32, device=w.device)
-    fp8_weight_block_quant(w, w_q, w_s)
+    w_s = torch.empty((-(-N // BLOCK), max(K // BLOCK, 0)), dtype=_scale_dtype(scale_fmt),
+                      device=w.device)
+    (fp8_weight_block_quant if scale_fmt == "float" else fp8_weight_block_quant_ue8m0)(w, w_q, w_s)
     return w_q, w_s
 
 
-def act_quant_group(x):
+def act_quant_group(x, scale_fmt="float"):
     M, K = x.shape
     x_q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
-    x_s = torch.empty((M, max(K // BLOCK, 0)), dtype=torch.float32, device=x.device)
-    fp8_act_quant_group(x, x_q, x_s)
+    x_s = torch.empty((M, max(K // BLOCK, 0)), dtype=_scale_dtype(scale_fmt), device=x.device)
+    (fp8_act_quant_group if scale_fmt == "float" else fp8_act_quant_group_ue8m0)(x, x_q, x_s)
     return x_q, x_s
 
 
 def block_gemm(x_q, x_scale, w_q, w_scale):
     y = torch.empty((x_q.shape[0], w_q.shape[0]), dtype=torch.bfloat16, device=x_q.device)
-    fp8_block_gemm(x_q, x_scale, w_q, w_scale, y)
+    (fp8_block_gemm_ue8m0 if _is_e8m0(w_scale) else fp8_block_gemm)(x_q, x_scale, w_q, w_scale, y)
     return y
 
 
 def grouped_block_gemm(x_q, x_scale, w_q, w_scale, offsets):
     y = torch.empty((x_q.shape[0], w_q.shape[1]), dtype=torch.bfloat16, device=x_q.device)
-    fp8_grouped_block_gemm(x_q, x_scale, w_q, w_scale, offsets, y)
+    fn = fp8_grouped_block_gemm_ue8m0 if _is_e8m0(w_scale) else fp8_grouped_block_gemm
+    fn(x_q, x_scale, w_q, w_scale, offsets, y)
     return y
 
 
 def linear(x, w_q, w_scale):
     """The FP8 linear layer: dynamic per-token-group quantization of x, then
-    the block-scaled GEMM, back to back on the current stream."""
-    x_q, x_s = act_quant_group(x)
+    the block-scaled GEMM, back to back on the current stream.  E8M0 weight
+    scales select power-of-two activation scales as well."""
+    x_q, x_s = act_quant_group(x, "ue8m0" if _is_e8m0(w_scale) else "float")
     return block_gemm(x_q, x_s, w_q, w_scale)

@@ -96,6 +96,28 @@ __device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float 
   return (uint32_t)w;
 }
 
+// Power-of-two (E8M0) scales: the exponent e of a set is the smallest
+// integer >= -127 with amax <= 448 * 2^e, taken from amax's bits exactly.
+// With amax = (1 + f) * 2^E (f from the fraction field) and 448 = 1.75 * 2^8,
+// e = E - 8 when 1 + f <= 1.75 and E - 7 otherwise; amax below 2^-126
+// (zero or subnormal) gives e <= -134, held at -127.  For finite amax
+// e <= 120, so the scale byte e + 127 is never the NaN byte 0xFF.
+__device__ __forceinline__ int e8m0_exponent(float amax) {
+  const uint32_t u = __float_as_uint(amax);
+  const int be = (int)(u >> 23);
+  if (be == 0) return -127;
+  const int e = be - 135 + ((u & 0x7fffffu) > 0x600000u ? 1 : 0);
+  return e < -127 ? -127 : e;
+}
+
+// 2^-e as fp32 for e in [-127, 120] (biased exponent 127 - e in [7, 254]).
+// x * e8m0_inv_scale(e) is exact for every bf16 x whose quotient is above
+// fp32's normal range floor; below it the quotient's E4M3 code is a signed
+// zero either way.
+__device__ __forceinline__ float e8m0_inv_scale(int e) {
+  return __uint_as_float((uint32_t)(127 - e) << 23);
+}
+
 // fp32 -> bf16 bits, round to nearest even (finite inputs).
 __device__ __forceinline__ uint32_t bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);

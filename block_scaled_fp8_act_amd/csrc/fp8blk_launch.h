@@ -10,10 +10,21 @@ hipError_t launch_act_quant(const void *x, int64_t M, int64_t K, void *q, float 
                             hipStream_t stream);
 hipError_t launch_weight_quant(const void *w, int64_t N, int64_t K, void *q, float *s,
                                hipStream_t stream);
+hipError_t launch_act_quant_e8m0(const void *x, int64_t M, int64_t K, void *q, uint8_t *s,
+                                 hipStream_t stream);
+hipError_t launch_weight_quant_e8m0(const void *w, int64_t N, int64_t K, void *q, uint8_t *s,
+                                    hipStream_t stream);
 hipError_t launch_block_gemm(const void *xq, const float *xs, const void *wq, const float *ws,
                              int64_t M, int64_t N, int64_t K, void *y, hipStream_t stream);
 hipError_t launch_grouped_gemm(const void *xq, const float *xs, const void *wq, const float *ws,
                                const int32_t *offsets, int32_t E, int64_t total_M, int64_t N,
                                int64_t K, void *y, hipStream_t stream);
+hipError_t launch_block_gemm_e8m0(const void *xq, const uint8_t *xs, const void *wq,
+                                  const uint8_t *ws, int64_t M, int64_t N, int64_t K, void *y,
+                                  hipStream_t stream);
+hipError_t launch_grouped_gemm_e8m0(const void *xq, const uint8_t *xs, const void *wq,
+                                    const uint8_t *ws, const int32_t *offsets, int32_t E,
+                                    int64_t total_M, int64_t N, int64_t K, void *y,
+                                    hipStream_t stream);
 
 }  // namespace fp8blk

@@ -14,7 +14,15 @@
 //
 // Three configurations: 256x256 and 128x128 LDS-staged tiles for M > 64,
 // and a weight-streaming split-K kernel for M <= 64 (decode).
+//
+// With power-of-two scales stored as E8M0 bytes (the "UE8M0 scale format"
+// section of the same page) the scale pair is applied by the matrix core
+// itself: v_mfma_scale_f32_16x16x128_f8f6f4 multiplies each product by
+// 2^(sa-127) * 2^(sb-127), sa taken per A row and sb per B column (each per
+// 32 K values; a 128-block scale is simply the same byte for all four), and
+// adds into the fp32 accumulator -- no per-block partials, no promotion FMAs.
 #include <algorithm>
+#include <type_traits>
 
 #include "fp8blk_device.h"
 #include "fp8blk_launch.h"
@@ -58,6 +66,10 @@ struct Tile {
     uint8_t b[2][TN * 128];
     float as[2][TM];
     float ws[2][64];  // weight-block scales of the tile's (<= 2) column blocks
+  };
+  struct SmemCodes {  // E8M0 scales travel in registers
+    uint8_t a[2][TM * 128];
+    uint8_t b[2][TN * 128];
   };
 };
 
@@ -266,6 +278,152 @@ __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ A,
     }
 }
 
+// The same tile with E8M0 scales.  A: x_q at the tile's first row; As: its
+// scale bytes (row stride KB); B, Bs: w_q and the scale-byte row of the
+// tile's first 128-column block; the rest as for gemm_tile.  Each lane loads
+// the scale bytes of its FM A-operand rows (row wm*FM*16 + 16*mi + lane%16)
+// and of its wave's column block for K block kb+1 together with that
+// stage's DMA; they are consumed as the MFMAs' scale operands.
+template <int WM, int WN, int FM>
+__device__ __forceinline__ void gemm_tile_mx(const uint8_t *__restrict__ A,
+                                             const uint8_t *__restrict__ As, int rows_a,
+                                             const uint8_t *__restrict__ B,
+                                             const uint8_t *__restrict__ Bs, int rows_b, int64_t K,
+                                             uint16_t *__restrict__ Y, int64_t ldy,
+                                             typename Tile<WM, WN, FM>::SmemCodes &sm) {
+  using T = Tile<WM, WN, FM>;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int KB = (int)(K / 128);
+  const int r16 = lane & 15;
+
+  uint32_t oa[T::kDmaA];
+  uint32_t ob[T::kDmaB];
+#pragma unroll
+  for (int i = 0; i < T::kDmaA; ++i) {
+    const int row = 8 * (T::kDmaA * wave + i) + (lane >> 3);
+    const int lchunk = (lane & 7) ^ swz_f(row);
+    oa[i] = (uint32_t)min(row, rows_a - 1) * (uint32_t)K + lchunk * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < T::kDmaB; ++i) {
+    const int row = 8 * (T::kDmaB * wave + i) + (lane >> 3);
+    const int lchunk = (lane & 7) ^ swz_f(row);
+    ob[i] = (uint32_t)min(row, rows_b - 1) * (uint32_t)K + lchunk * 16;
+  }
+  // scale-byte offsets (< 256 * KB) of this lane's A rows; the wave's 64
+  // columns lie in one 128-column block (clamped to the last one present)
+  uint32_t osa[FM];
+#pragma unroll
+  for (int mi = 0; mi < FM; ++mi)
+    osa[mi] = (uint32_t)min(wm * FM * 16 + mi * 16 + r16, rows_a - 1) * (uint32_t)KB;
+  const uint8_t *pbs = Bs + (int64_t)min((wn * 64) / 128, (rows_b + 127) / 128 - 1) * KB;
+
+  auto issue = [&](int kb, int st) {
+    const uint8_t *ak = A + (int64_t)kb * 128;
+    const uint8_t *bk = B + (int64_t)kb * 128;
+#pragma unroll
+    for (int i = 0; i < T::kDmaA; ++i)
+      lds_dma16(ak + oa[i], sm.a[st] + (T::kDmaA * wave + i) * 1024);
+#pragma unroll
+    for (int i = 0; i < T::kDmaB; ++i)
+      lds_dma16(bk + ob[i], sm.b[st] + (T::kDmaB * wave + i) * 1024);
+  };
+  int sa[FM], sb;
+  auto load_scales = [&](int kb, int *sa_, int &sb_) {
+#pragma unroll
+    for (int mi = 0; mi < FM; ++mi) sa_[mi] = As[osa[mi] + kb];
+    sb_ = pbs[kb];
+  };
+
+  v4f acc[FM][4];
+#pragma unroll
+  for (int mi = 0; mi < FM; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+  issue(0, 0);
+  load_scales(0, sa, sb);
+  asm volatile("" ::"s"(Y));  // no scalar load left in flight (see gemm_tile)
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  const int c0 = (lane >> 4) * 2;
+  const int arow0 = wm * FM * 16 + r16;
+  const int brow0 = wn * 64 + r16;
+
+  for (int kb = 0; kb < KB; ++kb) {
+    const int st = kb & 1;
+    const uint8_t *sa_lds = sm.a[st];
+    const uint8_t *sb_lds = sm.b[st];
+    auto read_a = [&](int mi) {
+      const int row = arow0 + mi * 16;
+      return frag_from(*reinterpret_cast<const uint4 *>(sa_lds + swz(row, c0)),
+                       *reinterpret_cast<const uint4 *>(sa_lds + swz(row, c0 + 1)));
+    };
+    v8i bfr[4];
+    bfr[0] = frag_from(*reinterpret_cast<const uint4 *>(sb_lds + swz(brow0, c0)),
+                       *reinterpret_cast<const uint4 *>(sb_lds + swz(brow0, c0 + 1)));
+    v8i af = read_a(0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ni = 1; ni < 4; ++ni) {
+      const int row = brow0 + ni * 16;
+      bfr[ni] = frag_from(*reinterpret_cast<const uint4 *>(sb_lds + swz(row, c0)),
+                          *reinterpret_cast<const uint4 *>(sb_lds + swz(row, c0 + 1)));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    v8i afn = read_a(1);
+    __builtin_amdgcn_sched_barrier(0);
+    v8i afn2 = afn;
+    int san[FM], sbn = sb;
+#pragma unroll
+    for (int mi = 0; mi < FM; ++mi) san[mi] = sa[mi];
+#pragma unroll
+    for (int mi = 0; mi < FM; ++mi) {
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni) {
+        acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            af, bfr[ni], acc[mi][ni], 0, 0, 0, sa[mi], 0, sb);
+        __builtin_amdgcn_sched_barrier(0);
+        if (ni == 0 && mi + 2 < FM) {
+          afn2 = read_a(mi + 2);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      if (mi == 0) {
+        if (kb + 1 < KB) {
+          issue(kb + 1, st ^ 1);
+          load_scales(kb + 1, san, sbn);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      af = afn;
+      afn = afn2;
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+#pragma unroll
+    for (int mi = 0; mi < FM; ++mi) sa[mi] = san[mi];
+    sb = sbn;
+  }
+
+#pragma unroll
+  for (int mi = 0; mi < FM; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) {
+      const int col = wn * 64 + ni * 16 + r16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = wm * FM * 16 + mi * 16 + 4 * (lane >> 4) + r;
+        if (row < rows_a && col < rows_b)
+          Y[(int64_t)row * ldy + col] = (uint16_t)bf16_rne(acc[mi][ni][r]);
+      }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Small-M ("decode") configuration, M <= 64: the GEMM is a stream of W from
 // HBM (arithmetic intensity 2..32 flop/byte).  One workgroup owns a slab of
@@ -282,14 +440,18 @@ constexpr int kDecThreads = kDecWaves * 64;
 constexpr int kDecMaxM = 64;
 constexpr int kDecMaxScaleBytes = 32 * 1024;  // x_scale staging limit (KB * MF * 16 * 4)
 
-template <int MF>
+// S = float: fp32 scales, promoted per K block with FMAs as in gemm_tile;
+// S = uint8_t: E8M0 scale bytes, loaded with the operands and applied by the
+// matrix core (nothing staged in LDS but the final partials).
+template <int MF, typename S>
 __global__ __launch_bounds__(kDecThreads) void decode_gemm_kernel(
-    const uint8_t *__restrict__ xq, const float *__restrict__ xs, const uint8_t *__restrict__ wq,
-    const float *__restrict__ ws, int M, int64_t N, int64_t K, uint16_t *__restrict__ y) {
+    const uint8_t *__restrict__ xq, const S *__restrict__ xs, const uint8_t *__restrict__ wq,
+    const S *__restrict__ ws, int M, int64_t N, int64_t K, uint16_t *__restrict__ y) {
+  constexpr bool MX = std::is_same<S, uint8_t>::value;
   constexpr int R = MF * 16;                  // staged rows
   constexpr int U = 4 / MF;                   // K blocks in flight per wave
   extern __shared__ __align__(16) float dsm[];
-  float *s_as = dsm;                          // [KB][R]
+  float *s_as = dsm;                          // [KB][R] (fp32 scales only)
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -302,34 +464,47 @@ __global__ __launch_bounds__(kDecThreads) void decode_gemm_kernel(
   const int kc = (lane >> 4) * 32;  // this lane's 32 K bytes within the block
   const uint8_t *pb = wq + (n0 + min(r16, rows_b - 1)) * K + kc;
   const uint8_t *pa[MF];
+  const S *psa[MF];                 // E8M0: scale row of this lane's A-operand row
 #pragma unroll
-  for (int f = 0; f < MF; ++f) pa[f] = xq + (int64_t)min(f * 16 + r16, M - 1) * K + kc;
-  const float *pws = ws + (n0 / 128) * KB;
+  for (int f = 0; f < MF; ++f) {
+    pa[f] = xq + (int64_t)min(f * 16 + r16, M - 1) * K + kc;
+    psa[f] = xs + (int64_t)min(f * 16 + r16, M - 1) * KB;
+  }
+  const S *pws = ws + (n0 / 128) * KB;
   const int nmine = wave < KB ? (KB - wave + kDecWaves - 1) / kDecWaves : 0;
 
   uint4 bw[U][2];
   v8i af[U][MF];
+  int sa[U][MF], sb[U];
   auto load = [&](int j0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (j0 + u < nmine) {
-        const int64_t ko = (int64_t)(wave + kDecWaves * (j0 + u)) * 128;
+        const int kb = wave + kDecWaves * (j0 + u);
+        const int64_t ko = (int64_t)kb * 128;
         bw[u][0] = *reinterpret_cast<const uint4 *>(pb + ko);
         bw[u][1] = *reinterpret_cast<const uint4 *>(pb + ko + 16);
 #pragma unroll
         for (int f = 0; f < MF; ++f)
           af[u][f] = frag_from(*reinterpret_cast<const uint4 *>(pa[f] + ko),
                                *reinterpret_cast<const uint4 *>(pa[f] + ko + 16));
+        if constexpr (MX) {
+#pragma unroll
+          for (int f = 0; f < MF; ++f) sa[u][f] = psa[f][kb];
+          sb[u] = pws[kb];
+        }
       }
     }
   };
   load(0);
 
-  for (int i = t; i < KB * R; i += kDecThreads) {
-    const int kb = i / R, m = i % R;
-    s_as[i] = xs[(int64_t)min(m, M - 1) * KB + kb];
+  if constexpr (!MX) {
+    for (int i = t; i < KB * R; i += kDecThreads) {
+      const int kb = i / R, m = i % R;
+      s_as[i] = xs[(int64_t)min(m, M - 1) * KB + kb];
+    }
+    __syncthreads();
   }
-  __syncthreads();
 
   v4f acc[MF];
 #pragma unroll
@@ -340,18 +515,25 @@ __global__ __launch_bounds__(kDecThreads) void decode_gemm_kernel(
     for (int u = 0; u < U; ++u) {
       if (j0 + u < nmine) {
         const int kb = wave + kDecWaves * (j0 + u);
-        const float wsc = pws[kb];
         const v8i bf = frag_from(bw[u][0], bw[u][1]);
+        if constexpr (MX) {
 #pragma unroll
-        for (int f = 0; f < MF; ++f) {
-          const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              af[u][f], bf, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 0, 0, 0);
-          const float4 s4 =
-              *reinterpret_cast<const float4 *>(&s_as[kb * R + f * 16 + 4 * (lane >> 4)]);
-          acc[f][0] = fmaf(p[0], s4.x * wsc, acc[f][0]);
-          acc[f][1] = fmaf(p[1], s4.y * wsc, acc[f][1]);
-          acc[f][2] = fmaf(p[2], s4.z * wsc, acc[f][2]);
-          acc[f][3] = fmaf(p[3], s4.w * wsc, acc[f][3]);
+          for (int f = 0; f < MF; ++f)
+            acc[f] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[u][f], bf, acc[f], 0, 0,
+                                                                      0, sa[u][f], 0, sb[u]);
+        } else {
+          const float wsc = pws[kb];
+#pragma unroll
+          for (int f = 0; f < MF; ++f) {
+            const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                af[u][f], bf, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 0, 0, 0);
+            const float4 s4 =
+                *reinterpret_cast<const float4 *>(&s_as[kb * R + f * 16 + 4 * (lane >> 4)]);
+            acc[f][0] = fmaf(p[0], s4.x * wsc, acc[f][0]);
+            acc[f][1] = fmaf(p[1], s4.y * wsc, acc[f][1]);
+            acc[f][2] = fmaf(p[2], s4.z * wsc, acc[f][2]);
+            acc[f][3] = fmaf(p[3], s4.w * wsc, acc[f][3]);
+          }
         }
       }
     }
@@ -377,13 +559,16 @@ __global__ __launch_bounds__(kDecThreads) void decode_gemm_kernel(
   }
 }
 
-template <int MF>
-static hipError_t launch_decode(const void *xq, const float *xs, const void *wq, const float *ws,
+template <int MF, typename S>
+static hipError_t launch_decode(const void *xq, const S *xs, const void *wq, const S *ws,
                                 int64_t M, int64_t N, int64_t K, void *y, hipStream_t stream) {
   const int64_t KB = K / 128;
-  const size_t lds = std::max((size_t)KB * MF * 16 * 4, (size_t)kDecWaves * MF * 64 * 16);
-  hipLaunchKernelGGL(decode_gemm_kernel<MF>, dim3((unsigned)((N + 15) / 16)), dim3(kDecThreads),
-                     lds, stream, static_cast<const uint8_t *>(xq), xs,
+  const size_t part = (size_t)kDecWaves * MF * 64 * 16;
+  const size_t lds = std::is_same<S, uint8_t>::value
+                         ? part
+                         : std::max((size_t)KB * MF * 16 * 4, part);
+  hipLaunchKernelGGL((decode_gemm_kernel<MF, S>), dim3((unsigned)((N + 15) / 16)),
+                     dim3(kDecThreads), lds, stream, static_cast<const uint8_t *>(xq), xs,
                      static_cast<const uint8_t *>(wq), ws, (int)M, N, K,
                      static_cast<uint16_t *>(y));
   return hipGetLastError();
@@ -406,20 +591,40 @@ __device__ __forceinline__ void tile_coords(int bid, int total, int tiles_m, int
   tn = in_group / gsz;
 }
 
-template <int WM, int WN, int FM>
+// One tile with either scale type: S = float -> gemm_tile, S = uint8_t
+// (E8M0 bytes) -> gemm_tile_mx.
+template <int WM, int WN, int FM, typename S>
+struct TileSmem {
+  using type = typename std::conditional<std::is_same<S, uint8_t>::value,
+                                         typename Tile<WM, WN, FM>::SmemCodes,
+                                         typename Tile<WM, WN, FM>::Smem>::type;
+};
+
+template <int WM, int WN, int FM, typename S>
+__device__ __forceinline__ void run_tile(const uint8_t *A, const S *As, int rows_a,
+                                         const uint8_t *B, const S *Bs, int rows_b, int64_t K,
+                                         uint16_t *Y, int64_t ldy,
+                                         typename TileSmem<WM, WN, FM, S>::type &sm) {
+  if constexpr (std::is_same<S, uint8_t>::value)
+    gemm_tile_mx<WM, WN, FM>(A, As, rows_a, B, Bs, rows_b, K, Y, ldy, sm);
+  else
+    gemm_tile<WM, WN, FM>(A, As, rows_a, B, Bs, rows_b, K, Y, ldy, sm);
+}
+
+template <int WM, int WN, int FM, typename S>
 __global__ __launch_bounds__(WM * WN * 64) void block_gemm_kernel(
-    const uint8_t *__restrict__ xq, const float *__restrict__ xs, const uint8_t *__restrict__ wq,
-    const float *__restrict__ ws, int64_t M, int64_t N, int64_t K, uint16_t *__restrict__ y,
+    const uint8_t *__restrict__ xq, const S *__restrict__ xs, const uint8_t *__restrict__ wq,
+    const S *__restrict__ ws, int64_t M, int64_t N, int64_t K, uint16_t *__restrict__ y,
     int tiles_m, int tiles_n) {
   using T = Tile<WM, WN, FM>;
-  __shared__ typename T::Smem sm;
+  __shared__ typename TileSmem<WM, WN, FM, S>::type sm;
   int tm, tn;
   tile_coords(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * T::TM, n0 = (int64_t)tn * T::TN;
   const int64_t KB = K / 128;
-  gemm_tile<WM, WN, FM>(xq + m0 * K, xs + m0 * KB, (int)min<int64_t>(T::TM, M - m0), wq + n0 * K,
-                        ws + (n0 / 128) * KB, (int)min<int64_t>(T::TN, N - n0), K, y + m0 * N + n0,
-                        N, sm);
+  run_tile<WM, WN, FM, S>(xq + m0 * K, xs + m0 * KB, (int)min<int64_t>(T::TM, M - m0),
+                          wq + n0 * K, ws + (n0 / 128) * KB, (int)min<int64_t>(T::TN, N - n0), K,
+                          y + m0 * N + n0, N, sm);
 }
 
 // Grouped variant.  The logical m-tiles of all experts are numbered
@@ -427,13 +632,13 @@ __global__ __launch_bounds__(WM * WN * 64) void block_gemm_kernel(
 // the upper bound ceil(total_M/TM) + E, and workgroups past the real count
 // exit at once.  Offsets are read on the device (no host sync) and clamped
 // to [0, total_M].
-template <int WM, int WN, int FM>
+template <int WM, int WN, int FM, typename S>
 __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(
-    const uint8_t *__restrict__ xq, const float *__restrict__ xs, const uint8_t *__restrict__ wq,
-    const float *__restrict__ ws, const int32_t *__restrict__ offsets, int E, int64_t total_M,
+    const uint8_t *__restrict__ xq, const S *__restrict__ xs, const uint8_t *__restrict__ wq,
+    const S *__restrict__ ws, const int32_t *__restrict__ offsets, int E, int64_t total_M,
     int64_t N, int64_t K, uint16_t *__restrict__ y, int tiles_n) {
   using T = Tile<WM, WN, FM>;
-  __shared__ typename T::Smem sm;
+  __shared__ typename TileSmem<WM, WN, FM, S>::type sm;
   const int tn = blockIdx.x % tiles_n;
   int mt = blockIdx.x / tiles_n;
   int64_t r0 = 0, r1 = 0;
@@ -454,49 +659,79 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(
   const int64_t n0 = (int64_t)tn * T::TN;
   const int64_t KB = K / 128;
   const int64_t NB = (N + 127) / 128;
-  gemm_tile<WM, WN, FM>(xq + r0 * K, xs + r0 * KB, (int)min<int64_t>(T::TM, r1 - r0),
-                        wq + (int64_t)e * N * K + n0 * K, ws + ((int64_t)e * NB + n0 / 128) * KB,
-                        (int)min<int64_t>(T::TN, N - n0), K, y + r0 * N + n0, N, sm);
+  run_tile<WM, WN, FM, S>(xq + r0 * K, xs + r0 * KB, (int)min<int64_t>(T::TM, r1 - r0),
+                          wq + (int64_t)e * N * K + n0 * K,
+                          ws + ((int64_t)e * NB + n0 / 128) * KB,
+                          (int)min<int64_t>(T::TN, N - n0), K, y + r0 * N + n0, N, sm);
 }
 
-template <int WM, int WN, int FM>
-static hipError_t launch_tiled(const void *xq, const float *xs, const void *wq, const float *ws,
+template <int WM, int WN, int FM, typename S>
+static hipError_t launch_tiled(const void *xq, const S *xs, const void *wq, const S *ws,
                                int64_t M, int64_t N, int64_t K, void *y, hipStream_t stream) {
   using T = Tile<WM, WN, FM>;
   const int tm = (int)((M + T::TM - 1) / T::TM), tn = (int)((N + T::TN - 1) / T::TN);
-  hipLaunchKernelGGL((block_gemm_kernel<WM, WN, FM>), dim3((unsigned)(tm * tn)), dim3(T::kThreads),
-                     0, stream, static_cast<const uint8_t *>(xq), xs,
+  hipLaunchKernelGGL((block_gemm_kernel<WM, WN, FM, S>), dim3((unsigned)(tm * tn)),
+                     dim3(T::kThreads), 0, stream, static_cast<const uint8_t *>(xq), xs,
                      static_cast<const uint8_t *>(wq), ws, M, N, K, static_cast<uint16_t *>(y),
                      tm, tn);
   return hipGetLastError();
 }
 
-hipError_t launch_block_gemm(const void *xq, const float *xs, const void *wq, const float *ws,
-                             int64_t M, int64_t N, int64_t K, void *y, hipStream_t stream) {
+// Configuration choice (both scale types): the decode kernel for M <= 64
+// (fp32 scales: while its LDS scale staging fits), 256x256 tiles when they
+// fill the chip (>= 192 tiles), 128x128 otherwise.
+template <typename S>
+static hipError_t dispatch_gemm(const void *xq, const S *xs, const void *wq, const S *ws,
+                                int64_t M, int64_t N, int64_t K, void *y, hipStream_t stream) {
   if (M <= kDecMaxM) {
     const int MF = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
-    if ((K / 128) * MF * 16 * 4 <= kDecMaxScaleBytes) {
-      if (MF == 1) return launch_decode<1>(xq, xs, wq, ws, M, N, K, y, stream);
-      if (MF == 2) return launch_decode<2>(xq, xs, wq, ws, M, N, K, y, stream);
-      return launch_decode<4>(xq, xs, wq, ws, M, N, K, y, stream);
+    if (std::is_same<S, uint8_t>::value || (K / 128) * MF * 16 * 4 <= kDecMaxScaleBytes) {
+      if (MF == 1) return launch_decode<1, S>(xq, xs, wq, ws, M, N, K, y, stream);
+      if (MF == 2) return launch_decode<2, S>(xq, xs, wq, ws, M, N, K, y, stream);
+      return launch_decode<4, S>(xq, xs, wq, ws, M, N, K, y, stream);
     }
   }
   const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
-  if (big_tiles >= 192) return launch_tiled<2, 4, 8>(xq, xs, wq, ws, M, N, K, y, stream);
-  return launch_tiled<2, 2, 4>(xq, xs, wq, ws, M, N, K, y, stream);
+  if (big_tiles >= 192) return launch_tiled<2, 4, 8, S>(xq, xs, wq, ws, M, N, K, y, stream);
+  return launch_tiled<2, 2, 4, S>(xq, xs, wq, ws, M, N, K, y, stream);
+}
+
+template <typename S>
+static hipError_t dispatch_grouped(const void *xq, const S *xs, const void *wq, const S *ws,
+                                   const int32_t *offsets, int32_t E, int64_t total_M, int64_t N,
+                                   int64_t K, void *y, hipStream_t stream) {
+  using T = Tile<2, 4, 8>;
+  const int64_t tiles_n = (N + T::TN - 1) / T::TN;
+  const int64_t tiles_m = (total_M + T::TM - 1) / T::TM + E;
+  hipLaunchKernelGGL((grouped_gemm_kernel<2, 4, 8, S>), dim3((unsigned)(tiles_m * tiles_n)),
+                     dim3(T::kThreads), 0, stream, static_cast<const uint8_t *>(xq), xs,
+                     static_cast<const uint8_t *>(wq), ws, offsets, (int)E, total_M, N, K,
+                     static_cast<uint16_t *>(y), (int)tiles_n);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_gemm(const void *xq, const float *xs, const void *wq, const float *ws,
+                             int64_t M, int64_t N, int64_t K, void *y, hipStream_t stream) {
+  return dispatch_gemm<float>(xq, xs, wq, ws, M, N, K, y, stream);
+}
+
+hipError_t launch_block_gemm_e8m0(const void *xq, const uint8_t *xs, const void *wq,
+                                  const uint8_t *ws, int64_t M, int64_t N, int64_t K, void *y,
+                                  hipStream_t stream) {
+  return dispatch_gemm<uint8_t>(xq, xs, wq, ws, M, N, K, y, stream);
 }
 
 hipError_t launch_grouped_gemm(const void *xq, const float *xs, const void *wq, const float *ws,
                                const int32_t *offsets, int32_t E, int64_t total_M, int64_t N,
                                int64_t K, void *y, hipStream_t stream) {
-  using T = Tile<2, 4, 8>;
-  const int64_t tiles_n = (N + T::TN - 1) / T::TN;
-  const int64_t tiles_m = (total_M + T::TM - 1) / T::TM + E;
-  hipLaunchKernelGGL((grouped_gemm_kernel<2, 4, 8>), dim3((unsigned)(tiles_m * tiles_n)),
-                     dim3(T::kThreads), 0, stream, static_cast<const uint8_t *>(xq), xs,
-                     static_cast<const uint8_t *>(wq), ws, offsets, (int)E, total_M, N, K,
-                     static_cast<uint16_t *>(y), (int)tiles_n);
-  return hipGetLastError();
+  return dispatch_grouped<float>(xq, xs, wq, ws, offsets, E, total_M, N, K, y, stream);
+}
+
+hipError_t launch_grouped_gemm_e8m0(const void *xq, const uint8_t *xs, const void *wq,
+                                    const uint8_t *ws, const int32_t *offsets, int32_t E,
+                                    int64_t total_M, int64_t N, int64_t K, void *y,
+                                    hipStream_t stream) {
+  return dispatch_grouped<uint8_t>(xq, xs, wq, ws, offsets, E, total_M, N, K, y, stream);
 }
 
 }  // namespace fp8blk

@@ -1,5 +1,6 @@
 // Activation (per token, per 128-channel group) and weight (per 128x128
-// block) quantizers to E4M3 with fp32 scales, for gfx950.
+// block) quantizers to E4M3, with fp32 scales or with power-of-two scales
+// stored as E8M0 bytes ("UE8M0 scale format"), for gfx950.
 //
 // Both apply one element map to a set of bf16 values sharing a scale
 // ("Fine-grained FP8" page of the transformers docs, introduction: weights
@@ -12,6 +13,11 @@
 // VALU work per element is kept small: the per-set division and reciprocal
 // are paid once per set, and each element costs one multiply, two FMAs and
 // half a packed conversion.
+//
+// E8M0 scales: the set's exponent e is the smallest integer >= -127 with
+// amax <= 448 * 2^e (the scale rounded up to a power of two, so no quotient
+// leaves E4M3's range), the stored byte is e + 127 and q = E4M3_RNE(x * 2^-e),
+// an exact product: one multiply and half a packed conversion per element.
 #include "fp8blk_device.h"
 #include "fp8blk_launch.h"
 
@@ -119,6 +125,42 @@ __global__ __launch_bounds__(kActThreads) void act_quant_kernel(
   }
 }
 
+// Power-of-two variant: same tiles and loads; one byte per group.
+__global__ __launch_bounds__(kActThreads) void act_quant_e8m0_kernel(
+    const uint4 *__restrict__ x, uint2 *__restrict__ q, uint8_t *__restrict__ scale,
+    int64_t n_groups) {
+  constexpr int L = 4 * kTilesPerIter;
+  const int lane = threadIdx.x & 63;
+  const int64_t n_tiles = (n_groups + kGroupsPerTile - 1) / kGroupsPerTile;
+  const int64_t stride = (int64_t)gridDim.x * kActWaves * kTilesPerIter;
+  for (int64_t tile0 = ((int64_t)blockIdx.x * kActWaves + (threadIdx.x >> 6)) * kTilesPerIter;
+       tile0 < n_tiles; tile0 += stride) {
+    uint4 v[L];
+    bool ok[L];
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      const int64_t g = tile0 * kGroupsPerTile + i * 4 + (lane >> 4);
+      ok[i] = g < n_groups;
+      v[i] = ok[i] ? x[tile0 * 256 + i * 64 + lane] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      float f[8];
+      unpack8(v[i], f);
+      const int e = e8m0_exponent(row16_max(absmax8(f)));
+      const float r = e8m0_inv_scale(e);
+      uint2 out;
+      out.x = pack4_e4m3(f[0] * r, f[1] * r, f[2] * r, f[3] * r);
+      out.y = pack4_e4m3(f[4] * r, f[5] * r, f[6] * r, f[7] * r);
+      if (ok[i]) {
+        q[tile0 * 256 + i * 64 + lane] = out;
+        if ((lane & 15) == 0)
+          scale[tile0 * kGroupsPerTile + i * 4 + (lane >> 4)] = (uint8_t)(e + 127);
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Weight quantizer: one workgroup per 128x128 block.  Thread t reads, for
 // i = 0..7, the 16 bytes at row i*16 + t/16, columns (t%16)*8 .. +8 of the
@@ -126,8 +168,10 @@ __global__ __launch_bounds__(kActThreads) void act_quant_kernel(
 // (a short last block row) are skipped and do not enter the amax.
 constexpr int kWqThreads = 256;
 
+// E8M0 selects power-of-two scales (one byte each) over fp32 scales.
+template <bool E8M0>
 __global__ __launch_bounds__(kWqThreads) void weight_quant_kernel(
-    const uint16_t *__restrict__ w, uint8_t *__restrict__ q, float *__restrict__ scale,
+    const uint16_t *__restrict__ w, uint8_t *__restrict__ q, void *__restrict__ scale,
     int64_t N, int64_t K) {
   __shared__ float wave_max[kWqThreads / 64];
   const int64_t KB = K / kBlock;
@@ -161,7 +205,15 @@ __global__ __launch_bounds__(kWqThreads) void weight_quant_kernel(
   if (lane == 0) wave_max[t >> 6] = m;
   __syncthreads();
   const float amax = fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3]));
-  const QParams p = make_qparams(amax);
+  QParams p;
+  int e = 0;
+  float r = 1.0f;
+  if constexpr (E8M0) {
+    e = e8m0_exponent(amax);
+    r = e8m0_inv_scale(e);
+  } else {
+    p = make_qparams(amax);
+  }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int64_t row = nb * kBlock + i * 16 + (t >> 4);
@@ -169,26 +221,44 @@ __global__ __launch_bounds__(kWqThreads) void weight_quant_kernel(
                   bf16_lo(v[i].z), bf16_hi(v[i].z), bf16_lo(v[i].w), bf16_hi(v[i].w)};
     float tq[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) tq[j] = quotient(ldexpf(f[j], p.k), p.sp, p.y);
+    for (int j = 0; j < 8; ++j) {
+      if constexpr (E8M0) tq[j] = f[j] * r;
+      else tq[j] = quotient(ldexpf(f[j], p.k), p.sp, p.y);
+    }
     uint2 out;
     out.x = pack4_e4m3(tq[0], tq[1], tq[2], tq[3]);
     out.y = pack4_e4m3(tq[4], tq[5], tq[6], tq[7]);
     if (ok[i]) *reinterpret_cast<uint2 *>(q + row * K + kb * kBlock + col) = out;
   }
-  if (t == 0) scale[nb * KB + kb] = p.s;
+  if (t == 0) {
+    if constexpr (E8M0) static_cast<uint8_t *>(scale)[nb * KB + kb] = (uint8_t)(e + 127);
+    else static_cast<float *>(scale)[nb * KB + kb] = p.s;
+  }
 }
 
 // ---------------------------------------------------------------------------
-hipError_t launch_act_quant(const void *x, int64_t M, int64_t K, void *q, float *s,
-                            hipStream_t stream) {
-  const int64_t n_groups = M * (K / kBlock);
+static unsigned act_quant_blocks(int64_t n_groups) {
   const int64_t n_tiles = (n_groups + kGroupsPerTile - 1) / kGroupsPerTile;
   const int64_t per_block = (int64_t)kActWaves * kTilesPerIter;
   int64_t blocks = (n_tiles + per_block - 1) / per_block;
   const int64_t cap = 256 * 8;  // grid-stride beyond 8 workgroups per CU
-  if (blocks > cap) blocks = cap;
-  hipLaunchKernelGGL(act_quant_kernel, dim3((unsigned)blocks), dim3(kActThreads), 0, stream,
-                     static_cast<const uint4 *>(x), static_cast<uint2 *>(q), s, n_groups);
+  return (unsigned)(blocks > cap ? cap : blocks);
+}
+
+hipError_t launch_act_quant(const void *x, int64_t M, int64_t K, void *q, float *s,
+                            hipStream_t stream) {
+  const int64_t n_groups = M * (K / kBlock);
+  hipLaunchKernelGGL(act_quant_kernel, dim3(act_quant_blocks(n_groups)), dim3(kActThreads), 0,
+                     stream, static_cast<const uint4 *>(x), static_cast<uint2 *>(q), s, n_groups);
+  return hipGetLastError();
+}
+
+hipError_t launch_act_quant_e8m0(const void *x, int64_t M, int64_t K, void *q, uint8_t *s,
+                                 hipStream_t stream) {
+  const int64_t n_groups = M * (K / kBlock);
+  hipLaunchKernelGGL(act_quant_e8m0_kernel, dim3(act_quant_blocks(n_groups)), dim3(kActThreads),
+                     0, stream, static_cast<const uint4 *>(x), static_cast<uint2 *>(q), s,
+                     n_groups);
   return hipGetLastError();
 }
 
@@ -196,8 +266,19 @@ hipError_t launch_weight_quant(const void *w, int64_t N, int64_t K, void *q, flo
                                hipStream_t stream) {
   const int64_t NB = (N + kBlock - 1) / kBlock;
   const int64_t KB = K / kBlock;
-  hipLaunchKernelGGL(weight_quant_kernel, dim3((unsigned)(NB * KB)), dim3(kWqThreads), 0,
-                     stream, static_cast<const uint16_t *>(w), static_cast<uint8_t *>(q), s, N, K);
+  hipLaunchKernelGGL(weight_quant_kernel<false>, dim3((unsigned)(NB * KB)), dim3(kWqThreads), 0,
+                     stream, static_cast<const uint16_t *>(w), static_cast<uint8_t *>(q),
+                     static_cast<void *>(s), N, K);
+  return hipGetLastError();
+}
+
+hipError_t launch_weight_quant_e8m0(const void *w, int64_t N, int64_t K, void *q, uint8_t *s,
+                                    hipStream_t stream) {
+  const int64_t NB = (N + kBlock - 1) / kBlock;
+  const int64_t KB = K / kBlock;
+  hipLaunchKernelGGL(weight_quant_kernel<true>, dim3((unsigned)(NB * KB)), dim3(kWqThreads), 0,
+                     stream, static_cast<const uint16_t *>(w), static_cast<uint8_t *>(q),
+                     static_cast<void *>(s), N, K);
   return hipGetLastError();
 }
 

@@ -37,7 +37,8 @@
  *     a last weight block row with fewer than 128 rows covers only the rows
  *     that exist.  M == 0 or N == 0 (or E == 0) is a no-op returning OK.
  *   - Every tensor base pointer must be 16-byte aligned (expert_offsets:
- *     4-byte aligned, as an int32 array).
+ *     4-byte aligned, as an int32 array; E8M0 scale-byte arrays: any
+ *     address).
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
  *     stream).  Inputs must stay valid until the stream reaches the launch.
  *     Outputs must not alias inputs.
@@ -126,6 +127,56 @@ FP8BLK_API fp8blk_status fp8_grouped_block_gemm(const void *x_q, const float *x_
                                                 const int32_t *expert_offsets, int32_t E,
                                                 int64_t total_M, int64_t N, int64_t K,
                                                 void *y_bf16, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Power-of-two scales stored as E8M0 bytes.
+ * "Fine-grained FP8" page, "UE8M0 scale format": pre-quantized
+ * DeepSeek-V4-style checkpoints keep their scales as packed float8_e8m0fnu
+ * (scale_fmt = "ue8m0") instead of fp32.  Readings fixed here:
+ *   - E8M0 is the OCP MX scale type: byte b encodes 2^(b - 127), 0xFF is NaN,
+ *     there is no zero.  One byte per scale, in the same layouts as the fp32
+ *     scales above ("packed" = 1 byte instead of 4).
+ *   - The scale of a block or group is 2^e, e the smallest integer >= -127
+ *     with amax <= 448 * 2^e (rounded up, so no code saturates); the byte is
+ *     e + 127 (never 0xFF for finite input; an all-zero set gets 0x00).
+ *   - q = E4M3_RNE(x * 2^-e), an exact quotient.
+ *   - Activations are quantized with power-of-two scales too, so both GEMM
+ *     operands carry E8M0 bytes and the matrix core applies them (each
+ *     128-block product enters the fp32 accumulator already scaled).
+ * Everything else (shapes, validation, errors, streams) is as above. */
+
+/* Weight quantization with E8M0 block scales.
+ *   w_bf16 [N,K] bf16 in; w_q [N,K] E4M3 codes out;
+ *   w_scale [ceil(N/128), K/128] E8M0 bytes out (blocks as above). */
+FP8BLK_API fp8blk_status fp8_weight_block_quant_ue8m0(const void *w_bf16, int64_t N, int64_t K,
+                                                      void *w_q, uint8_t *w_scale,
+                                                      void *stream);
+
+/* Dynamic activation quantization with E8M0 group scales.
+ *   x_bf16 [M,K] bf16 in; x_q [M,K] E4M3 codes out;
+ *   x_scale [M, K/128] E8M0 bytes out (groups as above). */
+FP8BLK_API fp8blk_status fp8_act_quant_group_ue8m0(const void *x_bf16, int64_t M, int64_t K,
+                                                   void *x_q, uint8_t *x_scale, void *stream);
+
+/* Block-scaled FP8 GEMM with E8M0 scales on both operands, y = x * W^T in
+ * bf16: y[m,n] = sum_kb 2^(x_scale[m,kb]-127) * 2^(w_scale[n/128,kb]-127) *
+ * sum_{k in kb} dec(x_q[m,k]) dec(w_q[n,k]), fp32 accumulation.
+ *   x_q [M,K], x_scale [M,K/128] bytes, w_q [N,K],
+ *   w_scale [ceil(N/128),K/128] bytes in; y_bf16 [M,N] out. */
+FP8BLK_API fp8blk_status fp8_block_gemm_ue8m0(const void *x_q, const uint8_t *x_scale,
+                                              const void *w_q, const uint8_t *w_scale,
+                                              int64_t M, int64_t N, int64_t K,
+                                              void *y_bf16, void *stream);
+
+/* Grouped variant with E8M0 scales (mixture-of-experts; "UE8M0 scale
+ * format": such checkpoints also run the expert matmuls).  Arguments as for
+ * fp8_grouped_block_gemm, with x_scale [total_M,K/128] and
+ * w_scale [E, ceil(N/128), K/128] as E8M0 bytes. */
+FP8BLK_API fp8blk_status fp8_grouped_block_gemm_ue8m0(const void *x_q, const uint8_t *x_scale,
+                                                      const void *w_q, const uint8_t *w_scale,
+                                                      const int32_t *expert_offsets, int32_t E,
+                                                      int64_t total_M, int64_t N, int64_t K,
+                                                      void *y_bf16, void *stream);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 FP8BLK_API const char *fp8blk_status_string(int status);

@@ -37,8 +37,11 @@ def say(*a):
 
 def assert_codes_equal(got_q, got_s, want_q, want_s, what=""):
     got_q = np.asarray(got_q); want_q = np.asarray(want_q)
-    gs = np.asarray(got_s, np.float32).view(np.uint32)
-    ws = np.asarray(want_s, np.float32).view(np.uint32)
+    if np.asarray(want_s).dtype == np.uint8:            # E8M0 scale bytes
+        gs, ws = np.asarray(got_s, np.uint8), np.asarray(want_s, np.uint8)
+    else:
+        gs = np.asarray(got_s, np.float32).view(np.uint32)
+        ws = np.asarray(want_s, np.float32).view(np.uint32)
     assert got_q.shape == want_q.shape and gs.shape == ws.shape, (got_q.shape, want_q.shape)
     bad_s = np.argwhere(gs != ws)
     assert bad_s.size == 0, f"{what}: {len(bad_s)} scales differ, first at {bad_s[:3].tolist()}: " \
@@ -58,5 +61,17 @@ def gpu_act_quant(x_bits):
 def gpu_weight_quant(w_bits):
     w = to_dev_bf16(w_bits)
     q, s = fb.weight_block_quant(w)
+    torch.cuda.synchronize()
+    return host(q), host(s)
+
+
+def gpu_act_quant_ue8m0(x_bits):
+    q, s = fb.act_quant_group(to_dev_bf16(x_bits), "ue8m0")
+    torch.cuda.synchronize()
+    return host(q), host(s)
+
+
+def gpu_weight_quant_ue8m0(w_bits):
+    q, s = fb.weight_block_quant(to_dev_bf16(w_bits), "ue8m0")
     torch.cuda.synchronize()
     return host(q), host(s)
