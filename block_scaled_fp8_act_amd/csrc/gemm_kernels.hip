@@ -67,9 +67,11 @@ struct Tile {
     float as[2][TM];
     float ws[2][64];  // weight-block scales of the tile's (<= 2) column blocks
   };
-  struct SmemCodes {  // E8M0 scales travel in registers
+  struct SmemMx {  // E8M0 scale bytes, one zero-extended dword per slot
     uint8_t a[2][TM * 128];
     uint8_t b[2][TN * 128];
+    int32_t as[2][TM];  // slot wm*FM*16 + r*FM + mi holds row wm*FM*16 + mi*16 + r
+    int32_t ws[2][64];  // the tile's (<= 2) 128-column blocks
   };
 };
 
@@ -80,6 +82,10 @@ __device__ __forceinline__ void lds_dma16(const void *g, void *lds_base) {
 }
 __device__ __forceinline__ void lds_dma4(const void *g, void *lds_base) {
   __builtin_amdgcn_global_load_lds(g, (lds_void *)lds_base, 4, 0, 0);
+}
+// One byte per lane, written zero-extended to LDS dword lds_base + 4*lane.
+__device__ __forceinline__ void lds_dma1(const void *g, void *lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void *)lds_base, 1, 0, 0);
 }
 
 // Chunk swizzle: chunk c of row r is stored at c ^ f(r) with
@@ -280,18 +286,20 @@ __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ A,
 
 // The same tile with E8M0 scales.  A: x_q at the tile's first row; As: its
 // scale bytes (row stride KB); B, Bs: w_q and the scale-byte row of the
-// tile's first 128-column block; the rest as for gemm_tile.  Each lane loads
-// the scale bytes of its FM A-operand rows (row wm*FM*16 + 16*mi + lane%16)
-// and of its wave's column block for K block kb+1 together with that
-// stage's DMA; they are consumed as the MFMAs' scale operands.
+// tile's first 128-column block; the rest as for gemm_tile.  The scale bytes
+// travel with each stage by LDS DMA like the operands (VGPR-returning global
+// loads in this loop would cost about half its rate), gathered so that the FM
+// A-row scales a lane needs -- rows wm*FM*16 + 16*mi + lane%16 -- sit in FM
+// consecutive dwords; they are the MFMAs' scale operands.
 template <int WM, int WN, int FM>
 __device__ __forceinline__ void gemm_tile_mx(const uint8_t *__restrict__ A,
                                              const uint8_t *__restrict__ As, int rows_a,
                                              const uint8_t *__restrict__ B,
                                              const uint8_t *__restrict__ Bs, int rows_b, int64_t K,
                                              uint16_t *__restrict__ Y, int64_t ldy,
-                                             typename Tile<WM, WN, FM>::SmemCodes &sm) {
+                                             typename Tile<WM, WN, FM>::SmemMx &sm) {
   using T = Tile<WM, WN, FM>;
+  static_assert(FM % 4 == 0, "scale slots are read four at a time");
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -313,13 +321,19 @@ __device__ __forceinline__ void gemm_tile_mx(const uint8_t *__restrict__ A,
     const int lchunk = (lane & 7) ^ swz_f(row);
     ob[i] = (uint32_t)min(row, rows_b - 1) * (uint32_t)K + lchunk * 16;
   }
-  // scale-byte offsets (< 256 * KB) of this lane's A rows; the wave's 64
-  // columns lie in one 128-column block (clamped to the last one present)
-  uint32_t osa[FM];
-#pragma unroll
-  for (int mi = 0; mi < FM; ++mi)
-    osa[mi] = (uint32_t)min(wm * FM * 16 + mi * 16 + r16, rows_a - 1) * (uint32_t)KB;
-  const uint8_t *pbs = Bs + (int64_t)min((wn * 64) / 128, (rows_b + 127) / 128 - 1) * KB;
+  // Scale slot 64*wave + lane (waves < TM/64) <- the byte of row
+  // g*FM*16 + mi*16 + r, where g = slot / (FM*16), r = (slot % (FM*16)) / FM,
+  // mi = slot % FM.
+  const uint8_t *ps;
+  {
+    const int slot = 64 * wave + lane;
+    const int g = slot / (FM * 16), rem = slot % (FM * 16);
+    const int row = g * FM * 16 + (rem % FM) * 16 + rem / FM;
+    ps = As + (int64_t)min(row, rows_a - 1) * KB;
+  }
+  constexpr int kNbTile = T::TN / 128;
+  const uint8_t *pws = Bs + (int64_t)min(lane, min(kNbTile, (rows_b + 127) / 128) - 1) * KB;
+  const int wsel = (wn * 64) / 128;
 
   auto issue = [&](int kb, int st) {
     const uint8_t *ak = A + (int64_t)kb * 128;
@@ -330,12 +344,8 @@ __device__ __forceinline__ void gemm_tile_mx(const uint8_t *__restrict__ A,
 #pragma unroll
     for (int i = 0; i < T::kDmaB; ++i)
       lds_dma16(bk + ob[i], sm.b[st] + (T::kDmaB * wave + i) * 1024);
-  };
-  int sa[FM], sb;
-  auto load_scales = [&](int kb, int *sa_, int &sb_) {
-#pragma unroll
-    for (int mi = 0; mi < FM; ++mi) sa_[mi] = As[osa[mi] + kb];
-    sb_ = pbs[kb];
+    if (wave < T::TM / 64) lds_dma1(ps + kb, &sm.as[st][64 * wave]);
+    if (wave == T::TM / 64 && lane < kNbTile) lds_dma1(pws + kb, &sm.ws[st][0]);
   };
 
   v4f acc[FM][4];
@@ -345,7 +355,6 @@ __device__ __forceinline__ void gemm_tile_mx(const uint8_t *__restrict__ A,
     for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
   issue(0, 0);
-  load_scales(0, sa, sb);
   asm volatile("" ::"s"(Y));  // no scalar load left in flight (see gemm_tile)
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -353,6 +362,7 @@ __device__ __forceinline__ void gemm_tile_mx(const uint8_t *__restrict__ A,
   const int c0 = (lane >> 4) * 2;
   const int arow0 = wm * FM * 16 + r16;
   const int brow0 = wn * 64 + r16;
+  const int slot0 = wm * FM * 16 + r16 * FM;
 
   for (int kb = 0; kb < KB; ++kb) {
     const int st = kb & 1;
@@ -363,10 +373,18 @@ __device__ __forceinline__ void gemm_tile_mx(const uint8_t *__restrict__ A,
       return frag_from(*reinterpret_cast<const uint4 *>(sa_lds + swz(row, c0)),
                        *reinterpret_cast<const uint4 *>(sa_lds + swz(row, c0 + 1)));
     };
+    // Reads in first-use order: B0, A0, the scales, B1..B3, A1.
     v8i bfr[4];
     bfr[0] = frag_from(*reinterpret_cast<const uint4 *>(sb_lds + swz(brow0, c0)),
                        *reinterpret_cast<const uint4 *>(sb_lds + swz(brow0, c0 + 1)));
     v8i af = read_a(0);
+    int sa[FM];
+#pragma unroll
+    for (int q = 0; q < FM / 4; ++q) {
+      const int4 v = *reinterpret_cast<const int4 *>(&sm.as[st][slot0 + 4 * q]);
+      sa[4 * q] = v.x; sa[4 * q + 1] = v.y; sa[4 * q + 2] = v.z; sa[4 * q + 3] = v.w;
+    }
+    const int sb = sm.ws[st][wsel];
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ni = 1; ni < 4; ++ni) {
@@ -378,9 +396,6 @@ __device__ __forceinline__ void gemm_tile_mx(const uint8_t *__restrict__ A,
     v8i afn = read_a(1);
     __builtin_amdgcn_sched_barrier(0);
     v8i afn2 = afn;
-    int san[FM], sbn = sb;
-#pragma unroll
-    for (int mi = 0; mi < FM; ++mi) san[mi] = sa[mi];
 #pragma unroll
     for (int mi = 0; mi < FM; ++mi) {
 #pragma unroll
@@ -394,10 +409,11 @@ __device__ __forceinline__ void gemm_tile_mx(const uint8_t *__restrict__ A,
         }
       }
       if (mi == 0) {
-        if (kb + 1 < KB) {
-          issue(kb + 1, st ^ 1);
-          load_scales(kb + 1, san, sbn);
-        }
+        // Branch-free, so the step stays one basic block and keeps the
+        // pinned order: the last step fetches block KB-1 again into the
+        // other stage, which no wave reads any more (every wave passed the
+        // barrier that ended the previous step).
+        issue(min(kb + 1, KB - 1), st ^ 1);
         __builtin_amdgcn_sched_barrier(0);
       }
       af = afn;
@@ -405,9 +421,6 @@ __device__ __forceinline__ void gemm_tile_mx(const uint8_t *__restrict__ A,
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-#pragma unroll
-    for (int mi = 0; mi < FM; ++mi) sa[mi] = san[mi];
-    sb = sbn;
   }
 
 #pragma unroll
@@ -596,7 +609,7 @@ __device__ __forceinline__ void tile_coords(int bid, int total, int tiles_m, int
 template <int WM, int WN, int FM, typename S>
 struct TileSmem {
   using type = typename std::conditional<std::is_same<S, uint8_t>::value,
-                                         typename Tile<WM, WN, FM>::SmemCodes,
+                                         typename Tile<WM, WN, FM>::SmemMx,
                                          typename Tile<WM, WN, FM>::Smem>::type;
 };
 
