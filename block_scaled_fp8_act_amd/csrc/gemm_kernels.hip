@@ -70,7 +70,7 @@ struct Tile {
   struct SmemMx {  // E8M0 scale bytes, one zero-extended dword per slot
     uint8_t a[2][TM * 128];
     uint8_t b[2][TN * 128];
-    int32_t as[2][TM];  // slot wm*FM*16 + r*FM + mi holds row wm*FM*16 + mi*16 + r
+    int32_t as[2][TM];  // slot wm*FM*16 + (mi/4)*64 + 4r + mi%4 holds row wm*FM*16 + 16mi + r
     int32_t ws[2][64];  // the tile's (<= 2) 128-column blocks
   };
 };
@@ -288,9 +288,11 @@ __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ A,
 // scale bytes (row stride KB); B, Bs: w_q and the scale-byte row of the
 // tile's first 128-column block; the rest as for gemm_tile.  The scale bytes
 // travel with each stage by LDS DMA like the operands (VGPR-returning global
-// loads in this loop would cost about half its rate), gathered so that the FM
-// A-row scales a lane needs -- rows wm*FM*16 + 16*mi + lane%16 -- sit in FM
-// consecutive dwords; they are the MFMAs' scale operands.
+// loads in this loop would cost about half its rate), gathered so that the
+// four A-row scales of fragments 4q..4q+3 that a lane needs -- rows
+// wm*FM*16 + 16*mi + lane%16 -- sit in one aligned 16-byte slot group, and
+// the 16 lanes of a row read 256 contiguous bytes (no bank conflict); they
+// are the MFMAs' scale operands.
 template <int WM, int WN, int FM>
 __device__ __forceinline__ void gemm_tile_mx(const uint8_t *__restrict__ A,
                                              const uint8_t *__restrict__ As, int rows_a,
@@ -322,13 +324,14 @@ __device__ __forceinline__ void gemm_tile_mx(const uint8_t *__restrict__ A,
     ob[i] = (uint32_t)min(row, rows_b - 1) * (uint32_t)K + lchunk * 16;
   }
   // Scale slot 64*wave + lane (waves < TM/64) <- the byte of row
-  // g*FM*16 + mi*16 + r, where g = slot / (FM*16), r = (slot % (FM*16)) / FM,
-  // mi = slot % FM.
+  // g*FM*16 + 16*mi + r, where g = slot / (FM*16) and, within that group,
+  // rem = slot % (FM*16) = 64*(mi/4) + 4r + mi%4.
   const uint8_t *ps;
   {
     const int slot = 64 * wave + lane;
     const int g = slot / (FM * 16), rem = slot % (FM * 16);
-    const int row = g * FM * 16 + (rem % FM) * 16 + rem / FM;
+    const int mi = (rem / 64) * 4 + (rem & 3), r = (rem & 63) >> 2;
+    const int row = g * FM * 16 + mi * 16 + r;
     ps = As + (int64_t)min(row, rows_a - 1) * KB;
   }
   constexpr int kNbTile = T::TN / 128;
@@ -362,7 +365,7 @@ __device__ __forceinline__ void gemm_tile_mx(const uint8_t *__restrict__ A,
   const int c0 = (lane >> 4) * 2;
   const int arow0 = wm * FM * 16 + r16;
   const int brow0 = wn * 64 + r16;
-  const int slot0 = wm * FM * 16 + r16 * FM;
+  const int slot0 = wm * FM * 16 + r16 * 4;
 
   for (int kb = 0; kb < KB; ++kb) {
     const int st = kb & 1;
@@ -381,7 +384,7 @@ __device__ __forceinline__ void gemm_tile_mx(const uint8_t *__restrict__ A,
     int sa[FM];
 #pragma unroll
     for (int q = 0; q < FM / 4; ++q) {
-      const int4 v = *reinterpret_cast<const int4 *>(&sm.as[st][slot0 + 4 * q]);
+      const int4 v = *reinterpret_cast<const int4 *>(&sm.as[st][slot0 + 64 * q]);
       sa[4 * q] = v.x; sa[4 * q + 1] = v.y; sa[4 * q + 2] = v.z; sa[4 * q + 3] = v.w;
     }
     const int sb = sm.ws[st][wsel];
