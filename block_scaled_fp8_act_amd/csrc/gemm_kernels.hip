@@ -88,6 +88,23 @@ __device__ __forceinline__ void lds_dma1(const void *g, void *lds_base) {
   __builtin_amdgcn_global_load_lds(g, (lds_void *)lds_base, 1, 0, 0);
 }
 
+// The same DMAs through a buffer resource: address = base + voff (a 32-bit
+// VGPR) + soff (an SGPR), range-checked against the resource's byte count
+// (reads past it return zeros).  Keeps per-load addresses at one VGPR.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, uint64_t bytes) {
+  const uint32_t n = bytes > 0xffffffffull ? 0xffffffffu : (uint32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)n,
+                                           0x00020000);
+}
+__device__ __forceinline__ void buf_dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                          void *lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds_base, 16, (int)voff, (int)soff, 0, 0);
+}
+__device__ __forceinline__ void buf_dma1(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                         void *lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds_base, 1, (int)voff, (int)soff, 0, 0);
+}
+
 // Chunk swizzle: chunk c of row r is stored at c ^ f(r) with
 // f(r) = ((r & 3) << 1) | ((r >> 2) & 1), a permutation of r's low three
 // bits.  A fragment read (16 lanes on 16 consecutive rows, one chunk each)
@@ -293,7 +310,7 @@ __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ A,
 // wm*FM*16 + 16*mi + lane%16 -- sit in one aligned 16-byte slot group, and
 // the 16 lanes of a row read 256 contiguous bytes (no bank conflict); they
 // are the MFMAs' scale operands.
-template <int WM, int WN, int FM>
+template <int WM, int WN, int FM, bool kDmaAtBarrier>
 __device__ __forceinline__ void gemm_tile_mx(const uint8_t *__restrict__ A,
                                              const uint8_t *__restrict__ As, int rows_a,
                                              const uint8_t *__restrict__ B,
@@ -326,29 +343,35 @@ __device__ __forceinline__ void gemm_tile_mx(const uint8_t *__restrict__ A,
   // Scale slot 64*wave + lane (waves < TM/64) <- the byte of row
   // g*FM*16 + 16*mi + r, where g = slot / (FM*16) and, within that group,
   // rem = slot % (FM*16) = 64*(mi/4) + 4r + mi%4.
-  const uint8_t *ps;
+  uint32_t ps;
   {
     const int slot = 64 * wave + lane;
     const int g = slot / (FM * 16), rem = slot % (FM * 16);
     const int mi = (rem / 64) * 4 + (rem & 3), r = (rem & 63) >> 2;
     const int row = g * FM * 16 + mi * 16 + r;
-    ps = As + (int64_t)min(row, rows_a - 1) * KB;
+    ps = (uint32_t)min(row, rows_a - 1) * (uint32_t)KB;
   }
   constexpr int kNbTile = T::TN / 128;
-  const uint8_t *pws = Bs + (int64_t)min(lane, min(kNbTile, (rows_b + 127) / 128) - 1) * KB;
+  const int nb_tile = min(kNbTile, (rows_b + 127) / 128);
+  const uint32_t pws = (uint32_t)min(lane, nb_tile - 1) * (uint32_t)KB;
   const int wsel = (wn * 64) / 128;
+  const __amdgpu_buffer_rsrc_t rAs = buffer_rsrc(As, (uint64_t)rows_a * (uint64_t)KB);
+  const __amdgpu_buffer_rsrc_t rBs = buffer_rsrc(Bs, (uint64_t)nb_tile * (uint64_t)KB);
 
+  // Operand resources are based at the K block (offsets then stay below
+  // 255*K + 128 < 2^32 for every K <= 2^24).
   auto issue = [&](int kb, int st) {
-    const uint8_t *ak = A + (int64_t)kb * 128;
-    const uint8_t *bk = B + (int64_t)kb * 128;
+    const uint64_t ko = (uint64_t)kb * 128u;
+    const __amdgpu_buffer_rsrc_t rA = buffer_rsrc(A + ko, (uint64_t)rows_a * (uint64_t)K - ko);
+    const __amdgpu_buffer_rsrc_t rB = buffer_rsrc(B + ko, (uint64_t)rows_b * (uint64_t)K - ko);
 #pragma unroll
     for (int i = 0; i < T::kDmaA; ++i)
-      lds_dma16(ak + oa[i], sm.a[st] + (T::kDmaA * wave + i) * 1024);
+      buf_dma16(rA, oa[i], 0, sm.a[st] + (T::kDmaA * wave + i) * 1024);
 #pragma unroll
     for (int i = 0; i < T::kDmaB; ++i)
-      lds_dma16(bk + ob[i], sm.b[st] + (T::kDmaB * wave + i) * 1024);
-    if (wave < T::TM / 64) lds_dma1(ps + kb, &sm.as[st][64 * wave]);
-    if (wave == T::TM / 64 && lane < kNbTile) lds_dma1(pws + kb, &sm.ws[st][0]);
+      buf_dma16(rB, ob[i], 0, sm.b[st] + (T::kDmaB * wave + i) * 1024);
+    if (wave < T::TM / 64) buf_dma1(rAs, ps, (uint32_t)kb, &sm.as[st][64 * wave]);
+    if (wave == T::TM / 64 && lane < kNbTile) buf_dma1(rBs, pws, (uint32_t)kb, &sm.ws[st][0]);
   };
 
   v4f acc[FM][4];
@@ -358,6 +381,7 @@ __device__ __forceinline__ void gemm_tile_mx(const uint8_t *__restrict__ A,
     for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
   issue(0, 0);
+  if constexpr (kDmaAtBarrier) issue(min(1, KB - 1), 1);
   asm volatile("" ::"s"(Y));  // no scalar load left in flight (see gemm_tile)
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -366,21 +390,36 @@ __device__ __forceinline__ void gemm_tile_mx(const uint8_t *__restrict__ A,
   const int arow0 = wm * FM * 16 + r16;
   const int brow0 = wn * 64 + r16;
   const int slot0 = wm * FM * 16 + r16 * 4;
+  auto read_a = [&](int st, int mi) {
+    const uint8_t *p = sm.a[st];
+    const int row = arow0 + mi * 16;
+    return frag_from(*reinterpret_cast<const uint4 *>(p + swz(row, c0)),
+                     *reinterpret_cast<const uint4 *>(p + swz(row, c0 + 1)));
+  };
+  auto read_b = [&](int st, int ni) {
+    const uint8_t *p = sm.b[st];
+    const int row = brow0 + ni * 16;
+    return frag_from(*reinterpret_cast<const uint4 *>(p + swz(row, c0)),
+                     *reinterpret_cast<const uint4 *>(p + swz(row, c0 + 1)));
+  };
 
+  // Step kb reads stage kb&1.  Its barrier sits before the last fragment's
+  // MFMAs: every wave has then finished reading stage kb&1 (waitcnt) and
+  // block kb+1 has landed in the other stage.  The first reads of stage kb+1
+  // go out right after it, their latency hidden under the last fragment's
+  // MFMAs instead of idling the matrix core at the step start.  Block kb+2
+  // is sent into stage kb&1 either right after that barrier (kDmaAtBarrier:
+  // a full step ahead; used where registers are plentiful) or once the
+  // first fragment of step kb+1 is running (fewer live registers).  Blocks
+  // past KB-1 are clamped to KB-1: an in-bounds re-fetch into a stage that
+  // nobody reads again, which keeps the step branch-free.
+  v8i b0n = read_b(0, 0);
+  v8i a0n = read_a(0, 0);
   for (int kb = 0; kb < KB; ++kb) {
     const int st = kb & 1;
-    const uint8_t *sa_lds = sm.a[st];
-    const uint8_t *sb_lds = sm.b[st];
-    auto read_a = [&](int mi) {
-      const int row = arow0 + mi * 16;
-      return frag_from(*reinterpret_cast<const uint4 *>(sa_lds + swz(row, c0)),
-                       *reinterpret_cast<const uint4 *>(sa_lds + swz(row, c0 + 1)));
-    };
-    // Reads in first-use order: B0, A0, the scales, B1..B3, A1.
     v8i bfr[4];
-    bfr[0] = frag_from(*reinterpret_cast<const uint4 *>(sb_lds + swz(brow0, c0)),
-                       *reinterpret_cast<const uint4 *>(sb_lds + swz(brow0, c0 + 1)));
-    v8i af = read_a(0);
+    bfr[0] = b0n;
+    v8i af = a0n;
     int sa[FM];
 #pragma unroll
     for (int q = 0; q < FM / 4; ++q) {
@@ -391,40 +430,44 @@ __device__ __forceinline__ void gemm_tile_mx(const uint8_t *__restrict__ A,
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ni = 1; ni < 4; ++ni) {
-      const int row = brow0 + ni * 16;
-      bfr[ni] = frag_from(*reinterpret_cast<const uint4 *>(sb_lds + swz(row, c0)),
-                          *reinterpret_cast<const uint4 *>(sb_lds + swz(row, c0 + 1)));
+      bfr[ni] = read_b(st, ni);
       __builtin_amdgcn_sched_barrier(0);
     }
-    v8i afn = read_a(1);
+    v8i afn = read_a(st, 1);
     __builtin_amdgcn_sched_barrier(0);
     v8i afn2 = afn;
 #pragma unroll
     for (int mi = 0; mi < FM; ++mi) {
+      if (mi == FM - 1) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if constexpr (kDmaAtBarrier) issue(min(kb + 2, KB - 1), st);
+        // the last step reads the re-fetched block KB-1 here (unused)
+        b0n = read_b(st ^ 1, 0);
+        a0n = read_a(st ^ 1, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
 #pragma unroll
       for (int ni = 0; ni < 4; ++ni) {
         acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
             af, bfr[ni], acc[mi][ni], 0, 0, 0, sa[mi], 0, sb);
         __builtin_amdgcn_sched_barrier(0);
         if (ni == 0 && mi + 2 < FM) {
-          afn2 = read_a(mi + 2);
+          afn2 = read_a(st, mi + 2);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      if (mi == 0) {
-        // Branch-free, so the step stays one basic block and keeps the
-        // pinned order: the last step fetches block KB-1 again into the
-        // other stage, which no wave reads any more (every wave passed the
-        // barrier that ended the previous step).
-        issue(min(kb + 1, KB - 1), st ^ 1);
-        __builtin_amdgcn_sched_barrier(0);
+      if constexpr (!kDmaAtBarrier) {
+        if (mi == 0) {
+          issue(min(kb + 1, KB - 1), st ^ 1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
       af = afn;
       afn = afn2;
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
   }
+  __builtin_amdgcn_s_waitcnt(0);
 
 #pragma unroll
   for (int mi = 0; mi < FM; ++mi)
@@ -622,7 +665,7 @@ __device__ __forceinline__ void run_tile(const uint8_t *A, const S *As, int rows
                                          uint16_t *Y, int64_t ldy,
                                          typename TileSmem<WM, WN, FM, S>::type &sm) {
   if constexpr (std::is_same<S, uint8_t>::value)
-    gemm_tile_mx<WM, WN, FM>(A, As, rows_a, B, Bs, rows_b, K, Y, ldy, sm);
+    gemm_tile_mx<WM, WN, FM, (FM <= 4)>(A, As, rows_a, B, Bs, rows_b, K, Y, ldy, sm);
   else
     gemm_tile<WM, WN, FM>(A, As, rows_a, B, Bs, rows_b, K, Y, ldy, sm);
 }
