@@ -9,7 +9,8 @@ Inputs are resident in HBM before the timed region; two input/output sets
 does not hold a step's working set.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
-                    [--rows]  (also time weight quant, decode and MoE rows)
+                    [--rows]  (also time weight quant, decode, MoE and the
+                               power-of-two (UE8M0) scale rows)
 
 Prints one JSON line.  ``value`` is the whole step's throughput in TFLOP/s
 (GEMM FLOPs of the four projections / step time, the activation
@@ -183,12 +184,16 @@ def main():
     ms_per_step = wall / args.steps * 1e3
 
     # --- per-kernel durations with events on the launch stream --------------
+    # (all steps enqueued back to back, one synchronisation at the end, so no
+    # event pair spans the host's launch latency)
     act_t = [0.0] * n_proj
     gemm_t = [0.0] * n_proj
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_proj)]
+           for _ in range(args.steps)]
     for i in range(args.steps):
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_proj)]
-        step(i, ev)
-        torch.cuda.synchronize()
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    for ev in evs:
         for p in range(n_proj):
             act_t[p] += ev[p][0].elapsed_time(ev[p][1]) / args.steps
             gemm_t[p] += ev[p][1].elapsed_time(ev[p][2]) / args.steps
@@ -278,6 +283,7 @@ def other_rows(torch, fb, dev, stream):
         t = _time(torch, stream, lambda: fb.fp8_block_gemm(xq, xsc, wq, wsc, y))
         byts = N * K + 16 * K + 2 * 16 * N
         rows[f"decode_M16_{name}"] = {"us": round(t * 1e6, 2), "GB/s": round(byts / t / 1e9, 1)}
+    rows.update(ue8m0_rows(torch, fb, dev, stream, g))
     # grouped MoE (32 experts, Zipf top-8 routing of 4096 tokens)
     _, off = synth.moe_routing()
     total = int(off[-1])
@@ -293,6 +299,68 @@ def other_rows(torch, fb, dev, stream):
         y = torch.empty((total, N), dtype=torch.bfloat16, device=dev)
         t = _time(torch, stream, lambda: fb.fp8_grouped_block_gemm(xq, xsc, wq, wsc, offd, y), iters=10)
         rows[f"moe_{name}"] = {"us": round(t * 1e6, 2), "TFLOP/s": round(2.0 * total * N * K / t / 1e12, 1)}
+    return rows
+
+
+def ue8m0_rows(torch, fb, dev, stream, g):
+    """Power-of-two (E8M0-byte) scales: the same prefill step (activation
+    quantization + GEMM per projection, two rotated input sets), the weight
+    quantizer on the largest weight, and the decode GEMMs."""
+    rows = {}
+    xs0, ws_bf16 = gen_inputs(torch, dev, 3000)
+    sets = [xs0, [torch.roll(x, 1, 0) for x in xs0]]
+    wq, we = zip(*[fb.weight_block_quant(w, "ue8m0") for w in ws_bf16])
+    del ws_bf16
+    outs = [[(torch.empty((M_PREFILL, K), dtype=torch.uint8, device=dev),
+              torch.empty((M_PREFILL, K // 128), dtype=torch.uint8, device=dev),
+              torch.empty((M_PREFILL, N), dtype=torch.bfloat16, device=dev))
+             for (_, N, K) in PREFILL_SHAPES] for _ in sets]
+    flops = sum(2.0 * M_PREFILL * N * K for (_, N, K) in PREFILL_SHAPES)
+
+    def step(i):
+        for p, (xq, xe, y) in enumerate(outs[i % 2]):
+            fb.fp8_act_quant_group_ue8m0(sets[i % 2][p], xq, xe)
+            fb.fp8_block_gemm_ue8m0(xq, xe, wq[p], we[p], y)
+
+    for i in range(3):
+        step(i)
+    torch.cuda.synchronize()
+    n = 10
+    t0 = time.perf_counter()
+    for i in range(n):
+        step(i)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / n
+    per = {}
+    gemm_s = 0.0
+    for p, (name, N, K) in enumerate(PREFILL_SHAPES):
+        xq, xe, y = outs[0][p]
+        ta = _time(torch, stream, lambda: fb.fp8_act_quant_group_ue8m0(sets[0][p], xq, xe))
+        tg = _time(torch, stream, lambda: fb.fp8_block_gemm_ue8m0(xq, xe, wq[p], we[p], y))
+        gemm_s += tg
+        per[name] = {"act_quant_us": round(ta * 1e6, 2), "gemm_us": round(tg * 1e6, 2),
+                     "gemm_TFLOP/s": round(2.0 * M_PREFILL * N * K / tg / 1e12, 1)}
+    rows["ue8m0_prefill_step"] = {"ms_per_step": round(dt * 1e3, 4),
+                                  "TFLOP/s": round(flops / dt / 1e12, 1),
+                                  "gemm_TFLOP/s": round(flops / gemm_s / 1e12, 1),
+                                  "per_projection": per}
+    del sets, outs, wq, we
+    w = (torch.randn((18432, 7168), generator=g, device=dev) * 0.01).to(torch.bfloat16)
+    q = torch.empty((18432, 7168), dtype=torch.uint8, device=dev)
+    e = torch.empty((144, 56), dtype=torch.uint8, device=dev)
+    t = _time(torch, stream, lambda: fb.fp8_weight_block_quant_ue8m0(w, q, e))
+    rows["ue8m0_weight_quant_18432x7168"] = {"us": round(t * 1e6, 2),
+                                             "GB/s": round(18432 * 7168 * 3 / t / 1e9, 1)}
+    del w, q, e
+    for name, N, K in PREFILL_SHAPES:
+        x = torch.randn((16, K), generator=g, device=dev).to(torch.bfloat16)
+        wq1, we1 = fb.weight_block_quant(
+            (torch.randn((N, K), generator=g, device=dev) * 0.02).to(torch.bfloat16), "ue8m0")
+        xq, xe = fb.act_quant_group(x, "ue8m0")
+        y = torch.empty((16, N), dtype=torch.bfloat16, device=dev)
+        t = _time(torch, stream, lambda: fb.fp8_block_gemm_ue8m0(xq, xe, wq1, we1, y))
+        byts = N * K + 16 * K + 2 * 16 * N
+        rows[f"ue8m0_decode_M16_{name}"] = {"us": round(t * 1e6, 2), "GB/s": round(byts / t / 1e9, 1)}
     return rows
 
 
