@@ -32,9 +32,14 @@ What is computed, and where it comes from:
   same page, ``scale_fmt="ue8m0"``): :mod:`oracle.ue8m0` states the
   readings (codec, round-up exponent, activations scaled the same way).
 
+* Static activation scales (same page, "DeepGEMM fast path": the static
+  activation scheme): :mod:`oracle.static` states the readings (one
+  calibrated fp32 scale per tensor, saturating quotient).
+
 Modules: :mod:`oracle.e4m3` (codec), :mod:`oracle.quant` (quantizers),
 :mod:`oracle.gemm` (block-scaled and grouped GEMM, linear layer),
-:mod:`oracle.ue8m0` (E8M0 scales: codec, quantizers, GEMM).
+:mod:`oracle.ue8m0` (E8M0 scales: codec, quantizers, GEMM),
+:mod:`oracle.static` (static activation scale: quantizer, GEMM).
 """
 from .e4m3 import E4M3_MAX, decode, encode, fl32_div
 from .quant import act_quant_group, weight_block_quant, quant_element_map
@@ -43,6 +48,7 @@ from .gemm import (bf16_rne_bits, block_gemm, dequant_act, dequant_weight,
                    tolerance_report)
 from .ue8m0 import (act_quant_group_ue8m0, block_gemm_ue8m0, e8m0_decode, e8m0_exponent,
                     grouped_block_gemm_ue8m0, weight_block_quant_ue8m0)
+from .static import act_quant_static, block_gemm_static
 
 __all__ = [
     "E4M3_MAX", "decode", "encode", "fl32_div",
@@ -52,4 +58,5 @@ __all__ = [
     "tolerance_report",
     "act_quant_group_ue8m0", "block_gemm_ue8m0", "e8m0_decode", "e8m0_exponent",
     "grouped_block_gemm_ue8m0", "weight_block_quant_ue8m0",
+    "act_quant_static", "block_gemm_static",
 ]

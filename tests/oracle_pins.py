@@ -19,6 +19,7 @@ from oracle import e4m3 as oe
 from oracle import gemm as og
 from oracle import quant as oq
 from oracle import ue8m0 as ou
+from oracle import static as ost
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -643,6 +644,79 @@ def pin_ue8m0_gemm(seed=61):
     np.testing.assert_array_equal(yg[1:], ou.block_gemm_ue8m0(xq[1:], xe[1:], wq2[1], we2[1]))
 
 
+# ----------------------------------------------------------------------------
+# static activation quantization pins
+
+def pin_static_hand_cases():
+    for row in read_golden("static_hand_cases.txt"):
+        s_s, xs_s, q_s = [p.strip() for p in row.split("|")]
+        scale = np.array([int(s_s, 16)], np.uint32).view(np.float32)[0]
+        xb = np.array([[int(v, 16) for v in xs_s.split()]], np.uint16)
+        # pad K to 128 (the quantizer is element-wise; K is free here)
+        x = np.zeros((1, 128), np.uint16); x[0, : xb.shape[1]] = xb
+        q = ost.act_quant_static(x, scale)
+        want = [int(v, 16) for v in q_s.split()]
+        assert list(q[0, : xb.shape[1]]) == want, (s_s, [hex(c) for c in q[0, : xb.shape[1]]], q_s)
+        assert np.all(q[0, xb.shape[1]:] == 0)
+
+
+def pin_static_brute_force(n=1500, seed=67):
+    """Random bf16 x and fp32 scales over a wide range: the code is the
+    nearest E4M3 value (ties to even) to the exactly rounded, saturated
+    quotient, found by exhaustive search over the 254 finite values."""
+    rng = np.random.default_rng(seed)
+    xb = rng.integers(0, 0x7F80, n).astype(np.uint32) | (rng.integers(0, 2, n).astype(np.uint32) << 15)
+    sb = (rng.integers(0x00800000, 0x7F000000, n)).astype(np.uint32)      # positive normal fp32
+    sb[:20] = np.array([0x3F800000 + (i << 23) for i in range(-10, 10)], np.uint32)  # powers of two
+    x = np.zeros((1, 128), np.uint16)
+    for i in range(n):
+        x[0, 0] = xb[i]
+        scale = np.array([sb[i]], np.uint32).view(np.float32)[0]
+        got = int(ost.act_quant_static(x, scale)[0, 0])
+        t = fl32_of(f32_value(int(xb[i]) << 16) / f32_value(int(sb[i])))
+        t = max(-448.0, min(448.0, t)) if math.isfinite(t) else math.copysign(448.0, t)
+        if t == 0.0:
+            want = 0x80 if (xb[i] >> 15) else 0x00
+        else:
+            want = brute_force_encode(t)
+        assert got == want, (hex(int(xb[i])), hex(int(sb[i])), hex(got), hex(want))
+
+
+def pin_static_invariants(seed=71):
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal((16, 256)) * 40).astype(np.float32)
+    xb = (x.view(np.uint32) >> 16).astype(np.uint16)
+    xv = (xb.astype(np.uint32) << 16).view(np.float32)
+    for j in (-3, 0, 2):
+        q = ost.act_quant_static(xb, np.float32(2.0 ** j))
+        # a power-of-two scale divides exactly: the fp32 map on x * 2^-j
+        assert np.array_equal(q, oe.encode(np.clip(xv * np.float32(2.0 ** -j), -448, 448)))
+    q = ost.act_quant_static(xb, np.float32(0.37))
+    qn = ost.act_quant_static(((xb.astype(np.uint32) ^ 0x8000)).astype(np.uint16), np.float32(0.37))
+    assert np.array_equal(qn, q ^ 0x80), "sign symmetry"
+    d = oe.decode(q)
+    order = np.argsort(xv.ravel(), kind="stable")
+    assert np.all(np.diff(d.ravel()[order]) >= 0), "monotone in x"
+    assert not np.any((q & 0x7F) == 0x7F)
+
+
+def pin_static_gemm(seed=73):
+    """Integer codes, a power-of-two activation scale and power-of-two weight
+    scales: the fp64 result equals the exact integer sum."""
+    rng = np.random.default_rng(seed)
+    M, N, K = 5, 130, 256
+    xi = rng.integers(-8, 9, (M, K)); wi = rng.integers(-8, 9, (N, K))
+    xq = oe.encode(xi.astype(np.float32)); wq = oe.encode(wi.astype(np.float32))
+    ws = np.exp2(rng.integers(-2, 3, (2, 2))).astype(np.float32)
+    y = ost.block_gemm_static(xq, np.float32(0.25), wq, ws)
+    for m in range(M):
+        for n in (0, 64, 127, 128, 129):
+            want = sum(Fraction(int(xi[m, k]) * int(wi[n, k])) * Fraction(float(ws[n // 128, k // 128]))
+                       for k in range(K)) * Fraction(1, 4)
+            assert Fraction(float(y[m, n])) == want, (m, n)
+    assert np.all(ost.term_magnitude_static(xq, 0.25, wq, ws) >= np.abs(y))
+
+
 ALL_PINS = [
     pin_format_points, pin_hand_encodings, pin_decode_matches_enumeration,
     pin_encode_roundtrip_and_monotone, pin_encode_brute_force, pin_fl32_div,
@@ -652,4 +726,5 @@ ALL_PINS = [
     pin_bf16_rounding, pin_grouped, pin_tolerance_report,
     pin_e8m0_codec, pin_e8m0_exponent_exhaustive, pin_ue8m0_hand_groups,
     pin_ue8m0_invariants, pin_ue8m0_weight_blocks, pin_ue8m0_gemm,
+    pin_static_hand_cases, pin_static_brute_force, pin_static_invariants, pin_static_gemm,
 ]

@@ -10,6 +10,7 @@ from oracle import e4m3 as oe
 from oracle import gemm as og
 from oracle import quant as oq
 from oracle import ue8m0 as ou
+from oracle import static as ost
 
 
 def _fails(pins):
@@ -61,6 +62,9 @@ MUTANTS = {
     "ue8m0_strict_bound": lambda mp: mp.setattr(ou, "e8m0_exponent", _e8m0_strict),
     "ue8m0_no_lower_clamp": lambda mp: mp.setattr(ou, "E_MIN", -133),
     "e8m0_bias_128": lambda mp: mp.setattr(ou, "E8M0_BIAS", 128),
+    "static_no_saturation": lambda mp: mp.setattr(ost, "act_quant_static", _static_nosat),
+    "static_reciprocal_multiply": lambda mp: mp.setattr(ost, "act_quant_static", _static_recip),
+    "static_scale_multiplies": lambda mp: mp.setattr(ost, "act_quant_static", _static_mul),
     "ue8m0_gemm_weight_bytes_reversed": lambda mp: mp.setattr(
         ou, "block_gemm_ue8m0", lambda xq, xe, wq, we: _orig_bg_ue(xq, xe, wq, we[::-1].copy())),
 }
@@ -68,6 +72,29 @@ MUTANTS = {
 _orig_decode = oe.decode
 _orig_e8m0_exponent = ou.e8m0_exponent
 _orig_bg_ue = ou.block_gemm_ue8m0
+
+
+def _static_nosat(x_bits, scale):
+    x = (np.asarray(x_bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
+    t = (x / np.float32(scale)).astype(np.float32)
+    a = np.abs(t).astype(np.float64)
+    e = np.floor(np.log2(np.maximum(a, 1e-300)))
+    q = np.exp2(np.maximum(e, -6) - 3)
+    v = np.rint(a / q) * q                  # no clamp: values above 448 stay large
+    v = np.where(v > 448, np.nan, v)        # which has no finite code
+    c = oe.encode(np.nan_to_num(np.copysign(v, t), nan=0.0).astype(np.float32))
+    return np.where(np.isnan(v), 0x7F, c).astype(np.uint8)
+
+
+def _static_recip(x_bits, scale):
+    x = (np.asarray(x_bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
+    r = np.float32(1.0) / np.float32(scale)
+    return oe.encode(np.clip((x * r).astype(np.float32), -448, 448))
+
+
+def _static_mul(x_bits, scale):
+    x = (np.asarray(x_bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
+    return oe.encode(np.clip((x * np.float32(scale)).astype(np.float32), -448, 448))
 
 
 def _e8m0_floor(amax):
