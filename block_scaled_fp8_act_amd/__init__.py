@@ -14,9 +14,12 @@ buffer (inputs and preallocated outputs):
     fp8_block_gemm(x_q, x_scale, w_q, w_scale, y)
     fp8_grouped_block_gemm(x_q, x_scale, w_q, w_scale, offsets, y)
 
-and their power-of-two-scale twins (scales as E8M0 bytes, uint8 or
+their power-of-two-scale twins (scales as E8M0 bytes, uint8 or
 torch.float8_e8m0fnu tensors): fp8_weight_block_quant_ue8m0,
-fp8_act_quant_group_ue8m0, fp8_block_gemm_ue8m0, fp8_grouped_block_gemm_ue8m0.
+fp8_act_quant_group_ue8m0, fp8_block_gemm_ue8m0, fp8_grouped_block_gemm_ue8m0,
+and the static-activation-scale pair (one fp32 scale in a 1-element device
+tensor): fp8_act_quant_static(x, x_scale, x_q),
+fp8_block_gemm_static(x_q, x_scale, w_q, w_scale, y).
 
 Convenience wrappers allocate the outputs; ``scale_fmt`` is "float" (fp32
 scales) or "ue8m0" (E8M0 bytes), and the GEMMs pick the path from the scale
@@ -27,6 +30,9 @@ tensors' dtype:
     block_gemm(x_q, x_scale, w_q, w_scale) -> y bf16 [M,N]
     grouped_block_gemm(x_q, x_scale, w_q, w_scale, offsets) -> y bf16 [sum M_e, N]
     linear(x, w_q, w_scale) -> y bf16 [M,N]   (dynamic act quant, then GEMM)
+    act_quant_static(x, x_scale) -> x_q uint8 [M,K]
+    block_gemm_static(x_q, x_scale, w_q, w_scale) -> y bf16 [M,N]
+    linear_static(x, x_scale, w_q, w_scale) -> y bf16 [M,N]
 """
 from __future__ import annotations
 
@@ -39,7 +45,9 @@ __all__ = [
     "Fp8BlkError", "BLOCK", "lib_path", "load_library", "status_string",
     "fp8_weight_block_quant", "fp8_act_quant_group", "fp8_block_gemm",
     "fp8_grouped_block_gemm", "fp8_weight_block_quant_ue8m0", "fp8_act_quant_group_ue8m0",
-    "fp8_block_gemm_ue8m0", "fp8_grouped_block_gemm_ue8m0", "weight_block_quant",
+    "fp8_block_gemm_ue8m0", "fp8_grouped_block_gemm_ue8m0", "fp8_act_quant_static",
+    "fp8_block_gemm_static", "act_quant_static", "block_gemm_static", "linear_static",
+    "weight_block_quant",
     "act_quant_group", "block_gemm", "grouped_block_gemm", "linear", "SCALE_FMTS",
 ]
 
@@ -81,6 +89,8 @@ def load_library() -> ctypes.CDLL:
         "fp8_act_quant_group": [vp, i64, i64, vp, vp, vp],
         "fp8_block_gemm": [vp, vp, vp, vp, i64, i64, i64, vp, vp],
         "fp8_grouped_block_gemm": [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp, vp],
+        "fp8_act_quant_static": [vp, i64, i64, vp, vp, vp],
+        "fp8_block_gemm_static": [vp, vp, vp, vp, i64, i64, i64, vp, vp],
         "fp8_weight_block_quant_ue8m0": [vp, i64, i64, vp, vp, vp],
         "fp8_act_quant_group_ue8m0": [vp, i64, i64, vp, vp, vp],
         "fp8_block_gemm_ue8m0": [vp, vp, vp, vp, i64, i64, i64, vp, vp],
@@ -221,6 +231,38 @@ def fp8_grouped_block_gemm(x_q, x_scale, w_q, w_scale, offsets, y):
     _grouped("fp8_grouped_block_gemm", _F32, x_q, x_scale, w_q, w_scale, offsets, y)
 
 
+def _static_scale(x_scale):
+    _need(x_scale, "x_scale", _F32)
+    if x_scale.numel() != 1:
+        raise ValueError("the static activation scale is one fp32 value")
+
+
+def fp8_act_quant_static(x, x_scale, x_q):
+    _need(x, "x", (torch.bfloat16,), 2)
+    M, K = x.shape
+    _static_scale(x_scale)
+    _need(x_q, "x_q", _CODES)
+    _shape_eq(x_q, (M, K), "x_q")
+    _check(load_library().fp8_act_quant_static(_ptr(x), M, K, _ptr(x_scale), _ptr(x_q), _stream()),
+           "fp8_act_quant_static")
+
+
+def fp8_block_gemm_static(x_q, x_scale, w_q, w_scale, y):
+    _need(x_q, "x_q", _CODES, 2); _need(w_q, "w_q", _CODES, 2)
+    _static_scale(x_scale); _need(w_scale, "w_scale", _F32, 2)
+    _need(y, "y", (torch.bfloat16,), 2)
+    M, K = x_q.shape
+    N = w_q.shape[0]
+    if w_q.shape[1] != K:
+        raise ValueError("x_q and w_q disagree on K")
+    if K % BLOCK == 0:
+        _shape_eq(w_scale, (-(-N // BLOCK), K // BLOCK), "w_scale")
+    _shape_eq(y, (M, N), "y")
+    _check(load_library().fp8_block_gemm_static(_ptr(x_q), _ptr(x_scale), _ptr(w_q),
+                                                _ptr(w_scale), M, N, K, _ptr(y), _stream()),
+           "fp8_block_gemm_static")
+
+
 def fp8_weight_block_quant_ue8m0(w, w_q, w_scale):
     _weight_quant("fp8_weight_block_quant_ue8m0", _E8M0, w, w_q, w_scale)
 
@@ -286,3 +328,21 @@ def linear(x, w_q, w_scale):
     scales select power-of-two activation scales as well."""
     x_q, x_s = act_quant_group(x, "ue8m0" if _is_e8m0(w_scale) else "float")
     return block_gemm(x_q, x_s, w_q, w_scale)
+
+
+def act_quant_static(x, x_scale):
+    x_q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    fp8_act_quant_static(x, x_scale, x_q)
+    return x_q
+
+
+def block_gemm_static(x_q, x_scale, w_q, w_scale):
+    y = torch.empty((x_q.shape[0], w_q.shape[0]), dtype=torch.bfloat16, device=x_q.device)
+    fp8_block_gemm_static(x_q, x_scale, w_q, w_scale, y)
+    return y
+
+
+def linear_static(x, x_scale, w_q, w_scale):
+    """The FP8 linear layer with a static (calibrated, per-tensor) activation
+    scale: quantization of x, then the block-scaled GEMM."""
+    return block_gemm_static(act_quant_static(x, x_scale), x_scale, w_q, w_scale)

@@ -18,7 +18,9 @@ constexpr int kMaxDevices = 64;
 // 0 = unknown, 1 = gfx950, 2 = other / unusable
 std::atomic<int> g_arch_state[kMaxDevices];
 
-bool misaligned(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+bool misaligned(const void *p, uintptr_t align = 16) {
+  return (reinterpret_cast<uintptr_t>(p) & (align - 1)) != 0;
+}
 
 fp8blk_status check_device() {
   int dev = -1;
@@ -47,21 +49,21 @@ bool bad_rows(int64_t r) { return r < 0 || r > kMaxRows; }
 bool bad_k(int64_t K) { return K <= 0 || K > kMaxK || (K % FP8BLK_BLOCK) != 0; }
 bool too_big(int64_t rows, int64_t K) { return rows > 0 && rows > kMaxElems / K; }
 
-// Validation of each operation, shared by its fp32-scale and E8M0-scale
-// entry points.  scale_align: fp32 scale arrays must be 16-byte aligned;
-// E8M0 byte arrays have no alignment requirement.
+// Validation of each operation, shared by its variants.  The scale arrays'
+// alignment (bytes) depends on the variant: fp32 scale arrays 16, one
+// static fp32 scale 4, E8M0 byte arrays 1 (none).
 fp8blk_status check_quant(const void *in, int64_t rows, int64_t K, const void *q,
-                          const void *scale, bool scale_align) {
+                          const void *scale, uintptr_t scale_align) {
   if (rows > 0 && (!in || !q || !scale)) return FP8BLK_ERR_NULL;
   if (bad_rows(rows) || bad_k(K) || too_big(rows, K)) return FP8BLK_ERR_SHAPE;
-  if (rows > 0 && (misaligned(in) || misaligned(q) || (scale_align && misaligned(scale))))
+  if (rows > 0 && (misaligned(in) || misaligned(q) || misaligned(scale, scale_align)))
     return FP8BLK_ERR_ALIGN;
   return check_device();
 }
 
 fp8blk_status check_gemm(const void *x_q, const void *x_scale, const void *w_q,
                          const void *w_scale, int64_t M, int64_t N, int64_t K, const void *y,
-                         bool scale_align) {
+                         uintptr_t xs_align, uintptr_t ws_align) {
   const bool work = M > 0 && N > 0;
   if (work && (!x_q || !x_scale || !w_q || !w_scale || !y)) return FP8BLK_ERR_NULL;
   if (bad_rows(M) || bad_rows(N) || bad_k(K) || too_big(M, K) || too_big(N, K) ||
@@ -69,7 +71,7 @@ fp8blk_status check_gemm(const void *x_q, const void *x_scale, const void *w_q,
     return FP8BLK_ERR_SHAPE;
   if (work && ((M + 127) / 128) * ((N + 127) / 128) > kMaxRows) return FP8BLK_ERR_SHAPE;
   if (work && (misaligned(x_q) || misaligned(w_q) || misaligned(y) ||
-               (scale_align && (misaligned(x_scale) || misaligned(w_scale)))))
+               misaligned(x_scale, xs_align) || misaligned(w_scale, ws_align)))
     return FP8BLK_ERR_ALIGN;
   return check_device();
 }
@@ -77,7 +79,7 @@ fp8blk_status check_gemm(const void *x_q, const void *x_scale, const void *w_q,
 fp8blk_status check_grouped(const void *x_q, const void *x_scale, const void *w_q,
                             const void *w_scale, const int32_t *offsets, int32_t E,
                             int64_t total_M, int64_t N, int64_t K, const void *y,
-                            bool scale_align) {
+                            uintptr_t scale_align) {
   const bool work = E > 0 && total_M > 0 && N > 0;
   if (work && (!x_q || !x_scale || !w_q || !w_scale || !offsets || !y)) return FP8BLK_ERR_NULL;
   if (E < 0 || bad_rows(total_M) || bad_rows(N) || bad_k(K) || too_big(total_M, K) ||
@@ -85,7 +87,7 @@ fp8blk_status check_grouped(const void *x_q, const void *x_scale, const void *w_
     return FP8BLK_ERR_SHAPE;
   if (work && ((total_M + 127) / 128 + E) * ((N + 127) / 128) > kMaxRows) return FP8BLK_ERR_SHAPE;
   if (work && (misaligned(x_q) || misaligned(w_q) || misaligned(y) ||
-               (scale_align && (misaligned(x_scale) || misaligned(w_scale)))))
+               misaligned(x_scale, scale_align) || misaligned(w_scale, scale_align)))
     return FP8BLK_ERR_ALIGN;
   return check_device();
 }
@@ -110,7 +112,7 @@ int fp8blk_abi_version(void) { return FP8BLK_ABI_VERSION; }
 
 fp8blk_status fp8_weight_block_quant(const void *w_bf16, int64_t N, int64_t K, void *w_q,
                                      float *w_scale, void *stream) {
-  if (fp8blk_status c = check_quant(w_bf16, N, K, w_q, w_scale, true)) return c;
+  if (fp8blk_status c = check_quant(w_bf16, N, K, w_q, w_scale, 16)) return c;
   if (N == 0) return FP8BLK_OK;
   return launched(fp8blk::launch_weight_quant(w_bf16, N, K, w_q, w_scale,
                                               static_cast<hipStream_t>(stream)));
@@ -118,7 +120,7 @@ fp8blk_status fp8_weight_block_quant(const void *w_bf16, int64_t N, int64_t K, v
 
 fp8blk_status fp8_act_quant_group(const void *x_bf16, int64_t M, int64_t K, void *x_q,
                                   float *x_scale, void *stream) {
-  if (fp8blk_status c = check_quant(x_bf16, M, K, x_q, x_scale, true)) return c;
+  if (fp8blk_status c = check_quant(x_bf16, M, K, x_q, x_scale, 16)) return c;
   if (M == 0) return FP8BLK_OK;
   return launched(fp8blk::launch_act_quant(x_bf16, M, K, x_q, x_scale,
                                            static_cast<hipStream_t>(stream)));
@@ -127,7 +129,7 @@ fp8blk_status fp8_act_quant_group(const void *x_bf16, int64_t M, int64_t K, void
 fp8blk_status fp8_block_gemm(const void *x_q, const float *x_scale, const void *w_q,
                              const float *w_scale, int64_t M, int64_t N, int64_t K, void *y_bf16,
                              void *stream) {
-  if (fp8blk_status c = check_gemm(x_q, x_scale, w_q, w_scale, M, N, K, y_bf16, true)) return c;
+  if (fp8blk_status c = check_gemm(x_q, x_scale, w_q, w_scale, M, N, K, y_bf16, 16, 16)) return c;
   if (M == 0 || N == 0) return FP8BLK_OK;
   return launched(fp8blk::launch_block_gemm(x_q, x_scale, w_q, w_scale, M, N, K, y_bf16,
                                             static_cast<hipStream_t>(stream)));
@@ -138,7 +140,7 @@ fp8blk_status fp8_grouped_block_gemm(const void *x_q, const float *x_scale, cons
                                      int32_t E, int64_t total_M, int64_t N, int64_t K,
                                      void *y_bf16, void *stream) {
   if (fp8blk_status c = check_grouped(x_q, x_scale, w_q, w_scale, expert_offsets, E, total_M, N,
-                                      K, y_bf16, true))
+                                      K, y_bf16, 16))
     return c;
   if (E == 0 || total_M == 0 || N == 0) return FP8BLK_OK;
   return launched(fp8blk::launch_grouped_gemm(x_q, x_scale, w_q, w_scale, expert_offsets, E,
@@ -146,9 +148,26 @@ fp8blk_status fp8_grouped_block_gemm(const void *x_q, const float *x_scale, cons
                                               static_cast<hipStream_t>(stream)));
 }
 
+fp8blk_status fp8_act_quant_static(const void *x_bf16, int64_t M, int64_t K,
+                                   const float *x_scale, void *x_q, void *stream) {
+  if (fp8blk_status c = check_quant(x_bf16, M, K, x_q, x_scale, 4)) return c;
+  if (M == 0) return FP8BLK_OK;
+  return launched(fp8blk::launch_act_quant_static(x_bf16, M, K, x_scale, x_q,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
+fp8blk_status fp8_block_gemm_static(const void *x_q, const float *x_scale, const void *w_q,
+                                    const float *w_scale, int64_t M, int64_t N, int64_t K,
+                                    void *y_bf16, void *stream) {
+  if (fp8blk_status c = check_gemm(x_q, x_scale, w_q, w_scale, M, N, K, y_bf16, 4, 16)) return c;
+  if (M == 0 || N == 0) return FP8BLK_OK;
+  return launched(fp8blk::launch_block_gemm_static(x_q, x_scale, w_q, w_scale, M, N, K, y_bf16,
+                                                   static_cast<hipStream_t>(stream)));
+}
+
 fp8blk_status fp8_weight_block_quant_ue8m0(const void *w_bf16, int64_t N, int64_t K, void *w_q,
                                            uint8_t *w_scale, void *stream) {
-  if (fp8blk_status c = check_quant(w_bf16, N, K, w_q, w_scale, false)) return c;
+  if (fp8blk_status c = check_quant(w_bf16, N, K, w_q, w_scale, 1)) return c;
   if (N == 0) return FP8BLK_OK;
   return launched(fp8blk::launch_weight_quant_e8m0(w_bf16, N, K, w_q, w_scale,
                                                    static_cast<hipStream_t>(stream)));
@@ -156,7 +175,7 @@ fp8blk_status fp8_weight_block_quant_ue8m0(const void *w_bf16, int64_t N, int64_
 
 fp8blk_status fp8_act_quant_group_ue8m0(const void *x_bf16, int64_t M, int64_t K, void *x_q,
                                         uint8_t *x_scale, void *stream) {
-  if (fp8blk_status c = check_quant(x_bf16, M, K, x_q, x_scale, false)) return c;
+  if (fp8blk_status c = check_quant(x_bf16, M, K, x_q, x_scale, 1)) return c;
   if (M == 0) return FP8BLK_OK;
   return launched(fp8blk::launch_act_quant_e8m0(x_bf16, M, K, x_q, x_scale,
                                                 static_cast<hipStream_t>(stream)));
@@ -165,7 +184,7 @@ fp8blk_status fp8_act_quant_group_ue8m0(const void *x_bf16, int64_t M, int64_t K
 fp8blk_status fp8_block_gemm_ue8m0(const void *x_q, const uint8_t *x_scale, const void *w_q,
                                    const uint8_t *w_scale, int64_t M, int64_t N, int64_t K,
                                    void *y_bf16, void *stream) {
-  if (fp8blk_status c = check_gemm(x_q, x_scale, w_q, w_scale, M, N, K, y_bf16, false)) return c;
+  if (fp8blk_status c = check_gemm(x_q, x_scale, w_q, w_scale, M, N, K, y_bf16, 1, 1)) return c;
   if (M == 0 || N == 0) return FP8BLK_OK;
   return launched(fp8blk::launch_block_gemm_e8m0(x_q, x_scale, w_q, w_scale, M, N, K, y_bf16,
                                                  static_cast<hipStream_t>(stream)));
@@ -177,7 +196,7 @@ fp8blk_status fp8_grouped_block_gemm_ue8m0(const void *x_q, const uint8_t *x_sca
                                            int64_t total_M, int64_t N, int64_t K, void *y_bf16,
                                            void *stream) {
   if (fp8blk_status c = check_grouped(x_q, x_scale, w_q, w_scale, expert_offsets, E, total_M, N,
-                                      K, y_bf16, false))
+                                      K, y_bf16, 1))
     return c;
   if (E == 0 || total_M == 0 || N == 0) return FP8BLK_OK;
   return launched(fp8blk::launch_grouped_gemm_e8m0(x_q, x_scale, w_q, w_scale, expert_offsets, E,

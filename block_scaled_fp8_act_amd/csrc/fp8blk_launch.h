@@ -10,6 +10,11 @@ hipError_t launch_act_quant(const void *x, int64_t M, int64_t K, void *q, float 
                             hipStream_t stream);
 hipError_t launch_weight_quant(const void *w, int64_t N, int64_t K, void *q, float *s,
                                hipStream_t stream);
+hipError_t launch_act_quant_static(const void *x, int64_t M, int64_t K, const float *s, void *q,
+                                   hipStream_t stream);
+hipError_t launch_block_gemm_static(const void *xq, const float *xs, const void *wq,
+                                    const float *ws, int64_t M, int64_t N, int64_t K, void *y,
+                                    hipStream_t stream);
 hipError_t launch_act_quant_e8m0(const void *x, int64_t M, int64_t K, void *q, uint8_t *s,
                                  hipStream_t stream);
 hipError_t launch_weight_quant_e8m0(const void *w, int64_t N, int64_t K, void *q, uint8_t *s,

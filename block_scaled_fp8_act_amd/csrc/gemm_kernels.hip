@@ -117,7 +117,9 @@ __device__ __forceinline__ int swz(int row, int chunk) {
 }
 
 // One output tile.  A: x_q at the tile's first row (row stride K bytes),
-// rows_a valid rows; As: x_scale at that row (row stride KB floats); B: w_q
+// rows_a valid rows; As: x_scale at that row, element (r, kb) at
+// As[r*xs_rs + kb*xs_ks] -- (KB, 1) for per-token-group scales, (0, 0) for
+// one static scale; B: w_q
 // at the tile's first column's row, rows_b valid rows; Bs: w_scale row of
 // that first column's 128-block; Y: y at the tile origin (row stride ldy).
 // Rows past rows_a / rows_b are read from the last valid row (never out of
@@ -130,8 +132,8 @@ __device__ __forceinline__ int swz(int row, int chunk) {
 // this order so the FMAs fill the MFMA shadow without waiting on a result.
 template <int WM, int WN, int FM>
 __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ A,
-                                          const float *__restrict__ As, int rows_a,
-                                          const uint8_t *__restrict__ B,
+                                          const float *__restrict__ As, int64_t xs_rs, int xs_ks,
+                                          int rows_a, const uint8_t *__restrict__ B,
                                           const float *__restrict__ Bs, int rows_b, int64_t K,
                                           uint16_t *__restrict__ Y, int64_t ldy,
                                           typename Tile<WM, WN, FM>::Smem &sm) {
@@ -162,7 +164,7 @@ __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ A,
     ob[i] = (uint32_t)min(row, rows_b - 1) * (uint32_t)K + lchunk * 16;
   }
   // Activation scales of rows 64w + l (waves w < TM/64).
-  const float *ps = As + (int64_t)min(64 * wave + lane, rows_a - 1) * KB;
+  const float *ps = As + (int64_t)min(64 * wave + lane, rows_a - 1) * xs_rs;
   // Weight-block scales of the tile's column blocks (TN / 128 of them),
   // DMA'd with the stage by lanes 0..TN/128-1 of wave TM/64 (clamped to the
   // last existing block row of a short tile; such columns are not stored).
@@ -181,7 +183,7 @@ __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ A,
 #pragma unroll
     for (int i = 0; i < T::kDmaB; ++i)
       lds_dma16(bk + ob[i], sm.b[st] + (T::kDmaB * wave + i) * 1024);
-    if (wave < T::TM / 64) lds_dma4(ps + kb, &sm.as[st][64 * wave]);
+    if (wave < T::TM / 64) lds_dma4(ps + (int64_t)kb * xs_ks, &sm.as[st][64 * wave]);
     if (wave == T::TM / 64 && lane < kNbTile) lds_dma4(pws + kb, &sm.ws[st][0]);
   };
 
@@ -504,8 +506,9 @@ constexpr int kDecMaxScaleBytes = 32 * 1024;  // x_scale staging limit (KB * MF 
 // matrix core (nothing staged in LDS but the final partials).
 template <int MF, typename S>
 __global__ __launch_bounds__(kDecThreads) void decode_gemm_kernel(
-    const uint8_t *__restrict__ xq, const S *__restrict__ xs, const uint8_t *__restrict__ wq,
-    const S *__restrict__ ws, int M, int64_t N, int64_t K, uint16_t *__restrict__ y) {
+    const uint8_t *__restrict__ xq, const S *__restrict__ xs, int64_t xs_rs, int xs_ks,
+    const uint8_t *__restrict__ wq, const S *__restrict__ ws, int M, int64_t N, int64_t K,
+    uint16_t *__restrict__ y) {
   constexpr bool MX = std::is_same<S, uint8_t>::value;
   constexpr int R = MF * 16;                  // staged rows
   constexpr int U = 4 / MF;                   // K blocks in flight per wave
@@ -560,7 +563,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_gemm_kernel(
   if constexpr (!MX) {
     for (int i = t; i < KB * R; i += kDecThreads) {
       const int kb = i / R, m = i % R;
-      s_as[i] = xs[(int64_t)min(m, M - 1) * KB + kb];
+      s_as[i] = xs[(int64_t)min(m, M - 1) * xs_rs + (int64_t)kb * xs_ks];
     }
     __syncthreads();
   }
@@ -619,16 +622,17 @@ __global__ __launch_bounds__(kDecThreads) void decode_gemm_kernel(
 }
 
 template <int MF, typename S>
-static hipError_t launch_decode(const void *xq, const S *xs, const void *wq, const S *ws,
-                                int64_t M, int64_t N, int64_t K, void *y, hipStream_t stream) {
+static hipError_t launch_decode(const void *xq, const S *xs, int64_t xs_rs, int xs_ks,
+                                const void *wq, const S *ws, int64_t M, int64_t N, int64_t K,
+                                void *y, hipStream_t stream) {
   const int64_t KB = K / 128;
   const size_t part = (size_t)kDecWaves * MF * 64 * 16;
   const size_t lds = std::is_same<S, uint8_t>::value
                          ? part
                          : std::max((size_t)KB * MF * 16 * 4, part);
   hipLaunchKernelGGL((decode_gemm_kernel<MF, S>), dim3((unsigned)((N + 15) / 16)),
-                     dim3(kDecThreads), lds, stream, static_cast<const uint8_t *>(xq), xs,
-                     static_cast<const uint8_t *>(wq), ws, (int)M, N, K,
+                     dim3(kDecThreads), lds, stream, static_cast<const uint8_t *>(xq), xs, xs_rs,
+                     xs_ks, static_cast<const uint8_t *>(wq), ws, (int)M, N, K,
                      static_cast<uint16_t *>(y));
   return hipGetLastError();
 }
@@ -659,31 +663,33 @@ struct TileSmem {
                                          typename Tile<WM, WN, FM>::Smem>::type;
 };
 
+// xs_rs / xs_ks address the fp32 activation scales (E8M0 bytes always use
+// the per-token-group layout).
 template <int WM, int WN, int FM, typename S>
-__device__ __forceinline__ void run_tile(const uint8_t *A, const S *As, int rows_a,
-                                         const uint8_t *B, const S *Bs, int rows_b, int64_t K,
-                                         uint16_t *Y, int64_t ldy,
+__device__ __forceinline__ void run_tile(const uint8_t *A, const S *As, int64_t xs_rs, int xs_ks,
+                                         int rows_a, const uint8_t *B, const S *Bs, int rows_b,
+                                         int64_t K, uint16_t *Y, int64_t ldy,
                                          typename TileSmem<WM, WN, FM, S>::type &sm) {
   if constexpr (std::is_same<S, uint8_t>::value)
     gemm_tile_mx<WM, WN, FM, (FM <= 4)>(A, As, rows_a, B, Bs, rows_b, K, Y, ldy, sm);
   else
-    gemm_tile<WM, WN, FM>(A, As, rows_a, B, Bs, rows_b, K, Y, ldy, sm);
+    gemm_tile<WM, WN, FM>(A, As, xs_rs, xs_ks, rows_a, B, Bs, rows_b, K, Y, ldy, sm);
 }
 
 template <int WM, int WN, int FM, typename S>
 __global__ __launch_bounds__(WM * WN * 64) void block_gemm_kernel(
-    const uint8_t *__restrict__ xq, const S *__restrict__ xs, const uint8_t *__restrict__ wq,
-    const S *__restrict__ ws, int64_t M, int64_t N, int64_t K, uint16_t *__restrict__ y,
-    int tiles_m, int tiles_n) {
+    const uint8_t *__restrict__ xq, const S *__restrict__ xs, int64_t xs_rs, int xs_ks,
+    const uint8_t *__restrict__ wq, const S *__restrict__ ws, int64_t M, int64_t N, int64_t K,
+    uint16_t *__restrict__ y, int tiles_m, int tiles_n) {
   using T = Tile<WM, WN, FM>;
   __shared__ typename TileSmem<WM, WN, FM, S>::type sm;
   int tm, tn;
   tile_coords(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * T::TM, n0 = (int64_t)tn * T::TN;
   const int64_t KB = K / 128;
-  run_tile<WM, WN, FM, S>(xq + m0 * K, xs + m0 * KB, (int)min<int64_t>(T::TM, M - m0),
-                          wq + n0 * K, ws + (n0 / 128) * KB, (int)min<int64_t>(T::TN, N - n0), K,
-                          y + m0 * N + n0, N, sm);
+  run_tile<WM, WN, FM, S>(xq + m0 * K, xs + m0 * xs_rs, xs_rs, xs_ks,
+                          (int)min<int64_t>(T::TM, M - m0), wq + n0 * K, ws + (n0 / 128) * KB,
+                          (int)min<int64_t>(T::TN, N - n0), K, y + m0 * N + n0, N, sm);
 }
 
 // Grouped variant.  The logical m-tiles of all experts are numbered
@@ -693,9 +699,10 @@ __global__ __launch_bounds__(WM * WN * 64) void block_gemm_kernel(
 // to [0, total_M].
 template <int WM, int WN, int FM, typename S>
 __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(
-    const uint8_t *__restrict__ xq, const S *__restrict__ xs, const uint8_t *__restrict__ wq,
-    const S *__restrict__ ws, const int32_t *__restrict__ offsets, int E, int64_t total_M,
-    int64_t N, int64_t K, uint16_t *__restrict__ y, int tiles_n) {
+    const uint8_t *__restrict__ xq, const S *__restrict__ xs, int64_t xs_rs, int xs_ks,
+    const uint8_t *__restrict__ wq, const S *__restrict__ ws,
+    const int32_t *__restrict__ offsets, int E, int64_t total_M, int64_t N, int64_t K,
+    uint16_t *__restrict__ y, int tiles_n) {
   using T = Tile<WM, WN, FM>;
   __shared__ typename TileSmem<WM, WN, FM, S>::type sm;
   const int tn = blockIdx.x % tiles_n;
@@ -718,21 +725,22 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(
   const int64_t n0 = (int64_t)tn * T::TN;
   const int64_t KB = K / 128;
   const int64_t NB = (N + 127) / 128;
-  run_tile<WM, WN, FM, S>(xq + r0 * K, xs + r0 * KB, (int)min<int64_t>(T::TM, r1 - r0),
-                          wq + (int64_t)e * N * K + n0 * K,
+  run_tile<WM, WN, FM, S>(xq + r0 * K, xs + r0 * xs_rs, xs_rs, xs_ks,
+                          (int)min<int64_t>(T::TM, r1 - r0), wq + (int64_t)e * N * K + n0 * K,
                           ws + ((int64_t)e * NB + n0 / 128) * KB,
                           (int)min<int64_t>(T::TN, N - n0), K, y + r0 * N + n0, N, sm);
 }
 
 template <int WM, int WN, int FM, typename S>
-static hipError_t launch_tiled(const void *xq, const S *xs, const void *wq, const S *ws,
-                               int64_t M, int64_t N, int64_t K, void *y, hipStream_t stream) {
+static hipError_t launch_tiled(const void *xq, const S *xs, int64_t xs_rs, int xs_ks,
+                               const void *wq, const S *ws, int64_t M, int64_t N, int64_t K,
+                               void *y, hipStream_t stream) {
   using T = Tile<WM, WN, FM>;
   const int tm = (int)((M + T::TM - 1) / T::TM), tn = (int)((N + T::TN - 1) / T::TN);
   hipLaunchKernelGGL((block_gemm_kernel<WM, WN, FM, S>), dim3((unsigned)(tm * tn)),
-                     dim3(T::kThreads), 0, stream, static_cast<const uint8_t *>(xq), xs,
-                     static_cast<const uint8_t *>(wq), ws, M, N, K, static_cast<uint16_t *>(y),
-                     tm, tn);
+                     dim3(T::kThreads), 0, stream, static_cast<const uint8_t *>(xq), xs, xs_rs,
+                     xs_ks, static_cast<const uint8_t *>(wq), ws, M, N, K,
+                     static_cast<uint16_t *>(y), tm, tn);
   return hipGetLastError();
 }
 
@@ -740,19 +748,21 @@ static hipError_t launch_tiled(const void *xq, const S *xs, const void *wq, cons
 // (fp32 scales: while its LDS scale staging fits), 256x256 tiles when they
 // fill the chip (>= 192 tiles), 128x128 otherwise.
 template <typename S>
-static hipError_t dispatch_gemm(const void *xq, const S *xs, const void *wq, const S *ws,
-                                int64_t M, int64_t N, int64_t K, void *y, hipStream_t stream) {
+static hipError_t dispatch_gemm(const void *xq, const S *xs, int64_t xs_rs, int xs_ks,
+                                const void *wq, const S *ws, int64_t M, int64_t N, int64_t K,
+                                void *y, hipStream_t stream) {
   if (M <= kDecMaxM) {
     const int MF = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
     if (std::is_same<S, uint8_t>::value || (K / 128) * MF * 16 * 4 <= kDecMaxScaleBytes) {
-      if (MF == 1) return launch_decode<1, S>(xq, xs, wq, ws, M, N, K, y, stream);
-      if (MF == 2) return launch_decode<2, S>(xq, xs, wq, ws, M, N, K, y, stream);
-      return launch_decode<4, S>(xq, xs, wq, ws, M, N, K, y, stream);
+      if (MF == 1) return launch_decode<1, S>(xq, xs, xs_rs, xs_ks, wq, ws, M, N, K, y, stream);
+      if (MF == 2) return launch_decode<2, S>(xq, xs, xs_rs, xs_ks, wq, ws, M, N, K, y, stream);
+      return launch_decode<4, S>(xq, xs, xs_rs, xs_ks, wq, ws, M, N, K, y, stream);
     }
   }
   const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
-  if (big_tiles >= 192) return launch_tiled<2, 4, 8, S>(xq, xs, wq, ws, M, N, K, y, stream);
-  return launch_tiled<2, 2, 4, S>(xq, xs, wq, ws, M, N, K, y, stream);
+  if (big_tiles >= 192)
+    return launch_tiled<2, 4, 8, S>(xq, xs, xs_rs, xs_ks, wq, ws, M, N, K, y, stream);
+  return launch_tiled<2, 2, 4, S>(xq, xs, xs_rs, xs_ks, wq, ws, M, N, K, y, stream);
 }
 
 template <typename S>
@@ -763,21 +773,27 @@ static hipError_t dispatch_grouped(const void *xq, const S *xs, const void *wq, 
   const int64_t tiles_n = (N + T::TN - 1) / T::TN;
   const int64_t tiles_m = (total_M + T::TM - 1) / T::TM + E;
   hipLaunchKernelGGL((grouped_gemm_kernel<2, 4, 8, S>), dim3((unsigned)(tiles_m * tiles_n)),
-                     dim3(T::kThreads), 0, stream, static_cast<const uint8_t *>(xq), xs,
-                     static_cast<const uint8_t *>(wq), ws, offsets, (int)E, total_M, N, K,
+                     dim3(T::kThreads), 0, stream, static_cast<const uint8_t *>(xq), xs, K / 128,
+                     1, static_cast<const uint8_t *>(wq), ws, offsets, (int)E, total_M, N, K,
                      static_cast<uint16_t *>(y), (int)tiles_n);
   return hipGetLastError();
 }
 
 hipError_t launch_block_gemm(const void *xq, const float *xs, const void *wq, const float *ws,
                              int64_t M, int64_t N, int64_t K, void *y, hipStream_t stream) {
-  return dispatch_gemm<float>(xq, xs, wq, ws, M, N, K, y, stream);
+  return dispatch_gemm<float>(xq, xs, K / 128, 1, wq, ws, M, N, K, y, stream);
+}
+
+hipError_t launch_block_gemm_static(const void *xq, const float *xs, const void *wq,
+                                    const float *ws, int64_t M, int64_t N, int64_t K, void *y,
+                                    hipStream_t stream) {
+  return dispatch_gemm<float>(xq, xs, 0, 0, wq, ws, M, N, K, y, stream);
 }
 
 hipError_t launch_block_gemm_e8m0(const void *xq, const uint8_t *xs, const void *wq,
                                   const uint8_t *ws, int64_t M, int64_t N, int64_t K, void *y,
                                   hipStream_t stream) {
-  return dispatch_gemm<uint8_t>(xq, xs, wq, ws, M, N, K, y, stream);
+  return dispatch_gemm<uint8_t>(xq, xs, K / 128, 1, wq, ws, M, N, K, y, stream);
 }
 
 hipError_t launch_grouped_gemm(const void *xq, const float *xs, const void *wq, const float *ws,

@@ -161,6 +161,37 @@ __global__ __launch_bounds__(kActThreads) void act_quant_e8m0_kernel(
   }
 }
 
+// Static variant: one caller-supplied scale for the whole tensor (device
+// memory, read once per thread), q = E4M3_RNE(sat(fl32(x / s))).  The
+// quotient is the IEEE division (the compiler's correctly rounded sequence;
+// an arbitrary calibrated s has no precomputed reciprocal that is exact for
+// every x), then clamped to +-448 -- here inputs can exceed the calibrated
+// range, and the conversion without its clamp bit returns NaN from 464.
+// Each thread converts 16 consecutive elements per iteration (two 16-byte
+// loads, one 16-byte store).
+constexpr int kStaticThreads = 256;
+
+__device__ __forceinline__ float sat448(float t) { return fminf(fmaxf(t, -448.0f), 448.0f); }
+
+__global__ __launch_bounds__(kStaticThreads) void act_quant_static_kernel(
+    const uint4 *__restrict__ x, uint4 *__restrict__ q, const float *__restrict__ scale,
+    int64_t n16) {
+  const float s = *scale;
+  const int64_t stride = (int64_t)gridDim.x * kStaticThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kStaticThreads + threadIdx.x; i < n16; i += stride) {
+    const uint4 v0 = x[2 * i], v1 = x[2 * i + 1];
+    float f[16];
+    unpack8(v0, f);
+    unpack8(v1, f + 8);
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      w[j] = pack4_e4m3(sat448(f[4 * j] / s), sat448(f[4 * j + 1] / s), sat448(f[4 * j + 2] / s),
+                        sat448(f[4 * j + 3] / s));
+    q[i] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Weight quantizer: one workgroup per 128x128 block.  Thread t reads, for
 // i = 0..7, the 16 bytes at row i*16 + t/16, columns (t%16)*8 .. +8 of the
@@ -259,6 +290,16 @@ hipError_t launch_act_quant_e8m0(const void *x, int64_t M, int64_t K, void *q, u
   hipLaunchKernelGGL(act_quant_e8m0_kernel, dim3(act_quant_blocks(n_groups)), dim3(kActThreads),
                      0, stream, static_cast<const uint4 *>(x), static_cast<uint2 *>(q), s,
                      n_groups);
+  return hipGetLastError();
+}
+
+hipError_t launch_act_quant_static(const void *x, int64_t M, int64_t K, const float *s, void *q,
+                                   hipStream_t stream) {
+  const int64_t n16 = M * K / 16;  // K % 128 == 0
+  int64_t blocks = (n16 + kStaticThreads - 1) / kStaticThreads;
+  if (blocks > 256 * 8) blocks = 256 * 8;
+  hipLaunchKernelGGL(act_quant_static_kernel, dim3((unsigned)blocks), dim3(kStaticThreads), 0,
+                     stream, static_cast<const uint4 *>(x), static_cast<uint4 *>(q), s, n16);
   return hipGetLastError();
 }
 

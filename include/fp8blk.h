@@ -37,8 +37,8 @@
  *     a last weight block row with fewer than 128 rows covers only the rows
  *     that exist.  M == 0 or N == 0 (or E == 0) is a no-op returning OK.
  *   - Every tensor base pointer must be 16-byte aligned (expert_offsets:
- *     4-byte aligned, as an int32 array; E8M0 scale-byte arrays: any
- *     address).
+ *     4-byte aligned, as an int32 array; a single static scale: 4-byte
+ *     aligned; E8M0 scale-byte arrays: any address).
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
  *     stream).  Inputs must stay valid until the stream reaches the launch.
  *     Outputs must not alias inputs.
@@ -127,6 +127,33 @@ FP8BLK_API fp8blk_status fp8_grouped_block_gemm(const void *x_q, const float *x_
                                                 const int32_t *expert_offsets, int32_t E,
                                                 int64_t total_M, int64_t N, int64_t K,
                                                 void *y_bf16, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Static activation scale.
+ * "Fine-grained FP8" page, "DeepGEMM fast path": besides the dynamic scheme
+ * the page names static activation quantization (its back-ends keep it on
+ * the Triton path).  Readings fixed here: one calibrated fp32 scale s for
+ * the whole activation tensor, supplied by the caller in DEVICE memory (one
+ * float, 4-byte aligned; it may change between calls without a host sync),
+ * with the meaning of the dynamic scales (x ~= dec(q) * s);
+ * q = E4M3_RNE(sat(fl32(x / s))), the IEEE quotient saturated to +-448 (the
+ * inputs may exceed the calibrated range).  s must be positive and finite;
+ * otherwise results are unspecified (the kernels stay in bounds). */
+
+/* Static activation quantization.
+ *   x_bf16 [M,K] bf16 in; x_scale DEVICE fp32 [1] in; x_q [M,K] E4M3 out. */
+FP8BLK_API fp8blk_status fp8_act_quant_static(const void *x_bf16, int64_t M, int64_t K,
+                                              const float *x_scale, void *x_q, void *stream);
+
+/* Block-scaled FP8 GEMM with one static activation scale:
+ * y[m,n] = bf16( sum_kb x_scale * w_scale[n/128,kb] * sum_{k in kb}
+ *                dec(x_q[m,k]) dec(w_q[n,k]) ), fp32 accumulation.
+ *   x_q [M,K], x_scale DEVICE fp32 [1], w_q [N,K], w_scale [ceil(N/128),K/128]
+ *   in; y_bf16 [M,N] out. */
+FP8BLK_API fp8blk_status fp8_block_gemm_static(const void *x_q, const float *x_scale,
+                                               const void *w_q, const float *w_scale,
+                                               int64_t M, int64_t N, int64_t K,
+                                               void *y_bf16, void *stream);
 
 /* ------------------------------------------------------------------------
  * Power-of-two scales stored as E8M0 bytes.

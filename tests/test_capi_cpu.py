@@ -136,3 +136,49 @@ def test_binding_raises_without_device():
     x = torch.zeros(4, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         fb.act_quant_group(x)  # CPU tensor: refused, no fallback
+
+
+MIS1 = 0x10001       # odd address
+MIS4 = 0x10004       # 4-byte aligned only
+
+
+@pytest.mark.parametrize("name", ["fp8_act_quant_group_ue8m0", "fp8_weight_block_quant_ue8m0"])
+def test_ue8m0_quant_validation(lib, name):
+    assert call(lib, name, NULL, 4, 128, B, C, NULL) == 1
+    assert call(lib, name, A, 4, 100, B, C, NULL) == 2
+    assert call(lib, name, MIS, 4, 128, B, C, NULL) == 3
+    # E8M0 byte arrays may sit at any address: the next check is the device
+    import torch
+    if not torch.cuda.is_available():
+        assert call(lib, name, A, 4, 128, B, MIS1, NULL) == 4
+
+
+def test_ue8m0_gemm_validation(lib):
+    assert call(lib, "fp8_block_gemm_ue8m0", NULL, B, C, D, 4, 256, 128, E_, NULL) == 1
+    assert call(lib, "fp8_block_gemm_ue8m0", A, B, C, D, 4, 256, 192, E_, NULL) == 2
+    assert call(lib, "fp8_block_gemm_ue8m0", A, B, C, D, 4, 256, 128, MIS, NULL) == 3
+    assert call(lib, "fp8_grouped_block_gemm_ue8m0", A, B, C, D, NULL, 4, 64, 256, 128, E_, NULL) == 1
+    assert call(lib, "fp8_grouped_block_gemm_ue8m0", A, B, MIS, D, A, 4, 64, 256, 128, E_, NULL) == 3
+    import torch
+    if not torch.cuda.is_available():
+        assert call(lib, "fp8_block_gemm_ue8m0", A, MIS1, C, MIS1, 4, 256, 128, E_, NULL) == 4
+
+
+def test_static_validation(lib):
+    # fp8_act_quant_static(x, M, K, x_scale, x_q, stream)
+    assert call(lib, "fp8_act_quant_static", NULL, 4, 128, B, C, NULL) == 1
+    assert call(lib, "fp8_act_quant_static", A, 4, 128, NULL, C, NULL) == 1
+    assert call(lib, "fp8_act_quant_static", A, 4, 96, B, C, NULL) == 2
+    assert call(lib, "fp8_act_quant_static", A, 4, 128, MIS1, C, NULL) == 3   # scale: 4-byte
+    assert call(lib, "fp8_act_quant_static", A, 4, 128, B, MIS, NULL) == 3
+    # fp8_block_gemm_static(x_q, x_scale, w_q, w_scale, M, N, K, y, stream)
+    assert call(lib, "fp8_block_gemm_static", A, NULL, C, D, 4, 256, 128, E_, NULL) == 1
+    assert call(lib, "fp8_block_gemm_static", A, B, C, D, 4, 256, 64, E_, NULL) == 2
+    assert call(lib, "fp8_block_gemm_static", A, MIS1, C, D, 4, 256, 128, E_, NULL) == 3
+    assert call(lib, "fp8_block_gemm_static", A, B, C, MIS, 4, 256, 128, E_, NULL) == 3
+    import torch
+    if not torch.cuda.is_available():
+        assert call(lib, "fp8_act_quant_static", A, 4, 128, MIS4, C, NULL) == 4
+        assert call(lib, "fp8_block_gemm_static", A, MIS4, C, D, 4, 256, 128, E_, NULL) == 4
+        # empty shapes validate fully, then the device check still comes first
+        assert call(lib, "fp8_block_gemm_static", A, B, C, D, 0, 256, 128, E_, NULL) == 4
