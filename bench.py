@@ -8,9 +8,10 @@ Inputs are resident in HBM before the timed region; two input/output sets
 (about 1 GB) are rotated between steps so that the 256 MB last-level cache
 does not hold a step's working set.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
-                    [--rows]  (also time weight quant, decode, MoE and the
-                               power-of-two (UE8M0) scale rows)
+    python bench.py [--gpus 1] [--steps 50] [--warmup 30] [--no-cpu-baseline]
+                    [--rows]  (also time weight quant, decode, MoE, the
+                               power-of-two (UE8M0) scale rows and the static
+                               activation scale rows)
 
 Prints one JSON line.  ``value`` is the whole step's throughput in TFLOP/s
 (GEMM FLOPs of the four projections / step time, the activation
@@ -42,8 +43,11 @@ ACT_BYTES_PER_ELEM = 2 + 1 + 4 / 128   # bf16 in, e4m3 out, one fp32 scale per 1
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    # the first ~20 steps of a fresh process run up to 20 % slower while the
+    # device ramps up (measured); 30 untimed steps put the timed ones in the
+    # steady state
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rows", action="store_true", help="also time the other hot-path rows")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -158,45 +162,22 @@ def main():
     gemm_flops = [2.0 * M_PREFILL * N * K for (_, N, K) in PREFILL_SHAPES]
     act_bytes = [M_PREFILL * K * ACT_BYTES_PER_ELEM for (_, N, K) in PREFILL_SHAPES]
 
-    def step(i, ev=None):
-        xset, oset = sets[i % 2], outs[i % 2]
-        for p in range(n_proj):
-            xq, xsc, y = oset[p]
-            if ev is not None:
-                ev[p][0].record(stream)
-            fb.fp8_act_quant_group(xset[p], xq, xsc)
-            if ev is not None:
-                ev[p][1].record(stream)
-            fb.fp8_block_gemm(xq, xsc, wq[p], wsc[p], y)
-            if ev is not None:
-                ev[p][2].record(stream)
+    def launch(i, p, ev):
+        xq, xsc, y = outs[i % 2][p]
+        if ev is not None:
+            ev[0].record(stream)
+        fb.fp8_act_quant_group(sets[i % 2][p], xq, xsc)
+        if ev is not None:
+            ev[1].record(stream)
+        fb.fp8_block_gemm(xq, xsc, wq[p], wsc[p], y)
+        if ev is not None:
+            ev[2].record(stream)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    # --- timed region: whole steps ----------------------------------------
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall / args.steps * 1e3
-
-    # --- per-kernel durations with events on the launch stream --------------
-    # (all steps enqueued back to back, one synchronisation at the end, so no
-    # event pair spans the host's launch latency)
-    act_t = [0.0] * n_proj
-    gemm_t = [0.0] * n_proj
-    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_proj)]
-           for _ in range(args.steps)]
-    for i in range(args.steps):
-        step(i, evs[i])
-    torch.cuda.synchronize()
-    for ev in evs:
-        for p in range(n_proj):
-            act_t[p] += ev[p][0].elapsed_time(ev[p][1]) / args.steps
-            gemm_t[p] += ev[p][1].elapsed_time(ev[p][2]) / args.steps
+    # --- timed region: whole steps (then the same steps with events) -------
+    wall, act_s, gemm_s = run_leg(torch, stream, launch, n_proj, args.steps, args.warmup)
+    ms_per_step = wall * 1e3
+    act_t = [t * 1e3 for t in act_s]
+    gemm_t = [t * 1e3 for t in gemm_s]
 
     step_flops = sum(gemm_flops)
     gemm_ms = sum(gemm_t)
@@ -247,6 +228,34 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+def run_leg(torch, stream, launch, n_proj, steps, warmup):
+    """Time one prefill leg.  launch(i, p, ev) enqueues projection p of step
+    i (activation quantization, then GEMM), recording ev[0] before, ev[1]
+    between and ev[2] after the two kernels when ev is given.  Returns the
+    wall time per step (s) and the mean in-step event times of each
+    projection's two kernels (s); all event-timed steps are enqueued back to
+    back with one synchronisation at the end."""
+    for i in range(warmup):
+        for p in range(n_proj):
+            launch(i, p, None)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        for p in range(n_proj):
+            launch(i, p, None)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_proj)]
+           for _ in range(steps)]
+    for i in range(steps):
+        for p in range(n_proj):
+            launch(i, p, evs[i][p])
+    torch.cuda.synchronize()
+    quant = [sum(ev[p][0].elapsed_time(ev[p][1]) for ev in evs) / steps * 1e-3 for p in range(n_proj)]
+    gemm = [sum(ev[p][1].elapsed_time(ev[p][2]) for ev in evs) / steps * 1e-3 for p in range(n_proj)]
+    return wall, quant, gemm
+
+
 def _time(torch, stream, fn, iters=20, warm=3):
     for _ in range(warm):
         fn()
@@ -284,6 +293,7 @@ def other_rows(torch, fb, dev, stream):
         byts = N * K + 16 * K + 2 * 16 * N
         rows[f"decode_M16_{name}"] = {"us": round(t * 1e6, 2), "GB/s": round(byts / t / 1e9, 1)}
     rows.update(ue8m0_rows(torch, fb, dev, stream, g))
+    rows.update(static_rows(torch, fb, dev, stream))
     # grouped MoE (32 experts, Zipf top-8 routing of 4096 tokens)
     _, off = synth.moe_routing()
     total = int(off[-1])
@@ -302,6 +312,43 @@ def other_rows(torch, fb, dev, stream):
     return rows
 
 
+def static_rows(torch, fb, dev, stream):
+    """Static (calibrated, per-tensor) activation scale: the same prefill
+    step with the static quantizer and GEMM, two rotated input sets."""
+    xs0, ws_bf16 = gen_inputs(torch, dev, 3000)
+    sets = [xs0, [torch.roll(x, 1, 0) for x in xs0]]
+    wq, wsc = zip(*[fb.weight_block_quant(w) for w in ws_bf16])
+    del ws_bf16
+    # a calibrated scale: the largest |x| of the first set / 448
+    scales = [(x.abs().amax().float() / 448.0).reshape(1).contiguous() for x in xs0]
+    outs = [[(torch.empty((M_PREFILL, K), dtype=torch.uint8, device=dev),
+              torch.empty((M_PREFILL, N), dtype=torch.bfloat16, device=dev))
+             for (_, N, K) in PREFILL_SHAPES] for _ in sets]
+    flops = sum(2.0 * M_PREFILL * N * K for (_, N, K) in PREFILL_SHAPES)
+
+    def launch(i, p, ev):
+        xq, y = outs[i % 2][p]
+        if ev is not None:
+            ev[0].record(stream)
+        fb.fp8_act_quant_static(sets[i % 2][p], scales[p], xq)
+        if ev is not None:
+            ev[1].record(stream)
+        fb.fp8_block_gemm_static(xq, scales[p], wq[p], wsc[p], y)
+        if ev is not None:
+            ev[2].record(stream)
+
+    dt, ta, tg = run_leg(torch, stream, launch, len(PREFILL_SHAPES), 30, 10)
+    per = {name: {"act_quant_us": round(ta[p] * 1e6, 2),
+                  "act_quant_GB/s": round(3 * M_PREFILL * K / ta[p] / 1e9, 1),
+                  "gemm_us": round(tg[p] * 1e6, 2),
+                  "gemm_TFLOP/s": round(2.0 * M_PREFILL * N * K / tg[p] / 1e12, 1)}
+           for p, (name, N, K) in enumerate(PREFILL_SHAPES)}
+    return {"static_prefill_step": {"ms_per_step": round(dt * 1e3, 4),
+                                    "TFLOP/s": round(flops / dt / 1e12, 1),
+                                    "gemm_TFLOP/s": round(flops / sum(tg) / 1e12, 1),
+                                    "per_projection": per}}
+
+
 def ue8m0_rows(torch, fb, dev, stream, g):
     """Power-of-two (E8M0-byte) scales: the same prefill step (activation
     quantization + GEMM per projection, two rotated input sets), the weight
@@ -317,29 +364,22 @@ def ue8m0_rows(torch, fb, dev, stream, g):
              for (_, N, K) in PREFILL_SHAPES] for _ in sets]
     flops = sum(2.0 * M_PREFILL * N * K for (_, N, K) in PREFILL_SHAPES)
 
-    def step(i):
-        for p, (xq, xe, y) in enumerate(outs[i % 2]):
-            fb.fp8_act_quant_group_ue8m0(sets[i % 2][p], xq, xe)
-            fb.fp8_block_gemm_ue8m0(xq, xe, wq[p], we[p], y)
+    def launch(i, p, ev):
+        xq, xe, y = outs[i % 2][p]
+        if ev is not None:
+            ev[0].record(stream)
+        fb.fp8_act_quant_group_ue8m0(sets[i % 2][p], xq, xe)
+        if ev is not None:
+            ev[1].record(stream)
+        fb.fp8_block_gemm_ue8m0(xq, xe, wq[p], we[p], y)
+        if ev is not None:
+            ev[2].record(stream)
 
-    for i in range(3):
-        step(i)
-    torch.cuda.synchronize()
-    n = 10
-    t0 = time.perf_counter()
-    for i in range(n):
-        step(i)
-    torch.cuda.synchronize()
-    dt = (time.perf_counter() - t0) / n
-    per = {}
-    gemm_s = 0.0
-    for p, (name, N, K) in enumerate(PREFILL_SHAPES):
-        xq, xe, y = outs[0][p]
-        ta = _time(torch, stream, lambda: fb.fp8_act_quant_group_ue8m0(sets[0][p], xq, xe))
-        tg = _time(torch, stream, lambda: fb.fp8_block_gemm_ue8m0(xq, xe, wq[p], we[p], y))
-        gemm_s += tg
-        per[name] = {"act_quant_us": round(ta * 1e6, 2), "gemm_us": round(tg * 1e6, 2),
-                     "gemm_TFLOP/s": round(2.0 * M_PREFILL * N * K / tg / 1e12, 1)}
+    dt, ta, tg = run_leg(torch, stream, launch, len(PREFILL_SHAPES), 30, 10)
+    per = {name: {"act_quant_us": round(ta[p] * 1e6, 2), "gemm_us": round(tg[p] * 1e6, 2),
+                  "gemm_TFLOP/s": round(2.0 * M_PREFILL * N * K / tg[p] / 1e12, 1)}
+           for p, (name, N, K) in enumerate(PREFILL_SHAPES)}
+    gemm_s = sum(tg)
     rows["ue8m0_prefill_step"] = {"ms_per_step": round(dt * 1e3, 4),
                                   "TFLOP/s": round(flops / dt / 1e12, 1),
                                   "gemm_TFLOP/s": round(flops / gemm_s / 1e12, 1),
