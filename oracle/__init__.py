@@ -36,10 +36,14 @@ What is computed, and where it comes from:
   activation scheme): :mod:`oracle.static` states the readings (one
   calibrated fp32 scale per tensor, saturating quotient).
 
+* The batched expert layout and row-wise ("fp8r") scales:
+  :mod:`oracle.layouts` states the readings.
+
 Modules: :mod:`oracle.e4m3` (codec), :mod:`oracle.quant` (quantizers),
 :mod:`oracle.gemm` (block-scaled and grouped GEMM, linear layer),
 :mod:`oracle.ue8m0` (E8M0 scales: codec, quantizers, GEMM),
-:mod:`oracle.static` (static activation scale: quantizer, GEMM).
+:mod:`oracle.static` (static activation scale: quantizer, GEMM),
+:mod:`oracle.layouts` (batched experts; row-wise quantizer and GEMM).
 """
 from .e4m3 import E4M3_MAX, decode, encode, fl32_div
 from .quant import act_quant_group, weight_block_quant, quant_element_map
@@ -49,6 +53,7 @@ from .gemm import (bf16_rne_bits, block_gemm, dequant_act, dequant_weight,
 from .ue8m0 import (act_quant_group_ue8m0, block_gemm_ue8m0, e8m0_decode, e8m0_exponent,
                     grouped_block_gemm_ue8m0, weight_block_quant_ue8m0)
 from .static import act_quant_static, block_gemm_static
+from .layouts import batched_block_gemm, rowwise_gemm, rowwise_quant
 
 __all__ = [
     "E4M3_MAX", "decode", "encode", "fl32_div",
@@ -59,4 +64,5 @@ __all__ = [
     "act_quant_group_ue8m0", "block_gemm_ue8m0", "e8m0_decode", "e8m0_exponent",
     "grouped_block_gemm_ue8m0", "weight_block_quant_ue8m0",
     "act_quant_static", "block_gemm_static",
+    "batched_block_gemm", "rowwise_gemm", "rowwise_quant",
 ]

@@ -20,6 +20,7 @@ from oracle import gemm as og
 from oracle import quant as oq
 from oracle import ue8m0 as ou
 from oracle import static as ost
+from oracle import layouts as olay
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -717,6 +718,75 @@ def pin_static_gemm(seed=73):
     assert np.all(ost.term_magnitude_static(xq, 0.25, wq, ws) >= np.abs(y))
 
 
+# ----------------------------------------------------------------------------
+# batched expert layout and row-wise ("fp8r") scale pins
+
+def pin_batched(seed=79):
+    """The batched layout is the grouped GEMM on each expert's first
+    count[e] rows; counts clamp to [0, C]; rows past the count are NaN."""
+    import synth
+    E, C, N, K = 4, 20, 160, 256
+    counts = np.array([0, 7, 20, 33], np.int32)          # 33 clamps to 20
+    x = synth.normal_bf16(seed, (E * C, K))
+    xq, xs = oq.act_quant_group(x)
+    xq, xs = xq.reshape(E, C, K), xs.reshape(E, C, K // 128)
+    wq = np.empty((E, N, K), np.uint8); ws = np.empty((E, 2, 2), np.float32)
+    for e in range(E):
+        wq[e], ws[e] = oq.weight_block_quant(synth.normal_bf16(seed + 1 + e, (N, K), 0.02))
+    y = olay.batched_block_gemm(xq, xs, wq, ws, counts)
+    used = [min(max(int(c), 0), C) for c in counts]
+    off = np.concatenate([[0], np.cumsum(used)]).astype(np.int32)
+    packed_q = np.concatenate([xq[e, :used[e]] for e in range(E)])
+    packed_s = np.concatenate([xs[e, :used[e]] for e in range(E)])
+    yg = og.grouped_block_gemm(packed_q, packed_s, wq, ws, off)
+    for e in range(E):
+        np.testing.assert_array_equal(y[e, :used[e]], yg[off[e]:off[e + 1]])
+        assert np.all(np.isnan(y[e, used[e]:]))
+    # a negative count is an empty expert
+    y2 = olay.batched_block_gemm(xq, xs, wq, ws, np.array([-3, 1, 1, 1], np.int32))
+    assert np.all(np.isnan(y2[0]))
+    np.testing.assert_allclose(y2[1, :1], y[1, :1], rtol=1e-13, atol=0)   # BLAS blocking may differ
+
+
+def pin_rowwise_quant(seed=83):
+    rng = np.random.default_rng(seed)
+    R, K = 40, 384
+    v = (rng.standard_normal((R, K)) * np.exp2(rng.integers(-20, 20, (R, 1)))).astype(np.float32)
+    v[3] = 0.0
+    v[4, 300] = 1e3                                      # amax in the last 128-group
+    vb = (v.view(np.uint32) >> 16).astype(np.uint16)
+    q, s = olay.rowwise_quant(vb)
+    assert q.shape == (R, K) and s.shape == (R,)
+    vv = (vb.astype(np.uint32) << 16).view(np.float32)
+    for r in range(R):
+        am = float(np.abs(vv[r]).max())
+        assert float(s[r]) == fl32_of(Fraction(am) / 448), r
+    assert s[3] == 0 and np.all((q[3] & 0x7F) == 0)
+    assert np.all(np.any((q.reshape(R, K) & 0x7F) == 0x7E, axis=1) | (s == 0))
+    # every row is quantized on its own
+    q2, s2 = olay.rowwise_quant(vb[10:13])
+    assert np.array_equal(q2, q[10:13]) and np.array_equal(s2, s[10:13])
+    # with K = 128 a row is one group: the group quantizer gives the same codes
+    qg, sg = oq.act_quant_group(vb[:, :128])
+    qr, sr = olay.rowwise_quant(vb[:, :128])
+    assert np.array_equal(qg, qr) and np.array_equal(sg[:, 0].view(np.uint32), sr.view(np.uint32))
+
+
+def pin_rowwise_gemm(seed=89):
+    rng = np.random.default_rng(seed)
+    M, N, K = 3, 5, 256
+    xi = rng.integers(-8, 9, (M, K)); wi = rng.integers(-8, 9, (N, K))
+    xq = oe.encode(xi.astype(np.float32)); wq = oe.encode(wi.astype(np.float32))
+    xs = np.exp2(rng.integers(-3, 4, M)).astype(np.float32)
+    ws = np.exp2(rng.integers(-3, 4, N)).astype(np.float32)
+    y = olay.rowwise_gemm(xq, xs, wq, ws)
+    for m in range(M):
+        for n in range(N):
+            want = sum(int(xi[m, k]) * int(wi[n, k]) for k in range(K)) * Fraction(float(xs[m])) * Fraction(float(ws[n]))
+            assert Fraction(float(y[m, n])) == want, (m, n)
+    assert np.all(olay.rowwise_term_magnitude(xq, xs, wq, ws) >= np.abs(y))
+
+
 ALL_PINS = [
     pin_format_points, pin_hand_encodings, pin_decode_matches_enumeration,
     pin_encode_roundtrip_and_monotone, pin_encode_brute_force, pin_fl32_div,
@@ -727,4 +797,5 @@ ALL_PINS = [
     pin_e8m0_codec, pin_e8m0_exponent_exhaustive, pin_ue8m0_hand_groups,
     pin_ue8m0_invariants, pin_ue8m0_weight_blocks, pin_ue8m0_gemm,
     pin_static_hand_cases, pin_static_brute_force, pin_static_invariants, pin_static_gemm,
+    pin_batched, pin_rowwise_quant, pin_rowwise_gemm,
 ]

@@ -11,6 +11,7 @@ from oracle import gemm as og
 from oracle import quant as oq
 from oracle import ue8m0 as ou
 from oracle import static as ost
+from oracle import layouts as olay
 
 
 def _fails(pins):
@@ -62,6 +63,11 @@ MUTANTS = {
     "ue8m0_strict_bound": lambda mp: mp.setattr(ou, "e8m0_exponent", _e8m0_strict),
     "ue8m0_no_lower_clamp": lambda mp: mp.setattr(ou, "E_MIN", -133),
     "e8m0_bias_128": lambda mp: mp.setattr(ou, "E8M0_BIAS", 128),
+    "batched_ignores_count": lambda mp: mp.setattr(
+        olay, "batched_block_gemm", lambda xq, xs, wq, ws, c: _orig_batched(xq, xs, wq, ws, np.full_like(c, xq.shape[1]))),
+    "rowwise_scale_per_group": lambda mp: mp.setattr(olay, "rowwise_quant", _rowwise_group),
+    "rowwise_gemm_swapped_scales": lambda mp: mp.setattr(
+        olay, "rowwise_gemm", lambda xq, xs, wq, ws: _orig_rowwise_gemm(xq, np.resize(ws, xs.shape), wq, np.resize(xs, ws.shape))),
     "static_no_saturation": lambda mp: mp.setattr(ost, "act_quant_static", _static_nosat),
     "static_reciprocal_multiply": lambda mp: mp.setattr(ost, "act_quant_static", _static_recip),
     "static_scale_multiplies": lambda mp: mp.setattr(ost, "act_quant_static", _static_mul),
@@ -72,6 +78,15 @@ MUTANTS = {
 _orig_decode = oe.decode
 _orig_e8m0_exponent = ou.e8m0_exponent
 _orig_bg_ue = ou.block_gemm_ue8m0
+
+
+_orig_batched = olay.batched_block_gemm
+_orig_rowwise_gemm = olay.rowwise_gemm
+
+
+def _rowwise_group(bits):
+    q, s = oq.act_quant_group(np.asarray(bits, np.uint16))
+    return q, s[:, 0].copy()
 
 
 def _static_nosat(x_bits, scale):
