@@ -19,7 +19,10 @@ torch.float8_e8m0fnu tensors): fp8_weight_block_quant_ue8m0,
 fp8_act_quant_group_ue8m0, fp8_block_gemm_ue8m0, fp8_grouped_block_gemm_ue8m0,
 and the static-activation-scale pair (one fp32 scale in a 1-element device
 tensor): fp8_act_quant_static(x, x_scale, x_q),
-fp8_block_gemm_static(x_q, x_scale, w_q, w_scale, y).
+fp8_block_gemm_static(x_q, x_scale, w_q, w_scale, y); the batched expert
+layout fp8_batched_block_gemm(x_q, x_scale, w_q, w_scale, counts, y) with
+x_q [E, C, K]; and row-wise scales fp8_rowwise_quant(x, q, scale),
+fp8_rowwise_gemm(x_q, x_scale, w_q, w_scale, y).
 
 Convenience wrappers allocate the outputs; ``scale_fmt`` is "float" (fp32
 scales) or "ue8m0" (E8M0 bytes), and the GEMMs pick the path from the scale
@@ -33,6 +36,10 @@ tensors' dtype:
     act_quant_static(x, x_scale) -> x_q uint8 [M,K]
     block_gemm_static(x_q, x_scale, w_q, w_scale) -> y bf16 [M,N]
     linear_static(x, x_scale, w_q, w_scale) -> y bf16 [M,N]
+    batched_block_gemm(x_q, x_scale, w_q, w_scale, counts) -> y bf16 [E,C,N]
+    rowwise_quant(x) -> (q uint8 [R,K], scale fp32 [R])
+    rowwise_gemm(x_q, x_scale, w_q, w_scale) -> y bf16 [M,N]
+    linear_rowwise(x, w_q, w_scale) -> y bf16 [M,N]
 """
 from __future__ import annotations
 
@@ -47,6 +54,8 @@ __all__ = [
     "fp8_grouped_block_gemm", "fp8_weight_block_quant_ue8m0", "fp8_act_quant_group_ue8m0",
     "fp8_block_gemm_ue8m0", "fp8_grouped_block_gemm_ue8m0", "fp8_act_quant_static",
     "fp8_block_gemm_static", "act_quant_static", "block_gemm_static", "linear_static",
+    "fp8_batched_block_gemm", "batched_block_gemm", "fp8_rowwise_quant", "fp8_rowwise_gemm",
+    "rowwise_quant", "rowwise_gemm", "linear_rowwise",
     "weight_block_quant",
     "act_quant_group", "block_gemm", "grouped_block_gemm", "linear", "SCALE_FMTS",
 ]
@@ -89,6 +98,9 @@ def load_library() -> ctypes.CDLL:
         "fp8_act_quant_group": [vp, i64, i64, vp, vp, vp],
         "fp8_block_gemm": [vp, vp, vp, vp, i64, i64, i64, vp, vp],
         "fp8_grouped_block_gemm": [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp, vp],
+        "fp8_batched_block_gemm": [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp, vp],
+        "fp8_rowwise_quant": [vp, i64, i64, vp, vp, vp],
+        "fp8_rowwise_gemm": [vp, vp, vp, vp, i64, i64, i64, vp, vp],
         "fp8_act_quant_static": [vp, i64, i64, vp, vp, vp],
         "fp8_block_gemm_static": [vp, vp, vp, vp, i64, i64, i64, vp, vp],
         "fp8_weight_block_quant_ue8m0": [vp, i64, i64, vp, vp, vp],
@@ -263,6 +275,49 @@ def fp8_block_gemm_static(x_q, x_scale, w_q, w_scale, y):
            "fp8_block_gemm_static")
 
 
+def fp8_batched_block_gemm(x_q, x_scale, w_q, w_scale, counts, y):
+    _need(x_q, "x_q", _CODES, 3); _need(w_q, "w_q", _CODES, 3)
+    _need(x_scale, "x_scale", _F32, 3); _need(w_scale, "w_scale", _F32, 3)
+    _need(counts, "counts", (torch.int32,), 1); _need(y, "y", (torch.bfloat16,), 3)
+    E, C, K = x_q.shape
+    E2, N, K2 = w_q.shape
+    if E2 != E or K2 != K:
+        raise ValueError("x_q [E,C,K] and w_q [E,N,K] disagree")
+    if counts.numel() != E:
+        raise ValueError("counts must have E entries")
+    if K % BLOCK == 0:
+        _shape_eq(x_scale, (E, C, K // BLOCK), "x_scale")
+        _shape_eq(w_scale, (E, -(-N // BLOCK), K // BLOCK), "w_scale")
+    _shape_eq(y, (E, C, N), "y")
+    _check(load_library().fp8_batched_block_gemm(
+        _ptr(x_q), _ptr(x_scale), _ptr(w_q), _ptr(w_scale), _ptr(counts), E, C, N, K, _ptr(y),
+        _stream()), "fp8_batched_block_gemm")
+
+
+def fp8_rowwise_quant(x, q, scale):
+    _need(x, "x", (torch.bfloat16,), 2)
+    R, K = x.shape
+    _need(q, "q", _CODES); _need(scale, "scale", _F32)
+    _shape_eq(q, (R, K), "q")
+    _shape_eq(scale, (R,), "scale")
+    _check(load_library().fp8_rowwise_quant(_ptr(x), R, K, _ptr(q), _ptr(scale), _stream()),
+           "fp8_rowwise_quant")
+
+
+def fp8_rowwise_gemm(x_q, x_scale, w_q, w_scale, y):
+    _need(x_q, "x_q", _CODES, 2); _need(w_q, "w_q", _CODES, 2)
+    _need(x_scale, "x_scale", _F32, 1); _need(w_scale, "w_scale", _F32, 1)
+    _need(y, "y", (torch.bfloat16,), 2)
+    M, K = x_q.shape
+    N = w_q.shape[0]
+    if w_q.shape[1] != K:
+        raise ValueError("x_q and w_q disagree on K")
+    _shape_eq(x_scale, (M,), "x_scale"); _shape_eq(w_scale, (N,), "w_scale")
+    _shape_eq(y, (M, N), "y")
+    _check(load_library().fp8_rowwise_gemm(_ptr(x_q), _ptr(x_scale), _ptr(w_q), _ptr(w_scale),
+                                           M, N, K, _ptr(y), _stream()), "fp8_rowwise_gemm")
+
+
 def fp8_weight_block_quant_ue8m0(w, w_q, w_scale):
     _weight_quant("fp8_weight_block_quant_ue8m0", _E8M0, w, w_q, w_scale)
 
@@ -346,3 +401,31 @@ def linear_static(x, x_scale, w_q, w_scale):
     """The FP8 linear layer with a static (calibrated, per-tensor) activation
     scale: quantization of x, then the block-scaled GEMM."""
     return block_gemm_static(act_quant_static(x, x_scale), x_scale, w_q, w_scale)
+
+
+def batched_block_gemm(x_q, x_scale, w_q, w_scale, counts):
+    """Rows past an expert's count are left as torch.empty returned them."""
+    y = torch.empty((x_q.shape[0], x_q.shape[1], w_q.shape[1]), dtype=torch.bfloat16,
+                    device=x_q.device)
+    fp8_batched_block_gemm(x_q, x_scale, w_q, w_scale, counts, y)
+    return y
+
+
+def rowwise_quant(x):
+    q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    s = torch.empty((x.shape[0],), dtype=torch.float32, device=x.device)
+    fp8_rowwise_quant(x, q, s)
+    return q, s
+
+
+def rowwise_gemm(x_q, x_scale, w_q, w_scale):
+    y = torch.empty((x_q.shape[0], w_q.shape[0]), dtype=torch.bfloat16, device=x_q.device)
+    fp8_rowwise_gemm(x_q, x_scale, w_q, w_scale, y)
+    return y
+
+
+def linear_rowwise(x, w_q, w_scale):
+    """Row-wise ("fp8r") linear layer: per-token quantization of x, then the
+    row-scaled GEMM."""
+    x_q, x_s = rowwise_quant(x)
+    return rowwise_gemm(x_q, x_s, w_q, w_scale)

@@ -165,6 +165,48 @@ fp8blk_status fp8_block_gemm_static(const void *x_q, const float *x_scale, const
                                                    static_cast<hipStream_t>(stream)));
 }
 
+fp8blk_status fp8_batched_block_gemm(const void *x_q, const float *x_scale, const void *w_q,
+                                     const float *w_scale, const int32_t *expert_counts,
+                                     int32_t E, int64_t capacity, int64_t N, int64_t K,
+                                     void *y_bf16, void *stream) {
+  const bool work = E > 0 && capacity > 0 && N > 0;
+  if (work && (!x_q || !x_scale || !w_q || !w_scale || !expert_counts || !y_bf16))
+    return FP8BLK_ERR_NULL;
+  if (E < 0 || capacity < 0 || bad_rows(N) || bad_k(K) || (E > 0 && capacity > kMaxRows / E))
+    return FP8BLK_ERR_SHAPE;
+  const int64_t total = int64_t(E) * capacity;
+  if (too_big(total, K) || too_big(total, N) || (E > 0 && too_big(int64_t(E) * N, K)) ||
+      too_big(int64_t(E), N))
+    return FP8BLK_ERR_SHAPE;
+  if (work && int64_t(E) * ((capacity + 127) / 128) * ((N + 127) / 128) > kMaxRows)
+    return FP8BLK_ERR_SHAPE;
+  if (work && (misaligned(x_q) || misaligned(x_scale) || misaligned(w_q) || misaligned(w_scale) ||
+               misaligned(y_bf16) || misaligned(expert_counts, 4)))
+    return FP8BLK_ERR_ALIGN;
+  if (fp8blk_status d = check_device()) return d;
+  if (!work) return FP8BLK_OK;
+  return launched(fp8blk::launch_batched_gemm(x_q, x_scale, w_q, w_scale, expert_counts, E,
+                                              capacity, N, K, y_bf16,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+fp8blk_status fp8_rowwise_quant(const void *in_bf16, int64_t R, int64_t K, void *q,
+                                float *scale, void *stream) {
+  if (fp8blk_status c = check_quant(in_bf16, R, K, q, scale, 16)) return c;
+  if (R == 0) return FP8BLK_OK;
+  return launched(fp8blk::launch_rowwise_quant(in_bf16, R, K, q, scale,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+fp8blk_status fp8_rowwise_gemm(const void *x_q, const float *x_scale, const void *w_q,
+                               const float *w_scale, int64_t M, int64_t N, int64_t K,
+                               void *y_bf16, void *stream) {
+  if (fp8blk_status c = check_gemm(x_q, x_scale, w_q, w_scale, M, N, K, y_bf16, 16, 16)) return c;
+  if (M == 0 || N == 0) return FP8BLK_OK;
+  return launched(fp8blk::launch_rowwise_gemm(x_q, x_scale, w_q, w_scale, M, N, K, y_bf16,
+                                              static_cast<hipStream_t>(stream)));
+}
+
 fp8blk_status fp8_weight_block_quant_ue8m0(const void *w_bf16, int64_t N, int64_t K, void *w_q,
                                            uint8_t *w_scale, void *stream) {
   if (fp8blk_status c = check_quant(w_bf16, N, K, w_q, w_scale, 1)) return c;

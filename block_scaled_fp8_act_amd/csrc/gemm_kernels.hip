@@ -312,13 +312,20 @@ __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ A,
 // wm*FM*16 + 16*mi + lane%16 -- sit in one aligned 16-byte slot group, and
 // the 16 lanes of a row read 256 contiguous bytes (no bank conflict); they
 // are the MFMAs' scale operands.
-template <int WM, int WN, int FM, bool kDmaAtBarrier>
+//
+// With kScaled = false (row-wise scales) there are no per-block scales: the
+// MFMAs accumulate unscaled products over all of K, and the epilogue
+// multiplies output (r, c) by xr[r] * wr[c] (fp32 scales of the tile's rows
+// and columns); As and Bs are unused.
+template <int WM, int WN, int FM, bool kDmaAtBarrier, bool kScaled = true>
 __device__ __forceinline__ void gemm_tile_mx(const uint8_t *__restrict__ A,
                                              const uint8_t *__restrict__ As, int rows_a,
                                              const uint8_t *__restrict__ B,
                                              const uint8_t *__restrict__ Bs, int rows_b, int64_t K,
                                              uint16_t *__restrict__ Y, int64_t ldy,
-                                             typename Tile<WM, WN, FM>::SmemMx &sm) {
+                                             typename Tile<WM, WN, FM>::SmemMx &sm,
+                                             const float *__restrict__ xr = nullptr,
+                                             const float *__restrict__ wr = nullptr) {
   using T = Tile<WM, WN, FM>;
   static_assert(FM % 4 == 0, "scale slots are read four at a time");
   const int t = threadIdx.x;
@@ -372,8 +379,10 @@ __device__ __forceinline__ void gemm_tile_mx(const uint8_t *__restrict__ A,
 #pragma unroll
     for (int i = 0; i < T::kDmaB; ++i)
       buf_dma16(rB, ob[i], 0, sm.b[st] + (T::kDmaB * wave + i) * 1024);
-    if (wave < T::TM / 64) buf_dma1(rAs, ps, (uint32_t)kb, &sm.as[st][64 * wave]);
-    if (wave == T::TM / 64 && lane < kNbTile) buf_dma1(rBs, pws, (uint32_t)kb, &sm.ws[st][0]);
+    if constexpr (kScaled) {
+      if (wave < T::TM / 64) buf_dma1(rAs, ps, (uint32_t)kb, &sm.as[st][64 * wave]);
+      if (wave == T::TM / 64 && lane < kNbTile) buf_dma1(rBs, pws, (uint32_t)kb, &sm.ws[st][0]);
+    }
   };
 
   v4f acc[FM][4];
@@ -422,13 +431,15 @@ __device__ __forceinline__ void gemm_tile_mx(const uint8_t *__restrict__ A,
     v8i bfr[4];
     bfr[0] = b0n;
     v8i af = a0n;
-    int sa[FM];
+    int sa[FM] = {}, sb = 0;
+    if constexpr (kScaled) {
 #pragma unroll
-    for (int q = 0; q < FM / 4; ++q) {
-      const int4 v = *reinterpret_cast<const int4 *>(&sm.as[st][slot0 + 64 * q]);
-      sa[4 * q] = v.x; sa[4 * q + 1] = v.y; sa[4 * q + 2] = v.z; sa[4 * q + 3] = v.w;
+      for (int q = 0; q < FM / 4; ++q) {
+        const int4 v = *reinterpret_cast<const int4 *>(&sm.as[st][slot0 + 64 * q]);
+        sa[4 * q] = v.x; sa[4 * q + 1] = v.y; sa[4 * q + 2] = v.z; sa[4 * q + 3] = v.w;
+      }
+      sb = sm.ws[st][wsel];
     }
-    const int sb = sm.ws[st][wsel];
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ni = 1; ni < 4; ++ni) {
@@ -451,8 +462,12 @@ __device__ __forceinline__ void gemm_tile_mx(const uint8_t *__restrict__ A,
       }
 #pragma unroll
       for (int ni = 0; ni < 4; ++ni) {
-        acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            af, bfr[ni], acc[mi][ni], 0, 0, 0, sa[mi], 0, sb);
+        if constexpr (kScaled)
+          acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              af, bfr[ni], acc[mi][ni], 0, 0, 0, sa[mi], 0, sb);
+        else
+          acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              af, bfr[ni], acc[mi][ni], 0, 0, 0, 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
         if (ni == 0 && mi + 2 < FM) {
           afn2 = read_a(st, mi + 2);
@@ -471,18 +486,30 @@ __device__ __forceinline__ void gemm_tile_mx(const uint8_t *__restrict__ A,
   }
   __builtin_amdgcn_s_waitcnt(0);
 
+  float cs[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+  if constexpr (!kScaled) {
 #pragma unroll
-  for (int mi = 0; mi < FM; ++mi)
+    for (int ni = 0; ni < 4; ++ni) cs[ni] = wr[min(wn * 64 + ni * 16 + r16, rows_b - 1)];
+  }
+#pragma unroll
+  for (int mi = 0; mi < FM; ++mi) {
+    float rs[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+    if constexpr (!kScaled) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) rs[r] = xr[min(wm * FM * 16 + mi * 16 + 4 * (lane >> 4) + r, rows_a - 1)];
+    }
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) {
       const int col = wn * 64 + ni * 16 + r16;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = wm * FM * 16 + mi * 16 + 4 * (lane >> 4) + r;
-        if (row < rows_a && col < rows_b)
-          Y[(int64_t)row * ldy + col] = (uint16_t)bf16_rne(acc[mi][ni][r]);
+        float v = acc[mi][ni][r];
+        if constexpr (!kScaled) v = v * (rs[r] * cs[ni]);
+        if (row < rows_a && col < rows_b) Y[(int64_t)row * ldy + col] = (uint16_t)bf16_rne(v);
       }
     }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -503,13 +530,16 @@ constexpr int kDecMaxScaleBytes = 32 * 1024;  // x_scale staging limit (KB * MF 
 
 // S = float: fp32 scales, promoted per K block with FMAs as in gemm_tile;
 // S = uint8_t: E8M0 scale bytes, loaded with the operands and applied by the
-// matrix core (nothing staged in LDS but the final partials).
-template <int MF, typename S>
+// matrix core (nothing staged in LDS but the final partials).  kRow: fp32
+// row-wise scales (xs[M], ws[N]): unscaled MFMAs accumulate over all of K and
+// the sum is scaled by xs[m] * ws[n] at the end.
+template <int MF, typename S, bool kRow = false>
 __global__ __launch_bounds__(kDecThreads) void decode_gemm_kernel(
     const uint8_t *__restrict__ xq, const S *__restrict__ xs, int64_t xs_rs, int xs_ks,
     const uint8_t *__restrict__ wq, const S *__restrict__ ws, int M, int64_t N, int64_t K,
     uint16_t *__restrict__ y) {
   constexpr bool MX = std::is_same<S, uint8_t>::value;
+  static_assert(!(kRow && MX), "row-wise scales are fp32");
   constexpr int R = MF * 16;                  // staged rows
   constexpr int U = 4 / MF;                   // K blocks in flight per wave
   extern __shared__ __align__(16) float dsm[];
@@ -560,7 +590,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_gemm_kernel(
   };
   load(0);
 
-  if constexpr (!MX) {
+  if constexpr (!MX && !kRow) {
     for (int i = t; i < KB * R; i += kDecThreads) {
       const int kb = i / R, m = i % R;
       s_as[i] = xs[(int64_t)min(m, M - 1) * xs_rs + (int64_t)kb * xs_ks];
@@ -583,6 +613,11 @@ __global__ __launch_bounds__(kDecThreads) void decode_gemm_kernel(
           for (int f = 0; f < MF; ++f)
             acc[f] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[u][f], bf, acc[f], 0, 0,
                                                                       0, sa[u][f], 0, sb[u]);
+        } else if constexpr (kRow) {
+#pragma unroll
+          for (int f = 0; f < MF; ++f)
+            acc[f] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[u][f], bf, acc[f], 0, 0,
+                                                                      0, 0, 0, 0);
         } else {
           const float wsc = pws[kb];
 #pragma unroll
@@ -613,24 +648,28 @@ __global__ __launch_bounds__(kDecThreads) void decode_gemm_kernel(
       const v4f v = s_part[(w * MF + wave) * 64 + lane];
       sum[0] += v[0]; sum[1] += v[1]; sum[2] += v[2]; sum[3] += v[3];
     }
+    float cs = 1.0f;
+    if constexpr (kRow) cs = ws[n0 + min(r16, rows_b - 1)];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = wave * 16 + 4 * (lane >> 4) + r;
-      if (row < M && r16 < rows_b) y[(int64_t)row * N + n0 + r16] = (uint16_t)bf16_rne(sum[r]);
+      float v = sum[r];
+      if constexpr (kRow) v = v * (xs[min(row, M - 1)] * cs);
+      if (row < M && r16 < rows_b) y[(int64_t)row * N + n0 + r16] = (uint16_t)bf16_rne(v);
     }
   }
 }
 
-template <int MF, typename S>
+template <int MF, typename S, bool kRow = false>
 static hipError_t launch_decode(const void *xq, const S *xs, int64_t xs_rs, int xs_ks,
                                 const void *wq, const S *ws, int64_t M, int64_t N, int64_t K,
                                 void *y, hipStream_t stream) {
   const int64_t KB = K / 128;
   const size_t part = (size_t)kDecWaves * MF * 64 * 16;
-  const size_t lds = std::is_same<S, uint8_t>::value
+  const size_t lds = (std::is_same<S, uint8_t>::value || kRow)
                          ? part
                          : std::max((size_t)KB * MF * 16 * 4, part);
-  hipLaunchKernelGGL((decode_gemm_kernel<MF, S>), dim3((unsigned)((N + 15) / 16)),
+  hipLaunchKernelGGL((decode_gemm_kernel<MF, S, kRow>), dim3((unsigned)((N + 15) / 16)),
                      dim3(kDecThreads), lds, stream, static_cast<const uint8_t *>(xq), xs, xs_rs,
                      xs_ks, static_cast<const uint8_t *>(wq), ws, (int)M, N, K,
                      static_cast<uint16_t *>(y));
@@ -696,32 +735,47 @@ __global__ __launch_bounds__(WM * WN * 64) void block_gemm_kernel(
 // consecutively (expert e owns ceil(M_e/TM) of them); the grid is sized for
 // the upper bound ceil(total_M/TM) + E, and workgroups past the real count
 // exit at once.  Offsets are read on the device (no host sync) and clamped
-// to [0, total_M].
+// to [0, total_M].  Batched layout (capacity > 0): expert e owns rows
+// [e*capacity, e*capacity + count[e]) with count[e] = offsets[e] clamped to
+// [0, capacity]; its tiles are numbered directly (ceil(capacity/TM) per
+// expert) and tiles past the count exit.
 template <int WM, int WN, int FM, typename S>
 __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(
     const uint8_t *__restrict__ xq, const S *__restrict__ xs, int64_t xs_rs, int xs_ks,
     const uint8_t *__restrict__ wq, const S *__restrict__ ws,
     const int32_t *__restrict__ offsets, int E, int64_t total_M, int64_t N, int64_t K,
-    uint16_t *__restrict__ y, int tiles_n) {
+    uint16_t *__restrict__ y, int tiles_n, int64_t capacity) {
   using T = Tile<WM, WN, FM>;
   __shared__ typename TileSmem<WM, WN, FM, S>::type sm;
   const int tn = blockIdx.x % tiles_n;
   int mt = blockIdx.x / tiles_n;
   int64_t r0 = 0, r1 = 0;
   int e = 0;
-  for (; e < E; ++e) {
-    int64_t a = offsets[e], b = offsets[e + 1];
-    a = a < 0 ? 0 : (a > total_M ? total_M : a);
-    b = b < a ? a : (b > total_M ? total_M : b);
-    const int cnt = (int)((b - a + T::TM - 1) / T::TM);
-    if (mt < cnt) {
-      r0 = a + (int64_t)mt * T::TM;
-      r1 = b;
-      break;
+  if (capacity > 0) {
+    const int tpe = (int)((capacity + T::TM - 1) / T::TM);
+    e = mt / tpe;
+    if (e >= E) return;
+    const int64_t lt = mt % tpe;
+    int64_t c = offsets[e];
+    c = c < 0 ? 0 : (c > capacity ? capacity : c);
+    if (lt * T::TM >= c) return;
+    r0 = (int64_t)e * capacity + lt * T::TM;
+    r1 = (int64_t)e * capacity + c;
+  } else {
+    for (; e < E; ++e) {
+      int64_t a = offsets[e], b = offsets[e + 1];
+      a = a < 0 ? 0 : (a > total_M ? total_M : a);
+      b = b < a ? a : (b > total_M ? total_M : b);
+      const int cnt = (int)((b - a + T::TM - 1) / T::TM);
+      if (mt < cnt) {
+        r0 = a + (int64_t)mt * T::TM;
+        r1 = b;
+        break;
+      }
+      mt -= cnt;
     }
-    mt -= cnt;
+    if (e == E) return;
   }
-  if (e == E) return;
   const int64_t n0 = (int64_t)tn * T::TN;
   const int64_t KB = K / 128;
   const int64_t NB = (N + 127) / 128;
@@ -768,14 +822,15 @@ static hipError_t dispatch_gemm(const void *xq, const S *xs, int64_t xs_rs, int 
 template <typename S>
 static hipError_t dispatch_grouped(const void *xq, const S *xs, const void *wq, const S *ws,
                                    const int32_t *offsets, int32_t E, int64_t total_M, int64_t N,
-                                   int64_t K, void *y, hipStream_t stream) {
+                                   int64_t K, void *y, hipStream_t stream, int64_t capacity = 0) {
   using T = Tile<2, 4, 8>;
   const int64_t tiles_n = (N + T::TN - 1) / T::TN;
-  const int64_t tiles_m = (total_M + T::TM - 1) / T::TM + E;
+  const int64_t tiles_m = capacity > 0 ? (int64_t)E * ((capacity + T::TM - 1) / T::TM)
+                                       : (total_M + T::TM - 1) / T::TM + E;
   hipLaunchKernelGGL((grouped_gemm_kernel<2, 4, 8, S>), dim3((unsigned)(tiles_m * tiles_n)),
                      dim3(T::kThreads), 0, stream, static_cast<const uint8_t *>(xq), xs, K / 128,
                      1, static_cast<const uint8_t *>(wq), ws, offsets, (int)E, total_M, N, K,
-                     static_cast<uint16_t *>(y), (int)tiles_n);
+                     static_cast<uint16_t *>(y), (int)tiles_n, capacity);
   return hipGetLastError();
 }
 
@@ -807,6 +862,56 @@ hipError_t launch_grouped_gemm_e8m0(const void *xq, const uint8_t *xs, const voi
                                     int64_t total_M, int64_t N, int64_t K, void *y,
                                     hipStream_t stream) {
   return dispatch_grouped<uint8_t>(xq, xs, wq, ws, offsets, E, total_M, N, K, y, stream);
+}
+
+// Row-wise scales: the E8M0 tile's loop without scales (unscaled MFMAs
+// accumulating over all of K), xs[M] and ws[N] applied in the epilogue.
+template <int WM, int WN, int FM>
+__global__ __launch_bounds__(WM * WN * 64) void rowwise_gemm_kernel(
+    const uint8_t *__restrict__ xq, const float *__restrict__ xs, const uint8_t *__restrict__ wq,
+    const float *__restrict__ ws, int64_t M, int64_t N, int64_t K, uint16_t *__restrict__ y,
+    int tiles_m, int tiles_n) {
+  using T = Tile<WM, WN, FM>;
+  __shared__ typename T::SmemMx sm;
+  int tm, tn;
+  tile_coords(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, tm, tn);
+  const int64_t m0 = (int64_t)tm * T::TM, n0 = (int64_t)tn * T::TN;
+  gemm_tile_mx<WM, WN, FM, (FM <= 4), false>(xq + m0 * K, nullptr, (int)min<int64_t>(T::TM, M - m0),
+                                             wq + n0 * K, nullptr, (int)min<int64_t>(T::TN, N - n0),
+                                             K, y + m0 * N + n0, N, sm, xs + m0, ws + n0);
+}
+
+template <int WM, int WN, int FM>
+static hipError_t launch_rowwise_tiled(const void *xq, const float *xs, const void *wq,
+                                       const float *ws, int64_t M, int64_t N, int64_t K, void *y,
+                                       hipStream_t stream) {
+  using T = Tile<WM, WN, FM>;
+  const int tm = (int)((M + T::TM - 1) / T::TM), tn = (int)((N + T::TN - 1) / T::TN);
+  hipLaunchKernelGGL((rowwise_gemm_kernel<WM, WN, FM>), dim3((unsigned)(tm * tn)),
+                     dim3(T::kThreads), 0, stream, static_cast<const uint8_t *>(xq), xs,
+                     static_cast<const uint8_t *>(wq), ws, M, N, K, static_cast<uint16_t *>(y),
+                     tm, tn);
+  return hipGetLastError();
+}
+
+hipError_t launch_rowwise_gemm(const void *xq, const float *xs, const void *wq, const float *ws,
+                               int64_t M, int64_t N, int64_t K, void *y, hipStream_t stream) {
+  if (M <= kDecMaxM) {
+    const int MF = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+    if (MF == 1) return launch_decode<1, float, true>(xq, xs, 1, 0, wq, ws, M, N, K, y, stream);
+    if (MF == 2) return launch_decode<2, float, true>(xq, xs, 1, 0, wq, ws, M, N, K, y, stream);
+    return launch_decode<4, float, true>(xq, xs, 1, 0, wq, ws, M, N, K, y, stream);
+  }
+  const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  if (big_tiles >= 192) return launch_rowwise_tiled<2, 4, 8>(xq, xs, wq, ws, M, N, K, y, stream);
+  return launch_rowwise_tiled<2, 2, 4>(xq, xs, wq, ws, M, N, K, y, stream);
+}
+
+hipError_t launch_batched_gemm(const void *xq, const float *xs, const void *wq, const float *ws,
+                               const int32_t *counts, int32_t E, int64_t capacity, int64_t N,
+                               int64_t K, void *y, hipStream_t stream) {
+  return dispatch_grouped<float>(xq, xs, wq, ws, counts, E, (int64_t)E * capacity, N, K, y,
+                                 stream, capacity);
 }
 
 }  // namespace fp8blk

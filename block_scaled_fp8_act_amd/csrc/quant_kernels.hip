@@ -193,6 +193,51 @@ __global__ __launch_bounds__(kStaticThreads) void act_quant_static_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Row-wise quantizer (one scale per row: weights' output rows, or tokens):
+// one workgroup per row, an amax pass and a quantize pass over the row (the
+// second pass re-reads the row from L2 for the usual K), with the element map
+// of make_qparams / quotient.
+constexpr int kRowThreads = 256;
+
+__global__ __launch_bounds__(kRowThreads) void rowwise_quant_kernel(
+    const uint16_t *__restrict__ x, int64_t K, uint8_t *__restrict__ q, float *__restrict__ scale) {
+  __shared__ float wave_max[kRowThreads / 64];
+  const int64_t row = blockIdx.x;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const uint4 *xr = reinterpret_cast<const uint4 *>(x + row * K);
+  const int64_t n8 = K / 8;
+  float m = 0.0f;
+  for (int64_t i = t; i < n8; i += kRowThreads) {
+    float f[8];
+    unpack8(xr[i], f);
+    m = fmaxf(m, absmax8(f));
+  }
+  m = row16_max(m);
+  m = fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 0)),
+                 __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 16))),
+            fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 32)),
+                  __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 48))));
+  if (lane == 0) wave_max[t >> 6] = m;
+  __syncthreads();
+  const float amax = fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3]));
+  const QParams p = make_qparams(amax);
+  uint2 *qr = reinterpret_cast<uint2 *>(q + row * K);
+  for (int64_t i = t; i < n8; i += kRowThreads) {
+    float f[8];
+    unpack8(xr[i], f);
+    float tq[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) tq[j] = quotient(ldexpf(f[j], p.k), p.sp, p.y);
+    uint2 out;
+    out.x = pack4_e4m3(tq[0], tq[1], tq[2], tq[3]);
+    out.y = pack4_e4m3(tq[4], tq[5], tq[6], tq[7]);
+    qr[i] = out;
+  }
+  if (t == 0) scale[row] = p.s;
+}
+
+// ---------------------------------------------------------------------------
 // Weight quantizer: one workgroup per 128x128 block.  Thread t reads, for
 // i = 0..7, the 16 bytes at row i*16 + t/16, columns (t%16)*8 .. +8 of the
 // block, so each wave covers four full 256-byte rows per load.  Rows past N
@@ -300,6 +345,13 @@ hipError_t launch_act_quant_static(const void *x, int64_t M, int64_t K, const fl
   if (blocks > 256 * 8) blocks = 256 * 8;
   hipLaunchKernelGGL(act_quant_static_kernel, dim3((unsigned)blocks), dim3(kStaticThreads), 0,
                      stream, static_cast<const uint4 *>(x), static_cast<uint4 *>(q), s, n16);
+  return hipGetLastError();
+}
+
+hipError_t launch_rowwise_quant(const void *x, int64_t R, int64_t K, void *q, float *s,
+                                hipStream_t stream) {
+  hipLaunchKernelGGL(rowwise_quant_kernel, dim3((unsigned)R), dim3(kRowThreads), 0, stream,
+                     static_cast<const uint16_t *>(x), K, static_cast<uint8_t *>(q), s);
   return hipGetLastError();
 }
 

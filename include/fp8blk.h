@@ -37,7 +37,7 @@
  *     a last weight block row with fewer than 128 rows covers only the rows
  *     that exist.  M == 0 or N == 0 (or E == 0) is a no-op returning OK.
  *   - Every tensor base pointer must be 16-byte aligned (expert_offsets:
- *     4-byte aligned, as an int32 array; a single static scale: 4-byte
+ *     and expert_counts: 4-byte aligned, as int32 arrays; a single static scale: 4-byte
  *     aligned; E8M0 scale-byte arrays: any address).
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
  *     stream).  Inputs must stay valid until the stream reaches the launch.
@@ -127,6 +127,43 @@ FP8BLK_API fp8blk_status fp8_grouped_block_gemm(const void *x_q, const float *x_
                                                 const int32_t *expert_offsets, int32_t E,
                                                 int64_t total_M, int64_t N, int64_t K,
                                                 void *y_bf16, void *stream);
+
+/* Batched (fixed-capacity) expert layout.  "Fine-grained FP8" page,
+ * "UE8M0 scale format": the batched_mm expert back-end takes fp32 scales
+ * directly.  Reading fixed here: expert e owns a slab of `capacity` rows of
+ * which the first counts[e] (clamped to [0, capacity]) hold tokens.
+ *   x_q [E*capacity, K], x_scale [E*capacity, K/128]  (i.e. [E, C, ...])
+ *   w_q [E,N,K], w_scale [E, ceil(N/128), K/128]
+ *   expert_counts: DEVICE int32 [E] (trusted, read on the device)
+ *   y_bf16 [E*capacity, N] out; rows past an expert's count are not written. */
+FP8BLK_API fp8blk_status fp8_batched_block_gemm(const void *x_q, const float *x_scale,
+                                                const void *w_q, const float *w_scale,
+                                                const int32_t *expert_counts, int32_t E,
+                                                int64_t capacity, int64_t N, int64_t K,
+                                                void *y_bf16, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Row-wise scales ("fp8r").
+ * "BFL (fp8r / nvfp4)" page of the diffusers docs, introduction: one fp32
+ * weight scale per row, activations quantized row-wise at run time;
+ * "Kernels": a row-scaled fp8 matrix product.  Readings fixed here: the
+ * element map of the block scheme with the set = one whole row of K values
+ * (s = fl32(amax_row / 448), q = E4M3_RNE(fl32(x / s)), all-zero rows get
+ * s = 0); y[m,n] = bf16( x_scale[m] * w_scale[n] * sum_k dec(x_q[m,k])
+ * dec(w_q[n,k]) ) with fp32 accumulation.  K must be a multiple of 128 as
+ * everywhere else. */
+
+/* Row-wise quantization (weights: R = N output rows; activations: R = M
+ * tokens).  in_bf16 [R,K] in; q [R,K] E4M3 codes out; scale [R] fp32 out. */
+FP8BLK_API fp8blk_status fp8_rowwise_quant(const void *in_bf16, int64_t R, int64_t K, void *q,
+                                           float *scale, void *stream);
+
+/* Row-scaled FP8 GEMM.  x_q [M,K], x_scale [M], w_q [N,K], w_scale [N] in;
+ * y_bf16 [M,N] out. */
+FP8BLK_API fp8blk_status fp8_rowwise_gemm(const void *x_q, const float *x_scale,
+                                          const void *w_q, const float *w_scale,
+                                          int64_t M, int64_t N, int64_t K,
+                                          void *y_bf16, void *stream);
 
 /* ------------------------------------------------------------------------
  * Static activation scale.

@@ -182,3 +182,27 @@ def test_static_validation(lib):
         assert call(lib, "fp8_block_gemm_static", A, MIS4, C, D, 4, 256, 128, E_, NULL) == 4
         # empty shapes validate fully, then the device check still comes first
         assert call(lib, "fp8_block_gemm_static", A, B, C, D, 0, 256, 128, E_, NULL) == 4
+
+
+def test_batched_and_rowwise_validation(lib):
+    # fp8_batched_block_gemm(x_q, x_s, w_q, w_s, counts, E, C, N, K, y, stream)
+    f = "fp8_batched_block_gemm"
+    assert call(lib, f, A, B, C, D, NULL, 4, 64, 256, 128, E_, NULL) == 1
+    assert call(lib, f, A, B, C, D, A, -1, 64, 256, 128, E_, NULL) == 2
+    assert call(lib, f, A, B, C, D, A, 4, -64, 256, 128, E_, NULL) == 2
+    assert call(lib, f, A, B, C, D, A, 4, 64, 256, 96, E_, NULL) == 2
+    assert call(lib, f, A, B, C, D, A, 1 << 20, 1 << 20, 256, 128, E_, NULL) == 2   # E*C over 2^31
+    assert call(lib, f, A, B, C, D, MIS1, 4, 64, 256, 128, E_, NULL) == 3       # counts: 4-byte
+    assert call(lib, f, A, MIS, C, D, A, 4, 64, 256, 128, E_, NULL) == 3
+    # fp8_rowwise_quant(in, R, K, q, scale, stream), fp8_rowwise_gemm(x_q, x_s, w_q, w_s, M, N, K, y, stream)
+    assert call(lib, "fp8_rowwise_quant", NULL, 4, 128, B, C, NULL) == 1
+    assert call(lib, "fp8_rowwise_quant", A, 4, 130, B, C, NULL) == 2
+    assert call(lib, "fp8_rowwise_quant", A, 4, 128, B, MIS, NULL) == 3
+    assert call(lib, "fp8_rowwise_gemm", A, B, C, NULL, 4, 256, 128, E_, NULL) == 1
+    assert call(lib, "fp8_rowwise_gemm", A, B, C, D, 4, 256, 100, E_, NULL) == 2
+    assert call(lib, "fp8_rowwise_gemm", A, B, C, MIS, 4, 256, 128, E_, NULL) == 3
+    import torch
+    if not torch.cuda.is_available():
+        assert call(lib, f, A, B, C, D, MIS4, 4, 64, 256, 128, E_, NULL) == 4
+        assert call(lib, "fp8_rowwise_quant", A, 4, 128, B, C, NULL) == 4
+        assert call(lib, "fp8_rowwise_gemm", A, B, C, D, 4, 256, 128, E_, NULL) == 4
