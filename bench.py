@@ -9,9 +9,9 @@ Inputs are resident in HBM before the timed region; two input/output sets
 does not hold a step's working set.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 30] [--no-cpu-baseline]
-                    [--rows]  (also time weight quant, decode, MoE, the
-                               power-of-two (UE8M0) scale rows and the static
-                               activation scale rows)
+                    [--rows]  (also time weight quant, decode, MoE (grouped
+                               and batched layouts), the power-of-two (UE8M0),
+                               static-activation-scale and row-wise (fp8r) rows)
 
 Prints one JSON line.  ``value`` is the whole step's throughput in TFLOP/s
 (GEMM FLOPs of the four projections / step time, the activation
@@ -294,6 +294,7 @@ def other_rows(torch, fb, dev, stream):
         rows[f"decode_M16_{name}"] = {"us": round(t * 1e6, 2), "GB/s": round(byts / t / 1e9, 1)}
     rows.update(ue8m0_rows(torch, fb, dev, stream, g))
     rows.update(static_rows(torch, fb, dev, stream))
+    rows.update(rowwise_rows(torch, fb, dev, stream))
     # grouped MoE (32 experts, Zipf top-8 routing of 4096 tokens)
     _, off = synth.moe_routing()
     total = int(off[-1])
@@ -309,7 +310,59 @@ def other_rows(torch, fb, dev, stream):
         y = torch.empty((total, N), dtype=torch.bfloat16, device=dev)
         t = _time(torch, stream, lambda: fb.fp8_grouped_block_gemm(xq, xsc, wq, wsc, offd, y), iters=10)
         rows[f"moe_{name}"] = {"us": round(t * 1e6, 2), "TFLOP/s": round(2.0 * total * N * K / t / 1e12, 1)}
+        # the same tokens in the batched layout: capacity = the largest load
+        # rounded up to 256 rows, counts = the loads
+        counts = np.diff(off).astype(np.int32)
+        cap = int(-(-int(counts.max()) // 256) * 256)
+        xb = torch.zeros((32, cap, K), dtype=torch.uint8, device=dev)
+        sb = torch.zeros((32, cap, K // 128), dtype=torch.float32, device=dev)
+        for e in range(32):
+            xb[e, :counts[e]] = xq[off[e]:off[e + 1]]
+            sb[e, :counts[e]] = xsc[off[e]:off[e + 1]]
+        yb = torch.empty((32, cap, N), dtype=torch.bfloat16, device=dev)
+        cnt = torch.from_numpy(counts).to(dev)
+        t = _time(torch, stream, lambda: fb.fp8_batched_block_gemm(xb, sb, wq, wsc, cnt, yb), iters=10)
+        rows[f"moe_batched_{name}"] = {"us": round(t * 1e6, 2), "capacity": cap,
+                                       "TFLOP/s": round(2.0 * total * N * K / t / 1e12, 1)}
+        del xb, sb, yb
     return rows
+
+
+def rowwise_rows(torch, fb, dev, stream):
+    """Row-wise ("fp8r") scales: the same prefill step with the row-wise
+    quantizer (per token) and the row-scaled GEMM; weights quantized
+    row-wise once."""
+    xs0, ws_bf16 = gen_inputs(torch, dev, 3000)
+    sets = [xs0, [torch.roll(x, 1, 0) for x in xs0]]
+    wq, wsc = zip(*[fb.rowwise_quant(w) for w in ws_bf16])
+    del ws_bf16
+    outs = [[(torch.empty((M_PREFILL, K), dtype=torch.uint8, device=dev),
+              torch.empty((M_PREFILL,), dtype=torch.float32, device=dev),
+              torch.empty((M_PREFILL, N), dtype=torch.bfloat16, device=dev))
+             for (_, N, K) in PREFILL_SHAPES] for _ in sets]
+    flops = sum(2.0 * M_PREFILL * N * K for (_, N, K) in PREFILL_SHAPES)
+
+    def launch(i, p, ev):
+        xq, xs, y = outs[i % 2][p]
+        if ev is not None:
+            ev[0].record(stream)
+        fb.fp8_rowwise_quant(sets[i % 2][p], xq, xs)
+        if ev is not None:
+            ev[1].record(stream)
+        fb.fp8_rowwise_gemm(xq, xs, wq[p], wsc[p], y)
+        if ev is not None:
+            ev[2].record(stream)
+
+    dt, ta, tg = run_leg(torch, stream, launch, len(PREFILL_SHAPES), 30, 10)
+    per = {name: {"act_quant_us": round(ta[p] * 1e6, 2),
+                  "act_quant_GB/s": round(3 * M_PREFILL * K / ta[p] / 1e9, 1),
+                  "gemm_us": round(tg[p] * 1e6, 2),
+                  "gemm_TFLOP/s": round(2.0 * M_PREFILL * N * K / tg[p] / 1e12, 1)}
+           for p, (name, N, K) in enumerate(PREFILL_SHAPES)}
+    return {"rowwise_prefill_step": {"ms_per_step": round(dt * 1e3, 4),
+                                     "TFLOP/s": round(flops / dt / 1e12, 1),
+                                     "gemm_TFLOP/s": round(flops / sum(tg) / 1e12, 1),
+                                     "per_projection": per}}
 
 
 def static_rows(torch, fb, dev, stream):
