@@ -54,7 +54,7 @@ __all__ = [
     "fp8_grouped_block_gemm", "fp8_weight_block_quant_ue8m0", "fp8_act_quant_group_ue8m0",
     "fp8_block_gemm_ue8m0", "fp8_grouped_block_gemm_ue8m0", "fp8_act_quant_static",
     "fp8_block_gemm_static", "act_quant_static", "block_gemm_static", "linear_static",
-    "fp8_batched_block_gemm", "batched_block_gemm", "fp8_rowwise_quant", "fp8_rowwise_gemm",
+    "fp8_linear", "fp8_batched_block_gemm", "batched_block_gemm", "fp8_rowwise_quant", "fp8_rowwise_gemm",
     "rowwise_quant", "rowwise_gemm", "linear_rowwise",
     "weight_block_quant",
     "act_quant_group", "block_gemm", "grouped_block_gemm", "linear", "SCALE_FMTS",
@@ -98,6 +98,7 @@ def load_library() -> ctypes.CDLL:
         "fp8_act_quant_group": [vp, i64, i64, vp, vp, vp],
         "fp8_block_gemm": [vp, vp, vp, vp, i64, i64, i64, vp, vp],
         "fp8_grouped_block_gemm": [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp, vp],
+        "fp8_linear": [vp, i64, i64, i64, vp, vp, vp, vp, vp, vp],
         "fp8_batched_block_gemm": [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp, vp],
         "fp8_rowwise_quant": [vp, i64, i64, vp, vp, vp],
         "fp8_rowwise_gemm": [vp, vp, vp, vp, i64, i64, i64, vp, vp],
@@ -275,6 +276,32 @@ def fp8_block_gemm_static(x_q, x_scale, w_q, w_scale, y):
            "fp8_block_gemm_static")
 
 
+FUSED_MAX_M = 64
+
+
+def fp8_linear(x, w_q, w_scale, y, x_q_ws=None, x_scale_ws=None):
+    """One C call for the linear layer: fused in one kernel for M <= 64, else
+    quantization into the workspaces (required then) and the GEMM."""
+    _need(x, "x", (torch.bfloat16,), 2); _need(w_q, "w_q", _CODES, 2)
+    _need(w_scale, "w_scale", _F32, 2); _need(y, "y", (torch.bfloat16,), 2)
+    M, K = x.shape
+    N = w_q.shape[0]
+    if w_q.shape[1] != K:
+        raise ValueError("x and w_q disagree on K")
+    if K % BLOCK == 0:
+        _shape_eq(w_scale, (-(-N // BLOCK), K // BLOCK), "w_scale")
+    _shape_eq(y, (M, N), "y")
+    if M > FUSED_MAX_M:
+        if x_q_ws is None or x_scale_ws is None:
+            raise ValueError("M > 64 needs the x_q_ws / x_scale_ws workspaces")
+        _need(x_q_ws, "x_q_ws", _CODES); _need(x_scale_ws, "x_scale_ws", _F32)
+        _shape_eq(x_q_ws, (M, K), "x_q_ws")
+        if K % BLOCK == 0:
+            _shape_eq(x_scale_ws, (M, K // BLOCK), "x_scale_ws")
+    _check(load_library().fp8_linear(_ptr(x), M, N, K, _ptr(w_q), _ptr(w_scale), _ptr(x_q_ws),
+                                     _ptr(x_scale_ws), _ptr(y), _stream()), "fp8_linear")
+
+
 def fp8_batched_block_gemm(x_q, x_scale, w_q, w_scale, counts, y):
     _need(x_q, "x_q", _CODES, 3); _need(w_q, "w_q", _CODES, 3)
     _need(x_scale, "x_scale", _F32, 3); _need(w_scale, "w_scale", _F32, 3)
@@ -379,10 +406,21 @@ def grouped_block_gemm(x_q, x_scale, w_q, w_scale, offsets):
 
 def linear(x, w_q, w_scale):
     """The FP8 linear layer: dynamic per-token-group quantization of x, then
-    the block-scaled GEMM, back to back on the current stream.  E8M0 weight
-    scales select power-of-two activation scales as well."""
-    x_q, x_s = act_quant_group(x, "ue8m0" if _is_e8m0(w_scale) else "float")
-    return block_gemm(x_q, x_s, w_q, w_scale)
+    the block-scaled GEMM on the current stream (fp32 scales: one C call,
+    fused into one kernel for M <= 64).  E8M0 weight scales select
+    power-of-two activation scales as well."""
+    if _is_e8m0(w_scale):
+        x_q, x_s = act_quant_group(x, "ue8m0")
+        return block_gemm(x_q, x_s, w_q, w_scale)
+    M, K = x.shape
+    y = torch.empty((M, w_q.shape[0]), dtype=torch.bfloat16, device=x.device)
+    if M <= FUSED_MAX_M:
+        fp8_linear(x, w_q, w_scale, y)
+    else:
+        x_q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+        x_s = torch.empty((M, max(K // BLOCK, 0)), dtype=torch.float32, device=x.device)
+        fp8_linear(x, w_q, w_scale, y, x_q, x_s)
+    return y
 
 
 def act_quant_static(x, x_scale):

@@ -165,6 +165,29 @@ fp8blk_status fp8_block_gemm_static(const void *x_q, const float *x_scale, const
                                                    static_cast<hipStream_t>(stream)));
 }
 
+fp8blk_status fp8_linear(const void *x_bf16, int64_t M, int64_t N, int64_t K, const void *w_q,
+                         const float *w_scale, void *x_q_ws, float *x_scale_ws, void *y_bf16,
+                         void *stream) {
+  constexpr int64_t kFusedMaxM = 64;
+  const bool work = M > 0 && N > 0;
+  const bool fused = M <= kFusedMaxM;
+  if (work && (!x_bf16 || !w_q || !w_scale || !y_bf16 || (!fused && (!x_q_ws || !x_scale_ws))))
+    return FP8BLK_ERR_NULL;
+  if (bad_rows(M) || bad_rows(N) || bad_k(K) || too_big(M, K) || too_big(N, K) || too_big(M, N))
+    return FP8BLK_ERR_SHAPE;
+  if (work && ((M + 127) / 128) * ((N + 127) / 128) > kMaxRows) return FP8BLK_ERR_SHAPE;
+  if (work && (misaligned(x_bf16) || misaligned(w_q) || misaligned(w_scale) ||
+               misaligned(y_bf16) || (!fused && (misaligned(x_q_ws) || misaligned(x_scale_ws)))))
+    return FP8BLK_ERR_ALIGN;
+  if (fp8blk_status d = check_device()) return d;
+  if (!work) return FP8BLK_OK;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (fused) return launched(fp8blk::launch_linear_decode(x_bf16, w_q, w_scale, M, N, K, y_bf16, st));
+  if (fp8blk_status e = launched(fp8blk::launch_act_quant(x_bf16, M, K, x_q_ws, x_scale_ws, st)))
+    return e;
+  return launched(fp8blk::launch_block_gemm(x_q_ws, x_scale_ws, w_q, w_scale, M, N, K, y_bf16, st));
+}
+
 fp8blk_status fp8_batched_block_gemm(const void *x_q, const float *x_scale, const void *w_q,
                                      const float *w_scale, const int32_t *expert_counts,
                                      int32_t E, int64_t capacity, int64_t N, int64_t K,

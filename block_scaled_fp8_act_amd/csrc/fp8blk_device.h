@@ -15,6 +15,19 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// Eight bf16 (one 16-byte load) -> fp32, and their largest magnitude.
+__device__ __forceinline__ void unpack8(const uint4 &v, float *f) {
+  f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
+  f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+  f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
+  f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+}
+
+__device__ __forceinline__ float absmax8(const float *f) {
+  return fmaxf(fmaxf(fmaxf(fabsf(f[0]), fabsf(f[1])), fmaxf(fabsf(f[2]), fabsf(f[3]))),
+               fmaxf(fmaxf(fabsf(f[4]), fabsf(f[5])), fmaxf(fabsf(f[6]), fabsf(f[7]))));
+}
+
 // DPP lane permutes inside a row of 16 lanes.
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {

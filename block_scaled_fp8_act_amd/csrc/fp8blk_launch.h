@@ -22,6 +22,8 @@ hipError_t launch_rowwise_gemm(const void *xq, const float *xs, const void *wq, 
 hipError_t launch_batched_gemm(const void *xq, const float *xs, const void *wq, const float *ws,
                                const int32_t *counts, int32_t E, int64_t capacity, int64_t N,
                                int64_t K, void *y, hipStream_t stream);
+hipError_t launch_linear_decode(const void *x, const void *wq, const float *ws, int64_t M,
+                                int64_t N, int64_t K, void *y, hipStream_t stream);
 hipError_t launch_act_quant_e8m0(const void *x, int64_t M, int64_t K, void *q, uint8_t *s,
                                  hipStream_t stream);
 hipError_t launch_weight_quant_e8m0(const void *w, int64_t N, int64_t K, void *q, uint8_t *s,

@@ -676,6 +676,143 @@ static hipError_t launch_decode(const void *xq, const S *xs, int64_t xs_rs, int 
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Fused decode linear layer (M <= 64): the dynamic activation quantization
+// runs inside the weight-streaming GEMM, so one launch turns bf16 x into y.
+// Each lane loads the 32 bf16 values whose fp8 codes its A fragment would
+// hold (row 16f + lane%16 of K block kb, values 32*(lane/16) .. +32); the
+// group amax is the max over the four lanes holding that row's 128 values
+// (xor-shuffles by 16 and 32); the element map is make_qparams / quotient,
+// bit-identical to the activation quantizer; the codes go straight into the
+// MFMA operand and the group scale into the promotion (fetched by shuffle
+// from the lane that holds each output row).  x is small and read by every
+// workgroup from L2; the redundant quantization hides under the W stream.
+// NW waves split the K blocks (16, or 8 for MF = 4, whose four bf16
+// fragments need the larger per-wave register budget).
+template <int MF, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_linear_kernel(
+    const uint16_t *__restrict__ x, const uint8_t *__restrict__ wq, const float *__restrict__ ws,
+    int M, int64_t N, int64_t K, uint16_t *__restrict__ y) {
+  constexpr int U = MF == 1 ? 2 : 1;  // K blocks in flight (bf16 x takes 16 VGPRs per fragment)
+  extern __shared__ __align__(16) float dsm[];
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int KB = (int)(K / 128);
+  v4f *s_part = reinterpret_cast<v4f *>(dsm);  // [waves][MF][64]
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int rows_b = (int)min<int64_t>(16, N - n0);
+
+  const int r16 = lane & 15;
+  const int g = lane >> 4;
+  const int kc = g * 32;
+  const uint8_t *pb = wq + (n0 + min(r16, rows_b - 1)) * K + kc;
+  const uint16_t *px[MF];
+#pragma unroll
+  for (int f = 0; f < MF; ++f) px[f] = x + (int64_t)min(f * 16 + r16, M - 1) * K + kc;
+  const float *pws = ws + (n0 / 128) * KB;
+  const int nmine = wave < KB ? (KB - wave + NW - 1) / NW : 0;
+
+  uint4 bw[U][2];
+  uint4 xr[U][MF][4];
+  auto load = [&](int j0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (j0 + u < nmine) {
+        const int64_t ko = (int64_t)(wave + NW * (j0 + u)) * 128;
+        bw[u][0] = *reinterpret_cast<const uint4 *>(pb + ko);
+        bw[u][1] = *reinterpret_cast<const uint4 *>(pb + ko + 16);
+#pragma unroll
+        for (int f = 0; f < MF; ++f)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) xr[u][f][c] = *reinterpret_cast<const uint4 *>(px[f] + ko + 8 * c);
+      }
+    }
+  };
+  load(0);
+
+  v4f acc[MF];
+#pragma unroll
+  for (int f = 0; f < MF; ++f) acc[f] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+  for (int j0 = 0; j0 < nmine; j0 += U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (j0 + u < nmine) {
+        const int kb = wave + NW * (j0 + u);
+        const float wsc = pws[kb];
+        const v8i bf = frag_from(bw[u][0], bw[u][1]);
+#pragma unroll
+        for (int f = 0; f < MF; ++f) {
+          float am = 0.0f;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            float v[8];
+            unpack8(xr[u][f][c], v);
+            am = fmaxf(am, absmax8(v));
+          }
+          am = fmaxf(am, __shfl_xor(am, 16));
+          am = fmaxf(am, __shfl_xor(am, 32));
+          const QParams p = make_qparams(am);
+          v8i af;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            float v[8];
+            unpack8(xr[u][f][c], v);
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+              af[2 * c + h] = (int)pack4_e4m3(quotient(ldexpf(v[4 * h], p.k), p.sp, p.y),
+                                              quotient(ldexpf(v[4 * h + 1], p.k), p.sp, p.y),
+                                              quotient(ldexpf(v[4 * h + 2], p.k), p.sp, p.y),
+                                              quotient(ldexpf(v[4 * h + 3], p.k), p.sp, p.y));
+          }
+          const v4f pc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              af, bf, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 0, 0, 0);
+          // output rows 4g + r of this fragment: their scales live in lanes 4g + r
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            acc[f][r] = fmaf(pc[r], __shfl(p.s, 4 * g + r) * wsc, acc[f][r]);
+        }
+      }
+    }
+    if (j0 + U < nmine) load(j0 + U);
+  }
+#pragma unroll
+  for (int f = 0; f < MF; ++f) s_part[(wave * MF + f) * 64 + lane] = acc[f];
+  __syncthreads();
+  if (wave < MF) {
+    v4f sum = s_part[wave * 64 + lane];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+      const v4f v = s_part[(w * MF + wave) * 64 + lane];
+      sum[0] += v[0]; sum[1] += v[1]; sum[2] += v[2]; sum[3] += v[3];
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = wave * 16 + 4 * g + r;
+      if (row < M && r16 < rows_b) y[(int64_t)row * N + n0 + r16] = (uint16_t)bf16_rne(sum[r]);
+    }
+  }
+}
+
+template <int MF, int NW>
+static hipError_t launch_decode_linear(const void *x, const void *wq, const float *ws, int64_t M,
+                                       int64_t N, int64_t K, void *y, hipStream_t stream) {
+  const size_t lds = (size_t)NW * MF * 64 * 16;
+  hipLaunchKernelGGL((decode_linear_kernel<MF, NW>), dim3((unsigned)((N + 15) / 16)),
+                     dim3(NW * 64), lds, stream, static_cast<const uint16_t *>(x),
+                     static_cast<const uint8_t *>(wq), ws, (int)M, N, K,
+                     static_cast<uint16_t *>(y));
+  return hipGetLastError();
+}
+
+hipError_t launch_linear_decode(const void *x, const void *wq, const float *ws, int64_t M,
+                                int64_t N, int64_t K, void *y, hipStream_t stream) {
+  if (M <= 16) return launch_decode_linear<1, 16>(x, wq, ws, M, N, K, y, stream);
+  if (M <= 32) return launch_decode_linear<2, 16>(x, wq, ws, M, N, K, y, stream);
+  return launch_decode_linear<4, 8>(x, wq, ws, M, N, K, y, stream);
+}
+
 // Map a linear workgroup id to (tile_m, tile_n).  Workgroups are dispatched
 // round-robin over the 8 XCDs (each with its own L2); consecutive logical
 // tiles are made to land on one XCD, and logical tiles are ordered in

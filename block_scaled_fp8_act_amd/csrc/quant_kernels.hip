@@ -47,17 +47,6 @@ constexpr int kGroupsPerTile = 16;
 constexpr int kTilesPerIter = 2;
 constexpr float kTinyAmax = 0x1p-50f;
 
-__device__ __forceinline__ void unpack8(const uint4 &v, float *f) {
-  f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
-  f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
-  f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
-  f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
-}
-
-__device__ __forceinline__ float absmax8(const float *f) {
-  return fmaxf(fmaxf(fmaxf(fabsf(f[0]), fabsf(f[1])), fmaxf(fabsf(f[2]), fabsf(f[3]))),
-               fmaxf(fmaxf(fabsf(f[4]), fabsf(f[5])), fmaxf(fabsf(f[6]), fabsf(f[7]))));
-}
 
 __global__ __launch_bounds__(kActThreads) void act_quant_kernel(
     const uint4 *__restrict__ x, uint2 *__restrict__ q, float *__restrict__ scale,

@@ -128,6 +128,24 @@ FP8BLK_API fp8blk_status fp8_grouped_block_gemm(const void *x_q, const float *x_
                                                 int64_t total_M, int64_t N, int64_t K,
                                                 void *y_bf16, void *stream);
 
+/* The whole FP8 linear layer, y = x * W^T from bf16 x: dynamic activation
+ * quantization then the block-scaled GEMM ("DeepGEMM fast path"; the
+ * quantization "fused ahead of the GEMM").  For M <= 64 (decode) one kernel
+ * does both: the activation codes and scales are formed in registers inside
+ * the weight-streaming GEMM and never reach memory (x_q_ws and x_scale_ws
+ * may be NULL and are not touched).  For M > 64 the two kernels run back to
+ * back on `stream` through the caller's workspaces x_q_ws [M,K] and
+ * x_scale_ws [M,K/128] (required, 16-byte aligned), which then hold the
+ * activation codes and scales.  The activation codes and scales are always
+ * those of fp8_act_quant_group; y is bit-identical to fp8_act_quant_group
+ * followed by fp8_block_gemm for M <= 32 and for M > 64 (for 32 < M <= 64 the
+ * fused kernel splits K over fewer waves, so its fp32 partial sums are added
+ * in another order).
+ *   x_bf16 [M,K], w_q [N,K], w_scale [ceil(N/128),K/128] in; y_bf16 [M,N] out. */
+FP8BLK_API fp8blk_status fp8_linear(const void *x_bf16, int64_t M, int64_t N, int64_t K,
+                                    const void *w_q, const float *w_scale, void *x_q_ws,
+                                    float *x_scale_ws, void *y_bf16, void *stream);
+
 /* Batched (fixed-capacity) expert layout.  "Fine-grained FP8" page,
  * "UE8M0 scale format": the batched_mm expert back-end takes fp32 scales
  * directly.  Reading fixed here: expert e owns a slab of `capacity` rows of

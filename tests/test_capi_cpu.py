@@ -206,3 +206,19 @@ def test_batched_and_rowwise_validation(lib):
         assert call(lib, f, A, B, C, D, MIS4, 4, 64, 256, 128, E_, NULL) == 4
         assert call(lib, "fp8_rowwise_quant", A, 4, 128, B, C, NULL) == 4
         assert call(lib, "fp8_rowwise_gemm", A, B, C, D, 4, 256, 128, E_, NULL) == 4
+
+
+def test_linear_validation(lib):
+    # fp8_linear(x, M, N, K, w_q, w_scale, x_q_ws, x_scale_ws, y, stream)
+    f = "fp8_linear"
+    assert call(lib, f, NULL, 16, 256, 128, C, D, NULL, NULL, E_, NULL) == 1
+    assert call(lib, f, A, 65, 256, 128, C, D, NULL, NULL, E_, NULL) == 1      # workspaces needed
+    assert call(lib, f, A, 65, 256, 128, C, D, B, NULL, E_, NULL) == 1
+    assert call(lib, f, A, 16, 256, 100, C, D, NULL, NULL, E_, NULL) == 2
+    assert call(lib, f, MIS, 16, 256, 128, C, D, NULL, NULL, E_, NULL) == 3
+    assert call(lib, f, A, 65, 256, 128, C, D, MIS, B, E_, NULL) == 3
+    import torch
+    if not torch.cuda.is_available():
+        # M <= 64 needs no workspace; a misaligned unused workspace is ignored
+        assert call(lib, f, A, 64, 256, 128, C, D, NULL, NULL, E_, NULL) == 4
+        assert call(lib, f, A, 16, 256, 128, C, D, MIS, MIS, E_, NULL) == 4

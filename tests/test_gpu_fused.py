@@ -1,0 +1,99 @@
+"""GPU parity of the whole linear layer in one C call (fp8_linear): the
+fused decode kernel (activation quantization inside the weight-streaming
+GEMM, M <= 64) and the two-kernel path through workspaces (M > 64).
+
+The fused result equals the two-launch result (fp8_act_quant_group then
+fp8_block_gemm) bit for bit where the summation order is the same (M <= 32
+and M > 64) and is within the GEMM tolerance of the oracle everywhere."""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_fp8_act_amd as fb
+import synth
+from oracle import gemm as og
+from oracle import quant as oq
+from gpu_helpers import bf16_to_host, dev, host, say, to_dev, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+def two_launch(xd, wq, ws):
+    xq, xs = fb.act_quant_group(xd)
+    return fb.block_gemm(xq, xs, wq, ws)
+
+
+def check(x, w, what, bit_identical, tol_rows=None):
+    xd = to_dev_bf16(x)
+    wq, ws = oq.weight_block_quant(w)
+    wqd, wsd = to_dev(wq), to_dev(ws)
+    y = fb.linear(xd, wqd, wsd)
+    y2 = two_launch(xd, wqd, wsd)
+    torch.cuda.synchronize()
+    y, y2 = bf16_to_host(y), bf16_to_host(y2)
+    if bit_identical:
+        bad = np.argwhere(y != y2)
+        assert bad.size == 0, f"{what}: {len(bad)} outputs differ from the two-launch path"
+    xq, xs = oq.act_quant_group(x)
+    rows = np.arange(x.shape[0]) if tol_rows is None else np.asarray(tol_rows)
+    rep = og.tolerance_report(y[rows], og.block_gemm(xq[rows], xs[rows], wq, ws),
+                              og.term_magnitude(xq[rows], xs[rows], wq, ws))
+    say(what, {k: (round(v, 6) if isinstance(v, float) else v) for k, v in rep.items()})
+    assert rep["ok"], (what, rep)
+
+
+@pytest.mark.parametrize("M", [1, 5, 16, 17, 32, 33, 64])
+@pytest.mark.parametrize("shape_index", range(4))
+def test_fused_decode_llama(M, shape_index):
+    x, w = synth.llama_inputs(shape_index, M, config=2)
+    check(x, w, f"fused {synth.LLAMA_SHAPES[shape_index][0]} M={M}", bit_identical=M <= 32)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 16, 128), (3, 100, 256), (16, 300, 384), (31, 576, 18432),
+                                   (40, 1000, 1280), (64, 24576, 1536), (7, 7168, 16384)])
+def test_fused_decode_ragged(M, N, K):
+    x = synth.dsv3_activations(M + K, M, K, N)
+    w = synth.normal_bf16(N + K, (N, K), 0.02)
+    check(x, w, f"fused {M}x{N}x{K}", bit_identical=M <= 32)
+
+
+def test_fused_decode_edge_values():
+    """Groups that are all zero, hold bf16 subnormals or reach bf16's
+    largest values: the fused quantizer must take the general path exactly
+    like the standalone one (bit-identical outputs on every row).  Rows 1
+    and 2 hold bf16-subnormal groups: their scales (~2e-43, ~3e-41) make the
+    promotion factor x_s * w_s fall below fp32's normal range (to 0 or to a
+    subnormal with a few significant bits), so any fp32-promoting GEMM
+    loses those outputs' precision while the fp64 oracle does not; those
+    rows are left out of the oracle tolerance."""
+    K = 512
+    x = np.zeros((8, K), np.uint16)
+    x[1, :128] = 0x0001                              # subnormal amax group
+    x[2, 128:256] = np.arange(128, dtype=np.uint16) | 0x0040
+    x[3, :] = synth.normal_bf16(1, (1, K))[0]
+    x[4, 256] = 0x7F7F                                 # largest bf16
+    x[5, 300] = 0x8000                                 # negative zero
+    x[6, :] = 0x3F80
+    w = synth.normal_bf16(2, (256, K), 0.02)
+    check(x, w, "fused edges", bit_identical=True, tol_rows=[0, 3, 4, 5, 6, 7])
+
+
+@pytest.mark.parametrize("M", [65, 300])
+def test_linear_workspace_path(M):
+    x, w = synth.llama_inputs(1, M, config=3)
+    xd = to_dev_bf16(x)
+    wq, ws = oq.weight_block_quant(w)
+    wqd, wsd = to_dev(wq), to_dev(ws)
+    K = x.shape[1]
+    xq_ws = torch.empty((M, K), dtype=torch.uint8, device=dev())
+    xs_ws = torch.empty((M, K // 128), dtype=torch.float32, device=dev())
+    y = torch.empty((M, w.shape[0]), dtype=torch.bfloat16, device=dev())
+    fb.fp8_linear(xd, wqd, wsd, y, xq_ws, xs_ws)
+    y2 = two_launch(xd, wqd, wsd)
+    torch.cuda.synchronize()
+    oxq, oxs = oq.act_quant_group(x)
+    assert np.array_equal(host(xq_ws), oxq)
+    assert np.array_equal(host(xs_ws).view(np.uint32), oxs.view(np.uint32))
+    assert np.array_equal(bf16_to_host(y), bf16_to_host(y2))
+    with pytest.raises(ValueError):
+        fb.fp8_linear(xd, wqd, wsd, y)
