@@ -295,6 +295,24 @@ def other_rows(torch, fb, dev, stream):
     rows.update(ue8m0_rows(torch, fb, dev, stream, g))
     rows.update(static_rows(torch, fb, dev, stream))
     rows.update(rowwise_rows(torch, fb, dev, stream))
+    # the whole decode linear layer from bf16 x (M = 16): one fused kernel
+    # against the two launches (act quant + GEMM)
+    for name, N, K in PREFILL_SHAPES:
+        x = torch.randn((16, K), generator=g, device=dev).to(torch.bfloat16)
+        wq, wsc = fb.weight_block_quant((torch.randn((N, K), generator=g, device=dev) * 0.02).to(torch.bfloat16))
+        y = torch.empty((16, N), dtype=torch.bfloat16, device=dev)
+        xq = torch.empty((16, K), dtype=torch.uint8, device=dev)
+        xsc = torch.empty((16, K // 128), dtype=torch.float32, device=dev)
+
+        def two():
+            fb.fp8_act_quant_group(x, xq, xsc)
+            fb.fp8_block_gemm(xq, xsc, wq, wsc, y)
+        t1 = _time(torch, stream, lambda: fb.fp8_linear(x, wq, wsc, y))
+        t2 = _time(torch, stream, two)
+        t3 = _time(torch, stream, lambda: fb.fp8_linear(x, wq, wsc, y, xq, xsc))
+        rows[f"decode_linear_M16_{name}"] = {"fused_us": round(t1 * 1e6, 2),
+                                             "two_launch_us": round(t2 * 1e6, 2),
+                                             "fp8_linear_with_workspace_us": round(t3 * 1e6, 2)}
     # grouped MoE (32 experts, Zipf top-8 routing of 4096 tokens)
     _, off = synth.moe_routing()
     total = int(off[-1])

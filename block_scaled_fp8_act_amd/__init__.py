@@ -280,8 +280,9 @@ FUSED_MAX_M = 64
 
 
 def fp8_linear(x, w_q, w_scale, y, x_q_ws=None, x_scale_ws=None):
-    """One C call for the linear layer: fused in one kernel for M <= 64, else
-    quantization into the workspaces (required then) and the GEMM."""
+    """One C call for the linear layer: fused in one kernel for M <= 64 when
+    N <= 6144 or no workspaces are given, else quantization into the
+    workspaces (required for M > 64) and the GEMM."""
     _need(x, "x", (torch.bfloat16,), 2); _need(w_q, "w_q", _CODES, 2)
     _need(w_scale, "w_scale", _F32, 2); _need(y, "y", (torch.bfloat16,), 2)
     M, K = x.shape
@@ -414,12 +415,9 @@ def linear(x, w_q, w_scale):
         return block_gemm(x_q, x_s, w_q, w_scale)
     M, K = x.shape
     y = torch.empty((M, w_q.shape[0]), dtype=torch.bfloat16, device=x.device)
-    if M <= FUSED_MAX_M:
-        fp8_linear(x, w_q, w_scale, y)
-    else:
-        x_q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
-        x_s = torch.empty((M, max(K // BLOCK, 0)), dtype=torch.float32, device=x.device)
-        fp8_linear(x, w_q, w_scale, y, x_q, x_s)
+    x_q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    x_s = torch.empty((M, max(K // BLOCK, 0)), dtype=torch.float32, device=x.device)
+    fp8_linear(x, w_q, w_scale, y, x_q, x_s)   # the library picks fused or two kernels
     return y
 
 

@@ -131,16 +131,18 @@ FP8BLK_API fp8blk_status fp8_grouped_block_gemm(const void *x_q, const float *x_
 /* The whole FP8 linear layer, y = x * W^T from bf16 x: dynamic activation
  * quantization then the block-scaled GEMM ("DeepGEMM fast path"; the
  * quantization "fused ahead of the GEMM").  For M <= 64 (decode) one kernel
- * does both: the activation codes and scales are formed in registers inside
- * the weight-streaming GEMM and never reach memory (x_q_ws and x_scale_ws
- * may be NULL and are not touched).  For M > 64 the two kernels run back to
- * back on `stream` through the caller's workspaces x_q_ws [M,K] and
- * x_scale_ws [M,K/128] (required, 16-byte aligned), which then hold the
- * activation codes and scales.  The activation codes and scales are always
+ * can do both: the activation codes and scales are formed in registers
+ * inside the weight-streaming GEMM and never reach memory.  It is used when
+ * M <= 64 and either N <= 6144 or no workspaces are given (x_q_ws and
+ * x_scale_ws may be NULL for M <= 64; they are then not touched).
+ * Otherwise the two kernels run back to back on `stream` through the
+ * caller's workspaces x_q_ws [M,K] and x_scale_ws [M,K/128] (required for
+ * M > 64, 16-byte aligned), which then hold the activation codes and
+ * scales.  The activation codes and scales are always
  * those of fp8_act_quant_group; y is bit-identical to fp8_act_quant_group
- * followed by fp8_block_gemm for M <= 32 and for M > 64 (for 32 < M <= 64 the
- * fused kernel splits K over fewer waves, so its fp32 partial sums are added
- * in another order).
+ * followed by fp8_block_gemm except in the fused kernel for 32 < M <= 64
+ * (it splits K over fewer waves, so its fp32 partial sums are added in
+ * another order).
  *   x_bf16 [M,K], w_q [N,K], w_scale [ceil(N/128),K/128] in; y_bf16 [M,N] out. */
 FP8BLK_API fp8blk_status fp8_linear(const void *x_bf16, int64_t M, int64_t N, int64_t K,
                                     const void *w_q, const float *w_scale, void *x_q_ws,

@@ -24,10 +24,12 @@ def two_launch(xd, wq, ws):
 
 
 def check(x, w, what, bit_identical, tol_rows=None):
+    """The fused kernel proper (no workspaces given, so M <= 64 always fuses)."""
     xd = to_dev_bf16(x)
     wq, ws = oq.weight_block_quant(w)
     wqd, wsd = to_dev(wq), to_dev(ws)
-    y = fb.linear(xd, wqd, wsd)
+    y = torch.empty((x.shape[0], w.shape[0]), dtype=torch.bfloat16, device=dev())
+    fb.fp8_linear(xd, wqd, wsd, y)
     y2 = two_launch(xd, wqd, wsd)
     torch.cuda.synchronize()
     y, y2 = bf16_to_host(y), bf16_to_host(y2)
@@ -97,3 +99,19 @@ def test_linear_workspace_path(M):
     assert np.array_equal(bf16_to_host(y), bf16_to_host(y2))
     with pytest.raises(ValueError):
         fb.fp8_linear(xd, wqd, wsd, y)
+
+
+@pytest.mark.parametrize("N", [4096, 14336])
+def test_linear_picks_a_path_and_agrees(N):
+    """fb.linear passes workspaces; the library fuses for N <= 6144 and runs
+    two kernels above: both agree with the two-launch path bit for bit at
+    M = 16."""
+    K = 4096
+    x = synth.llama_x(0, 16, config=2)
+    w = synth.normal_bf16(N, (N, K), 0.02)
+    wq, ws = oq.weight_block_quant(w)
+    xd, wqd, wsd = to_dev_bf16(x), to_dev(wq), to_dev(ws)
+    y = fb.linear(xd, wqd, wsd)
+    y2 = two_launch(xd, wqd, wsd)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_to_host(y), bf16_to_host(y2))
