@@ -39,11 +39,15 @@ What is computed, and where it comes from:
 * The batched expert layout and row-wise ("fp8r") scales:
   :mod:`oracle.layouts` states the readings.
 
+* SwiGLU ahead of the activation quantizer (the input of a mixture-of-
+  experts down projection): :mod:`oracle.swiglu` states the readings.
+
 Modules: :mod:`oracle.e4m3` (codec), :mod:`oracle.quant` (quantizers),
 :mod:`oracle.gemm` (block-scaled and grouped GEMM, linear layer),
 :mod:`oracle.ue8m0` (E8M0 scales: codec, quantizers, GEMM),
 :mod:`oracle.static` (static activation scale: quantizer, GEMM),
-:mod:`oracle.layouts` (batched experts; row-wise quantizer and GEMM).
+:mod:`oracle.layouts` (batched experts; row-wise quantizer and GEMM),
+:mod:`oracle.swiglu` (SwiGLU then the activation quantizer).
 """
 from .e4m3 import E4M3_MAX, decode, encode, fl32_div
 from .quant import act_quant_group, weight_block_quant, quant_element_map
@@ -54,6 +58,7 @@ from .ue8m0 import (act_quant_group_ue8m0, block_gemm_ue8m0, e8m0_decode, e8m0_e
                     grouped_block_gemm_ue8m0, weight_block_quant_ue8m0)
 from .static import act_quant_static, block_gemm_static
 from .layouts import batched_block_gemm, rowwise_gemm, rowwise_quant
+from .swiglu import swiglu_act_quant, swiglu_bf16
 
 __all__ = [
     "E4M3_MAX", "decode", "encode", "fl32_div",
@@ -65,4 +70,5 @@ __all__ = [
     "grouped_block_gemm_ue8m0", "weight_block_quant_ue8m0",
     "act_quant_static", "block_gemm_static",
     "batched_block_gemm", "rowwise_gemm", "rowwise_quant",
+    "swiglu_act_quant", "swiglu_bf16",
 ]

@@ -10,6 +10,7 @@ from __future__ import annotations
 
 import math
 import os
+from decimal import Decimal, localcontext
 from fractions import Fraction
 
 import numpy as np
@@ -21,6 +22,7 @@ from oracle import quant as oq
 from oracle import ue8m0 as ou
 from oracle import static as ost
 from oracle import layouts as olay
+from oracle import swiglu as osw
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -787,6 +789,132 @@ def pin_rowwise_gemm(seed=89):
     assert np.all(olay.rowwise_term_magnitude(xq, xs, wq, ws) >= np.abs(y))
 
 
+# ----------------------------------------------------------------------------
+# SwiGLU + activation quantizer pins
+
+def bf16_rne_exact(q: Fraction, zero_sign: int):
+    """Round an exact rational to bf16 bits (nearest, ties to even,
+    subnormals kept; finite results only).  Returns (bits, distance of the
+    scaled value from the nearest rounding midpoint, in quanta)."""
+    if q == 0:
+        return (0x8000 if zero_sign < 0 else 0), Fraction(1, 2)
+    sign = 0x8000 if q < 0 else 0
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1                                   # 2^e <= a < 2^(e+1)
+    qexp = max(e, -126) - 7                      # bf16 quantum of a's binade
+    scaled = a / Fraction(2) ** qexp
+    n = scaled.numerator // scaled.denominator
+    rem = scaled - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    dist = abs(rem - Fraction(1, 2))
+    if n == 0:
+        return sign, dist
+    # n * 2^qexp with n < 2^9: exponent and mantissa fields
+    if n >= 256:                                 # carried into the next binade
+        n //= 2
+        qexp += 1
+    if n < 128:                                  # subnormal (qexp == -133)
+        return sign | n, dist
+    field = qexp + 7 + 127
+    assert field < 255, "overflow is outside the contract"
+    return sign | (field << 7) | (n - 128), dist
+
+
+def swiglu_exact(g: float, u: float) -> Fraction:
+    """SiLU(g) * u to 80 significant digits (decimal arithmetic, no binary
+    floating point), as an exact rational of that decimal."""
+    with localcontext() as ctx:
+        ctx.prec = 80
+        dg, du = Decimal(g), Decimal(u)          # exact conversions
+        h = dg / (1 + (-dg).exp()) * du
+    return Fraction(h)
+
+
+def pin_swiglu_hand_cases():
+    rows = read_golden("swiglu_hand_cases.txt")
+    I = 128
+    gu = np.zeros((len(rows), 2 * I), np.uint16)
+    want = []
+    for i, row in enumerate(rows):
+        g_s, u_s, h_s = [p.strip() for p in row.split("|")]
+        gu[i, 0], gu[i, I] = int(g_s, 16), int(u_s, 16)
+        want.append(int(h_s, 16))
+    h = osw.swiglu_bf16(gu)
+    for i, w in enumerate(want):
+        assert int(h[i, 0]) == w, (rows[i], hex(int(h[i, 0])))
+    assert np.all(h[:, 1:] == 0)                 # g = u = +0 elsewhere: h = +0
+
+
+def _random_gate_up(rng, M, I):
+    """bf16 gate values over a wide range (typical N(0, 3) mixed with
+    +-2^[-30, 12) and a few specials) and up values +-2^[-60, 60)."""
+    g = rng.standard_normal((M, I)) * 3
+    wide = rng.random((M, I)) < 0.5
+    g = np.where(wide, np.sign(g) * np.exp2(rng.uniform(-30, 12, (M, I))), g)
+    u = np.sign(rng.standard_normal((M, I))) * np.exp2(rng.uniform(-60, 60, (M, I)))
+    flat = g.reshape(-1)
+    specials = [0.0, -0.0, -800.0, -500.0, 1e-40, -1e-40, 37.0, 48.0, -37.0]
+    flat[: len(specials)] = specials
+    gb = (g.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    ub = (u.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    return np.concatenate([gb, ub], axis=1)
+
+
+def pin_swiglu_brute_force(seed=97):
+    """Every h of a [3, 2*256] gate/up block against the exact SiLU(g) * u
+    (80-digit decimal) rounded to bf16 by an integer rule; g is read from
+    column j and u from column I + j.  Values within 2^-40 of a rounding
+    midpoint (in quanta) are where binary64 evaluation may round differently
+    from the exact value (hand case (6)); they are counted, not compared."""
+    rng = np.random.default_rng(seed)
+    M, I = 3, 256
+    gu = _random_gate_up(rng, M, I)
+    h = osw.swiglu_bf16(gu)
+    assert h.shape == (M, I)
+    near = 0
+    for m in range(M):
+        for j in range(I):
+            g = bf16_value(int(gu[m, j])); u = bf16_value(int(gu[m, I + j]))
+            zs = int(math.copysign(1, g) * math.copysign(1, u))
+            want, dist = bf16_rne_exact(swiglu_exact(g, u), zs)
+            if dist < Fraction(1, 2 ** 40):
+                near += 1
+                continue
+            assert int(h[m, j]) == want, (m, j, g, u, hex(int(h[m, j])), hex(want))
+    assert near < 8, near
+
+
+def pin_swiglu_quant(seed=101):
+    """The quantizer runs on the bf16-rounded h: every scale is
+    fl32(amax(h) / 448) and every code the nearest E4M3 value (exhaustive
+    search) to fl32(h / s), with h taken from the exact SiLU(g) * u."""
+    rng = np.random.default_rng(seed)
+    M, I = 2, 256
+    gu = _random_gate_up(rng, M, I)
+    gu[:, :I] = (((rng.standard_normal((M, I)) * 3).astype(np.float32)).view(np.uint32) >> 16).astype(np.uint16)
+    gu[:, I:] = (((rng.standard_normal((M, I))).astype(np.float32)).view(np.uint32) >> 16).astype(np.uint16)
+    q, s = osw.swiglu_act_quant(gu)
+    assert q.shape == (M, I) and s.shape == (M, I // 128)
+    for m in range(M):
+        hb = []
+        for j in range(I):
+            g = bf16_value(int(gu[m, j])); u = bf16_value(int(gu[m, I + j]))
+            zs = int(math.copysign(1, g) * math.copysign(1, u))
+            hb.append(bf16_rne_exact(swiglu_exact(g, u), zs)[0])
+        for grp in range(I // 128):
+            vals = [Fraction(bf16_value(b)) for b in hb[128 * grp: 128 * grp + 128]]
+            amax = max(abs(v) for v in vals)
+            sc = fl32_of(amax / 448)
+            assert float(s[m, grp]) == sc, (m, grp)
+            for k in range(0, 128, 7):
+                t = fl32_of(vals[k] / Fraction(sc))
+                want = brute_force_encode(t) if t != 0 else (0x80 if hb[128 * grp + k] >> 15 else 0)
+                assert int(q[m, 128 * grp + k]) == want, (m, grp, k)
+
+
 ALL_PINS = [
     pin_format_points, pin_hand_encodings, pin_decode_matches_enumeration,
     pin_encode_roundtrip_and_monotone, pin_encode_brute_force, pin_fl32_div,
@@ -798,4 +926,5 @@ ALL_PINS = [
     pin_ue8m0_invariants, pin_ue8m0_weight_blocks, pin_ue8m0_gemm,
     pin_static_hand_cases, pin_static_brute_force, pin_static_invariants, pin_static_gemm,
     pin_batched, pin_rowwise_quant, pin_rowwise_gemm,
+    pin_swiglu_hand_cases, pin_swiglu_brute_force, pin_swiglu_quant,
 ]

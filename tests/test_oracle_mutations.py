@@ -12,6 +12,7 @@ from oracle import quant as oq
 from oracle import ue8m0 as ou
 from oracle import static as ost
 from oracle import layouts as olay
+from oracle import swiglu as osw
 
 
 def _fails(pins):
@@ -71,6 +72,10 @@ MUTANTS = {
     "static_no_saturation": lambda mp: mp.setattr(ost, "act_quant_static", _static_nosat),
     "static_reciprocal_multiply": lambda mp: mp.setattr(ost, "act_quant_static", _static_recip),
     "static_scale_multiplies": lambda mp: mp.setattr(ost, "act_quant_static", _static_mul),
+    "swiglu_halves_swapped": lambda mp: mp.setattr(osw, "swiglu_bf16", _swiglu_swapped),
+    "swiglu_sigmoid_sign": lambda mp: mp.setattr(osw, "swiglu_bf16", lambda b: _swiglu_variant(b, sign=+1)),
+    "swiglu_rounds_silu_first": lambda mp: mp.setattr(osw, "swiglu_bf16", lambda b: _swiglu_variant(b, two_roundings=True)),
+    "swiglu_quantizes_unrounded_h": lambda mp: mp.setattr(osw, "swiglu_act_quant", _swiglu_quant_f32),
     "ue8m0_gemm_weight_bytes_reversed": lambda mp: mp.setattr(
         ou, "block_gemm_ue8m0", lambda xq, xe, wq, we: _orig_bg_ue(xq, xe, wq, we[::-1].copy())),
 }
@@ -78,6 +83,38 @@ MUTANTS = {
 _orig_decode = oe.decode
 _orig_e8m0_exponent = ou.e8m0_exponent
 _orig_bg_ue = ou.block_gemm_ue8m0
+
+
+_orig_swiglu = osw.swiglu_bf16
+
+
+def _swiglu_swapped(bits):
+    b = np.asarray(bits, np.uint16)
+    I = b.shape[1] // 2
+    return _orig_swiglu(np.concatenate([b[:, I:], b[:, :I]], axis=1))
+
+
+def _swiglu_variant(bits, sign=-1, two_roundings=False):
+    b = np.asarray(bits, np.uint16)
+    I = b.shape[1] // 2
+    v = (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    g, u = v[:, :I], v[:, I:]
+    with np.errstate(over="ignore"):
+        silu = g / (1.0 + np.exp(sign * g))
+    if two_roundings:
+        silu = og.bf16_bits_to_f64(og.bf16_rne_bits(silu))
+    return og.bf16_rne_bits(silu * u)
+
+
+def _swiglu_quant_f32(bits):
+    b = np.asarray(bits, np.uint16)
+    I = b.shape[1] // 2
+    v = (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    h = (v[:, :I] / (1.0 + np.exp(-v[:, :I])) * v[:, I:]).astype(np.float32)
+    M = h.shape[0]
+    hg = h.reshape(M, I // 128, 128)
+    q, s = oq.quant_element_map(hg, np.max(np.abs(hg), axis=2, keepdims=True))
+    return q.reshape(M, I), s.reshape(M, I // 128)
 
 
 _orig_batched = olay.batched_block_gemm
