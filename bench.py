@@ -343,6 +343,34 @@ def other_rows(torch, fb, dev, stream):
         rows[f"moe_batched_{name}"] = {"us": round(t * 1e6, 2), "capacity": cap,
                                        "TFLOP/s": round(2.0 * total * N * K / t / 1e12, 1)}
         del xb, sb, yb
+    # SwiGLU + activation quantizer ahead of the MoE down projection: the
+    # gate/up output [32768, 2 * 2048] -> codes [32768, 2048] and scales in
+    # one kernel, against torch's SwiGLU (bf16 h through memory) followed by
+    # the activation quantizer; three rotating inputs (805 MB)
+    I = synth.MOE_INTERMEDIATE
+    gus = [(torch.randn((total, 2 * I), generator=g, device=dev) * synth.MOE_GATE_UP_STD).to(torch.bfloat16)
+           for _ in range(3)]
+    xq = torch.empty((total, I), dtype=torch.uint8, device=dev)
+    xsc = torch.empty((total, I // 128), dtype=torch.float32, device=dev)
+    h = torch.empty((total, I), dtype=torch.bfloat16, device=dev)
+    k = [0]
+
+    def fused():
+        k[0] += 1
+        fb.fp8_swiglu_act_quant(gus[k[0] % 3], xq, xsc)
+
+    def unfused():
+        k[0] += 1
+        gu = gus[k[0] % 3]
+        torch.mul(torch.nn.functional.silu(gu[:, :I]), gu[:, I:], out=h)
+        fb.fp8_act_quant_group(h, xq, xsc)
+    t1 = _time(torch, stream, fused)
+    t2 = _time(torch, stream, unfused)
+    byts = total * I * (4 + 1) + total * (I // 128) * 4
+    rows["moe_swiglu_act_quant_32768x2048"] = {
+        "us": round(t1 * 1e6, 2), "GB/s": round(byts / t1 / 1e9, 1),
+        "torch_swiglu_then_act_quant_us": round(t2 * 1e6, 2)}
+    del gus, xq, xsc, h
     return rows
 
 

@@ -21,8 +21,11 @@ and the static-activation-scale pair (one fp32 scale in a 1-element device
 tensor): fp8_act_quant_static(x, x_scale, x_q),
 fp8_block_gemm_static(x_q, x_scale, w_q, w_scale, y); the batched expert
 layout fp8_batched_block_gemm(x_q, x_scale, w_q, w_scale, counts, y) with
-x_q [E, C, K]; and row-wise scales fp8_rowwise_quant(x, q, scale),
-fp8_rowwise_gemm(x_q, x_scale, w_q, w_scale, y).
+x_q [E, C, K]; row-wise scales fp8_rowwise_quant(x, q, scale),
+fp8_rowwise_gemm(x_q, x_scale, w_q, w_scale, y); and SwiGLU ahead of the
+activation quantizer fp8_swiglu_act_quant(gate_up, x_q, x_scale) (the
+input of a mixture-of-experts down projection, gate_up [M, 2I] with the
+gate first).
 
 Convenience wrappers allocate the outputs; ``scale_fmt`` is "float" (fp32
 scales) or "ue8m0" (E8M0 bytes), and the GEMMs pick the path from the scale
@@ -40,6 +43,7 @@ tensors' dtype:
     rowwise_quant(x) -> (q uint8 [R,K], scale fp32 [R])
     rowwise_gemm(x_q, x_scale, w_q, w_scale) -> y bf16 [M,N]
     linear_rowwise(x, w_q, w_scale) -> y bf16 [M,N]
+    swiglu_act_quant(gate_up) -> (x_q uint8 [M,I], x_scale fp32 [M, I/128])
 """
 from __future__ import annotations
 
@@ -55,7 +59,7 @@ __all__ = [
     "fp8_block_gemm_ue8m0", "fp8_grouped_block_gemm_ue8m0", "fp8_act_quant_static",
     "fp8_block_gemm_static", "act_quant_static", "block_gemm_static", "linear_static",
     "fp8_linear", "fp8_batched_block_gemm", "batched_block_gemm", "fp8_rowwise_quant", "fp8_rowwise_gemm",
-    "rowwise_quant", "rowwise_gemm", "linear_rowwise",
+    "rowwise_quant", "rowwise_gemm", "linear_rowwise", "fp8_swiglu_act_quant", "swiglu_act_quant",
     "weight_block_quant",
     "act_quant_group", "block_gemm", "grouped_block_gemm", "linear", "SCALE_FMTS",
 ]
@@ -101,6 +105,7 @@ def load_library() -> ctypes.CDLL:
         "fp8_linear": [vp, i64, i64, i64, vp, vp, vp, vp, vp, vp],
         "fp8_batched_block_gemm": [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp, vp],
         "fp8_rowwise_quant": [vp, i64, i64, vp, vp, vp],
+        "fp8_swiglu_act_quant": [vp, i64, i64, vp, vp, vp],
         "fp8_rowwise_gemm": [vp, vp, vp, vp, i64, i64, i64, vp, vp],
         "fp8_act_quant_static": [vp, i64, i64, vp, vp, vp],
         "fp8_block_gemm_static": [vp, vp, vp, vp, i64, i64, i64, vp, vp],
@@ -332,6 +337,23 @@ def fp8_rowwise_quant(x, q, scale):
            "fp8_rowwise_quant")
 
 
+def fp8_swiglu_act_quant(gate_up, x_q, x_scale):
+    """gate_up bf16 [M, 2I] (gate in columns [0, I), up in [I, 2I)) ->
+    codes of h = bf16(SiLU(gate) * up) in x_q [M, I] and fp32 group scales
+    in x_scale [M, I/128]."""
+    _need(gate_up, "gate_up", (torch.bfloat16,), 2)
+    M, two_i = gate_up.shape
+    if two_i % 2:
+        raise ValueError("gate_up must hold 2I columns")
+    I = two_i // 2
+    _need(x_q, "x_q", _CODES); _need(x_scale, "x_scale", _F32)
+    _shape_eq(x_q, (M, I), "x_q")
+    if I % BLOCK == 0:
+        _shape_eq(x_scale, (M, I // BLOCK), "x_scale")
+    _check(load_library().fp8_swiglu_act_quant(_ptr(gate_up), M, I, _ptr(x_q), _ptr(x_scale),
+                                               _stream()), "fp8_swiglu_act_quant")
+
+
 def fp8_rowwise_gemm(x_q, x_scale, w_q, w_scale, y):
     _need(x_q, "x_q", _CODES, 2); _need(w_q, "w_q", _CODES, 2)
     _need(x_scale, "x_scale", _F32, 1); _need(w_scale, "w_scale", _F32, 1)
@@ -451,6 +473,14 @@ def rowwise_quant(x):
     q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
     s = torch.empty((x.shape[0],), dtype=torch.float32, device=x.device)
     fp8_rowwise_quant(x, q, s)
+    return q, s
+
+
+def swiglu_act_quant(gate_up):
+    M, I = gate_up.shape[0], gate_up.shape[1] // 2
+    q = torch.empty((M, I), dtype=torch.uint8, device=gate_up.device)
+    s = torch.empty((M, I // BLOCK), dtype=torch.float32, device=gate_up.device)
+    fp8_swiglu_act_quant(gate_up, q, s)
     return q, s
 
 

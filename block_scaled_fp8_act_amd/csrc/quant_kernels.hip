@@ -302,6 +302,151 @@ __global__ __launch_bounds__(kWqThreads) void weight_quant_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// ---------------------------------------------------------------------------
+// SwiGLU ahead of the activation quantizer: the quantized input of a
+// mixture-of-experts down projection, straight from the gate/up projection's
+// bf16 output.  A token's gate/up row holds the gate g in columns [0, I) and
+// the up value u in [I, 2I); h = bf16_RNE(SiLU(g) * u) with SiLU(g) =
+// g / (1 + e^-g) is defined by its binary64 evaluation (IEEE division, the
+// math library's exp), whose bf16 rounding is that of the exact value except
+// within ~2^-52 of a rounding midpoint; an fp32 evaluation is used wherever
+// its rounding is certified to be the same (swiglu_h32).  h [M, I] is then
+// quantized per token per 128-group with the element map of make_qparams /
+// quotient (bit-identical to act_quant_kernel).  h never goes to memory: 4 bytes read and 1 + 4/128
+// written per element of h, against 4 + 2 and 2 + 1 + 4/128 for a SwiGLU
+// kernel followed by the quantizer.
+//
+// Tiles as in act_quant_kernel but of 8 groups, over h's groups (group G =
+// row G / (I/128), 128-column block G % (I/128)), one tile per wave per
+// iteration: load i of lane l holds 8 gate values of group 8*tile + 4i + l/16
+// and, I columns further, the matching 8 up values.  The small tile keeps
+// registers low (45) for occupancy: the kernel is about as much ALU work as
+// memory traffic.
+
+// binary64 -> the nearest bf16 value (ties to even), as an exact fp32.  At or
+// above 2^-126 the significand is rounded to 8 bits on the bit pattern (a
+// carry into the exponent field is the correct result; past bf16's largest
+// value the conversion to fp32 overflows to infinity); below, the quantum is
+// 2^-133 and the value is rounded by scaling.
+__device__ __forceinline__ float bf16_round_f64(double h) {
+  const uint64_t b = (uint64_t)__double_as_longlong(h);
+  if (((b >> 52) & 0x7ff) >= 1023 - 126) {
+    const uint64_t r = (b + 0xFFFFFFFFFFFull + ((b >> 45) & 1)) & ~0x1FFFFFFFFFFFull;
+    return (float)__longlong_as_double((long long)r);
+  }
+  return (float)(rint(h * 0x1p133) * 0x1p-133);
+}
+
+// Kept out of line: it runs for about one element in 2000, and inlined at
+// every element it would hold its constants in registers throughout.
+__device__ __attribute__((noinline)) float swiglu_h64(float g, float u) {
+  const double gd = g;
+  return bf16_round_f64(gd / (1.0 + exp(-gd)) * (double)u);
+}
+
+// e^x for x <= 80 in fp32 from the hardware base-2 exponential: x * log2(e)
+// is formed as th + tl with log2(e) split into an fp32 head and tail and the
+// head product's rounding error recovered exactly by an FMA, so th is an
+// fp32 value and |tl| < 2^-16; then e^x = 2^th * 2^tl with 2^tl = 1 + tl ln 2
+// to within 2^-33.  Relative error: v_exp_f32's (1 ulp) plus one rounding,
+// below 3 * 2^-24.  Results below 2^-126 may be flushed, and x is clamped
+// at -150 so that nothing overflows (callers only add such results to 1).
+__device__ __forceinline__ float exp_small(float x) {
+  constexpr float kL2eHi = 1.44269502162933349609375f;  // fp32(log2 e)
+  constexpr float kL2eLo = 1.925963033500011e-08f;      // log2 e - kL2eHi
+  x = fmaxf(x, -150.0f);
+  const float th = x * kL2eHi;
+  const float tl = fmaf(x, kL2eHi, -th) + x * kL2eLo;
+  const float e0 = __builtin_amdgcn_exp2f(th);
+  return fmaf(e0, tl * 0.693147180559945309f, e0);
+}
+
+// Fast path: the same expression in fp32 (exp_small, the hardware
+// reciprocal, within 1 ulp).  Relative to the exact value its error is
+// below 8 * 2^-24, i.e. at most 8 fp32 ulps of the result, provided nothing
+// over- or underflows: g >= -80 (e^-g finite), |g| >= 2^-100 (SiLU(g)
+// normal) and 2^-120 <= |h| < 2^126.  If moreover the result lies more than
+// 16 fp32 ulps from a bf16 rounding midpoint (its low 16 bits differ from
+// 0x8000 by more than 16), the exact value, the binary64 evaluation and this
+// result all round to the same bf16 value, which is returned with ok = true;
+// otherwise ok = false and the caller takes swiglu_h64 (about 1 element in
+// 2000).
+__device__ __forceinline__ float swiglu_h32(float g, float u, bool &ok) {
+  const float e = exp_small(-g);
+  const float hf = g * __builtin_amdgcn_rcpf(1.0f + e) * u;
+  const uint32_t b = __float_as_uint(hf);
+  const uint32_t mag = b & 0x7fffffffu;
+  const int dist = (int)(b & 0xffffu) - 0x8000;
+  ok = g >= -80.0f && fabsf(g) >= 0x1p-100f && mag >= 0x03800000u && mag < 0x7e800000u &&
+       (dist > 16 || dist < -16);
+  return __uint_as_float((b + 0x7fffu + ((b >> 16) & 1u)) & 0xffff0000u);
+}
+
+constexpr int kSwigluGpt = 8;  // groups per tile of swiglu_quant_kernel (4 per load)
+
+__global__ __launch_bounds__(kActThreads) void swiglu_quant_kernel(
+    const uint16_t *__restrict__ gu, uint32_t gpr, uint2 *__restrict__ q,
+    float *__restrict__ scale, uint32_t n_groups) {
+  constexpr int kGpt = kSwigluGpt;
+  constexpr int L = kGpt / 4;  // 16-byte gate and up loads per lane per tile
+  const int lane = threadIdx.x & 63;
+  const int64_t I = (int64_t)gpr * kBlock;
+  const uint32_t n_tiles = (n_groups + kGpt - 1) / kGpt;
+  const uint32_t stride = gridDim.x * kActWaves;
+  for (uint32_t tile = blockIdx.x * kActWaves + (threadIdx.x >> 6); tile < n_tiles;
+       tile += stride) {
+    uint4 vg[L], vu[L];
+    bool ok[L];
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      const uint32_t G = tile * kGpt + i * 4 + (lane >> 4);
+      ok[i] = G < n_groups;
+      const uint32_t Gc = ok[i] ? G : 0;
+      const uint32_t m = Gc / gpr, j = Gc - m * gpr;
+      const uint4 *p =
+          reinterpret_cast<const uint4 *>(gu + (int64_t)m * 2 * I + (int64_t)j * kBlock) +
+          (lane & 15);
+      vg[i] = ok[i] ? p[0] : make_uint4(0, 0, 0, 0);
+      vu[i] = ok[i] ? p[I / 8] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      float g[8], u[8], h[8];
+      unpack8(vg[i], g);
+      unpack8(vu[i], u);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        bool ok32;
+        h[j] = swiglu_h32(g[j], u[j], ok32);
+        if (!ok32) h[j] = swiglu_h64(g[j], u[j]);
+      }
+      const float amax = row16_max(absmax8(h));
+      float t[8], sc;
+      if (__builtin_amdgcn_ballot_w64(amax > 0.0f && amax < kTinyAmax) == 0) {
+        // as act_quant_kernel's fast path: no power-of-two rescale
+        sc = div448(amax);
+        const float sp = sc == 0.0f ? 1.0f : sc;
+        const float y = 1.0f / sp;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) t[j] = quotient(h[j], sp, y);
+      } else {
+        const QParams p = make_qparams(amax);
+        sc = p.s;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) t[j] = quotient(ldexpf(h[j], p.k), p.sp, p.y);
+      }
+      uint2 out;
+      out.x = pack4_e4m3(t[0], t[1], t[2], t[3]);
+      out.y = pack4_e4m3(t[4], t[5], t[6], t[7]);
+      if (ok[i]) {
+        const uint32_t G = tile * kGpt + i * 4 + (lane >> 4);
+        q[(int64_t)G * 16 + (lane & 15)] = out;
+        if ((lane & 15) == 0) scale[G] = sc;
+      }
+    }
+  }
+}
+
 static unsigned act_quant_blocks(int64_t n_groups) {
   const int64_t n_tiles = (n_groups + kGroupsPerTile - 1) / kGroupsPerTile;
   const int64_t per_block = (int64_t)kActWaves * kTilesPerIter;
@@ -315,6 +460,18 @@ hipError_t launch_act_quant(const void *x, int64_t M, int64_t K, void *q, float 
   const int64_t n_groups = M * (K / kBlock);
   hipLaunchKernelGGL(act_quant_kernel, dim3(act_quant_blocks(n_groups)), dim3(kActThreads), 0,
                      stream, static_cast<const uint4 *>(x), static_cast<uint2 *>(q), s, n_groups);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu_act_quant(const void *gu, int64_t M, int64_t I, void *q, float *s,
+                                   hipStream_t stream) {
+  const int64_t n_groups = M * (I / kBlock);  // < 2^31 (checked by the caller)
+  const int64_t n_tiles = (n_groups + kSwigluGpt - 1) / kSwigluGpt;
+  int64_t blocks = (n_tiles + kActWaves - 1) / kActWaves;
+  if (blocks > 256 * 8) blocks = 256 * 8;
+  hipLaunchKernelGGL(swiglu_quant_kernel, dim3((unsigned)blocks), dim3(kActThreads), 0, stream,
+                     static_cast<const uint16_t *>(gu), (uint32_t)(I / kBlock),
+                     static_cast<uint2 *>(q), s, (uint32_t)n_groups);
   return hipGetLastError();
 }
 

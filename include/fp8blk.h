@@ -186,6 +186,24 @@ FP8BLK_API fp8blk_status fp8_rowwise_gemm(const void *x_q, const float *x_scale,
                                           void *y_bf16, void *stream);
 
 /* ------------------------------------------------------------------------
+ * SwiGLU ahead of the activation quantizer (the quantized input of a
+ * mixture-of-experts down projection).  "Fine-grained FP8" page: experts
+ * run through grouped back-ends with fp32 scales, and activations are
+ * quantized per token per 128-channel group at run time ("DeepGEMM fast
+ * path").  The pages do not spell SwiGLU out; readings fixed here:
+ *   gate_up_bf16 [M, 2I] in: gate g in columns [0, I), up u in [I, 2I);
+ *   h = bf16_RNE(SiLU(g) * u), SiLU(g) = g / (1 + e^-g), evaluated in
+ *   binary64 (its bf16 rounding is the exact value's except within ~2^-52
+ *   of a rounding midpoint);
+ *   x_q [M, I] E4M3 codes and x_scale [M, I/128] fp32 out: exactly
+ *   fp8_act_quant_group applied to h (h itself is never written).
+ * I must be a positive multiple of 128 and M * I / 128 < 2^31
+ * (FP8BLK_ERR_SHAPE).  Every h must be finite (|SiLU(g) * u| below bf16's
+ * overflow threshold); otherwise the codes of its group are unspecified. */
+FP8BLK_API fp8blk_status fp8_swiglu_act_quant(const void *gate_up_bf16, int64_t M, int64_t I,
+                                              void *x_q, float *x_scale, void *stream);
+
+/* ------------------------------------------------------------------------
  * Static activation scale.
  * "Fine-grained FP8" page, "DeepGEMM fast path": besides the dynamic scheme
  * the page names static activation quantization (its back-ends keep it on

@@ -19,6 +19,11 @@ models; no weights or datasets are involved):
 * ``moe``        DeepSeek-V3 MoE share of one device: 32 experts, gate/up
                  4096x7168, down 7168x2048; 4096 tokens routed to 8
                  distinct experts each with Zipf(1.1) popularity.
+                 The SwiGLU step between the two projections takes the
+                 gate/up output [sum M_e, 2*2048], drawn directly as
+                 N(0, 1.34^2): the spread of a 7168-term sum of inputs with
+                 mean square ~2.5 (N(0,1) plus the 0.5 % t(3) tail) times
+                 N(0, 0.01) weights.
 
 Seeds follow ``1000*config + 10*shape_index + {1: x, 2: W, 3: outliers}``.
 """
@@ -170,6 +175,15 @@ def moe_inputs(which: int, config: int = 5, experts: int = MOE_EXPERTS,
         x = dsv3_activations(seed_of(config, which, 1), total, K, seed_of(config, which, 3))
     w = normal_bf16(seed_of(config, which, 2), (experts, N, K), std=0.01)
     return x, w, offsets
+
+
+MOE_INTERMEDIATE = 2048
+MOE_GATE_UP_STD = 1.34
+
+
+def moe_gate_up_output(seed: int, M: int, I: int = MOE_INTERMEDIATE) -> np.ndarray:
+    """Gate/up projection output [M, 2I] (gate columns first) as bf16 bits."""
+    return normal_bf16(seed, (M, 2 * I), std=MOE_GATE_UP_STD)
 
 
 def random_offsets(seed: int, experts: int, sizes=None, max_rows: int = 64):

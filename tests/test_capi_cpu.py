@@ -208,6 +208,25 @@ def test_batched_and_rowwise_validation(lib):
         assert call(lib, "fp8_rowwise_gemm", A, B, C, D, 4, 256, 128, E_, NULL) == 4
 
 
+def test_swiglu_validation(lib):
+    # fp8_swiglu_act_quant(gate_up, M, I, x_q, x_scale, stream)
+    f = "fp8_swiglu_act_quant"
+    assert call(lib, f, NULL, 4, 128, B, C, NULL) == 1
+    assert call(lib, f, A, 4, 128, NULL, C, NULL) == 1
+    assert call(lib, f, A, 4, 128, B, NULL, NULL) == 1
+    assert call(lib, f, A, -1, 128, B, C, NULL) == 2
+    assert call(lib, f, A, 4, 0, B, C, NULL) == 2
+    assert call(lib, f, A, 4, 192, B, C, NULL) == 2
+    assert call(lib, f, A, 1 << 30, 1 << 10, B, C, NULL) == 2     # 2^31 groups
+    assert call(lib, f, MIS, 4, 128, B, C, NULL) == 3
+    assert call(lib, f, A, 4, 128, MIS, C, NULL) == 3
+    assert call(lib, f, A, 4, 128, B, MIS, NULL) == 3
+    assert call(lib, f, NULL, 0, 128, NULL, NULL, NULL) in (0, 4)   # empty: no pointers needed
+    import torch
+    if not torch.cuda.is_available():
+        assert call(lib, f, A, 4, 128, B, C, NULL) == 4
+
+
 def test_linear_validation(lib):
     # fp8_linear(x, M, N, K, w_q, w_scale, x_q_ws, x_scale_ws, y, stream)
     f = "fp8_linear"
