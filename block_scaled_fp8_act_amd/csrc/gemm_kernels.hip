@@ -130,19 +130,31 @@ __device__ __forceinline__ int swz(int row, int chunk) {
 // fragment of mi-1 (whose MFMAs finished long ago), and the LDS reads for
 // fragment mi+1 go out right after the first MFMA; scheduling barriers pin
 // this order so the FMAs fill the MFMA shadow without waiting on a result.
-template <int WM, int WN, int FM>
+//
+// KS > 1 splits K inside the workgroup: KS groups of WM x WN waves, each with
+// its own two LDS stages (sm0 is the first of KS consecutive Smem), take K
+// blocks kg, kg + KS, ... in lockstep (one shared barrier per step); a group
+// past the last K block re-reads it with its weight scale zeroed.  At the end
+// groups 1.. hand their accumulators to group 0 through LDS, which adds them
+// (in group order) and stores the tile.  For grids too small to give a CU
+// more than one workgroup, this puts KS waves on each SIMD.
+template <int WM, int WN, int FM, int KS = 1>
 __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ A,
                                           const float *__restrict__ As, int64_t xs_rs, int xs_ks,
                                           int rows_a, const uint8_t *__restrict__ B,
                                           const float *__restrict__ Bs, int rows_b, int64_t K,
                                           uint16_t *__restrict__ Y, int64_t ldy,
-                                          typename Tile<WM, WN, FM>::Smem &sm) {
+                                          typename Tile<WM, WN, FM>::Smem &sm0) {
   using T = Tile<WM, WN, FM>;
   const int t = threadIdx.x;
   const int lane = t & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wave_all = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int kg = KS == 1 ? 0 : wave_all / T::kWaves;  // K group
+  const int wave = KS == 1 ? wave_all : wave_all % T::kWaves;
+  auto &sm = (&sm0)[kg];
   const int wm = wave / WN, wn = wave % WN;
   const int KB = (int)(K / 128);
+  const int KI = (KB + KS - 1) / KS;  // steps (the same for every group)
 
   // DMA load i of a wave fills LDS rows [8r, 8r+8), r = kDma*w + i; lane l
   // writes bytes [16l, 16l+16) of that 1 KB run = row 8r + l/8, physical
@@ -193,7 +205,7 @@ __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ A,
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-  issue(0, 0);
+  issue(min(kg, KB - 1), 0);
   // Y (a kernel argument) is first used by the epilogue; consuming it here
   // makes its scalar load complete before the loop.  With no scalar load in
   // flight the LDS reads of the loop can be waited on partially (LDS
@@ -209,9 +221,9 @@ __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ A,
   const int srow0 = wm * FM * 16 + 4 * (lane >> 4);
 
 
-  for (int kb = 0; kb < KB; ++kb) {
-    const int st = kb & 1;
-    const float wsc = sm.ws[st][wsel];
+  for (int it = 0; it < KI; ++it) {
+    const int st = it & 1;
+    const float wsc = (KS == 1 || it * KS + kg < KB) ? sm.ws[st][wsel] : 0.0f;
     __builtin_amdgcn_sched_barrier(0);
     const uint8_t *sa = sm.a[st];
     const float4 *sas = reinterpret_cast<const float4 *>(&sm.as[st][srow0]);
@@ -267,7 +279,7 @@ __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ A,
       if (mi == 0) {
         // next stage's DMA goes out once this step's first fragment is
         // running, so the step-start LDS reads can be waited on partially
-        if (kb + 1 < KB) issue(kb + 1, st ^ 1);
+        if (it + 1 < KI) issue(min((it + 1) * KS + kg, KB - 1), st ^ 1);
         __builtin_amdgcn_sched_barrier(0);
       }
       scp[0] = s4.x * wsc; scp[1] = s4.y * wsc; scp[2] = s4.z * wsc; scp[3] = s4.w * wsc;
@@ -286,6 +298,36 @@ __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ A,
     for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[FM - 1][ni][r] = fmaf(pp[ni][r], scp[r], acc[FM - 1][ni][r]);
+  }
+
+  if constexpr (KS > 1) {
+    // The last step's barrier ended every LDS read and DMA: the stages are
+    // free.  Groups 1.. write their accumulators (conflict-free: lane-major)
+    // into one group-sized slot each, group 0 adds them in order.
+    static_assert((size_t)(KS - 1) * T::TM * T::TN * 4 <= KS * sizeof(typename T::Smem),
+                  "reduction buffer does not fit in the stages");
+    float *red = reinterpret_cast<float *>(&sm0);
+    auto slot = [&](int g, int mi, int ni, int r) {
+      return (((((g - 1) * T::kWaves + wave) * FM + mi) * 4 + ni) * 4 + r) * 64 + lane;
+    };
+    if (kg > 0) {
+#pragma unroll
+      for (int mi = 0; mi < FM; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) red[slot(kg, mi, ni, r)] = acc[mi][ni][r];
+    }
+    __syncthreads();
+    if (kg > 0) return;
+#pragma unroll
+    for (int g = 1; g < KS; ++g)
+#pragma unroll
+      for (int mi = 0; mi < FM; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[mi][ni][r] += red[slot(g, mi, ni, r)];
   }
 
   // Epilogue: lane holds rows 4*(lane/16)+r of each 16x16 fragment, column lane%16.
@@ -868,6 +910,24 @@ __global__ __launch_bounds__(WM * WN * 64) void block_gemm_kernel(
                           (int)min<int64_t>(T::TN, N - n0), K, y + m0 * N + n0, N, sm);
 }
 
+// Split-K inside the workgroup (fp32 scales): KS groups of WM x WN waves on
+// one tile, for grids that leave CUs with a single workgroup.
+template <int WM, int WN, int FM, int KS>
+__global__ __launch_bounds__(WM * WN * 64 * KS) void block_gemm_ks_kernel(
+    const uint8_t *__restrict__ xq, const float *__restrict__ xs, int64_t xs_rs, int xs_ks,
+    const uint8_t *__restrict__ wq, const float *__restrict__ ws, int64_t M, int64_t N,
+    int64_t K, uint16_t *__restrict__ y, int tiles_m, int tiles_n) {
+  using T = Tile<WM, WN, FM>;
+  __shared__ typename T::Smem sm[KS];
+  int tm, tn;
+  tile_coords(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, tm, tn);
+  const int64_t m0 = (int64_t)tm * T::TM, n0 = (int64_t)tn * T::TN;
+  const int64_t KB = K / 128;
+  gemm_tile<WM, WN, FM, KS>(xq + m0 * K, xs + m0 * xs_rs, xs_rs, xs_ks,
+                            (int)min<int64_t>(T::TM, M - m0), wq + n0 * K, ws + (n0 / 128) * KB,
+                            (int)min<int64_t>(T::TN, N - n0), K, y + m0 * N + n0, N, sm[0]);
+}
+
 // Grouped variant.  The logical m-tiles of all experts are numbered
 // consecutively (expert e owns ceil(M_e/TM) of them); the grid is sized for
 // the upper bound ceil(total_M/TM) + E, and workgroups past the real count
@@ -935,6 +995,21 @@ static hipError_t launch_tiled(const void *xq, const S *xs, int64_t xs_rs, int x
   return hipGetLastError();
 }
 
+constexpr int64_t kKsMaxTiles = 256;
+
+template <int WM, int WN, int FM, int KS>
+static hipError_t launch_tiled_ks(const void *xq, const float *xs, int64_t xs_rs, int xs_ks,
+                                  const void *wq, const float *ws, int64_t M, int64_t N, int64_t K,
+                                  void *y, hipStream_t stream) {
+  using T = Tile<WM, WN, FM>;
+  const int tm = (int)((M + T::TM - 1) / T::TM), tn = (int)((N + T::TN - 1) / T::TN);
+  hipLaunchKernelGGL((block_gemm_ks_kernel<WM, WN, FM, KS>), dim3((unsigned)(tm * tn)),
+                     dim3(T::kThreads * KS), 0, stream, static_cast<const uint8_t *>(xq), xs, xs_rs,
+                     xs_ks, static_cast<const uint8_t *>(wq), ws, M, N, K,
+                     static_cast<uint16_t *>(y), tm, tn);
+  return hipGetLastError();
+}
+
 // Configuration choice (both scale types): the decode kernel for M <= 64
 // (fp32 scales: while its LDS scale staging fits), 256x256 tiles when they
 // fill the chip (>= 192 tiles), 128x128 otherwise.
@@ -953,6 +1028,12 @@ static hipError_t dispatch_gemm(const void *xq, const S *xs, int64_t xs_rs, int 
   const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
   if (big_tiles >= 192)
     return launch_tiled<2, 4, 8, S>(xq, xs, xs_rs, xs_ks, wq, ws, M, N, K, y, stream);
+  if constexpr (std::is_same<S, float>::value) {
+    // at most ~one 128x128 workgroup per CU: split K over two wave groups
+    const int64_t small_tiles = ((M + 127) / 128) * ((N + 127) / 128);
+    if (small_tiles <= kKsMaxTiles && K >= 256)
+      return launch_tiled_ks<2, 2, 4, 2>(xq, xs, xs_rs, xs_ks, wq, ws, M, N, K, y, stream);
+  }
   return launch_tiled<2, 2, 4, S>(xq, xs, xs_rs, xs_ks, wq, ws, M, N, K, y, stream);
 }
 

@@ -60,6 +60,38 @@ def test_gemm_exact_integer_operands(M, N, K):
     assert bad.size == 0, f"{len(bad)} outputs differ, first {bad[:3].tolist()}"
 
 
+@pytest.mark.parametrize("M,N,K", [(65, 128, 256), (130, 576, 384), (257, 1000, 640),
+                                   (1024, 1024, 1152), (300, 2000, 2048)])
+def test_gemm_split_k_tiles_exact(M, N, K):
+    """Grids of at most 320 128x128 tiles run with K split over two wave
+    groups inside the workgroup (odd K-block counts included: the second
+    group's extra step must add nothing).  Integer operands with
+    power-of-two scales keep every sum exact, so the order of the two
+    partial sums cannot matter: bit-exact against bf16_RNE(exact)."""
+    rng = np.random.default_rng(M * 7 + N + K)
+    xi = rng.integers(-8, 9, (M, K)); wi = rng.integers(-8, 9, (N, K))
+    xq = oe.encode(xi.astype(np.float32)); wq = oe.encode(wi.astype(np.float32))
+    KB, NB = K // 128, -(-N // 128)
+    xs = np.exp2(rng.integers(-1, 2, (M, KB))).astype(np.float32)
+    ws = np.exp2(rng.integers(0, 2, (NB, KB))).astype(np.float32)
+    y = gpu_gemm(xq, xs, wq, ws)
+    want = og.bf16_rne_bits(og.block_gemm(xq, xs, wq, ws))
+    bad = np.argwhere(y != want)
+    assert bad.size == 0, f"{len(bad)} outputs differ, first {bad[:3].tolist()}"
+
+
+@pytest.mark.parametrize("M,N,K", [(100, 300, 384), (520, 1100, 1408), (4096, 1024, 640)])
+def test_gemm_split_k_tiles_tolerance(M, N, K):
+    x = synth.dsv3_activations(M + 5 * K, M, K, N)
+    w = synth.normal_bf16(N + 3 * K, (N, K), 0.01)
+    xq, xs, wq, ws = quantized_operands(x, w)
+    rows = np.arange(M) if M <= 600 else np.sort(np.concatenate(
+        [[0, M - 1], np.random.default_rng(1).choice(np.arange(1, M - 1), 126, replace=False)]))
+    y = gpu_gemm(xq, xs, wq, ws)
+    check_tol(y[rows], og.block_gemm(xq[rows], xs[rows], wq, ws),
+              og.term_magnitude(xq[rows], xs[rows], wq, ws), f"split-K {M}x{N}x{K}")
+
+
 @pytest.mark.parametrize("M,N,K", [(8, 256, 1536), (33, 200, 1280)])
 def test_gemm_scale_indexing(M, N, K):
     """All codes 1.0; x_s[m,kb] = 2^((kb+m) % KB), w_s[nb,kb] = 2^(KB*((kb+nb)%2)):
