@@ -359,22 +359,31 @@ __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ A,
 // MFMAs accumulate unscaled products over all of K, and the epilogue
 // multiplies output (r, c) by xr[r] * wr[c] (fp32 scales of the tile's rows
 // and columns); As and Bs are unused.
-template <int WM, int WN, int FM, bool kDmaAtBarrier, bool kScaled = true>
+//
+// KS > 1 splits K inside the workgroup as in gemm_tile (KS groups, each with
+// its own stages in sm0[0..KS-1], K blocks kg, kg + KS, ...; group 0 sums
+// and stores).  Here the MFMAs accumulate directly, so a group cannot sit out
+// a step: the caller guarantees KB % KS == 0.
+template <int WM, int WN, int FM, bool kDmaAtBarrier, bool kScaled = true, int KS = 1>
 __device__ __forceinline__ void gemm_tile_mx(const uint8_t *__restrict__ A,
                                              const uint8_t *__restrict__ As, int rows_a,
                                              const uint8_t *__restrict__ B,
                                              const uint8_t *__restrict__ Bs, int rows_b, int64_t K,
                                              uint16_t *__restrict__ Y, int64_t ldy,
-                                             typename Tile<WM, WN, FM>::SmemMx &sm,
+                                             typename Tile<WM, WN, FM>::SmemMx &sm0,
                                              const float *__restrict__ xr = nullptr,
                                              const float *__restrict__ wr = nullptr) {
   using T = Tile<WM, WN, FM>;
   static_assert(FM % 4 == 0, "scale slots are read four at a time");
   const int t = threadIdx.x;
   const int lane = t & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wave_all = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int kg = KS == 1 ? 0 : wave_all / T::kWaves;  // K group
+  const int wave = KS == 1 ? wave_all : wave_all % T::kWaves;
+  auto &sm = (&sm0)[kg];
   const int wm = wave / WN, wn = wave % WN;
   const int KB = (int)(K / 128);
+  const int KI = KB / KS;  // steps (KB % KS == 0)
   const int r16 = lane & 15;
 
   uint32_t oa[T::kDmaA];
@@ -433,8 +442,8 @@ __device__ __forceinline__ void gemm_tile_mx(const uint8_t *__restrict__ A,
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-  issue(0, 0);
-  if constexpr (kDmaAtBarrier) issue(min(1, KB - 1), 1);
+  issue(kg, 0);
+  if constexpr (kDmaAtBarrier) issue(min(KS + kg, KB - 1), 1);
   asm volatile("" ::"s"(Y));  // no scalar load left in flight (see gemm_tile)
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -468,8 +477,8 @@ __device__ __forceinline__ void gemm_tile_mx(const uint8_t *__restrict__ A,
   // nobody reads again, which keeps the step branch-free.
   v8i b0n = read_b(0, 0);
   v8i a0n = read_a(0, 0);
-  for (int kb = 0; kb < KB; ++kb) {
-    const int st = kb & 1;
+  for (int it = 0; it < KI; ++it) {
+    const int st = it & 1;
     v8i bfr[4];
     bfr[0] = b0n;
     v8i af = a0n;
@@ -496,7 +505,7 @@ __device__ __forceinline__ void gemm_tile_mx(const uint8_t *__restrict__ A,
       if (mi == FM - 1) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if constexpr (kDmaAtBarrier) issue(min(kb + 2, KB - 1), st);
+        if constexpr (kDmaAtBarrier) issue(min((it + 2) * KS + kg, KB - 1), st);
         // the last step reads the re-fetched block KB-1 here (unused)
         b0n = read_b(st ^ 1, 0);
         a0n = read_a(st ^ 1, 0);
@@ -518,7 +527,7 @@ __device__ __forceinline__ void gemm_tile_mx(const uint8_t *__restrict__ A,
       }
       if constexpr (!kDmaAtBarrier) {
         if (mi == 0) {
-          issue(min(kb + 1, KB - 1), st ^ 1);
+          issue(min((it + 1) * KS + kg, KB - 1), st ^ 1);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -527,6 +536,35 @@ __device__ __forceinline__ void gemm_tile_mx(const uint8_t *__restrict__ A,
     }
   }
   __builtin_amdgcn_s_waitcnt(0);
+
+  if constexpr (KS > 1) {
+    // as in gemm_tile: groups 1.. hand their accumulators to group 0
+    static_assert((size_t)(KS - 1) * T::TM * T::TN * 4 <= KS * sizeof(typename T::SmemMx),
+                  "reduction buffer does not fit in the stages");
+    __syncthreads();  // every wave is past its last LDS read and DMA
+    float *red = reinterpret_cast<float *>(&sm0);
+    auto slot = [&](int g, int mi, int ni, int r) {
+      return (((((g - 1) * T::kWaves + wave) * FM + mi) * 4 + ni) * 4 + r) * 64 + lane;
+    };
+    if (kg > 0) {
+#pragma unroll
+      for (int mi = 0; mi < FM; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) red[slot(kg, mi, ni, r)] = acc[mi][ni][r];
+    }
+    __syncthreads();
+    if (kg > 0) return;
+#pragma unroll
+    for (int g = 1; g < KS; ++g)
+#pragma unroll
+      for (int mi = 0; mi < FM; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[mi][ni][r] += red[slot(g, mi, ni, r)];
+  }
 
   float cs[4] = {1.0f, 1.0f, 1.0f, 1.0f};
   if constexpr (!kScaled) {
@@ -910,22 +948,34 @@ __global__ __launch_bounds__(WM * WN * 64) void block_gemm_kernel(
                           (int)min<int64_t>(T::TN, N - n0), K, y + m0 * N + n0, N, sm);
 }
 
-// Split-K inside the workgroup (fp32 scales): KS groups of WM x WN waves on
-// one tile, for grids that leave CUs with a single workgroup.
-template <int WM, int WN, int FM, int KS>
+// Split-K inside the workgroup: KS groups of WM x WN waves on one tile, for
+// grids that leave CUs with a single workgroup.  S = float: fp32 scales
+// (any K); S = uint8_t: E8M0 bytes (K/128 a multiple of KS); kRow: row-wise
+// fp32 scales xs[M], ws[N] (K/128 a multiple of KS).
+template <int WM, int WN, int FM, int KS, typename S, bool kRow = false>
 __global__ __launch_bounds__(WM * WN * 64 * KS) void block_gemm_ks_kernel(
-    const uint8_t *__restrict__ xq, const float *__restrict__ xs, int64_t xs_rs, int xs_ks,
-    const uint8_t *__restrict__ wq, const float *__restrict__ ws, int64_t M, int64_t N,
+    const uint8_t *__restrict__ xq, const S *__restrict__ xs, int64_t xs_rs, int xs_ks,
+    const uint8_t *__restrict__ wq, const S *__restrict__ ws, int64_t M, int64_t N,
     int64_t K, uint16_t *__restrict__ y, int tiles_m, int tiles_n) {
   using T = Tile<WM, WN, FM>;
-  __shared__ typename T::Smem sm[KS];
+  constexpr bool kMx = std::is_same<S, uint8_t>::value || kRow;
+  __shared__ typename std::conditional<kMx, typename T::SmemMx, typename T::Smem>::type sm[KS];
   int tm, tn;
   tile_coords(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * T::TM, n0 = (int64_t)tn * T::TN;
   const int64_t KB = K / 128;
-  gemm_tile<WM, WN, FM, KS>(xq + m0 * K, xs + m0 * xs_rs, xs_rs, xs_ks,
-                            (int)min<int64_t>(T::TM, M - m0), wq + n0 * K, ws + (n0 / 128) * KB,
-                            (int)min<int64_t>(T::TN, N - n0), K, y + m0 * N + n0, N, sm[0]);
+  const int rows_a = (int)min<int64_t>(T::TM, M - m0), rows_b = (int)min<int64_t>(T::TN, N - n0);
+  if constexpr (kRow)
+    gemm_tile_mx<WM, WN, FM, (FM <= 4), false, KS>(xq + m0 * K, nullptr, rows_a, wq + n0 * K,
+                                                   nullptr, rows_b, K, y + m0 * N + n0, N, sm[0],
+                                                   xs + m0, ws + n0);
+  else if constexpr (kMx)
+    gemm_tile_mx<WM, WN, FM, (FM <= 4), true, KS>(xq + m0 * K, xs + m0 * KB, rows_a, wq + n0 * K,
+                                                  ws + (n0 / 128) * KB, rows_b, K, y + m0 * N + n0,
+                                                  N, sm[0]);
+  else
+    gemm_tile<WM, WN, FM, KS>(xq + m0 * K, xs + m0 * xs_rs, xs_rs, xs_ks, rows_a, wq + n0 * K,
+                              ws + (n0 / 128) * KB, rows_b, K, y + m0 * N + n0, N, sm[0]);
 }
 
 // Grouped variant.  The logical m-tiles of all experts are numbered
@@ -997,13 +1047,13 @@ static hipError_t launch_tiled(const void *xq, const S *xs, int64_t xs_rs, int x
 
 constexpr int64_t kKsMaxTiles = 256;
 
-template <int WM, int WN, int FM, int KS>
-static hipError_t launch_tiled_ks(const void *xq, const float *xs, int64_t xs_rs, int xs_ks,
-                                  const void *wq, const float *ws, int64_t M, int64_t N, int64_t K,
+template <int WM, int WN, int FM, int KS, typename S, bool kRow = false>
+static hipError_t launch_tiled_ks(const void *xq, const S *xs, int64_t xs_rs, int xs_ks,
+                                  const void *wq, const S *ws, int64_t M, int64_t N, int64_t K,
                                   void *y, hipStream_t stream) {
   using T = Tile<WM, WN, FM>;
   const int tm = (int)((M + T::TM - 1) / T::TM), tn = (int)((N + T::TN - 1) / T::TN);
-  hipLaunchKernelGGL((block_gemm_ks_kernel<WM, WN, FM, KS>), dim3((unsigned)(tm * tn)),
+  hipLaunchKernelGGL((block_gemm_ks_kernel<WM, WN, FM, KS, S, kRow>), dim3((unsigned)(tm * tn)),
                      dim3(T::kThreads * KS), 0, stream, static_cast<const uint8_t *>(xq), xs, xs_rs,
                      xs_ks, static_cast<const uint8_t *>(wq), ws, M, N, K,
                      static_cast<uint16_t *>(y), tm, tn);
@@ -1028,12 +1078,12 @@ static hipError_t dispatch_gemm(const void *xq, const S *xs, int64_t xs_rs, int 
   const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
   if (big_tiles >= 192)
     return launch_tiled<2, 4, 8, S>(xq, xs, xs_rs, xs_ks, wq, ws, M, N, K, y, stream);
-  if constexpr (std::is_same<S, float>::value) {
-    // at most ~one 128x128 workgroup per CU: split K over two wave groups
-    const int64_t small_tiles = ((M + 127) / 128) * ((N + 127) / 128);
-    if (small_tiles <= kKsMaxTiles && K >= 256)
-      return launch_tiled_ks<2, 2, 4, 2>(xq, xs, xs_rs, xs_ks, wq, ws, M, N, K, y, stream);
-  }
+  // at most one 128x128 workgroup per CU: split K over two wave groups
+  // (E8M0 scales: only for an even number of K blocks)
+  const int64_t small_tiles = ((M + 127) / 128) * ((N + 127) / 128);
+  if (small_tiles <= kKsMaxTiles && K >= 256 &&
+      (std::is_same<S, float>::value || (K / 128) % 2 == 0))
+    return launch_tiled_ks<2, 2, 4, 2, S>(xq, xs, xs_rs, xs_ks, wq, ws, M, N, K, y, stream);
   return launch_tiled<2, 2, 4, S>(xq, xs, xs_rs, xs_ks, wq, ws, M, N, K, y, stream);
 }
 
@@ -1122,6 +1172,9 @@ hipError_t launch_rowwise_gemm(const void *xq, const float *xs, const void *wq, 
   }
   const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
   if (big_tiles >= 192) return launch_rowwise_tiled<2, 4, 8>(xq, xs, wq, ws, M, N, K, y, stream);
+  const int64_t small_tiles = ((M + 127) / 128) * ((N + 127) / 128);
+  if (small_tiles <= kKsMaxTiles && K >= 256 && (K / 128) % 2 == 0)
+    return launch_tiled_ks<2, 2, 4, 2, float, true>(xq, xs, 0, 0, wq, ws, M, N, K, y, stream);
   return launch_rowwise_tiled<2, 2, 4>(xq, xs, wq, ws, M, N, K, y, stream);
 }
 

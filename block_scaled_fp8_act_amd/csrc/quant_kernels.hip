@@ -377,8 +377,11 @@ __device__ __forceinline__ float swiglu_h32(float g, float u, bool &ok) {
   const uint32_t b = __float_as_uint(hf);
   const uint32_t mag = b & 0x7fffffffu;
   const int dist = (int)(b & 0xffffu) - 0x8000;
-  ok = g >= -80.0f && fabsf(g) >= 0x1p-100f && mag >= 0x03800000u && mag < 0x7e800000u &&
-       (dist > 16 || dist < -16);
+  // g = 0 or u = 0 (with e^-g finite): hf is the exact signed zero that
+  // the binary64 evaluation gives too
+  ok = g >= -80.0f && (g == 0.0f || u == 0.0f ||
+                       (fabsf(g) >= 0x1p-100f && mag >= 0x03800000u && mag < 0x7e800000u &&
+                        (dist > 16 || dist < -16)));
   return __uint_as_float((b + 0x7fffu + ((b >> 16) & 1u)) & 0xffff0000u);
 }
 

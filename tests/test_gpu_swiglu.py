@@ -108,6 +108,20 @@ def test_near_midpoints():
     check(gate_up_from_pairs(gg, uu, 512), "near midpoints")
 
 
+def test_zero_heavy():
+    """Half the gates and a third of the up values exact (signed) zeros:
+    the products are exact signed zeros on both sides."""
+    rng = np.random.default_rng(19)
+    gu = synth.moe_gate_up_output(23, 96, 512)
+    I = 512
+    zg = rng.random((96, I)) < 0.5
+    zu = rng.random((96, I)) < 0.33
+    gu[:, :I] = np.where(zg, (rng.integers(0, 2, (96, I)) << 15).astype(np.uint16), gu[:, :I])
+    gu[:, I:] = np.where(zu, (rng.integers(0, 2, (96, I)) << 15).astype(np.uint16), gu[:, I:])
+    gu[0, :I] = 0x8000                                   # a row of -0 gates: all-zero groups
+    check(gu, "zero-heavy")
+
+
 @pytest.mark.parametrize("M,I", [(1, 128), (3, 384), (17, 2048), (130, 256), (5, 7168), (64, 128)])
 def test_ragged(M, I):
     gu = synth.moe_gate_up_output(M * 31 + I, M, I)
