@@ -208,7 +208,9 @@ def main():
                    "M": M_PREFILL, "shapes_NxK": [[N, K] for (_, N, K) in PREFILL_SHAPES],
                    "block": 128, "parallelism": "single GPU"},
         "roofline": {
-            "bound": "mfma", "kernel": "block_gemm_kernel",
+            "bound": "mfma",
+            "kernel": "block-scaled GEMM: block_gemm_kernel (q/o, gate/up, down), "
+                      "block_gemm_ks_kernel (kv)",
             "achieved": round(gemm_tflops, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
             "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4), "traffic": measured_traffic(),
             "traffic_unit": "HBM bytes per launch (mean over the 4 projections)",
