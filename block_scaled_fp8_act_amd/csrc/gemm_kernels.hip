@@ -613,28 +613,34 @@ constexpr int kDecMaxScaleBytes = 32 * 1024;  // x_scale staging limit (KB * MF 
 // matrix core (nothing staged in LDS but the final partials).  kRow: fp32
 // row-wise scales (xs[M], ws[N]): unscaled MFMAs accumulate over all of K and
 // the sum is scaled by xs[m] * ws[n] at the end.
-template <int MF, typename S, bool kRow = false>
+template <int MF, typename S, bool kRow = false, int NS = 1>
 __global__ __launch_bounds__(kDecThreads) void decode_gemm_kernel(
     const uint8_t *__restrict__ xq, const S *__restrict__ xs, int64_t xs_rs, int xs_ks,
     const uint8_t *__restrict__ wq, const S *__restrict__ ws, int M, int64_t N, int64_t K,
     uint16_t *__restrict__ y) {
   constexpr bool MX = std::is_same<S, uint8_t>::value;
   static_assert(!(kRow && MX), "row-wise scales are fp32");
-  constexpr int R = MF * 16;                  // staged rows
-  constexpr int U = 4 / MF;                   // K blocks in flight per wave
+  static_assert(NS == 1 || NS == 2 || NS == 4, "slabs per workgroup: 1, 2 or 4");
+  constexpr int R = MF * 16;                          // staged rows
+  // register buffers of U K blocks: two (the next batch's loads go out
+  // before the current batch's MFMAs) unless four row fragments leave no
+  // room (then one, reloaded after its MFMAs)
+  constexpr int NB = MF >= 4 ? 1 : 2;
+  constexpr int U = (4 / NB) / (MF * NS) > 0 ? (4 / NB) / (MF * NS) : 1;
   extern __shared__ __align__(16) float dsm[];
-  float *s_as = dsm;                          // [KB][R] (fp32 scales only)
+  float *s_as = dsm;                                  // [KB][R] (fp32 scales only)
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int KB = (int)(K / 128);
-  v4f *s_part = reinterpret_cast<v4f *>(dsm);   // [waves][MF][64], reuses s_as after the loop
-  const int64_t n0 = (int64_t)blockIdx.x * 16;
-  const int rows_b = (int)min<int64_t>(16, N - n0);
+  v4f *s_part = reinterpret_cast<v4f *>(dsm);  // [waves][NS][MF][64], reuses s_as after the loop
+  const int64_t n0 = (int64_t)blockIdx.x * 16 * NS;
 
   const int r16 = lane & 15;
   const int kc = (lane >> 4) * 32;  // this lane's 32 K bytes within the block
-  const uint8_t *pb = wq + (n0 + min(r16, rows_b - 1)) * K + kc;
+  const uint8_t *pb[NS];            // weight row of this lane's column in slab s (clamped)
+#pragma unroll
+  for (int sl = 0; sl < NS; ++sl) pb[sl] = wq + min<int64_t>(n0 + 16 * sl + r16, N - 1) * K + kc;
   const uint8_t *pa[MF];
   const S *psa[MF];                 // E8M0: scale row of this lane's A-operand row
 #pragma unroll
@@ -642,33 +648,39 @@ __global__ __launch_bounds__(kDecThreads) void decode_gemm_kernel(
     pa[f] = xq + (int64_t)min(f * 16 + r16, M - 1) * K + kc;
     psa[f] = xs + (int64_t)min(f * 16 + r16, M - 1) * KB;
   }
+  // the NS slabs (16 * NS <= 64 columns from a multiple of 16 * NS) share
+  // one 128-column weight block
   const S *pws = ws + (n0 / 128) * KB;
   const int nmine = wave < KB ? (KB - wave + kDecWaves - 1) / kDecWaves : 0;
 
-  uint4 bw[U][2];
-  v8i af[U][MF];
-  int sa[U][MF], sb[U];
-  auto load = [&](int j0) {
+  uint4 bw[NB][U][NS][2];
+  v8i af[NB][U][MF];
+  int sa[NB][U][MF], sb[NB][U];
+  auto load = [&](auto bufc, int j0) {
+    constexpr int buf = decltype(bufc)::value;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (j0 + u < nmine) {
         const int kb = wave + kDecWaves * (j0 + u);
         const int64_t ko = (int64_t)kb * 128;
-        bw[u][0] = *reinterpret_cast<const uint4 *>(pb + ko);
-        bw[u][1] = *reinterpret_cast<const uint4 *>(pb + ko + 16);
+#pragma unroll
+        for (int sl = 0; sl < NS; ++sl) {
+          bw[buf][u][sl][0] = *reinterpret_cast<const uint4 *>(pb[sl] + ko);
+          bw[buf][u][sl][1] = *reinterpret_cast<const uint4 *>(pb[sl] + ko + 16);
+        }
 #pragma unroll
         for (int f = 0; f < MF; ++f)
-          af[u][f] = frag_from(*reinterpret_cast<const uint4 *>(pa[f] + ko),
-                               *reinterpret_cast<const uint4 *>(pa[f] + ko + 16));
+          af[buf][u][f] = frag_from(*reinterpret_cast<const uint4 *>(pa[f] + ko),
+                                    *reinterpret_cast<const uint4 *>(pa[f] + ko + 16));
         if constexpr (MX) {
 #pragma unroll
-          for (int f = 0; f < MF; ++f) sa[u][f] = psa[f][kb];
-          sb[u] = pws[kb];
+          for (int f = 0; f < MF; ++f) sa[buf][u][f] = psa[f][kb];
+          sb[buf][u] = pws[kb];
         }
       }
     }
   };
-  load(0);
+  load(std::integral_constant<int, 0>{}, 0);
 
   if constexpr (!MX && !kRow) {
     for (int i = t; i < KB * R; i += kDecThreads) {
@@ -678,81 +690,129 @@ __global__ __launch_bounds__(kDecThreads) void decode_gemm_kernel(
     __syncthreads();
   }
 
-  v4f acc[MF];
+  v4f acc[NS][MF];
 #pragma unroll
-  for (int f = 0; f < MF; ++f) acc[f] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int sl = 0; sl < NS; ++sl)
+#pragma unroll
+    for (int f = 0; f < MF; ++f) acc[sl][f] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-  for (int j0 = 0; j0 < nmine; j0 += U) {
+  auto compute = [&](auto bufc, int j0) {
+    constexpr int buf = decltype(bufc)::value;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (j0 + u < nmine) {
         const int kb = wave + kDecWaves * (j0 + u);
-        const v8i bf = frag_from(bw[u][0], bw[u][1]);
-        if constexpr (MX) {
+        float4 s4[MF];
+        float wsc = 1.0f;
+        if constexpr (!MX && !kRow) {
+          wsc = pws[kb];
 #pragma unroll
           for (int f = 0; f < MF; ++f)
-            acc[f] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[u][f], bf, acc[f], 0, 0,
-                                                                      0, sa[u][f], 0, sb[u]);
-        } else if constexpr (kRow) {
+            s4[f] = *reinterpret_cast<const float4 *>(&s_as[kb * R + f * 16 + 4 * (lane >> 4)]);
+        }
 #pragma unroll
-          for (int f = 0; f < MF; ++f)
-            acc[f] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[u][f], bf, acc[f], 0, 0,
-                                                                      0, 0, 0, 0);
-        } else {
-          const float wsc = pws[kb];
+        for (int sl = 0; sl < NS; ++sl) {
+          const v8i bf = frag_from(bw[buf][u][sl][0], bw[buf][u][sl][1]);
 #pragma unroll
           for (int f = 0; f < MF; ++f) {
-            const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                af[u][f], bf, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 0, 0, 0);
-            const float4 s4 =
-                *reinterpret_cast<const float4 *>(&s_as[kb * R + f * 16 + 4 * (lane >> 4)]);
-            acc[f][0] = fmaf(p[0], s4.x * wsc, acc[f][0]);
-            acc[f][1] = fmaf(p[1], s4.y * wsc, acc[f][1]);
-            acc[f][2] = fmaf(p[2], s4.z * wsc, acc[f][2]);
-            acc[f][3] = fmaf(p[3], s4.w * wsc, acc[f][3]);
+            if constexpr (MX) {
+              acc[sl][f] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                  af[buf][u][f], bf, acc[sl][f], 0, 0, 0, sa[buf][u][f], 0, sb[buf][u]);
+            } else if constexpr (kRow) {
+              acc[sl][f] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                  af[buf][u][f], bf, acc[sl][f], 0, 0, 0, 0, 0, 0);
+            } else {
+              const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                  af[buf][u][f], bf, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 0, 0, 0);
+              acc[sl][f][0] = fmaf(p[0], s4[f].x * wsc, acc[sl][f][0]);
+              acc[sl][f][1] = fmaf(p[1], s4[f].y * wsc, acc[sl][f][1]);
+              acc[sl][f][2] = fmaf(p[2], s4[f].z * wsc, acc[sl][f][2]);
+              acc[sl][f][3] = fmaf(p[3], s4[f].w * wsc, acc[sl][f][3]);
+            }
           }
         }
       }
     }
-    if (j0 + U < nmine) load(j0 + U);
+  };
+  if constexpr (NB == 2) {
+    for (int j0 = 0; j0 < nmine; j0 += 2 * U) {
+      load(std::integral_constant<int, 1>{}, j0 + U);
+      compute(std::integral_constant<int, 0>{}, j0);
+      load(std::integral_constant<int, 0>{}, j0 + 2 * U);
+      compute(std::integral_constant<int, 1>{}, j0 + U);
+    }
+  } else {
+    for (int j0 = 0; j0 < nmine; j0 += U) {
+      compute(std::integral_constant<int, 0>{}, j0);
+      load(std::integral_constant<int, 0>{}, j0 + U);
+    }
   }
   __syncthreads();  // every wave is done with s_as
 #pragma unroll
-  for (int f = 0; f < MF; ++f) s_part[(wave * MF + f) * 64 + lane] = acc[f];
+  for (int sl = 0; sl < NS; ++sl)
+#pragma unroll
+    for (int f = 0; f < MF; ++f) s_part[((wave * NS + sl) * MF + f) * 64 + lane] = acc[sl][f];
   __syncthreads();
-  // wave f (< MF) sums fragment f over the waves and stores it
-  if (wave < MF) {
-    v4f sum = s_part[wave * 64 + lane];
+  // wave q (< NS * MF) sums (slab q / MF, fragment q % MF) over the waves
+  if (wave < NS * MF) {
+    const int sl = wave / MF, f = wave % MF;
+    v4f sum = s_part[(sl * MF + f) * 64 + lane];
 #pragma unroll
     for (int w = 1; w < kDecWaves; ++w) {
-      const v4f v = s_part[(w * MF + wave) * 64 + lane];
+      const v4f v = s_part[((w * NS + sl) * MF + f) * 64 + lane];
       sum[0] += v[0]; sum[1] += v[1]; sum[2] += v[2]; sum[3] += v[3];
     }
+    const int64_t col = n0 + 16 * sl + r16;
     float cs = 1.0f;
-    if constexpr (kRow) cs = ws[n0 + min(r16, rows_b - 1)];
+    if constexpr (kRow) cs = ws[min<int64_t>(col, N - 1)];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int row = wave * 16 + 4 * (lane >> 4) + r;
+      const int row = f * 16 + 4 * (lane >> 4) + r;
       float v = sum[r];
       if constexpr (kRow) v = v * (xs[min(row, M - 1)] * cs);
-      if (row < M && r16 < rows_b) y[(int64_t)row * N + n0 + r16] = (uint16_t)bf16_rne(v);
+      if (row < M && col < N) y[(int64_t)row * N + col] = (uint16_t)bf16_rne(v);
     }
   }
 }
-
 template <int MF, typename S, bool kRow = false>
 static hipError_t launch_decode(const void *xq, const S *xs, int64_t xs_rs, int xs_ks,
                                 const void *wq, const S *ws, int64_t M, int64_t N, int64_t K,
                                 void *y, hipStream_t stream) {
   const int64_t KB = K / 128;
-  const size_t part = (size_t)kDecWaves * MF * 64 * 16;
+  // 16-column slabs per workgroup (one row fragment of x: MF = 1): 1, 2 or
+  // 4 (2 at most with E8M0 scales, for registers).  More slabs make each
+  // workgroup stream more weight bytes; with one workgroup per CU the count
+  // is picked for the fullest last round (ties: more slabs).
+  const int64_t slabs = (N + 15) / 16;
+  constexpr bool kMx = std::is_same<S, uint8_t>::value;
+  int NS = 1;
+  if (MF == 1) {
+    double best = 0.0;
+    for (int ns = 1; ns <= (kMx ? 2 : 4); ns *= 2) {
+      const int64_t wgs = (slabs + ns - 1) / ns;
+      const double fill = (double)wgs / (double)(((wgs + 255) / 256) * 256);
+      if (fill >= best - 1e-9) { best = fill; NS = ns; }
+    }
+  }
+  const size_t part = (size_t)kDecWaves * NS * MF * 64 * 16;
   const size_t lds = (std::is_same<S, uint8_t>::value || kRow)
                          ? part
                          : std::max((size_t)KB * MF * 16 * 4, part);
-  hipLaunchKernelGGL((decode_gemm_kernel<MF, S, kRow>), dim3((unsigned)((N + 15) / 16)),
-                     dim3(kDecThreads), lds, stream, static_cast<const uint8_t *>(xq), xs, xs_rs,
-                     xs_ks, static_cast<const uint8_t *>(wq), ws, (int)M, N, K,
-                     static_cast<uint16_t *>(y));
+  const dim3 grid((unsigned)((slabs + NS - 1) / NS));
+  const auto *a = static_cast<const uint8_t *>(xq);
+  const auto *b = static_cast<const uint8_t *>(wq);
+  auto *out = static_cast<uint16_t *>(y);
+  if (NS == 4)
+    hipLaunchKernelGGL((decode_gemm_kernel<MF, S, kRow, (MF == 1 && !kMx ? 4 : 1)>), grid,
+                       dim3(kDecThreads), lds, stream, a, xs, xs_rs, xs_ks, b, ws, (int)M, N, K,
+                       out);
+  else if (NS == 2)
+    hipLaunchKernelGGL((decode_gemm_kernel<MF, S, kRow, (MF == 1 ? 2 : 1)>), grid,
+                       dim3(kDecThreads), lds, stream, a, xs, xs_rs, xs_ks, b, ws, (int)M, N, K,
+                       out);
+  else
+    hipLaunchKernelGGL((decode_gemm_kernel<MF, S, kRow, 1>), grid, dim3(kDecThreads), lds,
+                       stream, a, xs, xs_rs, xs_ks, b, ws, (int)M, N, K, out);
   return hipGetLastError();
 }
 

@@ -92,6 +92,26 @@ def test_gemm_split_k_tiles_tolerance(M, N, K):
               og.term_magnitude(xq[rows], xs[rows], wq, ws), f"split-K {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 14380, 256), (7, 7176, 384), (16, 14380, 512),
+                                   (16, 14336, 1024), (3, 4100, 768)])
+def test_gemm_decode_multi_slab_exact(M, N, K):
+    """Decode shapes (M <= 16) for which the launcher packs four (N = 14380,
+    14336) or two (N = 7176) 16-column slabs per workgroup, with a partly
+    empty last workgroup and a ragged last slab, and one unpacked ragged
+    shape: integer operands, power-of-two scales, bit-exact against
+    bf16_RNE(exact)."""
+    rng = np.random.default_rng(M * 5 + N + K)
+    xi = rng.integers(-8, 9, (M, K)); wi = rng.integers(-8, 9, (N, K))
+    xq = oe.encode(xi.astype(np.float32)); wq = oe.encode(wi.astype(np.float32))
+    KB, NB = K // 128, -(-N // 128)
+    xs = np.exp2(rng.integers(-1, 2, (M, KB))).astype(np.float32)
+    ws = np.exp2(rng.integers(0, 2, (NB, KB))).astype(np.float32)
+    y = gpu_gemm(xq, xs, wq, ws)
+    want = og.bf16_rne_bits(og.block_gemm(xq, xs, wq, ws))
+    bad = np.argwhere(y != want)
+    assert bad.size == 0, f"{len(bad)} outputs differ, first {bad[:3].tolist()}"
+
+
 @pytest.mark.parametrize("M,N,K", [(8, 256, 1536), (33, 200, 1280)])
 def test_gemm_scale_indexing(M, N, K):
     """All codes 1.0; x_s[m,kb] = 2^((kb+m) % KB), w_s[nb,kb] = 2^(KB*((kb+nb)%2)):

@@ -123,7 +123,8 @@ def gpu_rowwise_gemm(xq, xs, wq, ws):
 
 @pytest.mark.parametrize("M,N,K", [(16, 16, 128), (1, 300, 512), (64, 192, 1024),
                                    (130, 576, 4096), (2048, 4096, 512), (257, 1000, 640),
-                                   (300, 2000, 2048)])
+                                   (300, 2000, 2048), (1, 14380, 256), (7, 7176, 384),
+                                   (16, 14380, 512)])
 def test_rowwise_gemm_exact_integer_operands(M, N, K):
     rng = np.random.default_rng(M + N + K)
     xq = oe.encode(rng.integers(-8, 9, (M, K)).astype(np.float32))
