@@ -263,6 +263,28 @@ def run_leg(torch, stream, launch, n_proj, steps, warmup):
     return wall, quant, gemm
 
 
+ROTATE_BYTES = 600 * 2 ** 20   # > twice the 256 MB MALL
+
+
+def _weight_copies(wq, *extra):
+    """Enough copies of a quantized weight (codes and scales) that the bytes
+    touched between two uses of one copy exceed twice the MALL: the decode
+    timings then stream the weights from HBM, not from the cache."""
+    n = max(2, -(-ROTATE_BYTES // wq.numel()))
+    return [(wq.clone(), *[e.clone() for e in extra]) for _ in range(n)]
+
+
+def _rotating(copies, fn):
+    """fn(*copy) over the copies in turn, one per call."""
+    k = [0]
+
+    def call():
+        c = copies[k[0] % len(copies)]
+        k[0] += 1
+        fn(*c)
+    return call
+
+
 def _time(torch, stream, fn, iters=20, warm=3):
     for _ in range(warm):
         fn()
@@ -290,33 +312,37 @@ def other_rows(torch, fb, dev, stream):
     t = _time(torch, stream, lambda: fb.fp8_weight_block_quant(w, q, s))
     rows["weight_quant_18432x7168"] = {"us": round(t * 1e6, 2), "GB/s": round(18432 * 7168 * 3 / t / 1e9, 1)}
     del w, q, s
-    # decode GEMMs (HBM-bound): M = 16
+    # decode GEMMs (HBM-bound): M = 16, weights rotated through HBM
     for name, N, K in PREFILL_SHAPES:
         x = torch.randn((16, K), generator=g, device=dev).to(torch.bfloat16)
         wq, wsc = fb.weight_block_quant((torch.randn((N, K), generator=g, device=dev) * 0.02).to(torch.bfloat16))
         xq, xsc = fb.act_quant_group(x)
         y = torch.empty((16, N), dtype=torch.bfloat16, device=dev)
-        t = _time(torch, stream, lambda: fb.fp8_block_gemm(xq, xsc, wq, wsc, y))
+        copies = _weight_copies(wq, wsc)
+        t = _time(torch, stream, _rotating(copies, lambda w, s: fb.fp8_block_gemm(xq, xsc, w, s, y)))
+        del copies
         byts = N * K + 16 * K + 2 * 16 * N
         rows[f"decode_M16_{name}"] = {"us": round(t * 1e6, 2), "GB/s": round(byts / t / 1e9, 1)}
     rows.update(ue8m0_rows(torch, fb, dev, stream, g))
     rows.update(static_rows(torch, fb, dev, stream))
     rows.update(rowwise_rows(torch, fb, dev, stream))
     # the whole decode linear layer from bf16 x (M = 16): one fused kernel
-    # against the two launches (act quant + GEMM)
+    # against the two launches (act quant + GEMM); weights rotated
     for name, N, K in PREFILL_SHAPES:
         x = torch.randn((16, K), generator=g, device=dev).to(torch.bfloat16)
         wq, wsc = fb.weight_block_quant((torch.randn((N, K), generator=g, device=dev) * 0.02).to(torch.bfloat16))
         y = torch.empty((16, N), dtype=torch.bfloat16, device=dev)
         xq = torch.empty((16, K), dtype=torch.uint8, device=dev)
         xsc = torch.empty((16, K // 128), dtype=torch.float32, device=dev)
+        copies = _weight_copies(wq, wsc)
 
-        def two():
+        def two(w, s):
             fb.fp8_act_quant_group(x, xq, xsc)
-            fb.fp8_block_gemm(xq, xsc, wq, wsc, y)
-        t1 = _time(torch, stream, lambda: fb.fp8_linear(x, wq, wsc, y))
-        t2 = _time(torch, stream, two)
-        t3 = _time(torch, stream, lambda: fb.fp8_linear(x, wq, wsc, y, xq, xsc))
+            fb.fp8_block_gemm(xq, xsc, w, s, y)
+        t1 = _time(torch, stream, _rotating(copies, lambda w, s: fb.fp8_linear(x, w, s, y)))
+        t2 = _time(torch, stream, _rotating(copies, two))
+        t3 = _time(torch, stream, _rotating(copies, lambda w, s: fb.fp8_linear(x, w, s, y, xq, xsc)))
+        del copies
         rows[f"decode_linear_M16_{name}"] = {"fused_us": round(t1 * 1e6, 2),
                                              "two_launch_us": round(t2 * 1e6, 2),
                                              "fp8_linear_with_workspace_us": round(t3 * 1e6, 2)}
@@ -504,7 +530,9 @@ def ue8m0_rows(torch, fb, dev, stream, g):
             (torch.randn((N, K), generator=g, device=dev) * 0.02).to(torch.bfloat16), "ue8m0")
         xq, xe = fb.act_quant_group(x, "ue8m0")
         y = torch.empty((16, N), dtype=torch.bfloat16, device=dev)
-        t = _time(torch, stream, lambda: fb.fp8_block_gemm_ue8m0(xq, xe, wq1, we1, y))
+        copies = _weight_copies(wq1, we1)
+        t = _time(torch, stream, _rotating(copies, lambda w, e: fb.fp8_block_gemm_ue8m0(xq, xe, w, e, y)))
+        del copies
         byts = N * K + 16 * K + 2 * 16 * N
         rows[f"ue8m0_decode_M16_{name}"] = {"us": round(t * 1e6, 2), "GB/s": round(byts / t / 1e9, 1)}
     return rows

@@ -286,7 +286,7 @@ FUSED_MAX_M = 64
 
 def fp8_linear(x, w_q, w_scale, y, x_q_ws=None, x_scale_ws=None):
     """One C call for the linear layer: fused in one kernel for M <= 64 when
-    N <= 6144 or no workspaces are given, else quantization into the
+    N * K <= 2^25 or no workspaces are given, else quantization into the
     workspaces (required for M > 64) and the GEMM."""
     _need(x, "x", (torch.bfloat16,), 2); _need(w_q, "w_q", _CODES, 2)
     _need(w_scale, "w_scale", _F32, 2); _need(y, "y", (torch.bfloat16,), 2)

@@ -169,15 +169,17 @@ fp8blk_status fp8_linear(const void *x_bf16, int64_t M, int64_t N, int64_t K, co
                          const float *w_scale, void *x_q_ws, float *x_scale_ws, void *y_bf16,
                          void *stream) {
   // The fused decode kernel re-quantizes x in every workgroup (N/16 of
-  // them); past ~1.5 workgroups per CU (N > 6144) that redundant work costs
-  // more than the quantizer's own launch, so with workspaces at hand the two
-  // kernels run instead (measured at M = 16: N = 4096 fused 9.4 us against
-  // 19.8; N = 14336 fused 30.9 us against 23.6).
+  // them, each reading all of x in bf16 from L2); for weights past ~32M
+  // elements that redundant work costs more than the quantizer's own
+  // launch, so with workspaces at hand the two kernels run instead
+  // (measured at M = 16, weights streamed from HBM: 4096x4096 fused 10.2 us
+  // against 18.1; 14336x4096 33.7 against 18.3; 4096x14336 27.5 against
+  // 22.2).
   constexpr int64_t kFusedMaxM = 64;
-  constexpr int64_t kFusedMaxN = 6144;
+  constexpr int64_t kFusedMaxWeight = int64_t(1) << 25;  // N * K elements
   const bool work = M > 0 && N > 0;
   const bool have_ws = x_q_ws != nullptr && x_scale_ws != nullptr;
-  const bool fused = M <= kFusedMaxM && (N <= kFusedMaxN || !have_ws);
+  const bool fused = M <= kFusedMaxM && (N * K <= kFusedMaxWeight || !have_ws);
   if (work && (!x_bf16 || !w_q || !w_scale || !y_bf16 || (!fused && (!x_q_ws || !x_scale_ws))))
     return FP8BLK_ERR_NULL;
   if (bad_rows(M) || bad_rows(N) || bad_k(K) || too_big(M, K) || too_big(N, K) || too_big(M, N))

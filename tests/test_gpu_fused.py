@@ -101,13 +101,12 @@ def test_linear_workspace_path(M):
         fb.fp8_linear(xd, wqd, wsd, y)
 
 
-@pytest.mark.parametrize("N", [4096, 14336])
-def test_linear_picks_a_path_and_agrees(N):
-    """fb.linear passes workspaces; the library fuses for N <= 6144 and runs
-    two kernels above: both agree with the two-launch path bit for bit at
-    M = 16."""
-    K = 4096
-    x = synth.llama_x(0, 16, config=2)
+@pytest.mark.parametrize("N,K", [(4096, 4096), (14336, 4096), (4096, 14336)])
+def test_linear_picks_a_path_and_agrees(N, K):
+    """fb.linear passes workspaces; the library fuses for N * K <= 2^25 and
+    runs two kernels above: both agree with the two-launch path bit for bit
+    at M = 16."""
+    x = synth.llama_activations(N + K, 16, K, 7)
     w = synth.normal_bf16(N, (N, K), 0.02)
     wq, ws = oq.weight_block_quant(w)
     xd, wqd, wsd = to_dev_bf16(x), to_dev(wq), to_dev(ws)
