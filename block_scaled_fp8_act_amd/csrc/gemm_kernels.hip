@@ -116,6 +116,37 @@ __device__ __forceinline__ int swz(int row, int chunk) {
   return row * 128 + ((chunk ^ swz_f(row)) << 4);
 }
 
+// Epilogue for a full tile with 16-byte aligned output rows: each wave
+// writes its (FM*16) x 64 bf16 sub-tile row-major into its own 2*FM KB of
+// LDS (the 32-byte column chunks of rows 4q..4q+3 of a fragment XOR-swizzled
+// by q, so the four row groups of a write land in different banks), then
+// stores it 16 bytes per lane: 2*FM store instructions of 1 KB per wave
+// instead of 16*FM of 128 bytes.  `stage` must be LDS that no other wave
+// touches meanwhile.
+template <int FM>
+__device__ __forceinline__ void store_tile_rows16(const v4f (&acc)[FM][4], uint16_t *stage,
+                                                  uint16_t *__restrict__ Yw, int64_t ldy,
+                                                  int lane) {
+  const int r16 = lane & 15, q = lane >> 4;
+#pragma unroll
+  for (int mi = 0; mi < FM; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = mi * 16 + 4 * q + r;
+        stage[row * 64 + ((ni ^ q) << 4) + r16] = (uint16_t)bf16_rne(acc[mi][ni][r]);
+      }
+#pragma unroll
+  for (int j = 0; j < FM * 2; ++j) {
+    const int e = j * 512 + lane * 8;  // logical element: row e / 64, columns e % 64 .. +8
+    const int row = e >> 6, col = e & 63;
+    const int phys = row * 64 + ((((col >> 4) ^ ((row >> 2) & 3))) << 4) + (col & 15);
+    const uint4 v = *reinterpret_cast<const uint4 *>(stage + phys);
+    *reinterpret_cast<uint4 *>(Yw + (int64_t)row * ldy + col) = v;
+  }
+}
+
 // One output tile.  A: x_q at the tile's first row (row stride K bytes),
 // rows_a valid rows; As: x_scale at that row, element (r, kb) at
 // As[r*xs_rs + kb*xs_ks] -- (KB, 1) for per-token-group scales, (0, 0) for
@@ -331,6 +362,18 @@ __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ A,
   }
 
   // Epilogue: lane holds rows 4*(lane/16)+r of each 16x16 fragment, column lane%16.
+  // Full tiles with 16-byte aligned rows go through LDS (free since the last
+  // barrier; past the split-K reduction slots), others element by element.
+  static_assert((size_t)(KS - 1) * T::TM * T::TN * 4 + (size_t)T::TM * T::TN * 2 <=
+                    KS * sizeof(typename T::Smem),
+                "epilogue staging does not fit in the stages");
+  if (rows_a == T::TM && rows_b == T::TN && (ldy & 7) == 0) {
+    uint16_t *stage = reinterpret_cast<uint16_t *>(reinterpret_cast<uint8_t *>(&sm0) +
+                                                   (size_t)(KS - 1) * T::TM * T::TN * 4) +
+                      wave * (FM * 16 * 64);
+    store_tile_rows16<FM>(acc, stage, Y + (int64_t)(wm * FM * 16) * ldy + wn * 64, ldy, lane);
+    return;
+  }
 #pragma unroll
   for (int mi = 0; mi < FM; ++mi)
 #pragma unroll
@@ -570,6 +613,30 @@ __device__ __forceinline__ void gemm_tile_mx(const uint8_t *__restrict__ A,
   if constexpr (!kScaled) {
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) cs[ni] = wr[min(wn * 64 + ni * 16 + r16, rows_b - 1)];
+  }
+  static_assert((size_t)(KS - 1) * T::TM * T::TN * 4 + (size_t)T::TM * T::TN * 2 <=
+                    KS * sizeof(typename T::SmemMx),
+                "epilogue staging does not fit in the stages");
+  if (rows_a == T::TM && rows_b == T::TN && (ldy & 7) == 0) {
+    // as in gemm_tile; the barrier ends the last step's (unused) reads of
+    // the other stage (with KS > 1 the reduction's barriers already did, and
+    // groups 1.. have left)
+    if constexpr (!kScaled) {
+#pragma unroll
+      for (int mi = 0; mi < FM; ++mi)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float rs = xr[wm * FM * 16 + mi * 16 + 4 * (lane >> 4) + r];
+#pragma unroll
+          for (int ni = 0; ni < 4; ++ni) acc[mi][ni][r] = acc[mi][ni][r] * (rs * cs[ni]);
+        }
+    }
+    if constexpr (KS == 1) __syncthreads();
+    uint16_t *stage = reinterpret_cast<uint16_t *>(reinterpret_cast<uint8_t *>(&sm0) +
+                                                   (size_t)(KS - 1) * T::TM * T::TN * 4) +
+                      wave * (FM * 16 * 64);
+    store_tile_rows16<FM>(acc, stage, Y + (int64_t)(wm * FM * 16) * ldy + wn * 64, ldy, lane);
+    return;
   }
 #pragma unroll
   for (int mi = 0; mi < FM; ++mi) {
