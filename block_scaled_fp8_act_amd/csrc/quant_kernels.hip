@@ -32,8 +32,10 @@ namespace fp8blk {
 // groups = 4 KB of bf16: load i (0..3) of lane l reads 16 bytes at
 // tile*4096 + i*1024 + l*16, so every load instruction is one contiguous
 // 1 KB run and each group is one DPP row of 16 lanes (8 values per lane).
-// A wave handles two tiles per iteration (eight 16-byte loads in flight per
-// lane).
+// A wave handles one tile per iteration (four 16-byte loads in flight per
+// lane) and the grid holds up to 32 workgroups per CU: more, shorter-lived
+// waves measured 2-11 % faster than two tiles per wave and 8 workgroups
+// per CU (4096x4096: 12.0 -> 10.7 us from HBM).
 //
 // Fast path: when no group of the wave's tiles has 0 < amax < 2^-50 (always, in
 // practice), s comes from div448, the power-of-two rescale is skipped
@@ -44,7 +46,7 @@ namespace fp8blk {
 constexpr int kActThreads = 256;
 constexpr int kActWaves = kActThreads / 64;
 constexpr int kGroupsPerTile = 16;
-constexpr int kTilesPerIter = 2;
+constexpr int kTilesPerIter = 1;
 constexpr float kTinyAmax = 0x1p-50f;
 
 
@@ -454,7 +456,7 @@ static unsigned act_quant_blocks(int64_t n_groups) {
   const int64_t n_tiles = (n_groups + kGroupsPerTile - 1) / kGroupsPerTile;
   const int64_t per_block = (int64_t)kActWaves * kTilesPerIter;
   int64_t blocks = (n_tiles + per_block - 1) / per_block;
-  const int64_t cap = 256 * 8;  // grid-stride beyond 8 workgroups per CU
+  const int64_t cap = 256 * 32;  // grid-stride beyond 32 workgroups per CU
   return (unsigned)(blocks > cap ? cap : blocks);
 }
 
