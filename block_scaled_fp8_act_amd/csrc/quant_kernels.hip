@@ -473,7 +473,7 @@ hipError_t launch_swiglu_act_quant(const void *gu, int64_t M, int64_t I, void *q
   const int64_t n_groups = M * (I / kBlock);  // < 2^31 (checked by the caller)
   const int64_t n_tiles = (n_groups + kSwigluGpt - 1) / kSwigluGpt;
   int64_t blocks = (n_tiles + kActWaves - 1) / kActWaves;
-  if (blocks > 256 * 8) blocks = 256 * 8;
+  if (blocks > 256 * 32) blocks = 256 * 32;  // up to 32 workgroups per CU
   hipLaunchKernelGGL(swiglu_quant_kernel, dim3((unsigned)blocks), dim3(kActThreads), 0, stream,
                      static_cast<const uint16_t *>(gu), (uint32_t)(I / kBlock),
                      static_cast<uint2 *>(q), s, (uint32_t)n_groups);
@@ -493,7 +493,7 @@ hipError_t launch_act_quant_static(const void *x, int64_t M, int64_t K, const fl
                                    hipStream_t stream) {
   const int64_t n16 = M * K / 16;  // K % 128 == 0
   int64_t blocks = (n16 + kStaticThreads - 1) / kStaticThreads;
-  if (blocks > 256 * 8) blocks = 256 * 8;
+  if (blocks > 256 * 32) blocks = 256 * 32;  // up to 32 workgroups per CU
   hipLaunchKernelGGL(act_quant_static_kernel, dim3((unsigned)blocks), dim3(kStaticThreads), 0,
                      stream, static_cast<const uint4 *>(x), static_cast<uint4 *>(q), s, n16);
   return hipGetLastError();
