@@ -12,8 +12,10 @@
 // block, fp32 result) and the scale pair is applied with one fp32 FMA per
 // output per K block ("promotion" into the fp32 accumulator).
 //
-// Three configurations: 256x256 and 128x128 LDS-staged tiles for M > 64,
-// and a weight-streaming split-K kernel for M <= 64 (decode).
+// Configurations: 256x256 LDS-staged tiles for M > 64 when they fill the
+// chip; 128x128 tiles otherwise (with K split over two wave groups inside
+// the workgroup when there is at most one workgroup per CU); and a
+// weight-streaming kernel with K split over its waves for M <= 64 (decode).
 //
 // With power-of-two scales stored as E8M0 bytes (the "UE8M0 scale format"
 // section of the same page) the scale pair is applied by the matrix core
