@@ -185,11 +185,15 @@ __global__ __launch_bounds__(kStaticThreads) void act_quant_static_kernel(
 
 // ---------------------------------------------------------------------------
 // Row-wise quantizer (one scale per row: weights' output rows, or tokens):
-// one workgroup per row, an amax pass and a quantize pass over the row (the
-// second pass re-reads the row from L2 for the usual K), with the element map
-// of make_qparams / quotient.
+// one workgroup per row, an amax pass and a quantize pass over the row, with
+// the element map of make_qparams / quotient.  Rows of up to 32768 values
+// stay in registers between the passes; longer rows are re-read.
 constexpr int kRowThreads = 256;
 
+// C > 0: rows of at most C * 8 * kRowThreads values, held in registers
+// between the amax and the quantization (one pass over HBM); C = 0: any
+// length, the row re-read (from L2 for the usual K) for the second pass.
+template <int C>
 __global__ __launch_bounds__(kRowThreads) void rowwise_quant_kernel(
     const uint16_t *__restrict__ x, int64_t K, uint8_t *__restrict__ q, float *__restrict__ scale) {
   __shared__ float wave_max[kRowThreads / 64];
@@ -199,10 +203,25 @@ __global__ __launch_bounds__(kRowThreads) void rowwise_quant_kernel(
   const uint4 *xr = reinterpret_cast<const uint4 *>(x + row * K);
   const int64_t n8 = K / 8;
   float m = 0.0f;
-  for (int64_t i = t; i < n8; i += kRowThreads) {
-    float f[8];
-    unpack8(xr[i], f);
-    m = fmaxf(m, absmax8(f));
+  uint4 v[C > 0 ? C : 1];
+  if constexpr (C > 0) {
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const int64_t i = t + (int64_t)c * kRowThreads;
+      v[c] = i < n8 ? xr[i] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      float f[8];
+      unpack8(v[c], f);
+      m = fmaxf(m, absmax8(f));
+    }
+  } else {
+    for (int64_t i = t; i < n8; i += kRowThreads) {
+      float f[8];
+      unpack8(xr[i], f);
+      m = fmaxf(m, absmax8(f));
+    }
   }
   m = row16_max(m);
   m = fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 0)),
@@ -214,16 +233,25 @@ __global__ __launch_bounds__(kRowThreads) void rowwise_quant_kernel(
   const float amax = fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3]));
   const QParams p = make_qparams(amax);
   uint2 *qr = reinterpret_cast<uint2 *>(q + row * K);
-  for (int64_t i = t; i < n8; i += kRowThreads) {
+  auto quant8 = [&](const uint4 &w) {
     float f[8];
-    unpack8(xr[i], f);
+    unpack8(w, f);
     float tq[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) tq[j] = quotient(ldexpf(f[j], p.k), p.sp, p.y);
     uint2 out;
     out.x = pack4_e4m3(tq[0], tq[1], tq[2], tq[3]);
     out.y = pack4_e4m3(tq[4], tq[5], tq[6], tq[7]);
-    qr[i] = out;
+    return out;
+  };
+  if constexpr (C > 0) {
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const int64_t i = t + (int64_t)c * kRowThreads;
+      if (i < n8) qr[i] = quant8(v[c]);
+    }
+  } else {
+    for (int64_t i = t; i < n8; i += kRowThreads) qr[i] = quant8(xr[i]);
   }
   if (t == 0) scale[row] = p.s;
 }
@@ -501,8 +529,24 @@ hipError_t launch_act_quant_static(const void *x, int64_t M, int64_t K, const fl
 
 hipError_t launch_rowwise_quant(const void *x, int64_t R, int64_t K, void *q, float *s,
                                 hipStream_t stream) {
-  hipLaunchKernelGGL(rowwise_quant_kernel, dim3((unsigned)R), dim3(kRowThreads), 0, stream,
-                     static_cast<const uint16_t *>(x), K, static_cast<uint8_t *>(q), s);
+  const int64_t chunks = (K / 8 + kRowThreads - 1) / kRowThreads;  // 16-byte loads per thread
+  const auto *xp = static_cast<const uint16_t *>(x);
+  auto *qp = static_cast<uint8_t *>(q);
+  if (chunks <= 2)
+    hipLaunchKernelGGL(rowwise_quant_kernel<2>, dim3((unsigned)R), dim3(kRowThreads), 0, stream,
+                       xp, K, qp, s);
+  else if (chunks <= 4)
+    hipLaunchKernelGGL(rowwise_quant_kernel<4>, dim3((unsigned)R), dim3(kRowThreads), 0, stream,
+                       xp, K, qp, s);
+  else if (chunks <= 8)
+    hipLaunchKernelGGL(rowwise_quant_kernel<8>, dim3((unsigned)R), dim3(kRowThreads), 0, stream,
+                       xp, K, qp, s);
+  else if (chunks <= 16)
+    hipLaunchKernelGGL(rowwise_quant_kernel<16>, dim3((unsigned)R), dim3(kRowThreads), 0, stream,
+                       xp, K, qp, s);
+  else
+    hipLaunchKernelGGL(rowwise_quant_kernel<0>, dim3((unsigned)R), dim3(kRowThreads), 0, stream,
+                       xp, K, qp, s);
   return hipGetLastError();
 }
 

@@ -93,7 +93,8 @@ def assert_rowwise_equal(got, want, what):
 
 
 @pytest.mark.parametrize("R,K", [(1, 128), (3, 384), (17, 4096), (64, 14336), (300, 7168),
-                                 (4096, 4096), (5, 18432), (1000, 256)])
+                                 (4096, 4096), (5, 18432), (1000, 256), (2, 32768),
+                                 (3, 33024), (2, 40960)])
 def test_rowwise_quant(R, K):
     x = synth.dsv3_activations(R * 3 + K, R, K, R + 5)
     say("rowwise quant", R, K)
