@@ -58,7 +58,7 @@ from .ue8m0 import (act_quant_group_ue8m0, block_gemm_ue8m0, e8m0_decode, e8m0_e
                     grouped_block_gemm_ue8m0, weight_block_quant_ue8m0)
 from .static import act_quant_static, block_gemm_static
 from .layouts import batched_block_gemm, rowwise_gemm, rowwise_quant
-from .swiglu import swiglu_act_quant, swiglu_bf16
+from .swiglu import swiglu_act_quant, swiglu_act_quant_ue8m0, swiglu_bf16
 
 __all__ = [
     "E4M3_MAX", "decode", "encode", "fl32_div",
@@ -70,5 +70,5 @@ __all__ = [
     "grouped_block_gemm_ue8m0", "weight_block_quant_ue8m0",
     "act_quant_static", "block_gemm_static",
     "batched_block_gemm", "rowwise_gemm", "rowwise_quant",
-    "swiglu_act_quant", "swiglu_bf16",
+    "swiglu_act_quant", "swiglu_act_quant_ue8m0", "swiglu_bf16",
 ]

@@ -23,6 +23,9 @@ readings):
   :mod:`oracle.quant` applied to h [M, I] (I % 128 == 0).
 * h must be finite (|SiLU(g) * u| below bf16's overflow threshold);
   anything else is outside the contract, as non-finite inputs are.
+* With power-of-two scales (the "UE8M0 scale format" section of the same
+  page) the quantizer is :func:`oracle.ue8m0.act_quant_group_ue8m0` on the
+  same h.
 """
 from __future__ import annotations
 
@@ -30,6 +33,7 @@ import numpy as np
 
 from .gemm import bf16_rne_bits
 from .quant import act_quant_group
+from .ue8m0 import act_quant_group_ue8m0
 
 
 def _bf16_to_f64(bits) -> np.ndarray:
@@ -61,3 +65,8 @@ def swiglu_act_quant(gu_bits):
     """gate/up bf16 bits [M, 2I] (I % 128 == 0) -> (codes uint8 [M, I],
     scales fp32 [M, I/128]) of h = bf16(SiLU(g) * u)."""
     return act_quant_group(swiglu_bf16(gu_bits))
+
+
+def swiglu_act_quant_ue8m0(gu_bits):
+    """As :func:`swiglu_act_quant` with E8M0 scale bytes [M, I/128]."""
+    return act_quant_group_ue8m0(swiglu_bf16(gu_bits))

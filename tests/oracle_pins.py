@@ -915,6 +915,38 @@ def pin_swiglu_quant(seed=101):
                 assert int(q[m, 128 * grp + k]) == want, (m, grp, k)
 
 
+
+def pin_swiglu_quant_ue8m0(seed=103):
+    """Power-of-two scales on the same h: every byte is 127 + e with e the
+    smallest integer >= -127 such that amax(h) <= 448 * 2^e (exact
+    rationals), and every code the nearest E4M3 value (exhaustive search) to
+    the exact quotient h / 2^e."""
+    rng = np.random.default_rng(seed)
+    M, I = 2, 256
+    gu = np.concatenate([
+        (((rng.standard_normal((M, I)) * 3).astype(np.float32)).view(np.uint32) >> 16).astype(np.uint16),
+        (((rng.standard_normal((M, I))).astype(np.float32)).view(np.uint32) >> 16).astype(np.uint16)], axis=1)
+    q, b = osw.swiglu_act_quant_ue8m0(gu)
+    assert q.shape == (M, I) and b.shape == (M, I // 128) and b.dtype == np.uint8
+    for m in range(M):
+        hb = []
+        for j in range(I):
+            g = bf16_value(int(gu[m, j])); u = bf16_value(int(gu[m, I + j]))
+            zs = int(math.copysign(1, g) * math.copysign(1, u))
+            hb.append(bf16_rne_exact(swiglu_exact(g, u), zs)[0])
+        for grp in range(I // 128):
+            vals = [Fraction(bf16_value(x)) for x in hb[128 * grp: 128 * grp + 128]]
+            amax = max(abs(v) for v in vals)
+            e = -127
+            while amax > 448 * Fraction(2) ** e:
+                e += 1
+            assert int(b[m, grp]) == e + 127, (m, grp)
+            for k in range(0, 128, 7):
+                t = vals[k] / Fraction(2) ** e
+                want = brute_force_encode(float(t)) if t != 0 else (0x80 if hb[128 * grp + k] >> 15 else 0)
+                assert int(q[m, 128 * grp + k]) == want, (m, grp, k)
+
+
 ALL_PINS = [
     pin_format_points, pin_hand_encodings, pin_decode_matches_enumeration,
     pin_encode_roundtrip_and_monotone, pin_encode_brute_force, pin_fl32_div,
@@ -926,5 +958,5 @@ ALL_PINS = [
     pin_ue8m0_invariants, pin_ue8m0_weight_blocks, pin_ue8m0_gemm,
     pin_static_hand_cases, pin_static_brute_force, pin_static_invariants, pin_static_gemm,
     pin_batched, pin_rowwise_quant, pin_rowwise_gemm,
-    pin_swiglu_hand_cases, pin_swiglu_brute_force, pin_swiglu_quant,
+    pin_swiglu_hand_cases, pin_swiglu_brute_force, pin_swiglu_quant, pin_swiglu_quant_ue8m0,
 ]
