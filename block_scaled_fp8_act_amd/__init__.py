@@ -43,7 +43,7 @@ tensors' dtype:
     rowwise_quant(x) -> (q uint8 [R,K], scale fp32 [R])
     rowwise_gemm(x_q, x_scale, w_q, w_scale) -> y bf16 [M,N]
     linear_rowwise(x, w_q, w_scale) -> y bf16 [M,N]
-    swiglu_act_quant(gate_up) -> (x_q uint8 [M,I], x_scale fp32 [M, I/128])
+    swiglu_act_quant(gate_up, scale_fmt) -> (x_q uint8 [M,I], x_scale [M, I/128])
 """
 from __future__ import annotations
 
@@ -59,7 +59,8 @@ __all__ = [
     "fp8_block_gemm_ue8m0", "fp8_grouped_block_gemm_ue8m0", "fp8_act_quant_static",
     "fp8_block_gemm_static", "act_quant_static", "block_gemm_static", "linear_static",
     "fp8_linear", "fp8_batched_block_gemm", "batched_block_gemm", "fp8_rowwise_quant", "fp8_rowwise_gemm",
-    "rowwise_quant", "rowwise_gemm", "linear_rowwise", "fp8_swiglu_act_quant", "swiglu_act_quant",
+    "rowwise_quant", "rowwise_gemm", "linear_rowwise", "fp8_swiglu_act_quant",
+    "fp8_swiglu_act_quant_ue8m0", "swiglu_act_quant",
     "weight_block_quant",
     "act_quant_group", "block_gemm", "grouped_block_gemm", "linear", "SCALE_FMTS",
 ]
@@ -106,6 +107,7 @@ def load_library() -> ctypes.CDLL:
         "fp8_batched_block_gemm": [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp, vp],
         "fp8_rowwise_quant": [vp, i64, i64, vp, vp, vp],
         "fp8_swiglu_act_quant": [vp, i64, i64, vp, vp, vp],
+        "fp8_swiglu_act_quant_ue8m0": [vp, i64, i64, vp, vp, vp],
         "fp8_rowwise_gemm": [vp, vp, vp, vp, i64, i64, i64, vp, vp],
         "fp8_act_quant_static": [vp, i64, i64, vp, vp, vp],
         "fp8_block_gemm_static": [vp, vp, vp, vp, i64, i64, i64, vp, vp],
@@ -337,21 +339,30 @@ def fp8_rowwise_quant(x, q, scale):
            "fp8_rowwise_quant")
 
 
-def fp8_swiglu_act_quant(gate_up, x_q, x_scale):
-    """gate_up bf16 [M, 2I] (gate in columns [0, I), up in [I, 2I)) ->
-    codes of h = bf16(SiLU(gate) * up) in x_q [M, I] and fp32 group scales
-    in x_scale [M, I/128]."""
+def _swiglu(cname, sdt, gate_up, x_q, x_scale):
     _need(gate_up, "gate_up", (torch.bfloat16,), 2)
     M, two_i = gate_up.shape
     if two_i % 2:
         raise ValueError("gate_up must hold 2I columns")
     I = two_i // 2
-    _need(x_q, "x_q", _CODES); _need(x_scale, "x_scale", _F32)
+    _need(x_q, "x_q", _CODES); _need(x_scale, "x_scale", sdt)
     _shape_eq(x_q, (M, I), "x_q")
     if I % BLOCK == 0:
         _shape_eq(x_scale, (M, I // BLOCK), "x_scale")
-    _check(load_library().fp8_swiglu_act_quant(_ptr(gate_up), M, I, _ptr(x_q), _ptr(x_scale),
-                                               _stream()), "fp8_swiglu_act_quant")
+    _check(getattr(load_library(), cname)(_ptr(gate_up), M, I, _ptr(x_q), _ptr(x_scale),
+                                          _stream()), cname)
+
+
+def fp8_swiglu_act_quant(gate_up, x_q, x_scale):
+    """gate_up bf16 [M, 2I] (gate in columns [0, I), up in [I, 2I)) ->
+    codes of h = bf16(SiLU(gate) * up) in x_q [M, I] and fp32 group scales
+    in x_scale [M, I/128]."""
+    _swiglu("fp8_swiglu_act_quant", _F32, gate_up, x_q, x_scale)
+
+
+def fp8_swiglu_act_quant_ue8m0(gate_up, x_q, x_scale):
+    """As fp8_swiglu_act_quant with E8M0 scale bytes (uint8 or float8_e8m0fnu)."""
+    _swiglu("fp8_swiglu_act_quant_ue8m0", _E8M0, gate_up, x_q, x_scale)
 
 
 def fp8_rowwise_gemm(x_q, x_scale, w_q, w_scale, y):
@@ -476,11 +487,11 @@ def rowwise_quant(x):
     return q, s
 
 
-def swiglu_act_quant(gate_up):
+def swiglu_act_quant(gate_up, scale_fmt="float"):
     M, I = gate_up.shape[0], gate_up.shape[1] // 2
     q = torch.empty((M, I), dtype=torch.uint8, device=gate_up.device)
-    s = torch.empty((M, I // BLOCK), dtype=torch.float32, device=gate_up.device)
-    fp8_swiglu_act_quant(gate_up, q, s)
+    s = torch.empty((M, I // BLOCK), dtype=_scale_dtype(scale_fmt), device=gate_up.device)
+    (fp8_swiglu_act_quant if scale_fmt == "float" else fp8_swiglu_act_quant_ue8m0)(gate_up, q, s)
     return q, s
 
 

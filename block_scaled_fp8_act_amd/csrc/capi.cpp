@@ -92,6 +92,16 @@ fp8blk_status check_grouped(const void *x_q, const void *x_scale, const void *w_
   return check_device();
 }
 
+fp8blk_status check_swiglu(const void *gate_up_bf16, int64_t M, int64_t I, const void *x_q,
+                           const void *x_scale, uintptr_t scale_align) {
+  if (M > 0 && (!gate_up_bf16 || !x_q || !x_scale)) return FP8BLK_ERR_NULL;
+  if (bad_rows(M) || bad_k(I) || too_big(M, 2 * I) || M * (I / FP8BLK_BLOCK) > kMaxRows)
+    return FP8BLK_ERR_SHAPE;
+  if (M > 0 && (misaligned(gate_up_bf16) || misaligned(x_q) || misaligned(x_scale, scale_align)))
+    return FP8BLK_ERR_ALIGN;
+  return check_device();
+}
+
 }  // namespace
 
 extern "C" {
@@ -241,15 +251,18 @@ fp8blk_status fp8_rowwise_gemm(const void *x_q, const float *x_scale, const void
 
 fp8blk_status fp8_swiglu_act_quant(const void *gate_up_bf16, int64_t M, int64_t I, void *x_q,
                                    float *x_scale, void *stream) {
-  if (M > 0 && (!gate_up_bf16 || !x_q || !x_scale)) return FP8BLK_ERR_NULL;
-  if (bad_rows(M) || bad_k(I) || too_big(M, 2 * I) || M * (I / FP8BLK_BLOCK) > kMaxRows)
-    return FP8BLK_ERR_SHAPE;
-  if (M > 0 && (misaligned(gate_up_bf16) || misaligned(x_q) || misaligned(x_scale)))
-    return FP8BLK_ERR_ALIGN;
-  if (fp8blk_status d = check_device()) return d;
+  if (fp8blk_status c = check_swiglu(gate_up_bf16, M, I, x_q, x_scale, 16)) return c;
   if (M == 0) return FP8BLK_OK;
   return launched(fp8blk::launch_swiglu_act_quant(gate_up_bf16, M, I, x_q, x_scale,
                                                   static_cast<hipStream_t>(stream)));
+}
+
+fp8blk_status fp8_swiglu_act_quant_ue8m0(const void *gate_up_bf16, int64_t M, int64_t I,
+                                         void *x_q, uint8_t *x_scale, void *stream) {
+  if (fp8blk_status c = check_swiglu(gate_up_bf16, M, I, x_q, x_scale, 1)) return c;
+  if (M == 0) return FP8BLK_OK;
+  return launched(fp8blk::launch_swiglu_act_quant_e8m0(gate_up_bf16, M, I, x_q, x_scale,
+                                                       static_cast<hipStream_t>(stream)));
 }
 
 fp8blk_status fp8_weight_block_quant_ue8m0(const void *w_bf16, int64_t N, int64_t K, void *w_q,

@@ -28,6 +28,8 @@ hipError_t launch_act_quant_e8m0(const void *x, int64_t M, int64_t K, void *q, u
                                  hipStream_t stream);
 hipError_t launch_swiglu_act_quant(const void *gu, int64_t M, int64_t I, void *q, float *s,
                                    hipStream_t stream);
+hipError_t launch_swiglu_act_quant_e8m0(const void *gu, int64_t M, int64_t I, void *q,
+                                        uint8_t *s, hipStream_t stream);
 hipError_t launch_weight_quant_e8m0(const void *w, int64_t N, int64_t K, void *q, uint8_t *s,
                                     hipStream_t stream);
 hipError_t launch_block_gemm(const void *xq, const float *xs, const void *wq, const float *ws,

@@ -417,9 +417,11 @@ __device__ __forceinline__ float swiglu_h32(float g, float u, bool &ok) {
 
 constexpr int kSwigluGpt = 8;  // groups per tile of swiglu_quant_kernel (4 per load)
 
+// E8M0: power-of-two scales as in act_quant_e8m0_kernel (scale = bytes).
+template <bool E8M0>
 __global__ __launch_bounds__(kActThreads) void swiglu_quant_kernel(
     const uint16_t *__restrict__ gu, uint32_t gpr, uint2 *__restrict__ q,
-    float *__restrict__ scale, uint32_t n_groups) {
+    void *__restrict__ scale, uint32_t n_groups) {
   constexpr int kGpt = kSwigluGpt;
   constexpr int L = kGpt / 4;  // 16-byte gate and up loads per lane per tile
   const int lane = threadIdx.x & 63;
@@ -454,6 +456,19 @@ __global__ __launch_bounds__(kActThreads) void swiglu_quant_kernel(
         if (!ok32) h[j] = swiglu_h64(g[j], u[j]);
       }
       const float amax = row16_max(absmax8(h));
+      if constexpr (E8M0) {
+        const int e = e8m0_exponent(amax);
+        const float r = e8m0_inv_scale(e);
+        uint2 out;
+        out.x = pack4_e4m3(h[0] * r, h[1] * r, h[2] * r, h[3] * r);
+        out.y = pack4_e4m3(h[4] * r, h[5] * r, h[6] * r, h[7] * r);
+        if (ok[i]) {
+          const uint32_t G = tile * kGpt + i * 4 + (lane >> 4);
+          q[(int64_t)G * 16 + (lane & 15)] = out;
+          if ((lane & 15) == 0) static_cast<uint8_t *>(scale)[G] = (uint8_t)(e + 127);
+        }
+        continue;
+      }
       float t[8], sc;
       if (__builtin_amdgcn_ballot_w64(amax > 0.0f && amax < kTinyAmax) == 0) {
         // as act_quant_kernel's fast path: no power-of-two rescale
@@ -474,7 +489,7 @@ __global__ __launch_bounds__(kActThreads) void swiglu_quant_kernel(
       if (ok[i]) {
         const uint32_t G = tile * kGpt + i * 4 + (lane >> 4);
         q[(int64_t)G * 16 + (lane & 15)] = out;
-        if ((lane & 15) == 0) scale[G] = sc;
+        if ((lane & 15) == 0) static_cast<float *>(scale)[G] = sc;
       }
     }
   }
@@ -496,16 +511,27 @@ hipError_t launch_act_quant(const void *x, int64_t M, int64_t K, void *q, float 
   return hipGetLastError();
 }
 
-hipError_t launch_swiglu_act_quant(const void *gu, int64_t M, int64_t I, void *q, float *s,
-                                   hipStream_t stream) {
+template <bool E8M0>
+static hipError_t launch_swiglu(const void *gu, int64_t M, int64_t I, void *q, void *s,
+                                hipStream_t stream) {
   const int64_t n_groups = M * (I / kBlock);  // < 2^31 (checked by the caller)
   const int64_t n_tiles = (n_groups + kSwigluGpt - 1) / kSwigluGpt;
   int64_t blocks = (n_tiles + kActWaves - 1) / kActWaves;
   if (blocks > 256 * 32) blocks = 256 * 32;  // up to 32 workgroups per CU
-  hipLaunchKernelGGL(swiglu_quant_kernel, dim3((unsigned)blocks), dim3(kActThreads), 0, stream,
-                     static_cast<const uint16_t *>(gu), (uint32_t)(I / kBlock),
+  hipLaunchKernelGGL(swiglu_quant_kernel<E8M0>, dim3((unsigned)blocks), dim3(kActThreads), 0,
+                     stream, static_cast<const uint16_t *>(gu), (uint32_t)(I / kBlock),
                      static_cast<uint2 *>(q), s, (uint32_t)n_groups);
   return hipGetLastError();
+}
+
+hipError_t launch_swiglu_act_quant(const void *gu, int64_t M, int64_t I, void *q, float *s,
+                                   hipStream_t stream) {
+  return launch_swiglu<false>(gu, M, I, q, s, stream);
+}
+
+hipError_t launch_swiglu_act_quant_e8m0(const void *gu, int64_t M, int64_t I, void *q,
+                                        uint8_t *s, hipStream_t stream) {
+  return launch_swiglu<true>(gu, M, I, q, s, stream);
 }
 
 hipError_t launch_act_quant_e8m0(const void *x, int64_t M, int64_t K, void *q, uint8_t *s,

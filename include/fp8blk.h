@@ -203,6 +203,13 @@ FP8BLK_API fp8blk_status fp8_rowwise_gemm(const void *x_q, const float *x_scale,
 FP8BLK_API fp8blk_status fp8_swiglu_act_quant(const void *gate_up_bf16, int64_t M, int64_t I,
                                               void *x_q, float *x_scale, void *stream);
 
+/* The same with power-of-two scales ("UE8M0 scale format"): x_scale [M, I/128]
+ * E8M0 bytes (no alignment needed), exactly fp8_act_quant_group_ue8m0
+ * applied to h. */
+FP8BLK_API fp8blk_status fp8_swiglu_act_quant_ue8m0(const void *gate_up_bf16, int64_t M,
+                                                    int64_t I, void *x_q, uint8_t *x_scale,
+                                                    void *stream);
+
 /* ------------------------------------------------------------------------
  * Static activation scale.
  * "Fine-grained FP8" page, "DeepGEMM fast path": besides the dynamic scheme

@@ -222,9 +222,15 @@ def test_swiglu_validation(lib):
     assert call(lib, f, A, 4, 128, MIS, C, NULL) == 3
     assert call(lib, f, A, 4, 128, B, MIS, NULL) == 3
     assert call(lib, f, NULL, 0, 128, NULL, NULL, NULL) in (0, 4)   # empty: no pointers needed
+    g = "fp8_swiglu_act_quant_ue8m0"
+    assert call(lib, g, NULL, 4, 128, B, C, NULL) == 1
+    assert call(lib, g, A, 4, 192, B, C, NULL) == 2
+    assert call(lib, g, A, 4, 128, MIS, C, NULL) == 3
+    assert call(lib, g, A, 4, 128, B, MIS1, NULL) in (0, 4)          # byte scales: no alignment
     import torch
     if not torch.cuda.is_available():
         assert call(lib, f, A, 4, 128, B, C, NULL) == 4
+        assert call(lib, g, A, 4, 128, B, MIS1, NULL) == 4
 
 
 def test_linear_validation(lib):

@@ -166,3 +166,69 @@ def test_fused_equals_quantizer_of_oracle_h():
     q2, s2 = fb.act_quant_group(to_dev_bf16(h))
     torch.cuda.synchronize()
     assert_codes_equal(q1, s1, host(q2), host(s2), "fused vs quantizer of h")
+
+
+# ----------------------------------------------------------------------------
+# power-of-two (E8M0) scales on the same h
+
+def gpu_swiglu_quant_ue8m0(gu_bits):
+    q, s = fb.swiglu_act_quant(to_dev_bf16(gu_bits), "ue8m0")
+    torch.cuda.synchronize()
+    return host(q), host(s)
+
+
+def check_ue8m0(gu_bits, what):
+    say("swiglu quant ue8m0", what, gu_bits.shape)
+    q, s = gpu_swiglu_quant_ue8m0(gu_bits)
+    wq, ws = osw.swiglu_act_quant_ue8m0(gu_bits)
+    assert_codes_equal(q, s, wq, ws, what)
+
+
+@pytest.mark.parametrize("which", ["one", "wide"])
+def test_ue8m0_every_bf16_gate(which):
+    g = all_finite_gates()
+    gv = (g.astype(np.uint32) << 16).view(np.float32)
+    rng = np.random.default_rng(3 + len(which))
+    if which == "one":
+        u = np.full(len(g), 0x3F80, np.uint16)
+    else:
+        u = bits_of(np.sign(rng.standard_normal(len(g))) * np.exp2(rng.uniform(-60, 60, len(g))))
+        g = np.where(np.abs(gv) < 2.0 ** 60, g, 0).astype(np.uint16)
+    check_ue8m0(gate_up_from_pairs(g, u, 1024), f"ue8m0 all gates, up={which}")
+
+
+@pytest.mark.parametrize("M,I", [(1, 128), (17, 2048), (130, 384), (8195, 256)])
+def test_ue8m0_ragged(M, I):
+    check_ue8m0(synth.moe_gate_up_output(M * 13 + I, M, I), f"ue8m0 {M}x{I}")
+
+
+def test_ue8m0_hand_cases_and_zeros():
+    from oracle_pins import read_golden
+    rows = read_golden("swiglu_hand_cases.txt")
+    gu = np.zeros((len(rows) + 1, 256), np.uint16)
+    for i, r in enumerate(rows):
+        gu[i, 0], gu[i, 128] = int(r.split("|")[0], 16), int(r.split("|")[1], 16)
+    gu[-1, :128] = 0x8000                                 # an all-zero group: byte 0
+    check_ue8m0(gu, "ue8m0 hand cases")
+
+
+def test_ue8m0_moe_down_input_full_size():
+    M, I = synth.MOE_TOKENS * synth.MOE_TOPK, synth.MOE_INTERMEDIATE
+    gu = synth.moe_gate_up_output(synth.seed_of(5, 1, 5), M, I)
+    q, s = gpu_swiglu_quant_ue8m0(gu)
+    rows = np.sort(np.concatenate([[0, M - 1], np.random.default_rng(4).choice(np.arange(1, M - 1), 62, replace=False)]))
+    wq, ws = osw.swiglu_act_quant_ue8m0(gu[rows])
+    assert_codes_equal(q[rows], s[rows], wq, ws, "ue8m0 moe down input (sampled rows)")
+
+
+def test_ue8m0_accepts_float8_e8m0fnu():
+    if not hasattr(torch, "float8_e8m0fnu"):
+        pytest.skip("torch has no float8_e8m0fnu")
+    gu = synth.moe_gate_up_output(31, 8, 256)
+    gd = to_dev_bf16(gu)
+    q = torch.empty((8, 256), dtype=torch.uint8, device=dev())
+    s = torch.empty((8, 2), dtype=torch.float8_e8m0fnu, device=dev())
+    fb.fp8_swiglu_act_quant_ue8m0(gd, q, s)
+    torch.cuda.synchronize()
+    wq, ws = osw.swiglu_act_quant_ue8m0(gu)
+    assert_codes_equal(host(q), s.view(torch.uint8).cpu().numpy(), wq, ws, "e8m0fnu scales")
