@@ -124,9 +124,16 @@ def cpu_baseline():
         og.bf16_rne_bits(y)
         flops += 2.0 * M_PREFILL * N * K
         del x, wq, ws, xq, xs, y
+    cpu = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+    except Exception:  # pragma: no cover
+        pass
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"one whole step (the four projections at M={M_PREFILL}): act quant + fp64 "
-                      f"dequantize-then-matmul, {dt:.1f} s"}
+                      f"dequantize-then-matmul, {dt:.1f} s on {cpu} "
+                      f"({len(os.sched_getaffinity(0))} CPUs in the affinity mask)"}
 
 
 def main():
@@ -322,7 +329,8 @@ def other_rows(torch, fb, dev, stream):
         t = _time(torch, stream, _rotating(copies, lambda w, s: fb.fp8_block_gemm(xq, xsc, w, s, y)))
         del copies
         byts = N * K + 16 * K + 2 * 16 * N
-        rows[f"decode_M16_{name}"] = {"us": round(t * 1e6, 2), "GB/s": round(byts / t / 1e9, 1)}
+        rows[f"decode_M16_{name}"] = {"us": round(t * 1e6, 2), "GB/s": round(byts / t / 1e9, 1),
+                                      "frac_hbm": round(byts / t / 1e9 / PEAK_HBM_GBS, 4)}
     rows.update(ue8m0_rows(torch, fb, dev, stream, g))
     rows.update(static_rows(torch, fb, dev, stream))
     rows.update(rowwise_rows(torch, fb, dev, stream))
@@ -534,7 +542,8 @@ def ue8m0_rows(torch, fb, dev, stream, g):
         t = _time(torch, stream, _rotating(copies, lambda w, e: fb.fp8_block_gemm_ue8m0(xq, xe, w, e, y)))
         del copies
         byts = N * K + 16 * K + 2 * 16 * N
-        rows[f"ue8m0_decode_M16_{name}"] = {"us": round(t * 1e6, 2), "GB/s": round(byts / t / 1e9, 1)}
+        rows[f"ue8m0_decode_M16_{name}"] = {"us": round(t * 1e6, 2), "GB/s": round(byts / t / 1e9, 1),
+                                            "frac_hbm": round(byts / t / 1e9 / PEAK_HBM_GBS, 4)}
     return rows
 
 
