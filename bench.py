@@ -354,6 +354,32 @@ def other_rows(torch, fb, dev, stream):
         rows[f"decode_linear_M16_{name}"] = {"fused_us": round(t1 * 1e6, 2),
                                              "two_launch_us": round(t2 * 1e6, 2),
                                              "fp8_linear_with_workspace_us": round(t3 * 1e6, 2)}
+    # the decode step (the four projections at M = 16, each one fp8_linear
+    # call) launched eagerly and replayed as one captured HIP graph; the same
+    # fixed weights in both legs
+    lin = []
+    for name, N, K in PREFILL_SHAPES:
+        x = torch.randn((16, K), generator=g, device=dev).to(torch.bfloat16)
+        wq, wsc = fb.weight_block_quant((torch.randn((N, K), generator=g, device=dev) * 0.02).to(torch.bfloat16))
+        lin.append((x, wq, wsc, torch.empty((16, N), dtype=torch.bfloat16, device=dev),
+                    torch.empty((16, K), dtype=torch.uint8, device=dev),
+                    torch.empty((16, K // 128), dtype=torch.float32, device=dev)))
+
+    def dec_step():
+        for x, wq, wsc, y, xq, xsc in lin:
+            fb.fp8_linear(x, wq, wsc, y, xq, xsc)
+    t_eager = _time(torch, stream, dec_step)
+    side = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        dec_step()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=side):
+            dec_step()
+    torch.cuda.synchronize()
+    t_graph = _time(torch, stream, graph.replay)
+    rows["decode_step_M16"] = {"eager_us": round(t_eager * 1e6, 2), "graph_us": round(t_graph * 1e6, 2)}
+    del lin, graph
     # grouped MoE (32 experts, Zipf top-8 routing of 4096 tokens)
     _, off = synth.moe_routing()
     total = int(off[-1])
