@@ -288,8 +288,9 @@ FUSED_MAX_M = 64
 
 def fp8_linear(x, w_q, w_scale, y, x_q_ws=None, x_scale_ws=None):
     """One C call for the linear layer: fused in one kernel for M <= 64 when
-    N * K <= 2^25 or no workspaces are given, else quantization into the
-    workspaces (required for M > 64) and the GEMM."""
+    N * K <= 2^25, when the fused kernel packs several 16-column slabs per
+    workgroup (M <= 16, K <= 8192, wide N), or when no workspaces are given; else
+    quantization into the workspaces (required for M > 64) and the GEMM."""
     _need(x, "x", (torch.bfloat16,), 2); _need(w_q, "w_q", _CODES, 2)
     _need(w_scale, "w_scale", _F32, 2); _need(y, "y", (torch.bfloat16,), 2)
     M, K = x.shape

@@ -178,18 +178,23 @@ fp8blk_status fp8_block_gemm_static(const void *x_q, const float *x_scale, const
 fp8blk_status fp8_linear(const void *x_bf16, int64_t M, int64_t N, int64_t K, const void *w_q,
                          const float *w_scale, void *x_q_ws, float *x_scale_ws, void *y_bf16,
                          void *stream) {
-  // The fused decode kernel re-quantizes x in every workgroup (N/16 of
-  // them, each reading all of x in bf16 from L2); for weights past ~32M
-  // elements that redundant work costs more than the quantizer's own
-  // launch, so with workspaces at hand the two kernels run instead
-  // (measured at M = 16, weights streamed from HBM: 4096x4096 fused 10.2 us
-  // against 18.1; 14336x4096 33.7 against 18.3; 4096x14336 27.5 against
-  // 22.2).
+  // The fused decode kernel re-quantizes x in every workgroup (each reads
+  // all of x in bf16 from L2), once per K block for all the workgroup's
+  // 16-column slabs.  It pays for small weights (the second launch costs
+  // more), and for K <= 8192 when the launcher packs two or more slabs per
+  // workgroup; otherwise the two kernels run when workspaces are at hand.
+  // Measured at M = 16, weights streamed from HBM (fused against two
+  // kernels): 4096x4096 10.1 us / 19.4; 14336x4096 (4 slabs) 15.9 / 19.5;
+  // 24576x1536 (2 slabs) 16.5 / 19.5; 4096x14336 (1 slab) 26.7 / 21.1;
+  // 7168x16384 (2 slabs) 38.4 / 33.5; 18432x7168 (1 slab) 66.4 / 47.2.
   constexpr int64_t kFusedMaxM = 64;
   constexpr int64_t kFusedMaxWeight = int64_t(1) << 25;  // N * K elements
+  constexpr int64_t kFusedSlabsMaxK = 8192;
   const bool work = M > 0 && N > 0;
   const bool have_ws = x_q_ws != nullptr && x_scale_ws != nullptr;
-  const bool fused = M <= kFusedMaxM && (N * K <= kFusedMaxWeight || !have_ws);
+  const bool fused = M <= kFusedMaxM &&
+                     (!have_ws || N * K <= kFusedMaxWeight ||
+                      (K <= kFusedSlabsMaxK && fp8blk::linear_decode_slabs(M, N) >= 2));
   if (work && (!x_bf16 || !w_q || !w_scale || !y_bf16 || (!fused && (!x_q_ws || !x_scale_ws))))
     return FP8BLK_ERR_NULL;
   if (bad_rows(M) || bad_rows(N) || bad_k(K) || too_big(M, K) || too_big(N, K) || too_big(M, N))

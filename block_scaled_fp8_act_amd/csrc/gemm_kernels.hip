@@ -843,26 +843,35 @@ __global__ __launch_bounds__(kDecThreads) void decode_gemm_kernel(
     }
   }
 }
+// 16-column slabs per decode workgroup for one row fragment of x (M <= 16):
+// 1, 2 or up to max_ns.  More slabs make each workgroup stream more weight
+// bytes (and, in the fused layer, amortize its quantization of x); with one
+// workgroup per CU the count is picked for the fullest last round of
+// workgroups (ties: more slabs).
+static int decode_slabs(int64_t N, int max_ns) {
+  const int64_t slabs = (N + 15) / 16;
+  int ns_best = 1;
+  double best = 0.0;
+  for (int ns = 1; ns <= max_ns; ns *= 2) {
+    const int64_t wgs = (slabs + ns - 1) / ns;
+    const double fill = (double)wgs / (double)(((wgs + 255) / 256) * 256);
+    if (fill >= best - 1e-9) { best = fill; ns_best = ns; }
+  }
+  return ns_best;
+}
+
+int linear_decode_slabs(int64_t M, int64_t N) { return M <= 16 ? decode_slabs(N, 4) : 1; }
+
 template <int MF, typename S, bool kRow = false>
 static hipError_t launch_decode(const void *xq, const S *xs, int64_t xs_rs, int xs_ks,
                                 const void *wq, const S *ws, int64_t M, int64_t N, int64_t K,
                                 void *y, hipStream_t stream) {
   const int64_t KB = K / 128;
-  // 16-column slabs per workgroup (one row fragment of x: MF = 1): 1, 2 or
-  // 4 (2 at most with E8M0 scales, for registers).  More slabs make each
-  // workgroup stream more weight bytes; with one workgroup per CU the count
-  // is picked for the fullest last round (ties: more slabs).
+  // slabs per workgroup for one row fragment (2 at most with E8M0 scales,
+  // for registers)
   const int64_t slabs = (N + 15) / 16;
   constexpr bool kMx = std::is_same<S, uint8_t>::value;
-  int NS = 1;
-  if (MF == 1) {
-    double best = 0.0;
-    for (int ns = 1; ns <= (kMx ? 2 : 4); ns *= 2) {
-      const int64_t wgs = (slabs + ns - 1) / ns;
-      const double fill = (double)wgs / (double)(((wgs + 255) / 256) * 256);
-      if (fill >= best - 1e-9) { best = fill; NS = ns; }
-    }
-  }
+  const int NS = MF == 1 ? decode_slabs(N, kMx ? 2 : 4) : 1;
   const size_t part = (size_t)kDecWaves * NS * MF * 64 * 16;
   const size_t lds = (std::is_same<S, uint8_t>::value || kRow)
                          ? part
@@ -898,39 +907,47 @@ static hipError_t launch_decode(const void *xq, const S *xs, int64_t xs_rs, int 
 // workgroup from L2; the redundant quantization hides under the W stream.
 // NW waves split the K blocks (16, or 8 for MF = 4, whose four bf16
 // fragments need the larger per-wave register budget).
-template <int MF, int NW>
+template <int MF, int NW, int NS = 1>
 __global__ __launch_bounds__(NW * 64) void decode_linear_kernel(
     const uint16_t *__restrict__ x, const uint8_t *__restrict__ wq, const float *__restrict__ ws,
     int M, int64_t N, int64_t K, uint16_t *__restrict__ y) {
-  constexpr int U = MF == 1 ? 2 : 1;  // K blocks in flight (bf16 x takes 16 VGPRs per fragment)
+  static_assert(NS == 1 || NS == 2 || NS == 4, "slabs per workgroup: 1, 2 or 4");
+  // K blocks in flight (bf16 x takes 16 VGPRs per fragment)
+  constexpr int U = (MF == 1 && NS < 4) ? 2 : 1;
   extern __shared__ __align__(16) float dsm[];
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int KB = (int)(K / 128);
-  v4f *s_part = reinterpret_cast<v4f *>(dsm);  // [waves][MF][64]
-  const int64_t n0 = (int64_t)blockIdx.x * 16;
-  const int rows_b = (int)min<int64_t>(16, N - n0);
+  v4f *s_part = reinterpret_cast<v4f *>(dsm);  // [waves][NS][MF][64]
+  const int64_t n0 = (int64_t)blockIdx.x * 16 * NS;
 
   const int r16 = lane & 15;
   const int g = lane >> 4;
   const int kc = g * 32;
-  const uint8_t *pb = wq + (n0 + min(r16, rows_b - 1)) * K + kc;
+  const uint8_t *pb[NS];  // weight row of this lane's column in slab s (clamped)
+#pragma unroll
+  for (int sl = 0; sl < NS; ++sl) pb[sl] = wq + min<int64_t>(n0 + 16 * sl + r16, N - 1) * K + kc;
   const uint16_t *px[MF];
 #pragma unroll
   for (int f = 0; f < MF; ++f) px[f] = x + (int64_t)min(f * 16 + r16, M - 1) * K + kc;
+  // the NS slabs (16 * NS <= 64 columns from a multiple of 16 * NS) share
+  // one 128-column weight block
   const float *pws = ws + (n0 / 128) * KB;
   const int nmine = wave < KB ? (KB - wave + NW - 1) / NW : 0;
 
-  uint4 bw[U][2];
+  uint4 bw[U][NS][2];
   uint4 xr[U][MF][4];
   auto load = [&](int j0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (j0 + u < nmine) {
         const int64_t ko = (int64_t)(wave + NW * (j0 + u)) * 128;
-        bw[u][0] = *reinterpret_cast<const uint4 *>(pb + ko);
-        bw[u][1] = *reinterpret_cast<const uint4 *>(pb + ko + 16);
+#pragma unroll
+        for (int sl = 0; sl < NS; ++sl) {
+          bw[u][sl][0] = *reinterpret_cast<const uint4 *>(pb[sl] + ko);
+          bw[u][sl][1] = *reinterpret_cast<const uint4 *>(pb[sl] + ko + 16);
+        }
 #pragma unroll
         for (int f = 0; f < MF; ++f)
 #pragma unroll
@@ -940,9 +957,11 @@ __global__ __launch_bounds__(NW * 64) void decode_linear_kernel(
   };
   load(0);
 
-  v4f acc[MF];
+  v4f acc[NS][MF];
 #pragma unroll
-  for (int f = 0; f < MF; ++f) acc[f] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int sl = 0; sl < NS; ++sl)
+#pragma unroll
+    for (int f = 0; f < MF; ++f) acc[sl][f] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
   for (int j0 = 0; j0 < nmine; j0 += U) {
 #pragma unroll
@@ -950,7 +969,6 @@ __global__ __launch_bounds__(NW * 64) void decode_linear_kernel(
       if (j0 + u < nmine) {
         const int kb = wave + NW * (j0 + u);
         const float wsc = pws[kb];
-        const v8i bf = frag_from(bw[u][0], bw[u][1]);
 #pragma unroll
         for (int f = 0; f < MF; ++f) {
           float am = 0.0f;
@@ -975,31 +993,42 @@ __global__ __launch_bounds__(NW * 64) void decode_linear_kernel(
                                               quotient(ldexpf(v[4 * h + 2], p.k), p.sp, p.y),
                                               quotient(ldexpf(v[4 * h + 3], p.k), p.sp, p.y));
           }
-          const v4f pc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              af, bf, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 0, 0, 0);
           // output rows 4g + r of this fragment: their scales live in lanes 4g + r
+          float sr[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            acc[f][r] = fmaf(pc[r], __shfl(p.s, 4 * g + r) * wsc, acc[f][r]);
+          for (int r = 0; r < 4; ++r) sr[r] = __shfl(p.s, 4 * g + r) * wsc;
+          // the codes are formed once and serve every slab
+#pragma unroll
+          for (int sl = 0; sl < NS; ++sl) {
+            const v8i bf = frag_from(bw[u][sl][0], bw[u][sl][1]);
+            const v4f pc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                af, bf, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[sl][f][r] = fmaf(pc[r], sr[r], acc[sl][f][r]);
+          }
         }
       }
     }
     if (j0 + U < nmine) load(j0 + U);
   }
 #pragma unroll
-  for (int f = 0; f < MF; ++f) s_part[(wave * MF + f) * 64 + lane] = acc[f];
+  for (int sl = 0; sl < NS; ++sl)
+#pragma unroll
+    for (int f = 0; f < MF; ++f) s_part[((wave * NS + sl) * MF + f) * 64 + lane] = acc[sl][f];
   __syncthreads();
-  if (wave < MF) {
-    v4f sum = s_part[wave * 64 + lane];
+  if (wave < NS * MF) {
+    const int sl = wave / MF, f = wave % MF;
+    v4f sum = s_part[(sl * MF + f) * 64 + lane];
 #pragma unroll
     for (int w = 1; w < NW; ++w) {
-      const v4f v = s_part[(w * MF + wave) * 64 + lane];
+      const v4f v = s_part[((w * NS + sl) * MF + f) * 64 + lane];
       sum[0] += v[0]; sum[1] += v[1]; sum[2] += v[2]; sum[3] += v[3];
     }
+    const int64_t col = n0 + 16 * sl + r16;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int row = wave * 16 + 4 * g + r;
-      if (row < M && r16 < rows_b) y[(int64_t)row * N + n0 + r16] = (uint16_t)bf16_rne(sum[r]);
+      const int row = f * 16 + 4 * g + r;
+      if (row < M && col < N) y[(int64_t)row * N + col] = (uint16_t)bf16_rne(sum[r]);
     }
   }
 }
@@ -1007,11 +1036,21 @@ __global__ __launch_bounds__(NW * 64) void decode_linear_kernel(
 template <int MF, int NW>
 static hipError_t launch_decode_linear(const void *x, const void *wq, const float *ws, int64_t M,
                                        int64_t N, int64_t K, void *y, hipStream_t stream) {
-  const size_t lds = (size_t)NW * MF * 64 * 16;
-  hipLaunchKernelGGL((decode_linear_kernel<MF, NW>), dim3((unsigned)((N + 15) / 16)),
-                     dim3(NW * 64), lds, stream, static_cast<const uint16_t *>(x),
-                     static_cast<const uint8_t *>(wq), ws, (int)M, N, K,
-                     static_cast<uint16_t *>(y));
+  const int NS = MF == 1 ? decode_slabs(N, 4) : 1;
+  const size_t lds = (size_t)NW * NS * MF * 64 * 16;
+  const dim3 grid((unsigned)(((N + 15) / 16 + NS - 1) / NS));
+  const auto *xp = static_cast<const uint16_t *>(x);
+  const auto *wp = static_cast<const uint8_t *>(wq);
+  auto *yp = static_cast<uint16_t *>(y);
+  if (NS == 4)
+    hipLaunchKernelGGL((decode_linear_kernel<MF, NW, (MF == 1 ? 4 : 1)>), grid, dim3(NW * 64), lds,
+                       stream, xp, wp, ws, (int)M, N, K, yp);
+  else if (NS == 2)
+    hipLaunchKernelGGL((decode_linear_kernel<MF, NW, (MF == 1 ? 2 : 1)>), grid, dim3(NW * 64), lds,
+                       stream, xp, wp, ws, (int)M, N, K, yp);
+  else
+    hipLaunchKernelGGL((decode_linear_kernel<MF, NW, 1>), grid, dim3(NW * 64), lds, stream, xp, wp,
+                       ws, (int)M, N, K, yp);
   return hipGetLastError();
 }
 

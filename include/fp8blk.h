@@ -133,8 +133,10 @@ FP8BLK_API fp8blk_status fp8_grouped_block_gemm(const void *x_q, const float *x_
  * quantization "fused ahead of the GEMM").  For M <= 64 (decode) one kernel
  * can do both: the activation codes and scales are formed in registers
  * inside the weight-streaming GEMM and never reach memory.  It is used when
- * M <= 64 and either N * K <= 2^25 or no workspaces are given (x_q_ws and
- * x_scale_ws may be NULL for M <= 64; they are then not touched).
+ * M <= 64 and either N * K <= 2^25, or M <= 16, K <= 8192 and N wide
+ * enough for the kernel to pack several 16-column slabs per workgroup, or
+ * no workspaces are given (x_q_ws and x_scale_ws may be NULL for M <= 64; they are then
+ * not touched).
  * Otherwise the two kernels run back to back on `stream` through the
  * caller's workspaces x_q_ws [M,K] and x_scale_ws [M,K/128] (required for
  * M > 64, 16-byte aligned), which then hold the activation codes and

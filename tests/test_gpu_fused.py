@@ -101,11 +101,13 @@ def test_linear_workspace_path(M):
         fb.fp8_linear(xd, wqd, wsd, y)
 
 
-@pytest.mark.parametrize("N,K", [(4096, 4096), (14336, 4096), (4096, 14336)])
+@pytest.mark.parametrize("N,K", [(4096, 4096), (14336, 4096), (4096, 14336), (24576, 1536),
+                                 (7168, 16384)])
 def test_linear_picks_a_path_and_agrees(N, K):
     """fb.linear passes workspaces; the library fuses for N * K <= 2^25 and
-    runs two kernels above: both agree with the two-launch path bit for bit
-    at M = 16."""
+    for wide N with K <= 8192 (several slabs per workgroup: 14336 x 4096,
+    24576 x 1536) and runs two kernels for 4096 x 14336 and 7168 x 16384:
+    every path agrees with the two-launch path bit for bit at M = 16."""
     x = synth.llama_activations(N + K, 16, K, 7)
     w = synth.normal_bf16(N, (N, K), 0.02)
     wq, ws = oq.weight_block_quant(w)
