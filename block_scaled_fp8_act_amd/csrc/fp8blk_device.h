@@ -23,6 +23,16 @@ __device__ __forceinline__ void unpack8(const uint4 &v, float *f) {
   f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
 }
 
+// 16-byte load of input that is read exactly once (the quantizers' bf16
+// input): non-temporal, so the stream does not displace cached data.
+// Measured on 4096x14336 bf16 from HBM: 32.7 -> 29.4 us for the activation
+// quantizer (5.44 -> 6.07 TB/s).
+__device__ __forceinline__ uint4 ld_stream(const uint4 *p) {
+  typedef unsigned v4u __attribute__((ext_vector_type(4)));
+  const v4u t = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(p));
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+
 __device__ __forceinline__ float absmax8(const float *f) {
   return fmaxf(fmaxf(fmaxf(fabsf(f[0]), fabsf(f[1])), fmaxf(fabsf(f[2]), fabsf(f[3]))),
                fmaxf(fmaxf(fabsf(f[4]), fabsf(f[5])), fmaxf(fabsf(f[6]), fabsf(f[7]))));

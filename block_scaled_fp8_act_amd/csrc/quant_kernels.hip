@@ -65,7 +65,7 @@ __global__ __launch_bounds__(kActThreads) void act_quant_kernel(
     for (int i = 0; i < L; ++i) {
       const int64_t g = tile0 * kGroupsPerTile + i * 4 + (lane >> 4);
       ok[i] = g < n_groups;
-      v[i] = ok[i] ? x[tile0 * 256 + i * 64 + lane] : make_uint4(0, 0, 0, 0);
+      v[i] = ok[i] ? ld_stream(x + tile0 * 256 + i * 64 + lane) : make_uint4(0, 0, 0, 0);
     }
     float amax[L];
     bool tiny = false;
@@ -132,7 +132,7 @@ __global__ __launch_bounds__(kActThreads) void act_quant_e8m0_kernel(
     for (int i = 0; i < L; ++i) {
       const int64_t g = tile0 * kGroupsPerTile + i * 4 + (lane >> 4);
       ok[i] = g < n_groups;
-      v[i] = ok[i] ? x[tile0 * 256 + i * 64 + lane] : make_uint4(0, 0, 0, 0);
+      v[i] = ok[i] ? ld_stream(x + tile0 * 256 + i * 64 + lane) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < L; ++i) {
@@ -170,7 +170,7 @@ __global__ __launch_bounds__(kStaticThreads) void act_quant_static_kernel(
   const float s = *scale;
   const int64_t stride = (int64_t)gridDim.x * kStaticThreads;
   for (int64_t i = (int64_t)blockIdx.x * kStaticThreads + threadIdx.x; i < n16; i += stride) {
-    const uint4 v0 = x[2 * i], v1 = x[2 * i + 1];
+    const uint4 v0 = ld_stream(x + 2 * i), v1 = ld_stream(x + 2 * i + 1);
     float f[16];
     unpack8(v0, f);
     unpack8(v1, f + 8);
@@ -208,7 +208,7 @@ __global__ __launch_bounds__(kRowThreads) void rowwise_quant_kernel(
 #pragma unroll
     for (int c = 0; c < C; ++c) {
       const int64_t i = t + (int64_t)c * kRowThreads;
-      v[c] = i < n8 ? xr[i] : make_uint4(0, 0, 0, 0);
+      v[c] = i < n8 ? ld_stream(xr + i) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int c = 0; c < C; ++c) {
@@ -281,7 +281,7 @@ __global__ __launch_bounds__(kWqThreads) void weight_quant_kernel(
   for (int i = 0; i < 8; ++i) {
     const int64_t row = nb * kBlock + i * 16 + (t >> 4);
     ok[i] = row < N;
-    v[i] = ok[i] ? *reinterpret_cast<const uint4 *>(w + row * K + kb * kBlock + col)
+    v[i] = ok[i] ? ld_stream(reinterpret_cast<const uint4 *>(w + row * K + kb * kBlock + col))
                  : make_uint4(0, 0, 0, 0);
   }
   float m = 0.0f;
@@ -441,8 +441,8 @@ __global__ __launch_bounds__(kActThreads) void swiglu_quant_kernel(
       const uint4 *p =
           reinterpret_cast<const uint4 *>(gu + (int64_t)m * 2 * I + (int64_t)j * kBlock) +
           (lane & 15);
-      vg[i] = ok[i] ? p[0] : make_uint4(0, 0, 0, 0);
-      vu[i] = ok[i] ? p[I / 8] : make_uint4(0, 0, 0, 0);
+      vg[i] = ok[i] ? ld_stream(p) : make_uint4(0, 0, 0, 0);
+      vu[i] = ok[i] ? ld_stream(p + I / 8) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < L; ++i) {
