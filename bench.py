@@ -17,8 +17,10 @@ Prints one JSON line.  ``value`` is the whole step's throughput in TFLOP/s
 (GEMM FLOPs of the four projections / step time, the activation
 quantization included); ``roofline`` is for the GEMM kernel alone (FLOPs /
 its average launch time measured with HIP events on the launch stream,
-against the dense fp8 MFMA peak); ``cpu_baseline`` times the CPU oracle on
-one projection.
+against the dense fp8 MFMA peak); ``ceilings`` gives what the matrix cores
+sustain on this chip with operands in registers (plain fp8 MFMAs, and the
+same with the GEMM's fp32 promotion FMAs), as context for that fraction;
+``cpu_baseline`` times the CPU oracle on one whole step.
 """
 from __future__ import annotations
 
@@ -227,6 +229,7 @@ def main():
         "per_projection_us": {name: {"act_quant": round(act_t[p] * 1e3, 2), "gemm": round(gemm_t[p] * 1e3, 2)}
                               for p, (name, _, _) in enumerate(PREFILL_SHAPES)},
     }
+    out["ceilings"] = ceilings(torch, stream, gemm_tflops)
     if args.rows:
         out["rows"] = other_rows(torch, fb, dev, stream)
     if not args.no_cpu_baseline:
@@ -290,6 +293,40 @@ def _rotating(copies, fn):
         k[0] += 1
         fn(*c)
     return call
+
+
+CEIL_BLOCKS = 2048   # 8 workgroups of 8 waves per CU
+CEIL_ITERS = 500     # 32 MFMAs per wave per iteration (~3.5 ms per launch)
+
+
+def ceilings(torch, stream, gemm_tflops):
+    """Matrix-core ceilings measured on this chip (libfp8ceil.so; every
+    operand in registers, no memory traffic in the loop): back-to-back fp8
+    MFMAs, and the same MFMAs each followed by the fp32 promotion (one FMA per
+    output per 128-wide K block) that the block GEMM's inner loop carries.
+    roofline.frac stays against the published peak; these are context."""
+    import ctypes
+    path = os.path.join(ROOT, "block_scaled_fp8_act_amd", "lib", "libfp8ceil.so")
+    if not os.path.exists(path):
+        from block_scaled_fp8_act_amd import build
+        build.build()
+    f = ctypes.CDLL(path).fp8ceil_mfma
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    out = torch.empty(CEIL_BLOCKS * 512, dtype=torch.float32, device="cuda")
+    flops = CEIL_BLOCKS * 8 * CEIL_ITERS * 32 * 65536.0
+    res = {}
+    for promote, key in ((0, "mfma_fp8"), (1, "mfma_fp8_with_fp32_promotion")):
+        def run():
+            rc = f(promote, out.data_ptr(), CEIL_BLOCKS, CEIL_ITERS, stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"fp8ceil_mfma failed ({rc})")
+        best = min(_time(torch, stream, run, iters=3, warm=1) for _ in range(3))
+        res[key] = round(flops / best / 1e12, 1)
+    res["unit"] = "TFLOP/s"
+    res["gemm_frac_of_mfma_fp8"] = round(gemm_tflops / res["mfma_fp8"], 4)
+    res["gemm_frac_of_promotion_ceiling"] = round(gemm_tflops / res["mfma_fp8_with_fp32_promotion"], 4)
+    return res
 
 
 def _time(torch, stream, fn, iters=20, warm=3):
