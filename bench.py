@@ -475,6 +475,25 @@ def other_rows(torch, fb, dev, stream):
         "us": round(t1 * 1e6, 2), "GB/s": round(byts / t1 / 1e9, 1),
         "torch_swiglu_then_act_quant_us": round(t2 * 1e6, 2)}
     del gus, xq, xsc, h
+    # DeepSeek-V3 q_a and kv_a at M = 512 (48 and 20 tiles of 128x128 for
+    # 256 CUs): fp8_block_gemm against the K split over workgroups
+    # (fp8_block_gemm_ws, its workspace allocated once before timing)
+    M = 512
+    for name, N, K in (("q_a", 1536, 7168), ("kv_a", 576, 7168)):
+        x = torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16)
+        xq, xsc = fb.act_quant_group(x)
+        wq, wsc = fb.weight_block_quant(
+            (torch.randn((N, K), generator=g, device=dev) * 0.01).to(torch.bfloat16))
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        work = torch.empty(fb.fp8_block_gemm_workspace_bytes(M, N, K), dtype=torch.uint8,
+                           device=dev)
+        t0 = _time(torch, stream, lambda: fb.fp8_block_gemm(xq, xsc, wq, wsc, y))
+        t1 = _time(torch, stream, lambda: fb.fp8_block_gemm_ws(xq, xsc, wq, wsc, y, work))
+        fl = 2.0 * M * N * K
+        rows[f"dsv3_{name}_M512_split_k"] = {
+            "plain_us": round(t0 * 1e6, 2), "split_us": round(t1 * 1e6, 2),
+            "split_TFLOP/s": round(fl / t1 / 1e12, 1), "workspace_MB": round(work.numel() / 1e6, 2)}
+        del x, xq, xsc, wq, wsc, y, work
     return rows
 
 

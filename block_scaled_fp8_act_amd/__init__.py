@@ -55,7 +55,8 @@ import torch
 __all__ = [
     "Fp8BlkError", "BLOCK", "lib_path", "load_library", "status_string",
     "fp8_weight_block_quant", "fp8_act_quant_group", "fp8_block_gemm",
-    "fp8_grouped_block_gemm", "fp8_weight_block_quant_ue8m0", "fp8_act_quant_group_ue8m0",
+    "fp8_grouped_block_gemm", "fp8_block_gemm_ws", "fp8_block_gemm_workspace_bytes",
+    "fp8_weight_block_quant_ue8m0", "fp8_act_quant_group_ue8m0",
     "fp8_block_gemm_ue8m0", "fp8_grouped_block_gemm_ue8m0", "fp8_act_quant_static",
     "fp8_block_gemm_static", "act_quant_static", "block_gemm_static", "linear_static",
     "fp8_linear", "fp8_batched_block_gemm", "batched_block_gemm", "fp8_rowwise_quant", "fp8_rowwise_gemm",
@@ -102,6 +103,7 @@ def load_library() -> ctypes.CDLL:
         "fp8_weight_block_quant": [vp, i64, i64, vp, vp, vp],
         "fp8_act_quant_group": [vp, i64, i64, vp, vp, vp],
         "fp8_block_gemm": [vp, vp, vp, vp, i64, i64, i64, vp, vp],
+        "fp8_block_gemm_ws": [vp, vp, vp, vp, i64, i64, i64, vp, vp, ctypes.c_size_t, vp],
         "fp8_grouped_block_gemm": [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp, vp],
         "fp8_linear": [vp, i64, i64, i64, vp, vp, vp, vp, vp, vp],
         "fp8_batched_block_gemm": [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp, vp],
@@ -120,6 +122,8 @@ def load_library() -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = ctypes.c_int
+    lib.fp8_block_gemm_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.fp8_block_gemm_workspace_bytes.restype = ctypes.c_size_t
     lib.fp8blk_status_string.argtypes = [ctypes.c_int]
     lib.fp8blk_status_string.restype = ctypes.c_char_p
     lib.fp8blk_abi_version.argtypes = []
@@ -245,6 +249,37 @@ def fp8_act_quant_group(x, x_q, x_scale):
 
 def fp8_block_gemm(x_q, x_scale, w_q, w_scale, y):
     _gemm("fp8_block_gemm", _F32, x_q, x_scale, w_q, w_scale, y)
+
+
+def fp8_block_gemm_workspace_bytes(M, N, K):
+    """Workspace bytes fp8_block_gemm_ws splits K with for these sizes (0:
+    no split; the call is then fp8_block_gemm)."""
+    return int(load_library().fp8_block_gemm_workspace_bytes(int(M), int(N), int(K)))
+
+
+def fp8_block_gemm_ws(x_q, x_scale, w_q, w_scale, y, workspace=None):
+    """fp8_block_gemm with K split over workgroups through ``workspace`` (a
+    device tensor of at least fp8_block_gemm_workspace_bytes bytes) for
+    grids that would leave most CUs idle; without a large enough workspace
+    it is fp8_block_gemm."""
+    _need(x_q, "x_q", _CODES, 2); _need(w_q, "w_q", _CODES, 2)
+    _need(x_scale, "x_scale", _F32, 2); _need(w_scale, "w_scale", _F32, 2)
+    _need(y, "y", (torch.bfloat16,), 2)
+    M, K = x_q.shape
+    N = w_q.shape[0]
+    if w_q.shape[1] != K:
+        raise ValueError("x_q and w_q disagree on K")
+    if K % BLOCK == 0:
+        _shape_eq(x_scale, (M, K // BLOCK), "x_scale")
+        _shape_eq(w_scale, (-(-N // BLOCK), K // BLOCK), "w_scale")
+    _shape_eq(y, (M, N), "y")
+    wbytes = 0
+    if workspace is not None:
+        _need(workspace, "workspace", (workspace.dtype,))
+        wbytes = workspace.numel() * workspace.element_size()
+    _check(load_library().fp8_block_gemm_ws(_ptr(x_q), _ptr(x_scale), _ptr(w_q), _ptr(w_scale),
+                                            M, N, K, _ptr(y), _ptr(workspace), wbytes, _stream()),
+           "fp8_block_gemm_ws")
 
 
 def fp8_grouped_block_gemm(x_q, x_scale, w_q, w_scale, offsets, y):
@@ -427,8 +462,19 @@ def act_quant_group(x, scale_fmt="float"):
 
 
 def block_gemm(x_q, x_scale, w_q, w_scale):
-    y = torch.empty((x_q.shape[0], w_q.shape[0]), dtype=torch.bfloat16, device=x_q.device)
-    (fp8_block_gemm_ue8m0 if _is_e8m0(w_scale) else fp8_block_gemm)(x_q, x_scale, w_q, w_scale, y)
+    """y = x * W^T in bf16.  fp32 scales: with K split over workgroups (and a
+    workspace from torch's allocator) when the library asks for one."""
+    M, N, K = x_q.shape[0], w_q.shape[0], x_q.shape[1]
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=x_q.device)
+    if _is_e8m0(w_scale):
+        fp8_block_gemm_ue8m0(x_q, x_scale, w_q, w_scale, y)
+        return y
+    need = fp8_block_gemm_workspace_bytes(M, N, K)
+    if need:
+        work = torch.empty(need, dtype=torch.uint8, device=x_q.device)
+        fp8_block_gemm_ws(x_q, x_scale, w_q, w_scale, y, work)
+    else:
+        fp8_block_gemm(x_q, x_scale, w_q, w_scale, y)
     return y
 
 
@@ -442,12 +488,16 @@ def grouped_block_gemm(x_q, x_scale, w_q, w_scale, offsets):
 def linear(x, w_q, w_scale):
     """The FP8 linear layer: dynamic per-token-group quantization of x, then
     the block-scaled GEMM on the current stream (fp32 scales: one C call,
-    fused into one kernel for M <= 64).  E8M0 weight scales select
-    power-of-two activation scales as well."""
+    fused into one kernel for M <= 64; the quantizer then the split-K GEMM
+    when the output grid is too small to fill the chip).  E8M0 weight
+    scales select power-of-two activation scales as well."""
     if _is_e8m0(w_scale):
         x_q, x_s = act_quant_group(x, "ue8m0")
         return block_gemm(x_q, x_s, w_q, w_scale)
     M, K = x.shape
+    if fp8_block_gemm_workspace_bytes(M, w_q.shape[0], K):
+        x_q, x_s = act_quant_group(x)
+        return block_gemm(x_q, x_s, w_q, w_scale)
     y = torch.empty((M, w_q.shape[0]), dtype=torch.bfloat16, device=x.device)
     x_q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
     x_s = torch.empty((M, max(K // BLOCK, 0)), dtype=torch.float32, device=x.device)

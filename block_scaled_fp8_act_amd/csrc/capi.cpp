@@ -47,7 +47,7 @@ fp8blk_status launched(hipError_t e) { return e == hipSuccess ? FP8BLK_OK : FP8B
 // multiple of 128 up to 2^24, element counts up to 2^40.
 bool bad_rows(int64_t r) { return r < 0 || r > kMaxRows; }
 bool bad_k(int64_t K) { return K <= 0 || K > kMaxK || (K % FP8BLK_BLOCK) != 0; }
-bool too_big(int64_t rows, int64_t K) { return rows > 0 && rows > kMaxElems / K; }
+bool too_big(int64_t rows, int64_t K) { return rows > 0 && K > 0 && rows > kMaxElems / K; }
 
 // Validation of each operation, shared by its variants.  The scale arrays'
 // alignment (bytes) depends on the variant: fp32 scale arrays 16, one
@@ -61,9 +61,11 @@ fp8blk_status check_quant(const void *in, int64_t rows, int64_t K, const void *q
   return check_device();
 }
 
+// `work`: a workspace that the call will use (checked for 16-byte alignment
+// with the other pointers), or NULL.
 fp8blk_status check_gemm(const void *x_q, const void *x_scale, const void *w_q,
                          const void *w_scale, int64_t M, int64_t N, int64_t K, const void *y,
-                         uintptr_t xs_align, uintptr_t ws_align) {
+                         uintptr_t xs_align, uintptr_t ws_align, const void *work_buf = nullptr) {
   const bool work = M > 0 && N > 0;
   if (work && (!x_q || !x_scale || !w_q || !w_scale || !y)) return FP8BLK_ERR_NULL;
   if (bad_rows(M) || bad_rows(N) || bad_k(K) || too_big(M, K) || too_big(N, K) ||
@@ -71,7 +73,8 @@ fp8blk_status check_gemm(const void *x_q, const void *x_scale, const void *w_q,
     return FP8BLK_ERR_SHAPE;
   if (work && ((M + 127) / 128) * ((N + 127) / 128) > kMaxRows) return FP8BLK_ERR_SHAPE;
   if (work && (misaligned(x_q) || misaligned(w_q) || misaligned(y) ||
-               misaligned(x_scale, xs_align) || misaligned(w_scale, ws_align)))
+               misaligned(x_scale, xs_align) || misaligned(w_scale, ws_align) ||
+               (work_buf && misaligned(work_buf))))
     return FP8BLK_ERR_ALIGN;
   return check_device();
 }
@@ -143,6 +146,30 @@ fp8blk_status fp8_block_gemm(const void *x_q, const float *x_scale, const void *
   if (M == 0 || N == 0) return FP8BLK_OK;
   return launched(fp8blk::launch_block_gemm(x_q, x_scale, w_q, w_scale, M, N, K, y_bf16,
                                             static_cast<hipStream_t>(stream)));
+}
+
+size_t fp8_block_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (bad_rows(M) || bad_rows(N) || bad_k(K) || too_big(M, K) || too_big(N, K) || too_big(M, N))
+    return 0;
+  return fp8blk::block_gemm_workspace_bytes(M, N, K);
+}
+
+fp8blk_status fp8_block_gemm_ws(const void *x_q, const float *x_scale, const void *w_q,
+                                const float *w_scale, int64_t M, int64_t N, int64_t K,
+                                void *y_bf16, void *workspace, size_t workspace_bytes,
+                                void *stream) {
+  // whether the workspace will be used (known before validation so that its
+  // alignment is checked with the other pointers; check_gemm still rejects
+  // bad sizes before anything runs)
+  const size_t need = fp8blk::block_gemm_workspace_bytes(M, N, K);
+  const bool use = need > 0 && workspace != nullptr && workspace_bytes >= need;
+  if (fp8blk_status c = check_gemm(x_q, x_scale, w_q, w_scale, M, N, K, y_bf16, 16, 16,
+                                   use ? workspace : nullptr))
+    return c;
+  if (M == 0 || N == 0) return FP8BLK_OK;
+  return launched(fp8blk::launch_block_gemm_ws(x_q, x_scale, w_q, w_scale, M, N, K, y_bf16,
+                                               use ? workspace : nullptr, use ? workspace_bytes : 0,
+                                               static_cast<hipStream_t>(stream)));
 }
 
 fp8blk_status fp8_grouped_block_gemm(const void *x_q, const float *x_scale, const void *w_q,

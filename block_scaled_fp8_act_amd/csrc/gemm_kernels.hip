@@ -171,13 +171,18 @@ __device__ __forceinline__ void store_tile_rows16(const v4f (&acc)[FM][4], uint1
 // groups 1.. hand their accumulators to group 0 through LDS, which adds them
 // (in group order) and stores the tile.  For grids too small to give a CU
 // more than one workgroup, this puts KS waves on each SIMD.
-template <int WM, int WN, int FM, int KS = 1>
+//
+// nkb >= 1 runs only the first nkb K blocks from A, As, B, Bs (K stays the
+// row stride of A and B, K/128 that of the weight scales); with kPartial
+// the tile's fp32 sums go unrounded to Y reinterpreted as float (row
+// stride ldy floats), one K range of a split over workgroups.
+template <int WM, int WN, int FM, int KS = 1, bool kPartial = false>
 __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ A,
                                           const float *__restrict__ As, int64_t xs_rs, int xs_ks,
                                           int rows_a, const uint8_t *__restrict__ B,
                                           const float *__restrict__ Bs, int rows_b, int64_t K,
                                           uint16_t *__restrict__ Y, int64_t ldy,
-                                          typename Tile<WM, WN, FM>::Smem &sm0) {
+                                          typename Tile<WM, WN, FM>::Smem &sm0, int nkb = -1) {
   using T = Tile<WM, WN, FM>;
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -186,8 +191,9 @@ __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ A,
   const int wave = KS == 1 ? wave_all : wave_all % T::kWaves;
   auto &sm = (&sm0)[kg];
   const int wm = wave / WN, wn = wave % WN;
-  const int KB = (int)(K / 128);
-  const int KI = (KB + KS - 1) / KS;  // steps (the same for every group)
+  const int KB = (int)(K / 128);           // row stride of the weight scales
+  const int NKB = nkb > 0 ? nkb : KB;      // K blocks run by this tile
+  const int KI = (NKB + KS - 1) / KS;  // steps (the same for every group)
 
   // DMA load i of a wave fills LDS rows [8r, 8r+8), r = kDma*w + i; lane l
   // writes bytes [16l, 16l+16) of that 1 KB run = row 8r + l/8, physical
@@ -238,7 +244,7 @@ __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ A,
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-  issue(min(kg, KB - 1), 0);
+  issue(min(kg, NKB - 1), 0);
   // Y (a kernel argument) is first used by the epilogue; consuming it here
   // makes its scalar load complete before the loop.  With no scalar load in
   // flight the LDS reads of the loop can be waited on partially (LDS
@@ -256,7 +262,7 @@ __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ A,
 
   for (int it = 0; it < KI; ++it) {
     const int st = it & 1;
-    const float wsc = (KS == 1 || it * KS + kg < KB) ? sm.ws[st][wsel] : 0.0f;
+    const float wsc = (KS == 1 || it * KS + kg < NKB) ? sm.ws[st][wsel] : 0.0f;
     __builtin_amdgcn_sched_barrier(0);
     const uint8_t *sa = sm.a[st];
     const float4 *sas = reinterpret_cast<const float4 *>(&sm.as[st][srow0]);
@@ -312,7 +318,7 @@ __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ A,
       if (mi == 0) {
         // next stage's DMA goes out once this step's first fragment is
         // running, so the step-start LDS reads can be waited on partially
-        if (it + 1 < KI) issue(min((it + 1) * KS + kg, KB - 1), st ^ 1);
+        if (it + 1 < KI) issue(min((it + 1) * KS + kg, NKB - 1), st ^ 1);
         __builtin_amdgcn_sched_barrier(0);
       }
       scp[0] = s4.x * wsc; scp[1] = s4.y * wsc; scp[2] = s4.z * wsc; scp[3] = s4.w * wsc;
@@ -364,6 +370,22 @@ __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ A,
   }
 
   // Epilogue: lane holds rows 4*(lane/16)+r of each 16x16 fragment, column lane%16.
+  if constexpr (kPartial) {
+    // fp32 partial sums; 16 lanes store 64 contiguous bytes of a row
+    float *Yf = reinterpret_cast<float *>(Y);
+#pragma unroll
+    for (int mi = 0; mi < FM; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni) {
+        const int col = wn * 64 + ni * 16 + r16;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = wm * FM * 16 + mi * 16 + 4 * (lane >> 4) + r;
+          if (row < rows_a && col < rows_b) Yf[(int64_t)row * ldy + col] = acc[mi][ni][r];
+        }
+      }
+    return;
+  }
   // Full tiles with 16-byte aligned rows go through LDS (free since the last
   // barrier; past the split-K reduction slots), others element by element.
   static_assert((size_t)(KS - 1) * T::TM * T::TN * 4 + (size_t)T::TM * T::TN * 2 <=
@@ -1146,6 +1168,60 @@ __global__ __launch_bounds__(WM * WN * 64 * KS) void block_gemm_ks_kernel(
                               ws + (n0 / 128) * KB, rows_b, K, y + m0 * N + n0, N, sm[0]);
 }
 
+// K split over workgroups, for grids of 128x128 tiles that would leave most
+// CUs idle (small M and N, long K: DeepSeek-V3 q_a and kv_a at M = 512 have
+// 48 and 20 tiles for 256 CUs).  Workgroup b runs tile b % tiles over K
+// blocks [split * kb_per, min(KB, (split + 1) * kb_per)), split = b / tiles,
+// with the two wave groups of block_gemm_ks_kernel inside, and writes the
+// tile's unrounded fp32 sums to slice `split` of the workspace (slices of
+// slice_elems floats, row stride N).  splitk_reduce_kernel then adds the
+// slices in split order and rounds once to bf16.
+template <int WM, int WN, int FM, int KS>
+__global__ __launch_bounds__(WM * WN * 64 * KS) void block_gemm_splitk_kernel(
+    const uint8_t *__restrict__ xq, const float *__restrict__ xs, const uint8_t *__restrict__ wq,
+    const float *__restrict__ ws, int64_t M, int64_t N, int64_t K, float *__restrict__ part,
+    int64_t slice_elems, int tiles_m, int tiles_n, int kb_per) {
+  using T = Tile<WM, WN, FM>;
+  __shared__ typename T::Smem sm[KS];
+  const int tiles = tiles_m * tiles_n;
+  const int split = blockIdx.x / tiles;
+  int tm, tn;
+  tile_coords(blockIdx.x - split * tiles, tiles, tiles_m, tiles_n, tm, tn);
+  const int64_t m0 = (int64_t)tm * T::TM, n0 = (int64_t)tn * T::TN;
+  const int64_t KB = K / 128;
+  const int64_t kb0 = (int64_t)split * kb_per;
+  const int nkb = (int)min<int64_t>(kb_per, KB - kb0);
+  gemm_tile<WM, WN, FM, KS, true>(
+      xq + m0 * K + kb0 * 128, xs + m0 * KB + kb0, KB, 1, (int)min<int64_t>(T::TM, M - m0),
+      wq + n0 * K + kb0 * 128, ws + (n0 / 128) * KB + kb0, (int)min<int64_t>(T::TN, N - n0), K,
+      reinterpret_cast<uint16_t *>(part + split * slice_elems + m0 * N + n0), N, sm[0], nkb);
+}
+
+// y[i] = bf16(sum over s = 0, 1, ... of part[s * slice_elems + i]), i < MN;
+// slice_elems is a multiple of 4, so every slice is 16-byte aligned.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restrict__ part,
+                                                            int splits, int64_t slice_elems,
+                                                            int64_t MN, uint16_t *__restrict__ y) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  const int64_t n4 = MN / 4;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride) {
+    float4 a = reinterpret_cast<const float4 *>(part)[i];
+    for (int sp = 1; sp < splits; ++sp) {
+      const float4 b = reinterpret_cast<const float4 *>(part + sp * slice_elems)[i];
+      a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+    }
+    uint2 o;
+    o.x = bf16_rne(a.x) | (bf16_rne(a.y) << 16);
+    o.y = bf16_rne(a.z) | (bf16_rne(a.w) << 16);
+    reinterpret_cast<uint2 *>(y)[i] = o;
+  }
+  for (int64_t i = n4 * 4 + (int64_t)blockIdx.x * 256 + threadIdx.x; i < MN; i += stride) {
+    float a = part[i];
+    for (int sp = 1; sp < splits; ++sp) a += part[sp * slice_elems + i];
+    y[i] = (uint16_t)bf16_rne(a);
+  }
+}
+
 // Grouped variant.  The logical m-tiles of all experts are numbered
 // consecutively (expert e owns ceil(M_e/TM) of them); the grid is sized for
 // the upper bound ceil(total_M/TM) + E, and workgroups past the real count
@@ -1253,6 +1329,76 @@ static hipError_t dispatch_gemm(const void *xq, const S *xs, int64_t xs_rs, int 
       (std::is_same<S, float>::value || (K / 128) % 2 == 0))
     return launch_tiled_ks<2, 2, 4, 2, S>(xq, xs, xs_rs, xs_ks, wq, ws, M, N, K, y, stream);
   return launch_tiled<2, 2, 4, S>(xq, xs, xs_rs, xs_ks, wq, ws, M, N, K, y, stream);
+}
+
+// Split-K over workgroups (fp32 per-token-group scales), for grids of at
+// most kSplitMaxTiles 128x128 tiles (at most half the CUs busy).  The split
+// count S (2 .. min(256 / tiles, KB / kSplitMinKb)) maximises a time model
+// fitted to measurements on MI355X (plain and split times of seven shapes
+// with M = 128..1024, K = 2048..7168): the plain kernel spends ~0.85 us per
+// step of two K blocks, so S ranges save 0.85 (KB/2)(1 - 1/S) us, and the
+// split costs ~4.2 us more of fixed overhead (second launch, prologue and
+// tail) plus its traffic (S*M*N fp32 written and read, M*N bf16 written,
+// mostly in cache) at ~10 TB/s.  No split unless the model gains more than
+// 2 us.  Measured: q_a 512x1536x7168 41.2 -> 21.2 us, kv_a 512x576x7168
+// 30.5 -> 18.7 us, 1024x1024x4096 25.3 -> 19.3 us; 256x7168x2048 (12.6 ->
+// 19.6) and 300x576x2048 (12.5 -> 13.2) are slower split and stay whole.
+constexpr int64_t kSplitMaxTiles = 128;
+constexpr int kSplitMinKb = 4;
+
+static int splitk_plan(int64_t M, int64_t N, int64_t K, int &kb_per, int64_t &slice_elems) {
+  if (M <= kDecMaxM || N <= 0 || K <= 0) return 0;
+  const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+  if (tiles > kSplitMaxTiles) return 0;
+  const int64_t KB = K / 128;
+  const int64_t smax = std::min<int64_t>(256 / tiles, KB / kSplitMinKb);
+  const double mn = (double)M * (double)N;
+  int64_t best = 0;
+  double best_gain = 2.0;  // us
+  for (int64_t sp = 2; sp <= smax; ++sp) {
+    const double saved = 0.85 * 0.5 * (double)KB * (1.0 - 1.0 / (double)sp);
+    const double cost = 4.2 + ((double)sp * mn * 8.0 + mn * 2.0) / 1.0e7;
+    if (saved - cost > best_gain) {
+      best_gain = saved - cost;
+      best = sp;
+    }
+  }
+  if (best < 2) return 0;
+  kb_per = (int)((KB + best - 1) / best);
+  const int splits = (int)((KB + kb_per - 1) / kb_per);
+  slice_elems = (M * N + 3) / 4 * 4;
+  return splits >= 2 ? splits : 0;
+}
+
+size_t block_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  int kb_per = 0;
+  int64_t slice = 0;
+  const int splits = splitk_plan(M, N, K, kb_per, slice);
+  return splits ? (size_t)splits * (size_t)slice * sizeof(float) : 0;
+}
+
+hipError_t launch_block_gemm_ws(const void *xq, const float *xs, const void *wq, const float *ws,
+                                int64_t M, int64_t N, int64_t K, void *y, void *work,
+                                size_t work_bytes, hipStream_t stream) {
+  int kb_per = 0;
+  int64_t slice = 0;
+  const int splits = splitk_plan(M, N, K, kb_per, slice);
+  if (splits == 0 || work == nullptr ||
+      work_bytes < (size_t)splits * (size_t)slice * sizeof(float))
+    return launch_block_gemm(xq, xs, wq, ws, M, N, K, y, stream);
+  using T = Tile<2, 2, 4>;
+  const int tm = (int)((M + T::TM - 1) / T::TM), tn = (int)((N + T::TN - 1) / T::TN);
+  float *part = static_cast<float *>(work);
+  hipLaunchKernelGGL((block_gemm_splitk_kernel<2, 2, 4, 2>), dim3((unsigned)(tm * tn * splits)),
+                     dim3(T::kThreads * 2), 0, stream, static_cast<const uint8_t *>(xq), xs,
+                     static_cast<const uint8_t *>(wq), ws, M, N, K, part, slice, tm, tn, kb_per);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t n4 = std::max<int64_t>(M * N / 4, 1);
+  const unsigned grid = (unsigned)std::min<int64_t>((n4 + 255) / 256, 256 * 8);
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(grid), dim3(256), 0, stream, part, splits, slice,
+                     M * N, static_cast<uint16_t *>(y));
+  return hipGetLastError();
 }
 
 template <typename S>

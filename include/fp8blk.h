@@ -54,6 +54,7 @@
 #ifndef FP8BLK_H
 #define FP8BLK_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #if defined(__GNUC__)
@@ -110,6 +111,36 @@ FP8BLK_API fp8blk_status fp8_block_gemm(const void *x_q, const float *x_scale,
                                         const void *w_q, const float *w_scale,
                                         int64_t M, int64_t N, int64_t K,
                                         void *y_bf16, void *stream);
+
+/* The same GEMM with a caller workspace, for shapes whose grid of 128x128
+ * output tiles would leave most compute units idle (small M and N, long K,
+ * e.g. the DeepSeek-V3 q_a and kv_a projections at a few hundred tokens).
+ * The same operation and passage as fp8_block_gemm: each workgroup runs one
+ * output tile over one contiguous range of K blocks, promoting each
+ * 128-long partial sum with its scale pair into fp32 as fp8_block_gemm does,
+ * and stores the range's unrounded fp32 sums in the workspace; a second
+ * kernel adds the ranges in K order and rounds once to bf16.  The result
+ * meets the same tolerance; it is not bit-identical to fp8_block_gemm (the
+ * fp32 sums are associated differently).
+ *   fp8_block_gemm_workspace_bytes(M, N, K): bytes this split needs, 0 when
+ *     it is not used for these sizes: M <= 64, more than 128 output tiles of
+ *     128x128, invalid sizes, or K too short for the split to gain (a time
+ *     model measured on MI355X picks the number of K ranges, 2 to
+ *     min(256 / tiles, K / 512), or none).  Host arithmetic only, no HIP call.
+ *   fp8_block_gemm_ws: arguments as fp8_block_gemm, plus `workspace`
+ *     (device, 16-byte aligned, owned by the caller, overwritten, not
+ *     initialised by the caller) of `workspace_bytes` bytes.  When the
+ *     workspace is NULL or smaller than fp8_block_gemm_workspace_bytes(M,
+ *     N, K), or that is 0, the call is exactly fp8_block_gemm (bit-identical
+ *     output) and the workspace is not touched.  Calls that share a
+ *     workspace must be ordered on one stream.  Errors as fp8_block_gemm;
+ *     a misaligned workspace that would be used is FP8BLK_ERR_ALIGN. */
+FP8BLK_API size_t fp8_block_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+FP8BLK_API fp8blk_status fp8_block_gemm_ws(const void *x_q, const float *x_scale,
+                                           const void *w_q, const float *w_scale,
+                                           int64_t M, int64_t N, int64_t K, void *y_bf16,
+                                           void *workspace, size_t workspace_bytes,
+                                           void *stream);
 
 /* Grouped block-scaled FP8 GEMM for mixture-of-experts layers: expert e
  * multiplies rows [off[e], off[e+1]) of x by its own W[e].  "Fine-grained

@@ -97,6 +97,55 @@ def test_gemm_validation(lib, args, want):
     assert call(lib, "fp8_block_gemm", *args) == want
 
 
+@pytest.mark.parametrize("M,N,K,want", [
+    (512, 1536, 7168, 5 * 512 * 1536 * 4),      # DeepSeek-V3 q_a: 48 tiles, 5 ranges of 12 K blocks
+    (512, 576, 7168, 10 * 512 * 576 * 4),       # kv_a: 20 tiles, 10 ranges of 6 (the last of 2)
+    (1024, 1024, 4096, 4 * 1024 * 1024 * 4),    # 64 tiles, 4 ranges of 8
+    (65, 1, 5120, 10 * 68 * 4),                 # slices padded to a multiple of 4 floats
+    (256, 7168, 2048, 0),                       # the model gains too little (measured slower)
+    (300, 576, 2048, 0),
+    (64, 1536, 7168, 0),                        # M <= 64: the decode kernel
+    (4096, 1024, 4096, 0),                      # 256 tiles: the chip is full
+    (-1, 1536, 7168, 0), (512, 1536, 100, 0), (512, 0, 7168, 0),
+])
+def test_gemm_workspace_bytes(lib, M, N, K, want):
+    """The split plan is host arithmetic only (a time model picks the number
+    of K ranges, then evens the ranges out); slices of M*N floats rounded up
+    to a multiple of 4."""
+    lib.fp8_block_gemm_workspace_bytes.restype = ctypes.c_size_t
+    lib.fp8_block_gemm_workspace_bytes.argtypes = [ctypes.c_int64] * 3
+    assert lib.fp8_block_gemm_workspace_bytes(M, N, K) == want
+
+
+@pytest.mark.parametrize("args,want", [
+    ((NULL, B, C, D, 512, 1536, 7168, E_, A, 1 << 26, NULL), 1),
+    ((A, B, C, D, 512, 1536, 7100, E_, A, 1 << 26, NULL), 2),
+    ((A, B, C, D, 512, 1536, 7168, E_, MIS, 1 << 26, NULL), 3),   # the workspace would be used
+    ((A, B, C, D, 512, 1536, 7168, MIS, A, 1 << 26, NULL), 3),
+])
+def test_gemm_ws_validation(lib, args, want):
+    f = lib.fp8_block_gemm_ws
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int64] * 3 + [ctypes.c_void_p] * 2 + \
+        [ctypes.c_size_t, ctypes.c_void_p]
+    assert f(*args) == want
+
+
+def test_gemm_ws_unused_workspace_is_not_checked(lib):
+    """A workspace too small to be used (or for a shape that needs none) is
+    ignored, misaligned or not: the call is fp8_block_gemm (here without a
+    GPU: FP8BLK_ERR_DEVICE after the argument checks)."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    f = lib.fp8_block_gemm_ws
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int64] * 3 + [ctypes.c_void_p] * 2 + \
+        [ctypes.c_size_t, ctypes.c_void_p]
+    assert f(A, B, C, D, 512, 1536, 7168, E_, MIS, 1024, NULL) == 4
+    assert f(A, B, C, D, 4096, 1024, 4096, E_, MIS, 1 << 30, NULL) == 4
+
+
 @pytest.mark.parametrize("args,want", [
     ((NULL, B, C, D, A, 4, 64, 256, 128, E_, NULL), 1),
     ((A, B, C, D, NULL, 4, 64, 256, 128, E_, NULL), 1),
@@ -117,6 +166,22 @@ def test_valid_arguments_without_gpu_report_device(lib):
         pytest.skip("a GPU is present")
     assert call(lib, "fp8_act_quant_group", A, 4, 128, B, C, NULL) == 4
     assert call(lib, "fp8_block_gemm", A, B, C, D, 4, 256, 128, E_, NULL) == 4
+
+
+@pytest.mark.parametrize("name", ["fp8_block_gemm", "fp8_block_gemm_static", "fp8_rowwise_gemm"])
+def test_gemm_with_zero_columns_is_empty_work(lib, name):
+    """N == 0 with M > 0 is empty work (no division by the zero size in the
+    size checks): OK with a GPU, FP8BLK_ERR_DEVICE without."""
+    import torch
+    want = 0 if torch.cuda.is_available() else 4
+    assert call(lib, name, NULL, NULL, NULL, NULL, 16, 0, 128, NULL, NULL) == want
+
+
+def test_grouped_with_zero_columns_is_empty_work(lib):
+    import torch
+    want = 0 if torch.cuda.is_available() else 4
+    assert call(lib, "fp8_grouped_block_gemm", NULL, NULL, NULL, NULL, NULL, 4, 64, 0, 128, NULL,
+                NULL) == want
 
 
 def test_empty_work_is_validated_then_ok_or_device(lib):

@@ -209,6 +209,128 @@ def test_gemm_empty_and_errors():
 
 
 # ----------------------------------------------------------------------------
+# K split over workgroups (fp8_block_gemm_ws): grids of at most 128 tiles of
+# 128x128 and at least 8 K blocks
+
+def gpu_gemm_ws(xq, xs, wq, ws, work_bytes=None, fill=0xFF):
+    """fp8_block_gemm_ws with a workspace of work_bytes (default: what the
+    library asks for) pre-filled with `fill` bytes (0xFF: fp32 NaN, so any
+    partial sum the kernels leave unwritten would show).  Returns y and the
+    workspace."""
+    M, K = xq.shape
+    N = wq.shape[0]
+    nbytes = fb.fp8_block_gemm_workspace_bytes(M, N, K) if work_bytes is None else work_bytes
+    work = torch.full((max(nbytes, 1),), fill, dtype=torch.uint8, device=dev())
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev())
+    fb.fp8_block_gemm_ws(to_dev(xq), to_dev(xs), to_dev(wq), to_dev(ws), y,
+                         work if nbytes else None)
+    torch.cuda.synchronize()
+    return bf16_to_host(y), work
+
+
+def gpu_gemm_plain(xq, xs, wq, ws):
+    M, N = xq.shape[0], wq.shape[0]
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev())
+    fb.fp8_block_gemm(to_dev(xq), to_dev(xs), to_dev(wq), to_dev(ws), y)
+    torch.cuda.synchronize()
+    return bf16_to_host(y)
+
+
+@pytest.mark.parametrize("M,N,K", [(65, 1536, 7168), (130, 100, 3072), (77, 333, 5760),
+                                   (1000, 700, 5632), (512, 1536, 7168), (257, 129, 4096)])
+def test_gemm_split_over_workgroups_exact(M, N, K):
+    """Integer operands with power-of-two scales: every partial sum of every
+    K range, and their sum, is exact in fp32, so the split result must equal
+    bf16_RNE(exact) bit for bit (ranges, scale offsets and the reduction
+    indexing are all checked).  The shapes cover ragged M and N, ranges of
+    an odd number of K blocks (77x333x5760: 9 ranges of 5) and a shorter
+    last range (1000x700x5632: 5 ranges of 9, the last of 8)."""
+    assert fb.fp8_block_gemm_workspace_bytes(M, N, K) > 0, "shape must take the split path"
+    rng = np.random.default_rng(M * 13 + N + K)
+    xi = rng.integers(-8, 9, (M, K)); wi = rng.integers(-8, 9, (N, K))
+    xq = oe.encode(xi.astype(np.float32)); wq = oe.encode(wi.astype(np.float32))
+    KB, NB = K // 128, -(-N // 128)
+    xs = np.exp2(rng.integers(-1, 2, (M, KB))).astype(np.float32)
+    ws = np.exp2(rng.integers(0, 2, (NB, KB))).astype(np.float32)
+    say("split", M, N, K, "workspace", fb.fp8_block_gemm_workspace_bytes(M, N, K))
+    y, _ = gpu_gemm_ws(xq, xs, wq, ws)
+    want = og.bf16_rne_bits(og.block_gemm(xq, xs, wq, ws))
+    bad = np.argwhere(y != want)
+    assert bad.size == 0, f"{len(bad)} outputs differ, first {bad[:3].tolist()}"
+
+
+@pytest.mark.parametrize("shape_index", [0, 2])
+def test_gemm_split_over_workgroups_dsv3_m512(shape_index):
+    """DeepSeek-V3 q_a (7168 -> 1536) and kv_a (7168 -> 576) at M = 512:
+    48 and 20 tiles, split 5 and 12 ways; every row against the oracle."""
+    x, w = synth.dsv3_inputs(shape_index, 512)
+    xq, xs, wq, ws = quantized_operands(x, w)
+    M, K = xq.shape
+    assert fb.fp8_block_gemm_workspace_bytes(M, wq.shape[0], K) > 0
+    y, _ = gpu_gemm_ws(xq, xs, wq, ws)
+    check_tol(y, og.block_gemm(xq, xs, wq, ws), og.term_magnitude(xq, xs, wq, ws),
+              f"split dsv3 {synth.DSV3_SHAPES[shape_index][0]} M=512")
+
+
+@pytest.mark.parametrize("M,N,K", [(77, 333, 5760), (300, 576, 4096)])
+def test_gemm_split_over_workgroups_tolerance_ragged(M, N, K):
+    x = synth.dsv3_activations(M + 3 * K, M, K, N)
+    w = synth.normal_bf16(N + 5 * K, (N, K), 0.01)
+    xq, xs, wq, ws = quantized_operands(x, w)
+    y, _ = gpu_gemm_ws(xq, xs, wq, ws)
+    check_tol(y, og.block_gemm(xq, xs, wq, ws), og.term_magnitude(xq, xs, wq, ws),
+              f"split {M}x{N}x{K}")
+
+
+def test_gemm_ws_without_usable_workspace_is_fp8_block_gemm():
+    """No workspace, or one byte too small: the call is fp8_block_gemm (same
+    bits) and a too-small workspace is left untouched."""
+    M, N, K = 300, 576, 4096
+    x = synth.dsv3_activations(11, M, K, 12)
+    w = synth.normal_bf16(13, (N, K), 0.01)
+    xq, xs, wq, ws = quantized_operands(x, w)
+    need = fb.fp8_block_gemm_workspace_bytes(M, N, K)
+    assert need > 0
+    plain = gpu_gemm_plain(xq, xs, wq, ws)
+    y0, _ = gpu_gemm_ws(xq, xs, wq, ws, work_bytes=0)
+    y1, work = gpu_gemm_ws(xq, xs, wq, ws, work_bytes=need - 1, fill=0x5A)
+    assert np.array_equal(y0, plain) and np.array_equal(y1, plain)
+    assert bool((work == 0x5A).all()), "a workspace that is not used was written"
+
+
+def test_gemm_ws_large_grid_ignores_workspace():
+    """4096x1024 outputs fill the chip (256 tiles of 128x128): no split, the
+    same bits as fp8_block_gemm even with a workspace given, which stays
+    untouched."""
+    M, N, K = 4096, 1024, 1024
+    assert fb.fp8_block_gemm_workspace_bytes(M, N, K) == 0
+    rng = np.random.default_rng(5)
+    xq = oe.encode(rng.integers(-8, 9, (M, K)).astype(np.float32))
+    wq = oe.encode(rng.integers(-8, 9, (N, K)).astype(np.float32))
+    xs = np.exp2(rng.integers(-3, 3, (M, K // 128))).astype(np.float32)
+    ws = np.exp2(rng.integers(-3, 3, (N // 128, K // 128))).astype(np.float32)
+    plain = gpu_gemm_plain(xq, xs, wq, ws)
+    y, work = gpu_gemm_ws(xq, xs, wq, ws, work_bytes=1 << 20, fill=0x5A)
+    assert np.array_equal(y, plain)
+    assert bool((work == 0x5A).all())
+
+
+def test_gemm_ws_misaligned_workspace_raises():
+    M, N, K = 512, 1536, 7168
+    need = fb.fp8_block_gemm_workspace_bytes(M, N, K)
+    d = dev()
+    xq = torch.zeros((M, K), dtype=torch.uint8, device=d)
+    xs = torch.zeros((M, K // 128), dtype=torch.float32, device=d)
+    wq = torch.zeros((N, K), dtype=torch.uint8, device=d)
+    ws = torch.zeros((N // 128, K // 128), dtype=torch.float32, device=d)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=d)
+    work = torch.empty(need + 16, dtype=torch.uint8, device=d)[1:]
+    with pytest.raises(fb.Fp8BlkError) as e:
+        fb.fp8_block_gemm_ws(xq, xs, wq, ws, y, work)
+    assert e.value.status == 3
+
+
+# ----------------------------------------------------------------------------
 # grouped GEMM
 
 def _grouped_case(sizes, N, K, seed):

@@ -159,7 +159,9 @@ def test_static_gemm_matches_dynamic_gemm_with_broadcast_scales():
     xq = ost.act_quant_static(x, s)
     wq, ws = oq.weight_block_quant(w)
     y1 = gpu_gemm_static(xq, s, wq, ws)
-    y2 = bf16_to_host(fb.block_gemm(to_dev(xq), to_dev(np.full((300, 8), s, np.float32)),
-                                    to_dev(wq), to_dev(ws)))
+    y2 = torch.empty((300, 700), dtype=torch.bfloat16, device=dev())
+    fb.fp8_block_gemm(to_dev(xq), to_dev(np.full((300, 8), s, np.float32)), to_dev(wq),
+                      to_dev(ws), y2)
     torch.cuda.synchronize()
+    y2 = bf16_to_host(y2)
     assert np.array_equal(y1, y2)
