@@ -229,6 +229,7 @@ def main():
         "per_projection_us": {name: {"act_quant": round(act_t[p] * 1e3, 2), "gemm": round(gemm_t[p] * 1e3, 2)}
                               for p, (name, _, _) in enumerate(PREFILL_SHAPES)},
     }
+    out["act_quant"]["standalone"] = act_quant_alone(torch, fb, dev, stream)
     out["ceilings"] = ceilings(torch, stream, gemm_tflops)
     if args.rows:
         out["rows"] = other_rows(torch, fb, dev, stream)
@@ -293,6 +294,34 @@ def _rotating(copies, fn):
         k[0] += 1
         fn(*c)
     return call
+
+
+def act_quant_alone(torch, fb, dev, stream):
+    """The activation quantizer on its own at the step's two shapes: 20
+    launches back to back between two HIP events, cycling through input
+    copies that add up to over 400 MB (so each call reads from HBM, not the
+    256 MB MALL).  The in-step figure brackets each launch with events, which
+    adds the dispatch gap to every ~11 us kernel."""
+    res = {}
+    g = torch.Generator(device=dev)
+    g.manual_seed(4000)
+    for K in (4096, 14336):
+        ncopy = max(2, -(-400 * 2**20 // (M_PREFILL * K * 2)))
+        xs = [torch.randn((M_PREFILL, K), generator=g, device=dev, dtype=torch.float32)
+              .to(torch.bfloat16) for _ in range(ncopy)]
+        xq = torch.empty((M_PREFILL, K), dtype=torch.uint8, device=dev)
+        xsc = torch.empty((M_PREFILL, K // 128), dtype=torch.float32, device=dev)
+        k = [0]
+
+        def run():
+            fb.fp8_act_quant_group(xs[k[0] % ncopy], xq, xsc)
+            k[0] += 1
+        t = min(_time(torch, stream, run, iters=20, warm=4) for _ in range(3))
+        gbs = M_PREFILL * K * ACT_BYTES_PER_ELEM / t / 1e9
+        res[f"{M_PREFILL}x{K}"] = {"us": round(t * 1e6, 2), "GB/s": round(gbs, 1),
+                                   "frac": round(gbs / PEAK_HBM_GBS, 4)}
+        del xs, xq, xsc
+    return res
 
 
 CEIL_BLOCKS = 2048   # 8 workgroups of 8 waves per CU

@@ -1216,10 +1216,11 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
       const float4 b = reinterpret_cast<const float4 *>(part + sp * slice_elems)[i];
       a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
     }
-    uint2 o;
+    typedef unsigned v2u __attribute__((ext_vector_type(2)));
+    v2u o;
     o.x = bf16_rne(a.x) | (bf16_rne(a.y) << 16);
     o.y = bf16_rne(a.z) | (bf16_rne(a.w) << 16);
-    reinterpret_cast<uint2 *>(y)[i] = o;
+    __builtin_nontemporal_store(o, reinterpret_cast<v2u *>(y) + i);  // as the GEMM epilogue
   }
   for (int64_t i = n4 * 4 + (int64_t)blockIdx.x * 256 + threadIdx.x; i < MN; i += stride) {
     float a = part[i];
