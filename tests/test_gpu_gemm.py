@@ -375,6 +375,33 @@ def test_grouped_matches_oracle_and_per_expert_gemm(sizes, N, K):
             assert np.all(diff <= 2e-2 * scale), f"expert {e}: grouped and plain GEMM disagree"
 
 
+@pytest.mark.parametrize("sizes,N,K", [
+    ([65, 300, 1, 129, 256, 0, 383, 128, 511], 300, 1024),
+    ([7, 200, 120], 256, 2048),
+])
+def test_grouped_ragged_tiles_exact(sizes, N, K):
+    """Integer operands with power-of-two scales: every sum is exact, so each
+    expert's rows must equal bf16_RNE(exact) bit for bit.  The sizes put
+    every kind of last row tile in play: at most 128 rows (its upper half
+    of waves idle and its rows unstaged), 129-255 rows, exactly 128 and 256,
+    single rows and empty experts."""
+    E = len(sizes)
+    off = synth.random_offsets(0, E, sizes=sizes)
+    total = int(off[-1])
+    rng = np.random.default_rng(sum(sizes) + N + K)
+    xq = oe.encode(rng.integers(-8, 9, (total, K)).astype(np.float32))
+    wq = oe.encode(rng.integers(-8, 9, (E, N, K)).astype(np.float32))
+    KB, NB = K // 128, -(-N // 128)
+    xs = np.exp2(rng.integers(-1, 2, (total, KB))).astype(np.float32)
+    ws = np.exp2(rng.integers(0, 2, (E, NB, KB))).astype(np.float32)
+    y = fb.grouped_block_gemm(to_dev(xq), to_dev(xs), to_dev(wq), to_dev(ws), to_dev(off))
+    torch.cuda.synchronize()
+    y = bf16_to_host(y)
+    want = og.bf16_rne_bits(og.grouped_block_gemm(xq, xs, wq, ws, off))
+    bad = np.argwhere(y != want)
+    assert bad.size == 0, f"{len(bad)} outputs differ, first {bad[:3].tolist()}"
+
+
 def test_grouped_rows_outside_experts_untouched():
     xq, xs, wq, ws, off = _grouped_case([3, 4], 128, 256, 77)
     total = int(off[-1]) + 5                            # 5 trailing rows of no expert
