@@ -14,8 +14,10 @@
 //
 // Configurations: 256x256 LDS-staged tiles for M > 64 when they fill the
 // chip; 128x128 tiles otherwise (with K split over two wave groups inside
-// the workgroup when there is at most one workgroup per CU); and a
-// weight-streaming kernel with K split over its waves for M <= 64 (decode).
+// the workgroup when there is at most one workgroup per CU, and, given a
+// caller workspace, over several workgroups when the grid would leave most
+// CUs idle); and a weight-streaming kernel with K split over its waves for
+// M <= 64 (decode).
 //
 // With power-of-two scales stored as E8M0 bytes (the "UE8M0 scale format"
 // section of the same page) the scale pair is applied by the matrix core
