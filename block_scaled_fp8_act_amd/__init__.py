@@ -56,6 +56,7 @@ __all__ = [
     "Fp8BlkError", "BLOCK", "lib_path", "load_library", "status_string",
     "fp8_weight_block_quant", "fp8_act_quant_group", "fp8_block_gemm",
     "fp8_grouped_block_gemm", "fp8_block_gemm_ws", "fp8_block_gemm_workspace_bytes",
+    "fp8_block_gemm_ue8m0_ws",
     "fp8_weight_block_quant_ue8m0", "fp8_act_quant_group_ue8m0",
     "fp8_block_gemm_ue8m0", "fp8_grouped_block_gemm_ue8m0", "fp8_act_quant_static",
     "fp8_block_gemm_static", "act_quant_static", "block_gemm_static", "linear_static",
@@ -116,14 +117,16 @@ def load_library() -> ctypes.CDLL:
         "fp8_weight_block_quant_ue8m0": [vp, i64, i64, vp, vp, vp],
         "fp8_act_quant_group_ue8m0": [vp, i64, i64, vp, vp, vp],
         "fp8_block_gemm_ue8m0": [vp, vp, vp, vp, i64, i64, i64, vp, vp],
+        "fp8_block_gemm_ue8m0_ws": [vp, vp, vp, vp, i64, i64, i64, vp, vp, ctypes.c_size_t, vp],
         "fp8_grouped_block_gemm_ue8m0": [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp, vp],
     }
     for name, args in sigs.items():
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = ctypes.c_int
-    lib.fp8_block_gemm_workspace_bytes.argtypes = [i64, i64, i64]
-    lib.fp8_block_gemm_workspace_bytes.restype = ctypes.c_size_t
+    for name in ("fp8_block_gemm_workspace_bytes", "fp8_block_gemm_ue8m0_workspace_bytes"):
+        getattr(lib, name).argtypes = [i64, i64, i64]
+        getattr(lib, name).restype = ctypes.c_size_t
     lib.fp8blk_status_string.argtypes = [ctypes.c_int]
     lib.fp8blk_status_string.restype = ctypes.c_char_p
     lib.fp8blk_abi_version.argtypes = []
@@ -251,10 +254,13 @@ def fp8_block_gemm(x_q, x_scale, w_q, w_scale, y):
     _gemm("fp8_block_gemm", _F32, x_q, x_scale, w_q, w_scale, y)
 
 
-def fp8_block_gemm_workspace_bytes(M, N, K):
-    """Workspace bytes fp8_block_gemm_ws splits K with for these sizes (0:
-    no split; the call is then fp8_block_gemm)."""
-    return int(load_library().fp8_block_gemm_workspace_bytes(int(M), int(N), int(K)))
+def fp8_block_gemm_workspace_bytes(M, N, K, scale_fmt="float"):
+    """Workspace bytes fp8_block_gemm_ws (scale_fmt "ue8m0":
+    fp8_block_gemm_ue8m0_ws) splits K with for these sizes (0: no split; the
+    call is then the plain GEMM)."""
+    name = ("fp8_block_gemm_ue8m0_workspace_bytes" if scale_fmt == "ue8m0"
+            else "fp8_block_gemm_workspace_bytes")
+    return int(getattr(load_library(), name)(int(M), int(N), int(K)))
 
 
 def fp8_block_gemm_ws(x_q, x_scale, w_q, w_scale, y, workspace=None):
@@ -262,8 +268,17 @@ def fp8_block_gemm_ws(x_q, x_scale, w_q, w_scale, y, workspace=None):
     device tensor of at least fp8_block_gemm_workspace_bytes bytes) for
     grids that would leave most CUs idle; without a large enough workspace
     it is fp8_block_gemm."""
+    _gemm_ws("fp8_block_gemm_ws", _F32, x_q, x_scale, w_q, w_scale, y, workspace)
+
+
+def fp8_block_gemm_ue8m0_ws(x_q, x_scale, w_q, w_scale, y, workspace=None):
+    """fp8_block_gemm_ue8m0 with K split over workgroups (as fp8_block_gemm_ws)."""
+    _gemm_ws("fp8_block_gemm_ue8m0_ws", _E8M0, x_q, x_scale, w_q, w_scale, y, workspace)
+
+
+def _gemm_ws(cname, sdt, x_q, x_scale, w_q, w_scale, y, workspace):
     _need(x_q, "x_q", _CODES, 2); _need(w_q, "w_q", _CODES, 2)
-    _need(x_scale, "x_scale", _F32, 2); _need(w_scale, "w_scale", _F32, 2)
+    _need(x_scale, "x_scale", sdt, 2); _need(w_scale, "w_scale", sdt, 2)
     _need(y, "y", (torch.bfloat16,), 2)
     M, K = x_q.shape
     N = w_q.shape[0]
@@ -277,9 +292,9 @@ def fp8_block_gemm_ws(x_q, x_scale, w_q, w_scale, y, workspace=None):
     if workspace is not None:
         _need(workspace, "workspace", (workspace.dtype,))
         wbytes = workspace.numel() * workspace.element_size()
-    _check(load_library().fp8_block_gemm_ws(_ptr(x_q), _ptr(x_scale), _ptr(w_q), _ptr(w_scale),
-                                            M, N, K, _ptr(y), _ptr(workspace), wbytes, _stream()),
-           "fp8_block_gemm_ws")
+    _check(getattr(load_library(), cname)(_ptr(x_q), _ptr(x_scale), _ptr(w_q), _ptr(w_scale),
+                                          M, N, K, _ptr(y), _ptr(workspace), wbytes, _stream()),
+           cname)
 
 
 def fp8_grouped_block_gemm(x_q, x_scale, w_q, w_scale, offsets, y):
@@ -466,15 +481,13 @@ def block_gemm(x_q, x_scale, w_q, w_scale):
     workspace from torch's allocator) when the library asks for one."""
     M, N, K = x_q.shape[0], w_q.shape[0], x_q.shape[1]
     y = torch.empty((M, N), dtype=torch.bfloat16, device=x_q.device)
-    if _is_e8m0(w_scale):
-        fp8_block_gemm_ue8m0(x_q, x_scale, w_q, w_scale, y)
-        return y
-    need = fp8_block_gemm_workspace_bytes(M, N, K)
+    e8m0 = _is_e8m0(w_scale)
+    need = fp8_block_gemm_workspace_bytes(M, N, K, "ue8m0" if e8m0 else "float")
     if need:
         work = torch.empty(need, dtype=torch.uint8, device=x_q.device)
-        fp8_block_gemm_ws(x_q, x_scale, w_q, w_scale, y, work)
+        (fp8_block_gemm_ue8m0_ws if e8m0 else fp8_block_gemm_ws)(x_q, x_scale, w_q, w_scale, y, work)
     else:
-        fp8_block_gemm(x_q, x_scale, w_q, w_scale, y)
+        (fp8_block_gemm_ue8m0 if e8m0 else fp8_block_gemm)(x_q, x_scale, w_q, w_scale, y)
     return y
 
 

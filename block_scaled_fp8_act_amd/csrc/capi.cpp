@@ -322,6 +322,28 @@ fp8blk_status fp8_block_gemm_ue8m0(const void *x_q, const uint8_t *x_scale, cons
                                                  static_cast<hipStream_t>(stream)));
 }
 
+size_t fp8_block_gemm_ue8m0_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (bad_rows(M) || bad_rows(N) || bad_k(K) || too_big(M, K) || too_big(N, K) || too_big(M, N))
+    return 0;
+  return fp8blk::block_gemm_e8m0_workspace_bytes(M, N, K);
+}
+
+fp8blk_status fp8_block_gemm_ue8m0_ws(const void *x_q, const uint8_t *x_scale, const void *w_q,
+                                      const uint8_t *w_scale, int64_t M, int64_t N, int64_t K,
+                                      void *y_bf16, void *workspace, size_t workspace_bytes,
+                                      void *stream) {
+  // as fp8_block_gemm_ws
+  const size_t need = fp8blk::block_gemm_e8m0_workspace_bytes(M, N, K);
+  const bool use = need > 0 && workspace != nullptr && workspace_bytes >= need;
+  if (fp8blk_status c = check_gemm(x_q, x_scale, w_q, w_scale, M, N, K, y_bf16, 1, 1,
+                                   use ? workspace : nullptr))
+    return c;
+  if (M == 0 || N == 0) return FP8BLK_OK;
+  return launched(fp8blk::launch_block_gemm_e8m0_ws(
+      x_q, x_scale, w_q, w_scale, M, N, K, y_bf16, use ? workspace : nullptr,
+      use ? workspace_bytes : 0, static_cast<hipStream_t>(stream)));
+}
+
 fp8blk_status fp8_grouped_block_gemm_ue8m0(const void *x_q, const uint8_t *x_scale,
                                            const void *w_q, const uint8_t *w_scale,
                                            const int32_t *expert_offsets, int32_t E,

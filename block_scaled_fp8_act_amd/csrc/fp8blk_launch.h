@@ -42,6 +42,10 @@ size_t block_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_block_gemm_ws(const void *xq, const float *xs, const void *wq, const float *ws,
                                 int64_t M, int64_t N, int64_t K, void *y, void *work,
                                 size_t work_bytes, hipStream_t stream);
+size_t block_gemm_e8m0_workspace_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_block_gemm_e8m0_ws(const void *xq, const uint8_t *xs, const void *wq,
+                                     const uint8_t *ws, int64_t M, int64_t N, int64_t K, void *y,
+                                     void *work, size_t work_bytes, hipStream_t stream);
 hipError_t launch_grouped_gemm(const void *xq, const float *xs, const void *wq, const float *ws,
                                const int32_t *offsets, int32_t E, int64_t total_M, int64_t N,
                                int64_t K, void *y, hipStream_t stream);

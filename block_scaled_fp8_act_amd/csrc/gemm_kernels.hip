@@ -439,7 +439,11 @@ __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ A,
 // its own stages in sm0[0..KS-1], K blocks kg, kg + KS, ...; group 0 sums
 // and stores).  Here the MFMAs accumulate directly, so a group cannot sit out
 // a step: the caller guarantees KB % KS == 0.
-template <int WM, int WN, int FM, bool kDmaAtBarrier, bool kScaled = true, int KS = 1>
+//
+// nkb and kPartial as in gemm_tile (one K range of a split over workgroups;
+// with KS > 1 the range's block count must be a multiple of KS).
+template <int WM, int WN, int FM, bool kDmaAtBarrier, bool kScaled = true, int KS = 1,
+          bool kPartial = false>
 __device__ __forceinline__ void gemm_tile_mx(const uint8_t *__restrict__ A,
                                              const uint8_t *__restrict__ As, int rows_a,
                                              const uint8_t *__restrict__ B,
@@ -447,9 +451,11 @@ __device__ __forceinline__ void gemm_tile_mx(const uint8_t *__restrict__ A,
                                              uint16_t *__restrict__ Y, int64_t ldy,
                                              typename Tile<WM, WN, FM>::SmemMx &sm0,
                                              const float *__restrict__ xr = nullptr,
-                                             const float *__restrict__ wr = nullptr) {
+                                             const float *__restrict__ wr = nullptr,
+                                             int nkb = -1) {
   using T = Tile<WM, WN, FM>;
   static_assert(FM % 4 == 0, "scale slots are read four at a time");
+  static_assert(kScaled || !kPartial, "partial sums only with per-block scales");
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave_all = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -457,8 +463,9 @@ __device__ __forceinline__ void gemm_tile_mx(const uint8_t *__restrict__ A,
   const int wave = KS == 1 ? wave_all : wave_all % T::kWaves;
   auto &sm = (&sm0)[kg];
   const int wm = wave / WN, wn = wave % WN;
-  const int KB = (int)(K / 128);
-  const int KI = KB / KS;  // steps (KB % KS == 0)
+  const int KB = (int)(K / 128);           // row stride of the scale bytes
+  const int NKB = nkb > 0 ? nkb : KB;      // K blocks run by this tile
+  const int KI = NKB / KS;  // steps (NKB % KS == 0)
   const int r16 = lane & 15;
 
   uint32_t oa[T::kDmaA];
@@ -518,7 +525,7 @@ __device__ __forceinline__ void gemm_tile_mx(const uint8_t *__restrict__ A,
     for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
   issue(kg, 0);
-  if constexpr (kDmaAtBarrier) issue(min(KS + kg, KB - 1), 1);
+  if constexpr (kDmaAtBarrier) issue(min(KS + kg, NKB - 1), 1);
   asm volatile("" ::"s"(Y));  // no scalar load left in flight (see gemm_tile)
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -580,7 +587,7 @@ __device__ __forceinline__ void gemm_tile_mx(const uint8_t *__restrict__ A,
       if (mi == FM - 1) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if constexpr (kDmaAtBarrier) issue(min((it + 2) * KS + kg, KB - 1), st);
+        if constexpr (kDmaAtBarrier) issue(min((it + 2) * KS + kg, NKB - 1), st);
         // the last step reads the re-fetched block KB-1 here (unused)
         b0n = read_b(st ^ 1, 0);
         a0n = read_a(st ^ 1, 0);
@@ -602,7 +609,7 @@ __device__ __forceinline__ void gemm_tile_mx(const uint8_t *__restrict__ A,
       }
       if constexpr (!kDmaAtBarrier) {
         if (mi == 0) {
-          issue(min((it + 1) * KS + kg, KB - 1), st ^ 1);
+          issue(min((it + 1) * KS + kg, NKB - 1), st ^ 1);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -641,6 +648,22 @@ __device__ __forceinline__ void gemm_tile_mx(const uint8_t *__restrict__ A,
           for (int r = 0; r < 4; ++r) acc[mi][ni][r] += red[slot(g, mi, ni, r)];
   }
 
+  if constexpr (kPartial) {
+    // fp32 partial sums, as in gemm_tile
+    float *Yf = reinterpret_cast<float *>(Y);
+#pragma unroll
+    for (int mi = 0; mi < FM; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni) {
+        const int col = wn * 64 + ni * 16 + r16;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = wm * FM * 16 + mi * 16 + 4 * (lane >> 4) + r;
+          if (row < rows_a && col < rows_b) Yf[(int64_t)row * ldy + col] = acc[mi][ni][r];
+        }
+      }
+    return;
+  }
   float cs[4] = {1.0f, 1.0f, 1.0f, 1.0f};
   if constexpr (!kScaled) {
 #pragma unroll
@@ -1184,13 +1207,15 @@ __global__ __launch_bounds__(WM * WN * 64 * KS) void block_gemm_ks_kernel(
 // tile's unrounded fp32 sums to slice `split` of the workspace (slices of
 // slice_elems floats, row stride N).  splitk_reduce_kernel then adds the
 // slices in split order and rounds once to bf16.
-template <int WM, int WN, int FM, int KS>
+// S = float: fp32 scales (any range length); S = uint8_t: E8M0 scale bytes
+// (range lengths multiples of KS).
+template <int WM, int WN, int FM, int KS, typename S>
 __global__ __launch_bounds__(WM * WN * 64 * KS) void block_gemm_splitk_kernel(
-    const uint8_t *__restrict__ xq, const float *__restrict__ xs, const uint8_t *__restrict__ wq,
-    const float *__restrict__ ws, int64_t M, int64_t N, int64_t K, float *__restrict__ part,
+    const uint8_t *__restrict__ xq, const S *__restrict__ xs, const uint8_t *__restrict__ wq,
+    const S *__restrict__ ws, int64_t M, int64_t N, int64_t K, float *__restrict__ part,
     int64_t slice_elems, int tiles_m, int tiles_n, int kb_per) {
   using T = Tile<WM, WN, FM>;
-  __shared__ typename T::Smem sm[KS];
+  __shared__ typename TileSmem<WM, WN, FM, S>::type sm[KS];
   const int tiles = tiles_m * tiles_n;
   const int split = blockIdx.x / tiles;
   int tm, tn;
@@ -1199,10 +1224,16 @@ __global__ __launch_bounds__(WM * WN * 64 * KS) void block_gemm_splitk_kernel(
   const int64_t KB = K / 128;
   const int64_t kb0 = (int64_t)split * kb_per;
   const int nkb = (int)min<int64_t>(kb_per, KB - kb0);
-  gemm_tile<WM, WN, FM, KS, true>(
-      xq + m0 * K + kb0 * 128, xs + m0 * KB + kb0, KB, 1, (int)min<int64_t>(T::TM, M - m0),
-      wq + n0 * K + kb0 * 128, ws + (n0 / 128) * KB + kb0, (int)min<int64_t>(T::TN, N - n0), K,
-      reinterpret_cast<uint16_t *>(part + split * slice_elems + m0 * N + n0), N, sm[0], nkb);
+  uint16_t *out = reinterpret_cast<uint16_t *>(part + split * slice_elems + m0 * N + n0);
+  const int rows_a = (int)min<int64_t>(T::TM, M - m0), rows_b = (int)min<int64_t>(T::TN, N - n0);
+  if constexpr (std::is_same<S, uint8_t>::value)
+    gemm_tile_mx<WM, WN, FM, (FM <= 4), true, KS, true>(
+        xq + m0 * K + kb0 * 128, xs + m0 * KB + kb0, rows_a, wq + n0 * K + kb0 * 128,
+        ws + (n0 / 128) * KB + kb0, rows_b, K, out, N, sm[0], nullptr, nullptr, nkb);
+  else
+    gemm_tile<WM, WN, FM, KS, true>(xq + m0 * K + kb0 * 128, xs + m0 * KB + kb0, KB, 1, rows_a,
+                                    wq + n0 * K + kb0 * 128, ws + (n0 / 128) * KB + kb0, rows_b,
+                                    K, out, N, sm[0], nkb);
 }
 
 // y[i] = bf16(sum over s = 0, 1, ... of part[s * slice_elems + i]), i < MN;
@@ -1355,7 +1386,10 @@ static hipError_t dispatch_gemm(const void *xq, const S *xs, int64_t xs_rs, int 
 constexpr int64_t kSplitMaxTiles = 128;
 constexpr int kSplitMinKb = 4;
 
-static int splitk_plan(int64_t M, int64_t N, int64_t K, int &kb_per, int64_t &slice_elems) {
+// even: every range a multiple of 2 K blocks (the E8M0 tile's two wave
+// groups cannot sit a step out), hence K/128 even too.
+static int splitk_plan(int64_t M, int64_t N, int64_t K, int &kb_per, int64_t &slice_elems,
+                       bool even = false) {
   if (M <= kDecMaxM || N <= 0 || K <= 0) return 0;
   const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
   if (tiles > kSplitMaxTiles) return 0;
@@ -1372,33 +1406,47 @@ static int splitk_plan(int64_t M, int64_t N, int64_t K, int &kb_per, int64_t &sl
       best = sp;
     }
   }
-  if (best < 2) return 0;
+  if (best < 2 || (even && KB % 2 != 0)) return 0;
   kb_per = (int)((KB + best - 1) / best);
+  if (even) kb_per += kb_per & 1;
   const int splits = (int)((KB + kb_per - 1) / kb_per);
   slice_elems = (M * N + 3) / 4 * 4;
   return splits >= 2 ? splits : 0;
 }
 
-size_t block_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+template <typename S>
+static size_t splitk_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   int kb_per = 0;
   int64_t slice = 0;
-  const int splits = splitk_plan(M, N, K, kb_per, slice);
+  const int splits = splitk_plan(M, N, K, kb_per, slice, std::is_same<S, uint8_t>::value);
   return splits ? (size_t)splits * (size_t)slice * sizeof(float) : 0;
 }
 
-hipError_t launch_block_gemm_ws(const void *xq, const float *xs, const void *wq, const float *ws,
+size_t block_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  return splitk_workspace_bytes<float>(M, N, K);
+}
+size_t block_gemm_e8m0_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  return splitk_workspace_bytes<uint8_t>(M, N, K);
+}
+
+template <typename S>
+static hipError_t launch_splitk(const void *xq, const S *xs, const void *wq, const S *ws,
                                 int64_t M, int64_t N, int64_t K, void *y, void *work,
                                 size_t work_bytes, hipStream_t stream) {
   int kb_per = 0;
   int64_t slice = 0;
-  const int splits = splitk_plan(M, N, K, kb_per, slice);
+  const int splits = splitk_plan(M, N, K, kb_per, slice, std::is_same<S, uint8_t>::value);
   if (splits == 0 || work == nullptr ||
-      work_bytes < (size_t)splits * (size_t)slice * sizeof(float))
-    return launch_block_gemm(xq, xs, wq, ws, M, N, K, y, stream);
+      work_bytes < (size_t)splits * (size_t)slice * sizeof(float)) {
+    if constexpr (std::is_same<S, uint8_t>::value)
+      return launch_block_gemm_e8m0(xq, xs, wq, ws, M, N, K, y, stream);
+    else
+      return launch_block_gemm(xq, xs, wq, ws, M, N, K, y, stream);
+  }
   using T = Tile<2, 2, 4>;
   const int tm = (int)((M + T::TM - 1) / T::TM), tn = (int)((N + T::TN - 1) / T::TN);
   float *part = static_cast<float *>(work);
-  hipLaunchKernelGGL((block_gemm_splitk_kernel<2, 2, 4, 2>), dim3((unsigned)(tm * tn * splits)),
+  hipLaunchKernelGGL((block_gemm_splitk_kernel<2, 2, 4, 2, S>), dim3((unsigned)(tm * tn * splits)),
                      dim3(T::kThreads * 2), 0, stream, static_cast<const uint8_t *>(xq), xs,
                      static_cast<const uint8_t *>(wq), ws, M, N, K, part, slice, tm, tn, kb_per);
   hipError_t e = hipGetLastError();
@@ -1408,6 +1456,18 @@ hipError_t launch_block_gemm_ws(const void *xq, const float *xs, const void *wq,
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3(grid), dim3(256), 0, stream, part, splits, slice,
                      M * N, static_cast<uint16_t *>(y));
   return hipGetLastError();
+}
+
+hipError_t launch_block_gemm_ws(const void *xq, const float *xs, const void *wq, const float *ws,
+                                int64_t M, int64_t N, int64_t K, void *y, void *work,
+                                size_t work_bytes, hipStream_t stream) {
+  return launch_splitk<float>(xq, xs, wq, ws, M, N, K, y, work, work_bytes, stream);
+}
+
+hipError_t launch_block_gemm_e8m0_ws(const void *xq, const uint8_t *xs, const void *wq,
+                                     const uint8_t *ws, int64_t M, int64_t N, int64_t K, void *y,
+                                     void *work, size_t work_bytes, hipStream_t stream) {
+  return launch_splitk<uint8_t>(xq, xs, wq, ws, M, N, K, y, work, work_bytes, stream);
 }
 
 template <typename S>

@@ -310,6 +310,18 @@ FP8BLK_API fp8blk_status fp8_block_gemm_ue8m0(const void *x_q, const uint8_t *x_
                                               int64_t M, int64_t N, int64_t K,
                                               void *y_bf16, void *stream);
 
+/* The E8M0 GEMM with K split over workgroups through a caller workspace,
+ * exactly as fp8_block_gemm_ws is to fp8_block_gemm (same operation and
+ * passage as fp8_block_gemm_ue8m0; the K ranges hold an even number of K
+ * blocks, so shapes with an odd K/128 are never split).  Without a usable
+ * workspace the call is fp8_block_gemm_ue8m0, bit for bit. */
+FP8BLK_API size_t fp8_block_gemm_ue8m0_workspace_bytes(int64_t M, int64_t N, int64_t K);
+FP8BLK_API fp8blk_status fp8_block_gemm_ue8m0_ws(const void *x_q, const uint8_t *x_scale,
+                                                 const void *w_q, const uint8_t *w_scale,
+                                                 int64_t M, int64_t N, int64_t K,
+                                                 void *y_bf16, void *workspace,
+                                                 size_t workspace_bytes, void *stream);
+
 /* Grouped variant with E8M0 scales (mixture-of-experts; "UE8M0 scale
  * format": such checkpoints also run the expert matmuls).  Arguments as for
  * fp8_grouped_block_gemm, with x_scale [total_M,K/128] and

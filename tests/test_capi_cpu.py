@@ -117,6 +117,18 @@ def test_gemm_workspace_bytes(lib, M, N, K, want):
     assert lib.fp8_block_gemm_workspace_bytes(M, N, K) == want
 
 
+@pytest.mark.parametrize("M,N,K,want", [
+    (512, 1536, 7168, 5 * 512 * 1536 * 4),      # even K-block ranges: 5 of 12
+    (1000, 700, 5632, 5 * 1000 * 700 * 4),      # 44 blocks: ranges of 10 (9 rounded up), last 4
+    (512, 1536, 7040, 0),                       # 55 K blocks: odd, never split
+    (64, 1536, 7168, 0),
+])
+def test_gemm_ue8m0_workspace_bytes(lib, M, N, K, want):
+    lib.fp8_block_gemm_ue8m0_workspace_bytes.restype = ctypes.c_size_t
+    lib.fp8_block_gemm_ue8m0_workspace_bytes.argtypes = [ctypes.c_int64] * 3
+    assert lib.fp8_block_gemm_ue8m0_workspace_bytes(M, N, K) == want
+
+
 @pytest.mark.parametrize("args,want", [
     ((NULL, B, C, D, 512, 1536, 7168, E_, A, 1 << 26, NULL), 1),
     ((A, B, C, D, 512, 1536, 7100, E_, A, 1 << 26, NULL), 2),

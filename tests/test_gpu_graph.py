@@ -82,3 +82,29 @@ def test_moe_pieces_graph():
     step()
     torch.cuda.synchronize()
     _replay_and_check(step, [y], [_bits(y)], lambda: fb.swiglu_act_quant(gu))
+
+
+def test_split_k_gemm_graph():
+    """The K split over workgroups (two kernels through a workspace, no
+    memset) captured and replayed: every replay equals the eager bits."""
+    d = dev()
+    M, N, K = 512, 1536, 7168
+    x = to_dev_bf16(synth.dsv3_activations(21, M, K, 22))
+    wq, wsc = fb.weight_block_quant(to_dev_bf16(synth.normal_bf16(23, (N, K), 0.01)))
+    xq, xsc = fb.act_quant_group(x)
+    need = fb.fp8_block_gemm_workspace_bytes(M, N, K)
+    assert need > 0
+    work = torch.empty(need, dtype=torch.uint8, device=d)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=d)
+
+    def step():
+        fb.fp8_block_gemm_ws(xq, xsc, wq, wsc, y, work)
+    step()
+    torch.cuda.synchronize()
+    ref = [_bits(y)]
+    junk = torch.randn((M, K), device=d).to(torch.bfloat16)
+
+    def other():
+        jq, js = fb.act_quant_group(junk)
+        fb.fp8_block_gemm_ws(jq, js, wq, wsc, torch.empty_like(y), work)
+    _replay_and_check(step, [y], ref, other)

@@ -269,6 +269,51 @@ def test_linear_ue8m0():
               ou.term_magnitude_ue8m0(xq, xe, wq, we), "linear ue8m0")
 
 
+@pytest.mark.parametrize("M,N,K", [(65, 1536, 7168), (130, 100, 3072), (1000, 700, 5632),
+                                   (257, 129, 4096), (512, 576, 7168)])
+def test_gemm_ue8m0_split_over_workgroups_exact(M, N, K):
+    """fp8_block_gemm_ue8m0_ws with its K ranges (even block counts; the
+    last shorter for 1000x700x5632 and 512x576x7168) on integer operands and
+    scale bytes 126..128: exact, so bit-equal to bf16_RNE(exact); the
+    workspace is pre-filled with NaN bytes."""
+    need = fb.fp8_block_gemm_workspace_bytes(M, N, K, "ue8m0")
+    assert need > 0
+    rng = np.random.default_rng(M * 3 + N + K)
+    xq = oe.encode(rng.integers(-8, 9, (M, K)).astype(np.float32))
+    wq = oe.encode(rng.integers(-8, 9, (N, K)).astype(np.float32))
+    KB, NB = K // 128, -(-N // 128)
+    xe = rng.integers(126, 129, (M, KB)).astype(np.uint8)
+    we = rng.integers(127, 129, (NB, KB)).astype(np.uint8)
+    work = torch.full((need,), 0xFF, dtype=torch.uint8, device=dev())
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev())
+    fb.fp8_block_gemm_ue8m0_ws(to_dev(xq), to_dev(xe), to_dev(wq), to_dev(we), y, work)
+    torch.cuda.synchronize()
+    want = og.bf16_rne_bits(ou.block_gemm_ue8m0(xq, xe, wq, we))
+    bad = np.argwhere(bf16_to_host(y) != want)
+    assert bad.size == 0, f"{len(bad)} outputs differ, first {bad[:3].tolist()}"
+
+
+def test_gemm_ue8m0_split_dsv3_q_a_and_plain_fallback():
+    """DeepSeek-V3 q_a at M = 512 with E8M0 scales: split (tolerance) and,
+    with no workspace, bit for bit fp8_block_gemm_ue8m0; K/128 odd is
+    never split."""
+    x, w = synth.dsv3_inputs(0, 512)
+    xq, xe, wq, we = operands(x, w)
+    M, K = xq.shape
+    N = wq.shape[0]
+    assert fb.fp8_block_gemm_workspace_bytes(M, N, K, "ue8m0") > 0
+    assert fb.fp8_block_gemm_workspace_bytes(512, 1536, 7040, "ue8m0") == 0      # 55 K blocks
+    y = gpu_gemm_ue8m0(xq, xe, wq, we)                   # block_gemm takes the split
+    check_tol(y, ou.block_gemm_ue8m0(xq, xe, wq, we), ou.term_magnitude_ue8m0(xq, xe, wq, we),
+              "ue8m0 split q_a M=512")
+    y0 = torch.empty((M, N), dtype=torch.bfloat16, device=dev())
+    y1 = torch.empty((M, N), dtype=torch.bfloat16, device=dev())
+    fb.fp8_block_gemm_ue8m0(to_dev(xq), to_dev(xe), to_dev(wq), to_dev(we), y0)
+    fb.fp8_block_gemm_ue8m0_ws(to_dev(xq), to_dev(xe), to_dev(wq), to_dev(we), y1, None)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_to_host(y0), bf16_to_host(y1))
+
+
 def test_gemm_ue8m0_accepts_float8_e8m0fnu_and_rejects_fp32():
     if not hasattr(torch, "float8_e8m0fnu"):
         pytest.skip("torch lacks float8_e8m0fnu")
