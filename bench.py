@@ -329,11 +329,12 @@ CEIL_ITERS = 500     # 32 MFMAs per wave per iteration (~3.5 ms per launch)
 
 
 def ceilings(torch, stream, gemm_tflops):
-    """Matrix-core ceilings measured on this chip (libfp8ceil.so; every
+    """Ceilings measured on this chip.  Matrix cores (libfp8ceil.so; every
     operand in registers, no memory traffic in the loop): back-to-back fp8
     MFMAs, and the same MFMAs each followed by the fp32 promotion (one FMA per
     output per 128-wide K block) that the block GEMM's inner loop carries.
-    roofline.frac stays against the published peak; these are context."""
+    HBM: a plain 512 MiB device-to-device copy.  roofline.frac and
+    act_quant.frac stay against the published peaks; these are context."""
     import ctypes
     path = os.path.join(ROOT, "block_scaled_fp8_act_amd", "lib", "libfp8ceil.so")
     if not os.path.exists(path):
@@ -355,6 +356,12 @@ def ceilings(torch, stream, gemm_tflops):
     res["unit"] = "TFLOP/s"
     res["gemm_frac_of_mfma_fp8"] = round(gemm_tflops / res["mfma_fp8"], 4)
     res["gemm_frac_of_promotion_ceiling"] = round(gemm_tflops / res["mfma_fp8_with_fp32_promotion"], 4)
+    # HBM: the runtime's own device-to-device copy of 512 MiB (read + write)
+    src = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    t = min(_time(torch, stream, lambda: dst.copy_(src), iters=5, warm=1) for _ in range(3))
+    res["hbm_copy_512MiB_GBps"] = round(2 * src.numel() / t / 1e9, 1)
+    del src, dst
     return res
 
 
