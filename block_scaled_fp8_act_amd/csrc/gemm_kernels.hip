@@ -1390,7 +1390,10 @@ constexpr int kSplitMinKb = 4;
 // groups cannot sit a step out), hence K/128 even too.
 static int splitk_plan(int64_t M, int64_t N, int64_t K, int &kb_per, int64_t &slice_elems,
                        bool even = false) {
+  // (also called before argument validation: sizes past the library's
+  // limits are simply not split)
   if (M <= kDecMaxM || N <= 0 || K <= 0) return 0;
+  if (M > (int64_t(1) << 31) || N > (int64_t(1) << 31) || K > (int64_t(1) << 24)) return 0;
   const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
   if (tiles > kSplitMaxTiles) return 0;
   const int64_t KB = K / 128;

@@ -107,6 +107,7 @@ def test_gemm_validation(lib, args, want):
     (64, 1536, 7168, 0),                        # M <= 64: the decode kernel
     (4096, 1024, 4096, 0),                      # 256 tiles: the chip is full
     (-1, 1536, 7168, 0), (512, 1536, 100, 0), (512, 0, 7168, 0),
+    ((1 << 63) - 1, 1536, 7168, 0), (512, (1 << 63) - 1, 7168, 0), (512, 1536, (1 << 62), 0),
 ])
 def test_gemm_workspace_bytes(lib, M, N, K, want):
     """The split plan is host arithmetic only (a time model picks the number
@@ -134,6 +135,7 @@ def test_gemm_ue8m0_workspace_bytes(lib, M, N, K, want):
     ((A, B, C, D, 512, 1536, 7100, E_, A, 1 << 26, NULL), 2),
     ((A, B, C, D, 512, 1536, 7168, E_, MIS, 1 << 26, NULL), 3),   # the workspace would be used
     ((A, B, C, D, 512, 1536, 7168, MIS, A, 1 << 26, NULL), 3),
+    ((A, B, C, D, (1 << 63) - 1, 1536, 7168, E_, A, 1 << 26, NULL), 2),
 ])
 def test_gemm_ws_validation(lib, args, want):
     f = lib.fp8_block_gemm_ws
