@@ -392,18 +392,20 @@ def other_rows(torch, fb, dev, stream):
     t = _time(torch, stream, lambda: fb.fp8_weight_block_quant(w, q, s))
     rows["weight_quant_18432x7168"] = {"us": round(t * 1e6, 2), "GB/s": round(18432 * 7168 * 3 / t / 1e9, 1)}
     del w, q, s
-    # decode GEMMs (HBM-bound): M = 16, weights rotated through HBM
+    # decode GEMMs (HBM-bound): M = 1, 4, 16 (the Llama-3-8B decode
+    # configuration), weights rotated through HBM
     for name, N, K in PREFILL_SHAPES:
-        x = torch.randn((16, K), generator=g, device=dev).to(torch.bfloat16)
         wq, wsc = fb.weight_block_quant((torch.randn((N, K), generator=g, device=dev) * 0.02).to(torch.bfloat16))
-        xq, xsc = fb.act_quant_group(x)
-        y = torch.empty((16, N), dtype=torch.bfloat16, device=dev)
         copies = _weight_copies(wq, wsc)
-        t = _time(torch, stream, _rotating(copies, lambda w, s: fb.fp8_block_gemm(xq, xsc, w, s, y)))
+        for Md in (1, 4, 16):
+            x = torch.randn((Md, K), generator=g, device=dev).to(torch.bfloat16)
+            xq, xsc = fb.act_quant_group(x)
+            y = torch.empty((Md, N), dtype=torch.bfloat16, device=dev)
+            t = _time(torch, stream, _rotating(copies, lambda w, s: fb.fp8_block_gemm(xq, xsc, w, s, y)))
+            byts = N * K + Md * K + 2 * Md * N
+            rows[f"decode_M{Md}_{name}"] = {"us": round(t * 1e6, 2), "GB/s": round(byts / t / 1e9, 1),
+                                            "frac_hbm": round(byts / t / 1e9 / PEAK_HBM_GBS, 4)}
         del copies
-        byts = N * K + 16 * K + 2 * 16 * N
-        rows[f"decode_M16_{name}"] = {"us": round(t * 1e6, 2), "GB/s": round(byts / t / 1e9, 1),
-                                      "frac_hbm": round(byts / t / 1e9 / PEAK_HBM_GBS, 4)}
     rows.update(ue8m0_rows(torch, fb, dev, stream, g))
     rows.update(static_rows(torch, fb, dev, stream))
     rows.update(rowwise_rows(torch, fb, dev, stream))
