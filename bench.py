@@ -332,30 +332,50 @@ def ceilings(torch, stream, gemm_tflops):
     """Ceilings measured on this chip.  Matrix cores (libfp8ceil.so; every
     operand in registers, no memory traffic in the loop): back-to-back fp8
     MFMAs, and the same MFMAs each followed by the fp32 promotion (one FMA per
-    output per 128-wide K block) that the block GEMM's inner loop carries.
-    HBM: a plain 512 MiB device-to-device copy.  roofline.frac and
-    act_quant.frac stay against the published peaks; these are context."""
+    output per 128-wide K block) that the block GEMM's inner loop carries;
+    each once on near-constant operand registers and once on operands that
+    take fresh random bits every iteration (the switching activity of real
+    data), with the engine clock each held (shader-clock over wall-clock
+    ticks, read inside the kernel).  HBM: a plain 512 MiB device-to-device
+    copy.  roofline.frac and act_quant.frac stay against the published
+    peaks; these are context."""
     import ctypes
     path = os.path.join(ROOT, "block_scaled_fp8_act_amd", "lib", "libfp8ceil.so")
     if not os.path.exists(path):
         from block_scaled_fp8_act_amd import build
         build.build()
-    f = ctypes.CDLL(path).fp8ceil_mfma
+    lib = ctypes.CDLL(path)
+    f = lib.fp8ceil_mfma
     f.restype = ctypes.c_int
-    f.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    f.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_void_p]
+    lib.fp8ceil_wall_clock_khz.restype = ctypes.c_int
+    wall_khz = lib.fp8ceil_wall_clock_khz()
     out = torch.empty(CEIL_BLOCKS * 512, dtype=torch.float32, device="cuda")
+    clk = torch.zeros(CEIL_BLOCKS * 2, dtype=torch.int64, device="cuda")
     flops = CEIL_BLOCKS * 8 * CEIL_ITERS * 32 * 65536.0
     res = {}
-    for promote, key in ((0, "mfma_fp8"), (1, "mfma_fp8_with_fp32_promotion")):
-        def run():
-            rc = f(promote, out.data_ptr(), CEIL_BLOCKS, CEIL_ITERS, stream.cuda_stream)
+    clocks = {}
+    for mode, key in ((0, "mfma_fp8"), (1, "mfma_fp8_with_fp32_promotion"),
+                      (2, "mfma_fp8_random_operands"),
+                      (3, "mfma_fp8_with_fp32_promotion_random_operands")):
+        def run(c=None):
+            rc = f(mode, out.data_ptr(), c, CEIL_BLOCKS, CEIL_ITERS, stream.cuda_stream)
             if rc != 0:
                 raise RuntimeError(f"fp8ceil_mfma failed ({rc})")
         best = min(_time(torch, stream, run, iters=3, warm=1) for _ in range(3))
         res[key] = round(flops / best / 1e12, 1)
+        if wall_khz > 0:
+            run(clk.data_ptr())
+            torch.cuda.synchronize()
+            ticks = clk.view(CEIL_BLOCKS, 2).double().sum(0)
+            clocks[key] = round(float(ticks[0] / ticks[1]) * wall_khz / 1e6, 3)
     res["unit"] = "TFLOP/s"
+    res["clock_GHz"] = clocks
     res["gemm_frac_of_mfma_fp8"] = round(gemm_tflops / res["mfma_fp8"], 4)
     res["gemm_frac_of_promotion_ceiling"] = round(gemm_tflops / res["mfma_fp8_with_fp32_promotion"], 4)
+    res["gemm_frac_of_promotion_ceiling_random_operands"] = round(
+        gemm_tflops / res["mfma_fp8_with_fp32_promotion_random_operands"], 4)
     # HBM: the runtime's own device-to-device copy of 512 MiB (read + write)
     src = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)

@@ -328,9 +328,9 @@ def test_linear_validation(lib):
         assert call(lib, f, A, 16, 256, 128, C, D, MIS, MIS, E_, NULL) == 4
 
 
-def test_ceiling_library_exports_one_symbol_and_checks_arguments():
+def test_ceiling_library_exports_and_checks_arguments():
     """libfp8ceil.so (the measurement-only matrix-core ceiling kernels timed
-    by bench.py) exports exactly its one entry point and refuses bad
+    by bench.py) exports exactly its two entry points and refuses bad
     arguments before any HIP call."""
     import subprocess
     from block_scaled_fp8_act_amd import build
@@ -338,10 +338,14 @@ def test_ceiling_library_exports_one_symbol_and_checks_arguments():
         build.build()
     out = subprocess.run(["nm", "-D", "--defined-only", build.CEIL_LIB], capture_output=True,
                          text=True).stdout
-    assert {l.split()[-1] for l in out.splitlines() if " T " in l} == {"fp8ceil_mfma"}
+    assert {l.split()[-1] for l in out.splitlines() if " T " in l} == {
+        "fp8ceil_mfma", "fp8ceil_wall_clock_khz"}
     f = ctypes.CDLL(build.CEIL_LIB).fp8ceil_mfma
     f.restype = ctypes.c_int
-    f.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
-    assert f(0, None, 8, 8, None) == -1
-    assert f(1, A, 0, 8, None) == -1
-    assert f(1, A, 8, 0, None) == -1
+    f.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_void_p]
+    assert f(0, None, None, 8, 8, None) == -1
+    assert f(1, A, None, 0, 8, None) == -1
+    assert f(1, A, None, 8, 0, None) == -1
+    assert f(-1, A, None, 8, 8, None) == -1
+    assert f(4, A, A, 8, 8, None) == -1
