@@ -301,7 +301,9 @@ def act_quant_alone(torch, fb, dev, stream):
     launches back to back between two HIP events, cycling through input
     copies that add up to over 400 MB (so each call reads from HBM, not the
     256 MB MALL).  The in-step figure brackets each launch with events, which
-    adds the dispatch gap to every ~11 us kernel."""
+    adds the dispatch gap to every ~11 us kernel.  Beside each, the runtime's
+    own device-to-device copy of the same byte count (read + write), the
+    practical HBM ceiling at that size."""
     res = {}
     g = torch.Generator(device=dev)
     g.manual_seed(4000)
@@ -318,9 +320,23 @@ def act_quant_alone(torch, fb, dev, stream):
             k[0] += 1
         t = min(_time(torch, stream, run, iters=20, warm=4) for _ in range(3))
         gbs = M_PREFILL * K * ACT_BYTES_PER_ELEM / t / 1e9
-        res[f"{M_PREFILL}x{K}"] = {"us": round(t * 1e6, 2), "GB/s": round(gbs, 1),
-                                   "frac": round(gbs / PEAK_HBM_GBS, 4)}
         del xs, xq, xsc
+        # context: the runtime's device-to-device copy moving the same bytes
+        # (half read, half written), sources cycled the same way
+        nb = int(M_PREFILL * K * ACT_BYTES_PER_ELEM) // 2
+        srcs = [torch.empty(nb, dtype=torch.uint8, device=dev) for _ in range(ncopy)]
+        dst = torch.empty(nb, dtype=torch.uint8, device=dev)
+        k[0] = 0
+
+        def copy():
+            dst.copy_(srcs[k[0] % ncopy])
+            k[0] += 1
+        tc = min(_time(torch, stream, copy, iters=20, warm=4) for _ in range(3))
+        del srcs, dst
+        res[f"{M_PREFILL}x{K}"] = {"us": round(t * 1e6, 2), "GB/s": round(gbs, 1),
+                                   "frac": round(gbs / PEAK_HBM_GBS, 4),
+                                   "copy_same_bytes_us": round(tc * 1e6, 2),
+                                   "frac_of_copy": round(tc / t, 4)}
     return res
 
 
