@@ -441,6 +441,15 @@ def other_rows(torch, fb, dev, stream):
             byts = N * K + Md * K + 2 * Md * N
             rows[f"decode_M{Md}_{name}"] = {"us": round(t * 1e6, 2), "GB/s": round(byts / t / 1e9, 1),
                                             "frac_hbm": round(byts / t / 1e9 / PEAK_HBM_GBS, 4)}
+            need = fb.fp8_block_gemm_workspace_bytes(Md, N, K)
+            if need:
+                # long K: four slabs per workgroup, K split over workgroups
+                work = torch.empty(need, dtype=torch.uint8, device=dev)
+                t = _time(torch, stream, _rotating(
+                    copies, lambda w, s: fb.fp8_block_gemm_ws(xq, xsc, w, s, y, work)))
+                rows[f"decode_M{Md}_{name}"].update(
+                    {"split_k_us": round(t * 1e6, 2), "split_k_GB/s": round(byts / t / 1e9, 1)})
+                del work
         del copies
     rows.update(ue8m0_rows(torch, fb, dev, stream, g))
     rows.update(static_rows(torch, fb, dev, stream))

@@ -502,7 +502,9 @@ def linear(x, w_q, w_scale):
     """The FP8 linear layer: dynamic per-token-group quantization of x, then
     the block-scaled GEMM on the current stream (fp32 scales: one C call,
     fused into one kernel for M <= 64; the quantizer then the split-K GEMM
-    when the output grid is too small to fill the chip).  E8M0 weight
+    when the library plans a K split: output grids too small to fill the
+    chip, and 9 <= M <= 16 with long K, where the fused kernel's per-column
+    re-reads of x cost more than the separate quantizer).  E8M0 weight
     scales select power-of-two activation scales as well."""
     if _is_e8m0(w_scale):
         x_q, x_s = act_quant_group(x, "ue8m0")

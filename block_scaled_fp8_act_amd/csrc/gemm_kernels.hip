@@ -734,14 +734,17 @@ constexpr int kDecMaxScaleBytes = 32 * 1024;  // x_scale staging limit (KB * MF 
 // S = uint8_t: E8M0 scale bytes, loaded with the operands and applied by the
 // matrix core (nothing staged in LDS but the final partials).  kRow: fp32
 // row-wise scales (xs[M], ws[N]): unscaled MFMAs accumulate over all of K and
-// the sum is scaled by xs[m] * ws[n] at the end.
-template <int MF, typename S, bool kRow = false, int NS = 1>
+// the sum is scaled by xs[m] * ws[n] at the end.  kPartial (fp32 block
+// scales only): workgroup (x, s) takes K blocks [s * kb_per, (s + 1) * kb_per)
+// and writes its unrounded fp32 sums to part + s * slice (row stride N).
+template <int MF, typename S, bool kRow = false, int NS = 1, bool kPartial = false>
 __global__ __launch_bounds__(kDecThreads) void decode_gemm_kernel(
     const uint8_t *__restrict__ xq, const S *__restrict__ xs, int64_t xs_rs, int xs_ks,
     const uint8_t *__restrict__ wq, const S *__restrict__ ws, int M, int64_t N, int64_t K,
-    uint16_t *__restrict__ y) {
+    uint16_t *__restrict__ y, float *__restrict__ part, int64_t slice, int kb_per) {
   constexpr bool MX = std::is_same<S, uint8_t>::value;
   static_assert(!(kRow && MX), "row-wise scales are fp32");
+  static_assert(!kPartial || (!MX && !kRow), "partial sums: fp32 block scales only");
   static_assert(NS == 1 || NS == 2 || NS == 4, "slabs per workgroup: 1, 2 or 4");
   constexpr int R = MF * 16;                          // staged rows
   // register buffers of U K blocks: two (the next batch's loads go out
@@ -755,6 +758,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_gemm_kernel(
   const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int KB = (int)(K / 128);
+  // this workgroup's K blocks: [kb0, kb0 + kbn)
+  const int kb0 = kPartial ? (int)blockIdx.y * kb_per : 0;
+  const int kbn = kPartial ? min(KB - kb0, kb_per) : KB;
   v4f *s_part = reinterpret_cast<v4f *>(dsm);  // [waves][NS][MF][64], reuses s_as after the loop
   const int64_t n0 = (int64_t)blockIdx.x * 16 * NS;
 
@@ -773,7 +779,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_gemm_kernel(
   // the NS slabs (16 * NS <= 64 columns from a multiple of 16 * NS) share
   // one 128-column weight block
   const S *pws = ws + (n0 / 128) * KB;
-  const int nmine = wave < KB ? (KB - wave + kDecWaves - 1) / kDecWaves : 0;
+  const int nmine = wave < kbn ? (kbn - wave + kDecWaves - 1) / kDecWaves : 0;
 
   uint4 bw[NB][U][NS][2];
   v8i af[NB][U][MF];
@@ -783,7 +789,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_gemm_kernel(
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (j0 + u < nmine) {
-        const int kb = wave + kDecWaves * (j0 + u);
+        const int kb = kb0 + wave + kDecWaves * (j0 + u);
         const int64_t ko = (int64_t)kb * 128;
 #pragma unroll
         for (int sl = 0; sl < NS; ++sl) {
@@ -805,8 +811,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_gemm_kernel(
   load(std::integral_constant<int, 0>{}, 0);
 
   if constexpr (!MX && !kRow) {
-    for (int i = t; i < KB * R; i += kDecThreads) {
-      const int kb = i / R, m = i % R;
+    for (int i = t; i < kbn * R; i += kDecThreads) {
+      const int kb = kb0 + i / R, m = i % R;
       s_as[i] = xs[(int64_t)min(m, M - 1) * xs_rs + (int64_t)kb * xs_ks];
     }
     __syncthreads();
@@ -823,14 +829,14 @@ __global__ __launch_bounds__(kDecThreads) void decode_gemm_kernel(
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (j0 + u < nmine) {
-        const int kb = wave + kDecWaves * (j0 + u);
+        const int kb = kb0 + wave + kDecWaves * (j0 + u);
         float4 s4[MF];
         float wsc = 1.0f;
         if constexpr (!MX && !kRow) {
           wsc = pws[kb];
 #pragma unroll
           for (int f = 0; f < MF; ++f)
-            s4[f] = *reinterpret_cast<const float4 *>(&s_as[kb * R + f * 16 + 4 * (lane >> 4)]);
+            s4[f] = *reinterpret_cast<const float4 *>(&s_as[(kb - kb0) * R + f * 16 + 4 * (lane >> 4)]);
         }
 #pragma unroll
         for (int sl = 0; sl < NS; ++sl) {
@@ -892,7 +898,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_gemm_kernel(
       const int row = f * 16 + 4 * (lane >> 4) + r;
       float v = sum[r];
       if constexpr (kRow) v = v * (xs[min(row, M - 1)] * cs);
-      if (row < M && col < N) y[(int64_t)row * N + col] = (uint16_t)bf16_rne(v);
+      if (row < M && col < N) {
+        if constexpr (kPartial)
+          part[(int64_t)blockIdx.y * slice + (int64_t)row * N + col] = v;
+        else
+          y[(int64_t)row * N + col] = (uint16_t)bf16_rne(v);
+      }
     }
   }
 }
@@ -936,14 +947,15 @@ static hipError_t launch_decode(const void *xq, const S *xs, int64_t xs_rs, int 
   if (NS == 4)
     hipLaunchKernelGGL((decode_gemm_kernel<MF, S, kRow, (MF == 1 && !kMx ? 4 : 1)>), grid,
                        dim3(kDecThreads), lds, stream, a, xs, xs_rs, xs_ks, b, ws, (int)M, N, K,
-                       out);
+                       out, nullptr, (int64_t)0, 0);
   else if (NS == 2)
     hipLaunchKernelGGL((decode_gemm_kernel<MF, S, kRow, (MF == 1 ? 2 : 1)>), grid,
                        dim3(kDecThreads), lds, stream, a, xs, xs_rs, xs_ks, b, ws, (int)M, N, K,
-                       out);
+                       out, nullptr, (int64_t)0, 0);
   else
     hipLaunchKernelGGL((decode_gemm_kernel<MF, S, kRow, 1>), grid, dim3(kDecThreads), lds,
-                       stream, a, xs, xs_rs, xs_ks, b, ws, (int)M, N, K, out);
+                       stream, a, xs, xs_rs, xs_ks, b, ws, (int)M, N, K, out, nullptr,
+                       (int64_t)0, 0);
   return hipGetLastError();
 }
 
@@ -1417,11 +1429,55 @@ static int splitk_plan(int64_t M, int64_t N, int64_t K, int &kb_per, int64_t &sl
   return splits >= 2 ? splits : 0;
 }
 
+// Decode (9 <= M <= 16, fp32 scales) with long K and few columns: four
+// 16-column slabs per workgroup read x once per 64 output columns instead of
+// once per 16, and the K blocks are split over gridDim.y so that the grid
+// still fills the chip.  Used where one to two slabs per workgroup would
+// otherwise be needed to fill it (decode_slabs < 4), with at least 16 K
+// blocks per split (one per wave) and at least 192 workgroups.  Partial sums
+// as in the tiled split (fp32, reduced in split order by
+// splitk_reduce_kernel).  Measured on MI355X, 4096 x 14336 weights streamed
+// from HBM: M = 16 17.7 -> 15.6 us; at M = 1 and 4 the x reads saved
+// (1/16 and 1/4 of the weight bytes) are worth less than the second launch
+// (13.7 -> 15.1, 14.3 -> 15.4 us), hence M > 8.
+constexpr int kDecSplitMinKb = kDecWaves;
+
+static int decode_split_plan(int64_t M, int64_t N, int64_t K, int &kb_per,
+                             int64_t &slice_elems) {
+  if (M <= 8 || M > 16 || N <= 0 || K <= 0) return 0;
+  if (N > (int64_t(1) << 31) || K > (int64_t(1) << 24)) return 0;
+  const int64_t KB = K / 128;
+  if (KB * 16 * 4 > kDecMaxScaleBytes) return 0;  // as the unsplit decode path
+  if (decode_slabs(N, 4) == 4) return 0;          // four slabs already fill the chip
+  const int64_t groups = ((N + 15) / 16 + 3) / 4;
+  const int64_t sp = std::min<int64_t>(256 / groups, KB / kDecSplitMinKb);
+  if (sp < 2 || groups * sp < 192) return 0;
+  kb_per = (int)((KB + sp - 1) / sp);
+  const int splits = (int)((KB + kb_per - 1) / kb_per);
+  slice_elems = (M * N + 3) / 4 * 4;
+  return splits >= 2 ? splits : 0;
+}
+
+// The split plan of either kind; dec = true for the decode kernel's.
+template <typename S>
+static int any_split_plan(int64_t M, int64_t N, int64_t K, int &kb_per, int64_t &slice_elems,
+                          bool &dec) {
+  dec = false;
+  if constexpr (std::is_same<S, float>::value) {
+    if (M <= 16) {
+      dec = true;
+      return decode_split_plan(M, N, K, kb_per, slice_elems);
+    }
+  }
+  return splitk_plan(M, N, K, kb_per, slice_elems, std::is_same<S, uint8_t>::value);
+}
+
 template <typename S>
 static size_t splitk_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   int kb_per = 0;
   int64_t slice = 0;
-  const int splits = splitk_plan(M, N, K, kb_per, slice, std::is_same<S, uint8_t>::value);
+  bool dec = false;
+  const int splits = any_split_plan<S>(M, N, K, kb_per, slice, dec);
   return splits ? (size_t)splits * (size_t)slice * sizeof(float) : 0;
 }
 
@@ -1438,7 +1494,8 @@ static hipError_t launch_splitk(const void *xq, const S *xs, const void *wq, con
                                 size_t work_bytes, hipStream_t stream) {
   int kb_per = 0;
   int64_t slice = 0;
-  const int splits = splitk_plan(M, N, K, kb_per, slice, std::is_same<S, uint8_t>::value);
+  bool dec = false;
+  const int splits = any_split_plan<S>(M, N, K, kb_per, slice, dec);
   if (splits == 0 || work == nullptr ||
       work_bytes < (size_t)splits * (size_t)slice * sizeof(float)) {
     if constexpr (std::is_same<S, uint8_t>::value)
@@ -1446,12 +1503,27 @@ static hipError_t launch_splitk(const void *xq, const S *xs, const void *wq, con
     else
       return launch_block_gemm(xq, xs, wq, ws, M, N, K, y, stream);
   }
-  using T = Tile<2, 2, 4>;
-  const int tm = (int)((M + T::TM - 1) / T::TM), tn = (int)((N + T::TN - 1) / T::TN);
   float *part = static_cast<float *>(work);
-  hipLaunchKernelGGL((block_gemm_splitk_kernel<2, 2, 4, 2, S>), dim3((unsigned)(tm * tn * splits)),
-                     dim3(T::kThreads * 2), 0, stream, static_cast<const uint8_t *>(xq), xs,
-                     static_cast<const uint8_t *>(wq), ws, M, N, K, part, slice, tm, tn, kb_per);
+  if constexpr (std::is_same<S, float>::value) {
+    if (dec) {
+      const int64_t groups = ((N + 15) / 16 + 3) / 4;
+      const size_t lds =
+          std::max((size_t)kb_per * 16 * 4, (size_t)kDecWaves * 4 * 64 * sizeof(v4f));
+      hipLaunchKernelGGL((decode_gemm_kernel<1, float, false, 4, true>),
+                         dim3((unsigned)groups, (unsigned)splits), dim3(kDecThreads), lds, stream,
+                         static_cast<const uint8_t *>(xq), xs, K / 128, 1,
+                         static_cast<const uint8_t *>(wq), ws, (int)M, N, K, nullptr, part, slice,
+                         kb_per);
+    }
+  }
+  if (!dec) {
+    using T = Tile<2, 2, 4>;
+    const int tm = (int)((M + T::TM - 1) / T::TM), tn = (int)((N + T::TN - 1) / T::TN);
+    hipLaunchKernelGGL((block_gemm_splitk_kernel<2, 2, 4, 2, S>),
+                       dim3((unsigned)(tm * tn * splits)), dim3(T::kThreads * 2), 0, stream,
+                       static_cast<const uint8_t *>(xq), xs, static_cast<const uint8_t *>(wq), ws,
+                       M, N, K, part, slice, tm, tn, kb_per);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t n4 = std::max<int64_t>(M * N / 4, 1);

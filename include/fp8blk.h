@@ -114,7 +114,10 @@ FP8BLK_API fp8blk_status fp8_block_gemm(const void *x_q, const float *x_scale,
 
 /* The same GEMM with a caller workspace, for shapes whose grid of 128x128
  * output tiles would leave most compute units idle (small M and N, long K,
- * e.g. the DeepSeek-V3 q_a and kv_a projections at a few hundred tokens).
+ * e.g. the DeepSeek-V3 q_a and kv_a projections at a few hundred tokens),
+ * and for decode batches of 9 to 16 rows with long K (e.g. a 4096 x 14336
+ * down projection), where a workgroup covering 64 output columns over part
+ * of K re-reads less of x than one covering 16 columns over all of it.
  * The same operation and passage as fp8_block_gemm: each workgroup runs one
  * output tile over one contiguous range of K blocks, promoting each
  * 128-long partial sum with its scale pair into fp32 as fp8_block_gemm does,
@@ -123,10 +126,14 @@ FP8BLK_API fp8blk_status fp8_block_gemm(const void *x_q, const float *x_scale,
  * meets the same tolerance; it is not bit-identical to fp8_block_gemm (the
  * fp32 sums are associated differently).
  *   fp8_block_gemm_workspace_bytes(M, N, K): bytes this split needs, 0 when
- *     it is not used for these sizes: M <= 64, more than 128 output tiles of
- *     128x128, invalid sizes, or K too short for the split to gain (a time
- *     model measured on MI355X picks the number of K ranges, 2 to
- *     min(256 / tiles, K / 512), or none).  Host arithmetic only, no HIP call.
+ *     it is not used for these sizes.  17 <= M <= 64 never splits.  M > 64:
+ *     at most 128 output tiles of 128x128 and K long enough for the split
+ *     to gain (a time model measured on MI355X picks the number of K
+ *     ranges, 2 to min(256 / tiles, K / 512), or none).  9 <= M <= 16:
+ *     ceil(N / 64) column groups times the number of K ranges (at most
+ *     256 / groups and K / 2048) must reach 192, where N is too small for
+ *     ceil(N / 64) groups alone to fill the chip and K is at most 65536.
+ *     Invalid sizes: 0.  Host arithmetic only, no HIP call.
  *   fp8_block_gemm_ws: arguments as fp8_block_gemm, plus `workspace`
  *     (device, 16-byte aligned, owned by the caller, overwritten, not
  *     initialised by the caller) of `workspace_bytes` bytes.  When the

@@ -104,8 +104,23 @@ def test_gemm_validation(lib, args, want):
     (65, 1, 5120, 10 * 68 * 4),                 # slices padded to a multiple of 4 floats
     (256, 7168, 2048, 0),                       # the model gains too little (measured slower)
     (300, 576, 2048, 0),
-    (64, 1536, 7168, 0),                        # M <= 64: the decode kernel
+    (64, 1536, 7168, 0),                        # 17 <= M <= 64: the decode kernel, whole
     (4096, 1024, 4096, 0),                      # 256 tiles: the chip is full
+    # 9 <= M <= 16: decode with four 16-column slabs per workgroup, K split
+    # so that (N/64 column groups) x (splits) fills the chip
+    (16, 4096, 14336, 4 * 16 * 4096 * 4),       # Llama down: 64 groups x 4 ranges of 28
+    (9, 4096, 14336, 4 * 9 * 4096 * 4),         # M = 9: slices of 9 x 4096 floats
+    (9, 4095, 14336, 4 * (9 * 4095 + 1) * 4),   # slices padded to a multiple of 4 floats
+    (8, 4096, 14336, 0),                        # M <= 8: x is too small to be worth a split
+    (1, 4096, 14336, 0),
+    (16, 7168, 16384, 2 * 16 * 7168 * 4),       # DeepSeek-V3 o_proj: 112 groups x 2
+    (16, 4000, 8192, 4 * 16 * 4000 * 4),        # ragged last group (250 slabs)
+    (16, 4004, 8192, 4 * 16 * 4004 * 4),        # ragged last slab
+    (16, 4096, 4096, 0),                        # 16 K blocks per range would leave 128 groups
+    (16, 14336, 4096, 0),                       # four slabs already fill the chip
+    (16, 1024, 4096, 0),                        # 16 groups: too few to split
+    (17, 4096, 14336, 0),                       # two row fragments: not split
+    (16, 4096, 128 * 600, 0),                   # past the scale-staging limit of the decode kernel
     (-1, 1536, 7168, 0), (512, 1536, 100, 0), (512, 0, 7168, 0),
     ((1 << 63) - 1, 1536, 7168, 0), (512, (1 << 63) - 1, 7168, 0), (512, 1536, (1 << 62), 0),
 ])
@@ -123,6 +138,7 @@ def test_gemm_workspace_bytes(lib, M, N, K, want):
     (1000, 700, 5632, 5 * 1000 * 700 * 4),      # 44 blocks: ranges of 10 (9 rounded up), last 4
     (512, 1536, 7040, 0),                       # 55 K blocks: odd, never split
     (64, 1536, 7168, 0),
+    (16, 4096, 14336, 0),                       # the decode split is fp32-scale only
 ])
 def test_gemm_ue8m0_workspace_bytes(lib, M, N, K, want):
     lib.fp8_block_gemm_ue8m0_workspace_bytes.restype = ctypes.c_size_t

@@ -109,13 +109,24 @@ def test_linear_workspace_path(M):
 def test_linear_picks_a_path_and_agrees(N, K):
     """fb.linear passes workspaces; the library fuses for N * K <= 2^25 and
     for wide N with K <= 8192 (several slabs per workgroup: 14336 x 4096,
-    24576 x 1536) and runs two kernels for 4096 x 14336 and 7168 x 16384:
-    every path agrees with the two-launch path bit for bit at M = 16."""
+    24576 x 1536): bit for bit the two-launch path at M = 16.  For
+    4096 x 14336 and 7168 x 16384 the library plans a K split at M = 16, and
+    fb.linear runs the quantizer then fp8_block_gemm_ws: bit for bit that
+    pair of calls (the split itself is checked against the oracle in the
+    GEMM tests)."""
     x = synth.llama_activations(N + K, 16, K, 7)
     w = synth.normal_bf16(N, (N, K), 0.02)
     wq, ws = oq.weight_block_quant(w)
     xd, wqd, wsd = to_dev_bf16(x), to_dev(wq), to_dev(ws)
     y = fb.linear(xd, wqd, wsd)
-    y2 = two_launch(xd, wqd, wsd)
+    need = fb.fp8_block_gemm_workspace_bytes(16, N, K)
+    assert (need > 0) == ((N, K) in ((4096, 14336), (7168, 16384)))
+    if need:
+        xq, xs = fb.act_quant_group(xd)
+        y2 = torch.empty_like(y)
+        work = torch.empty(need, dtype=torch.uint8, device=xd.device)
+        fb.fp8_block_gemm_ws(xq, xs, wqd, wsd, y2, work)
+    else:
+        y2 = two_launch(xd, wqd, wsd)
     torch.cuda.synchronize()
     assert np.array_equal(bf16_to_host(y), bf16_to_host(y2))

@@ -282,6 +282,51 @@ def test_gemm_split_over_workgroups_tolerance_ragged(M, N, K):
               f"split {M}x{N}x{K}")
 
 
+# Decode (9 <= M <= 16) with long K: four 16-column slabs per workgroup and the K
+# blocks split over workgroups (fp8_block_gemm_ws)
+
+@pytest.mark.parametrize("M,N,K", [(16, 4096, 8192), (16, 4096, 128 * 71), (9, 4000, 8192),
+                                   (11, 4004, 8192), (13, 4040, 8320), (16, 3072, 8192)])
+def test_decode_split_exact(M, N, K):
+    """Integer operands with power-of-two scales (every partial sum exact in
+    fp32): the split decode GEMM must equal bf16_RNE(exact) bit for bit.
+    Ranges of 16 K blocks (4096x8192), a shorter last range (71 blocks:
+    18, 18, 18, 17), a partial last 64-column group (N = 4000) and a
+    partial last slab (N = 4004, 4040), M = 9, 11 and 13 (rows past M
+    masked)."""
+    need = fb.fp8_block_gemm_workspace_bytes(M, N, K)
+    assert need > 0, "shape must take the split decode path"
+    rng = np.random.default_rng(M * 7 + N + K)
+    xi = rng.integers(-8, 9, (M, K)); wi = rng.integers(-8, 9, (N, K))
+    xq = oe.encode(xi.astype(np.float32)); wq = oe.encode(wi.astype(np.float32))
+    KB, NB = K // 128, -(-N // 128)
+    xs = np.exp2(rng.integers(-1, 2, (M, KB))).astype(np.float32)
+    ws = np.exp2(rng.integers(0, 2, (NB, KB))).astype(np.float32)
+    say("decode split", M, N, K, "workspace", need)
+    y, _ = gpu_gemm_ws(xq, xs, wq, ws)
+    want = og.bf16_rne_bits(og.block_gemm(xq, xs, wq, ws))
+    bad = np.argwhere(y != want)
+    assert bad.size == 0, f"{len(bad)} outputs differ, first {bad[:3].tolist()}"
+
+
+@pytest.mark.parametrize("M,N,K,seed", [(16, 4096, 14336, 1), (12, 7168, 16384, 2)])
+def test_decode_split_tolerance(M, N, K, seed):
+    """Llama-3-8B down (4096 x 14336) at M = 16 and DeepSeek-V3 o_proj
+    (7168 x 16384) at M = 12 on synthetic activations: the split decode GEMM
+    against the oracle within the GEMM tolerance, and two calls give the
+    same bits (fixed reduction order)."""
+    x = synth.dsv3_activations(seed, M, K, N)
+    w = synth.normal_bf16(seed + 100, (N, K), 0.01)
+    xq, xs, wq, ws = quantized_operands(x, w)
+    assert fb.fp8_block_gemm_workspace_bytes(M, N, K) > 0
+    say("decode split", M, N, K)
+    y, _ = gpu_gemm_ws(xq, xs, wq, ws)
+    y2, _ = gpu_gemm_ws(xq, xs, wq, ws, fill=0x00)
+    assert np.array_equal(y, y2)
+    check_tol(y, og.block_gemm(xq, xs, wq, ws), og.term_magnitude(xq, xs, wq, ws),
+              f"decode split {M}x{N}x{K}")
+
+
 def test_gemm_ws_without_usable_workspace_is_fp8_block_gemm():
     """No workspace, or one byte too small: the call is fp8_block_gemm (same
     bits) and a too-small workspace is left untouched."""
