@@ -84,11 +84,13 @@ def test_moe_pieces_graph():
     _replay_and_check(step, [y], [_bits(y)], lambda: fb.swiglu_act_quant(gu))
 
 
-def test_split_k_gemm_graph():
+@pytest.mark.parametrize("M,N,K", [(512, 1536, 7168), (16, 4096, 14336)])
+def test_split_k_gemm_graph(M, N, K):
     """The K split over workgroups (two kernels through a workspace, no
-    memset) captured and replayed: every replay equals the eager bits."""
+    memset) captured and replayed, for the tiled split (DeepSeek-V3 q_a at
+    M = 512) and the decode split (Llama down at M = 16): every replay
+    equals the eager bits."""
     d = dev()
-    M, N, K = 512, 1536, 7168
     x = to_dev_bf16(synth.dsv3_activations(21, M, K, 22))
     wq, wsc = fb.weight_block_quant(to_dev_bf16(synth.normal_bf16(23, (N, K), 0.01)))
     xq, xsc = fb.act_quant_group(x)
