@@ -488,11 +488,21 @@ def pin_tolerance_report(seed=47):
     i, j = np.unravel_index(np.argmax(np.abs(y)), y.shape)
     yb[i, j] ^= 0x8000
     assert not og.tolerance_report(yb, y, S)["ok"]
-    # an error of 2% on one output well above the floor must fail
+    # an error of 3% on the output with the largest |y|/S must fail
     yb = og.bf16_rne_bits(y)
     i, j = np.unravel_index(np.argmax(np.abs(y) / S), y.shape)
     yb[i, j] = og.bf16_rne_bits(np.array([y[i, j] * 1.03]))[0]
     assert not og.tolerance_report(yb, y, S)["ok"]
+    # on the output that cancels most, an error of 2^-12 S must fail and
+    # one of 2^-14 S must pass (the allowance is 2^-13 S)
+    i, j = np.unravel_index(np.argmin(np.abs(y) / S), y.shape)
+    for err, ok in ((2.0 ** -12, False), (2.0 ** -14, True)):
+        yt = y.copy()
+        yt[i, j] += err * S[i, j]
+        yb = og.bf16_rne_bits(yt)
+        assert og.tolerance_report(yb, y, S)["ok"] == ok, (err, ok)
+    # with the sum exact, the report's S-relative error beyond bf16 is zero
+    assert og.tolerance_report(og.bf16_rne_bits(y), y, S)["acc_err_over_S"] == 0.0
 
 
 # ----------------------------------------------------------------------------

@@ -2,9 +2,10 @@
 layer against the CPU oracle (fp64 dequantize-then-matmul).
 
 Tolerance (from the library's acceptance rule): relative Frobenius error
-<= 2e-3 and per-element |y - y_hat| <= 1e-2 * max(|y_hat|, 2^-6 * S) with
+<= 2e-3 and, for every element, |y - y_hat| <= 2^-8 |y_hat| + 2^-13 S with
 S = sum_k |A||B| the magnitude of the summed terms, against the unrounded
-fp64 y_hat.  Exact pins (integer operands with
+fp64 y_hat (bf16 output rounding plus the fp8 matrix instruction's own
+truncating summation, pinned by test_gpu_mfma_accum.py).  Exact pins (integer operands with
 power-of-two scales; unit codes with distinct power-of-two scales) must be
 bit-exact against bf16_RNE of the exact value."""
 import numpy as np
@@ -16,7 +17,7 @@ import synth
 from oracle import e4m3 as oe
 from oracle import gemm as og
 from oracle import quant as oq
-from gpu_helpers import bf16_to_host, dev, host, say, to_dev, to_dev_bf16
+from gpu_helpers import assert_codes_equal, bf16_to_host, dev, host, say, to_dev, to_dev_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -160,17 +161,21 @@ def test_gemm_llama_decode(shape_index, M):
 
 
 def _sampled_rows_check(x, w, rows, what):
-    """Full GEMM on the GPU, oracle on sampled rows (outputs of one row
-    depend on that row of x only)."""
+    """Full GEMM on the GPU from bf16 x (the GPU quantizes it), oracle on
+    sampled rows: the oracle quantizes those rows of x itself (row-local),
+    the GPU's codes and scales of those rows must equal the oracle's, and
+    the GEMM outputs of those rows are checked against the oracle's GEMM of
+    the oracle's operands."""
     xd = to_dev_bf16(x)
     xq, xs = fb.act_quant_group(xd)
     wq, ws = oq.weight_block_quant(w)
     y = fb.block_gemm(xq, xs, to_dev(wq), to_dev(ws))
     torch.cuda.synchronize()
     y = bf16_to_host(y)
-    xq_h, xs_h = host(xq), host(xs)
-    want = og.block_gemm(xq_h[rows], xs_h[rows], wq, ws)
-    return check_tol(y[rows], want, og.term_magnitude(xq_h[rows], xs_h[rows], wq, ws), what)
+    oxq, oxs = oq.act_quant_group(x[rows])
+    assert_codes_equal(host(xq)[rows], host(xs)[rows], oxq, oxs, what)
+    want = og.block_gemm(oxq, oxs, wq, ws)
+    return check_tol(y[rows], want, og.term_magnitude(oxq, oxs, wq, ws), what)
 
 
 @pytest.mark.parametrize("shape_index", range(4))
@@ -415,9 +420,11 @@ def test_grouped_matches_oracle_and_per_expert_gemm(sizes, N, K):
             check_tol(ye, og.block_gemm(xq[r0:r1], xs[r0:r1], wq[e], ws[e]),
                       og.term_magnitude(xq[r0:r1], xs[r0:r1], wq[e], ws[e]), f"plain expert {e}")
             diff = np.abs(og.bf16_bits_to_f64(ye) - og.bf16_bits_to_f64(y[r0:r1]))
-            scale = np.abs(og.bf16_bits_to_f64(ye)) + 2.0 ** -6 * og.term_magnitude(
+            # both within the allowance of the same y_hat: at most twice it apart
+            yh = og.block_gemm(xq[r0:r1], xs[r0:r1], wq[e], ws[e])
+            allow = og.BF16_U * np.abs(yh) + og.ACC_TOL * og.term_magnitude(
                 xq[r0:r1], xs[r0:r1], wq[e], ws[e])
-            assert np.all(diff <= 2e-2 * scale), f"expert {e}: grouped and plain GEMM disagree"
+            assert np.all(diff <= 2 * allow), f"expert {e}: grouped and plain GEMM disagree"
 
 
 @pytest.mark.parametrize("sizes,N,K", [
@@ -461,8 +468,14 @@ def test_grouped_rows_outside_experts_untouched():
 
 @pytest.mark.parametrize("which", [0, 1])
 def test_grouped_moe_sampled(which):
-    """DeepSeek-V3 MoE share (32 experts, ragged Zipf loads) on the GPU; the
-    oracle checks 3 rows of every expert."""
+    """DeepSeek-V3 MoE share (32 experts, ragged Zipf loads) on the GPU from
+    bf16 inputs (the GPU quantizes x and every expert's weights).  For every
+    expert the oracle quantizes 3 of its rows of x and one random 128-row
+    block row of its weights itself (both quantizers are local to a row
+    group or a block, so these equal the full quantization's), the GPU's
+    codes and scales there must equal the oracle's, and the GEMM outputs at
+    those rows and 128 columns are checked against the oracle's GEMM of the
+    oracle's operands."""
     x, w, off = synth.moe_inputs(which)
     E, N, K = w.shape
     say("moe", which, x.shape, w.shape, "sizes", np.diff(off).min(), np.diff(off).max())
@@ -477,14 +490,18 @@ def test_grouped_moe_sampled(which):
     y = bf16_to_host(y)
     xq_h, xs_h, wq_h, ws_h = host(xq), host(xs), host(wq), host(ws)
     rng = np.random.default_rng(which)
-    rows, want, mag = [], [], []
+    got, want, mag = [], [], []
     for e in range(E):
         r0, r1 = int(off[e]), int(off[e + 1])
         pick = np.unique(np.concatenate([[r0, r1 - 1], rng.integers(r0, r1, 1)]))
-        want.append(og.block_gemm(xq_h[pick], xs_h[pick], wq_h[e], ws_h[e]))
-        mag.append(og.term_magnitude(xq_h[pick], xs_h[pick], wq_h[e], ws_h[e]))
-        rows.append(pick)
-    check_tol(y[np.concatenate(rows)], np.concatenate(want), np.concatenate(mag), f"moe {which}")
-    # the GPU weight quantizer agrees with the oracle on one expert
-    q0, s0 = oq.weight_block_quant(w[5])
-    assert np.array_equal(wq_h[5], q0) and np.array_equal(ws_h[5].view(np.uint32), s0.view(np.uint32))
+        oxq, oxs = oq.act_quant_group(x[pick])
+        assert_codes_equal(xq_h[pick], xs_h[pick], oxq, oxs, f"moe {which} expert {e} rows")
+        nb = int(rng.integers(0, -(-N // 128)))
+        c0, c1 = 128 * nb, min(N, 128 * nb + 128)
+        owq, ows = oq.weight_block_quant(w[e][c0:c1])
+        assert_codes_equal(wq_h[e][c0:c1], ws_h[e][nb:nb + 1], owq, ows,
+                           f"moe {which} expert {e} weight block row {nb}")
+        got.append(y[pick][:, c0:c1])
+        want.append(og.block_gemm(oxq, oxs, owq, ows))
+        mag.append(og.term_magnitude(oxq, oxs, owq, ows))
+    check_tol(np.concatenate(got), np.concatenate(want), np.concatenate(mag), f"moe {which}")

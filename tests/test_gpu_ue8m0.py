@@ -232,13 +232,18 @@ def test_gemm_ue8m0_ragged(M, N, K):
 
 
 def _sampled_rows_check(x, w, rows, what):
+    """The GPU quantizes all of x; the oracle quantizes the sampled rows
+    itself (row-local), the GPU's codes and scale bytes there must equal
+    it, and the GEMM rows are checked against the oracle's GEMM of the
+    oracle's operands."""
     xq, xe = fb.act_quant_group(to_dev_bf16(x), "ue8m0")
     wq, we = ou.weight_block_quant_ue8m0(w)
     y = bf16_to_host(fb.block_gemm(xq, xe, to_dev(wq), to_dev(we)))
     torch.cuda.synchronize()
-    xq_h, xe_h = host(xq), host(xe)
-    want = ou.block_gemm_ue8m0(xq_h[rows], xe_h[rows], wq, we)
-    return check_tol(y[rows], want, ou.term_magnitude_ue8m0(xq_h[rows], xe_h[rows], wq, we), what)
+    oxq, oxe = ou.act_quant_group_ue8m0(x[rows])
+    assert_codes_equal(host(xq)[rows], host(xe)[rows], oxq, oxe, what)
+    want = ou.block_gemm_ue8m0(oxq, oxe, wq, we)
+    return check_tol(y[rows], want, ou.term_magnitude_ue8m0(oxq, oxe, wq, we), what)
 
 
 @pytest.mark.parametrize("shape_index", range(4))
@@ -392,13 +397,20 @@ def test_grouped_ue8m0_moe_sampled():
     torch.cuda.synchronize()
     xq_h, xe_h, wq_h, we_h = host(xq), host(xe), host(wq), host(we)
     rng = np.random.default_rng(0)
-    rows, want, mag = [], [], []
+    got, want, mag = [], [], []
     for e in range(E):
+        # the oracle quantizes 3 rows of x and one 128-row weight block row
+        # of every expert itself; the GPU's codes there must equal it
         r0, r1 = int(off[e]), int(off[e + 1])
         pick = np.unique(np.concatenate([[r0, r1 - 1], rng.integers(r0, r1, 1)]))
-        want.append(ou.block_gemm_ue8m0(xq_h[pick], xe_h[pick], wq_h[e], we_h[e]))
-        mag.append(ou.term_magnitude_ue8m0(xq_h[pick], xe_h[pick], wq_h[e], we_h[e]))
-        rows.append(pick)
-    check_tol(y[np.concatenate(rows)], np.concatenate(want), np.concatenate(mag), "moe ue8m0")
-    q0, s0 = ou.weight_block_quant_ue8m0(w[5])
-    assert np.array_equal(wq_h[5], q0) and np.array_equal(we_h[5], s0)
+        oxq, oxe = ou.act_quant_group_ue8m0(x[pick])
+        assert_codes_equal(xq_h[pick], xe_h[pick], oxq, oxe, f"moe ue8m0 expert {e} rows")
+        nb = int(rng.integers(0, -(-N // 128)))
+        c0, c1 = 128 * nb, min(N, 128 * nb + 128)
+        owq, owe = ou.weight_block_quant_ue8m0(w[e][c0:c1])
+        assert_codes_equal(wq_h[e][c0:c1], we_h[e][nb:nb + 1], owq, owe,
+                           f"moe ue8m0 expert {e} weight block row {nb}")
+        got.append(y[pick][:, c0:c1])
+        want.append(ou.block_gemm_ue8m0(oxq, oxe, owq, owe))
+        mag.append(ou.term_magnitude_ue8m0(oxq, oxe, owq, owe))
+    check_tol(np.concatenate(got), np.concatenate(want), np.concatenate(mag), "moe ue8m0")
