@@ -1,26 +1,33 @@
 """Benchmark of the fine-grained FP8 linear layer on one MI355X.
 
-One step = the Llama-3-8B prefill linear layers (M = 4096 tokens; q/o
-4096x4096, kv 1024x4096, gate/up 14336x4096, down 4096x14336): for each
-projection, dynamic per-token-group activation quantization of x followed
-by the block-scaled FP8 GEMM (weights quantized once, before timing).
-Inputs are resident in HBM before the timed region; two input/output sets
-(about 1 GB) are rotated between steps so that the 256 MB last-level cache
-does not hold a step's working set.
+One step = the DeepSeek-V3 dense projections at M = 8192 tokens (q_a
+7168->1536, q_b 1536->24576, kv_a 7168->576, o_proj 16384->7168, MLP up
+7168->18432 and down 18432->7168; 7.12 TFLOP): for each projection, dynamic
+per-token-group activation quantization of x followed by the block-scaled
+FP8 GEMM (weights quantized once, before timing).  This is the largest
+single-GPU workload of the library.  Inputs are resident in HBM before the
+timed region; two input/output sets are rotated between steps so that the
+256 MB last-level cache does not hold a step's working set.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 30] [--no-cpu-baseline]
+Before it, the same measurement runs on the Llama-3-8B prefill linear layers
+(M = 4096; q/o 4096x4096, kv 1024x4096, gate/up 14336x4096, down
+4096x14336), reported under ``llama_prefill``.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 10] [--no-cpu-baseline]
                     [--rows]  (also time weight quant, decode, MoE (grouped
-                               and batched layouts), the power-of-two (UE8M0),
-                               static-activation-scale and row-wise (fp8r) rows)
+                               and batched layouts), the DeepSeek-V3 shapes
+                               at M = 512, the tiny configuration, the
+                               power-of-two (UE8M0), static-activation-scale
+                               and row-wise (fp8r) rows)
 
 Prints one JSON line.  ``value`` is the whole step's throughput in TFLOP/s
-(GEMM FLOPs of the four projections / step time, the activation
-quantization included); ``roofline`` is for the GEMM kernel alone (FLOPs /
-its average launch time measured with HIP events on the launch stream,
-against the dense fp8 MFMA peak); ``ceilings`` gives what the matrix cores
-sustain on this chip with operands in registers (plain fp8 MFMAs, and the
-same with the GEMM's fp32 promotion FMAs), as context for that fraction;
-``cpu_baseline`` times the CPU oracle on one whole step.
+(GEMM FLOPs of the six projections / step time, the activation
+quantization included); ``roofline`` is for the GEMM kernels alone (FLOPs /
+their launch times measured with HIP events on the launch stream, against
+the dense fp8 MFMA peak); ``ceilings`` gives what the matrix cores sustain
+on this chip with operands in registers (plain fp8 MFMAs, and the same with
+the GEMM's fp32 promotion FMAs), as context for that fraction;
+``cpu_baseline`` times the CPU oracle on a row sample of the step.
 """
 from __future__ import annotations
 
@@ -39,17 +46,18 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 M_PREFILL = 4096
 PREFILL_SHAPES = (("qo", 4096, 4096), ("kv", 1024, 4096), ("gate_up", 14336, 4096),
                   ("down", 4096, 14336))
+M_DSV3 = 8192
+DSV3_SHAPES = (("q_a", 1536, 7168), ("q_b", 24576, 1536), ("kv_a", 576, 7168),
+               ("o_proj", 7168, 16384), ("mlp_up", 18432, 7168), ("mlp_down", 7168, 18432))
+CPU_SAMPLE_ROWS = 256    # rows of each DeepSeek-V3 projection the oracle runs
 ACT_BYTES_PER_ELEM = 2 + 1 + 4 / 128   # bf16 in, e4m3 out, one fp32 scale per 128
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    # the first ~20 steps of a fresh process run up to 20 % slower while the
-    # device ramps up (measured); 30 untimed steps put the timed ones in the
-    # steady state
-    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rows", action="store_true", help="also time the other hot-path rows")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -58,7 +66,7 @@ def parse():
 
 
 GEMM_SOURCE = os.path.join(ROOT, "block_scaled_fp8_act_amd", "csrc", "gemm_kernels.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "block_gemm_llama_prefill_traffic.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "block_gemm_dsv3_m8192_traffic.md")
 
 
 def source_digest(path):
@@ -100,12 +108,34 @@ def gen_inputs(torch, dev, seed):
     return xs, ws
 
 
+def gen_inputs_dsv3(torch, dev, seed):
+    """Seeded synthetic DeepSeek-V3-shaped inputs generated on the device:
+    x ~ N(0,1) with 0.5 % of entries (i.i.d. positions) replaced by
+    10 * t(3) (Student t with 3 degrees of freedom, drawn as Z / sqrt(V/3)
+    with V a sum of three squared normals); W ~ N(0, 0.01); both bf16."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    xs, ws = [], []
+    for name, N, K in DSV3_SHAPES:
+        x = torch.randn((M_DSV3, K), generator=g, device=dev, dtype=torch.float32)
+        mask = torch.rand((M_DSV3, K), generator=g, device=dev) < 0.005
+        n = int(mask.sum())
+        z = torch.randn(n, generator=g, device=dev)
+        v = torch.randn((n, 3), generator=g, device=dev).square().sum(1)
+        x[mask] = 10.0 * z / torch.sqrt(v / 3.0)
+        xs.append(x.to(torch.bfloat16))
+        del x, mask
+        ws.append((torch.randn((N, K), generator=g, device=dev, dtype=torch.float32) * 0.01)
+                  .to(torch.bfloat16))
+    return xs, ws
+
+
 def cpu_baseline():
-    """The CPU oracle (as it stands) on one whole step of the workload: for
-    each Llama-3-8B projection at M = 4096, activation quantization + fp64
-    dequantize-then-matmul (weights quantized beforehand, as on the GPU).
-    Returns step TFLOP/s (GEMM FLOPs of the step / oracle time) and the BLAS
-    thread count."""
+    """The CPU oracle (as it stands) on a row sample of the step: for each
+    DeepSeek-V3 projection, activation quantization + fp64
+    dequantize-then-matmul of CPU_SAMPLE_ROWS rows (weights quantized
+    beforehand, as on the GPU; same input distributions).  Returns TFLOP/s
+    (GEMM FLOPs of the sample / oracle time) and the BLAS thread count."""
     import numpy as np
     import synth
     from oracle import gemm as og
@@ -116,15 +146,16 @@ def cpu_baseline():
     except Exception:  # pragma: no cover
         threads = 1
     dt, flops = 0.0, 0.0
-    for i, (_, N, K) in enumerate(PREFILL_SHAPES):
-        x = synth.llama_x(i, M_PREFILL, config=3)
-        wq, ws = oq.weight_block_quant(synth.llama_weight(i))
+    for i, (_, N, K) in enumerate(DSV3_SHAPES):
+        x, w = synth.dsv3_inputs(i, CPU_SAMPLE_ROWS)
+        wq, ws = oq.weight_block_quant(w)
+        del w
         t0 = time.perf_counter()
         xq, xs = oq.act_quant_group(x)
         y = og.block_gemm(xq, xs, wq, ws)
         dt += time.perf_counter() - t0
         og.bf16_rne_bits(y)
-        flops += 2.0 * M_PREFILL * N * K
+        flops += 2.0 * CPU_SAMPLE_ROWS * N * K
         del x, wq, ws, xq, xs, y
     cpu = "unknown CPU"
     try:
@@ -133,9 +164,65 @@ def cpu_baseline():
     except Exception:  # pragma: no cover
         pass
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"one whole step (the four projections at M={M_PREFILL}): act quant + fp64 "
-                      f"dequantize-then-matmul, {dt:.1f} s on {cpu} "
+            "sample": f"{CPU_SAMPLE_ROWS} of the {M_DSV3} rows of each of the six DeepSeek-V3 "
+                      f"projections ({flops / 1e12:.3f} TFLOP, 1/{M_DSV3 // CPU_SAMPLE_ROWS} of "
+                      f"the step): act quant + fp64 dequantize-then-matmul, {dt:.1f} s on {cpu} "
                       f"({len(os.sched_getaffinity(0))} CPUs in the affinity mask)"}
+
+
+def linear_leg(torch, fb, dev, stream, shapes, M, xs0, ws_bf16, steps, warmup):
+    """Time a step of linear layers: for each (name, N, K) of `shapes`, the
+    activation quantizer on x [M, K] then the block-scaled GEMM against the
+    quantized weight, two rotated input sets.  Returns (ms_per_step,
+    per-projection act-quant and GEMM times in s, GEMM FLOPs of the step,
+    act-quant bytes of the step)."""
+    sets = [xs0, [torch.roll(x, 1, 0) for x in xs0]]
+    wq, wsc = [], []
+    for w in ws_bf16:
+        q, s = fb.weight_block_quant(w)
+        wq.append(q); wsc.append(s)
+    outs = [[(torch.empty((M, K), dtype=torch.uint8, device=dev),
+              torch.empty((M, K // 128), dtype=torch.float32, device=dev),
+              torch.empty((M, N), dtype=torch.bfloat16, device=dev))
+             for (_, N, K) in shapes] for _ in sets]
+    torch.cuda.synchronize()
+
+    def launch(i, p, ev):
+        xq, xsc, y = outs[i % 2][p]
+        if ev is not None:
+            ev[0].record(stream)
+        fb.fp8_act_quant_group(sets[i % 2][p], xq, xsc)
+        if ev is not None:
+            ev[1].record(stream)
+        fb.fp8_block_gemm(xq, xsc, wq[p], wsc[p], y)
+        if ev is not None:
+            ev[2].record(stream)
+
+    wall, act_s, gemm_s = run_leg(torch, stream, launch, len(shapes), steps, warmup)
+    flops = sum(2.0 * M * N * K for (_, N, K) in shapes)
+    act_bytes = sum(M * K * ACT_BYTES_PER_ELEM for (_, N, K) in shapes)
+    del sets, outs, wq, wsc
+    return wall, act_s, gemm_s, flops, act_bytes
+
+
+def leg_summary(shapes, M, wall, act_s, gemm_s, flops, act_bytes):
+    gemm_tflops = flops / sum(gemm_s) / 1e12
+    act_gbs = act_bytes / sum(act_s) / 1e9
+    return {
+        "ms_per_step": round(wall * 1e3, 4),
+        "TFLOP/s": round(flops / wall / 1e12, 2),
+        "gemm": {"achieved": round(gemm_tflops, 2), "unit": "TFLOP/s",
+                 "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4)},
+        "act_quant": {"achieved": round(act_gbs, 1), "unit": "GB/s",
+                      "frac": round(act_gbs / PEAK_HBM_GBS, 4)},
+        "per_projection": {
+            name: {"act_quant_us": round(act_s[p] * 1e6, 2),
+                   "act_quant_GB/s": round(M * K * ACT_BYTES_PER_ELEM / act_s[p] / 1e9, 1),
+                   "gemm_us": round(gemm_s[p] * 1e6, 2),
+                   "gemm_TFLOP/s": round(2.0 * M * N * K / gemm_s[p] / 1e12, 1),
+                   "gemm_frac": round(2.0 * M * N * K / gemm_s[p] / 1e12 / PEAK_FP8_TFLOPS, 4)}
+            for p, (name, N, K) in enumerate(shapes)},
+    }
 
 
 def main():
@@ -149,56 +236,27 @@ def main():
     import block_scaled_fp8_act_amd as fb
 
     if not os.path.exists(fb.lib_path()):
-        from block_scaled_fp8_act_amd import build
-        build.build()
+        raise RuntimeError("libfp8blk.so is not built (python -m block_scaled_fp8_act_amd.build)")
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
 
-    # --- inputs (resident before timing) ---------------------------------
+    # --- Llama-3-8B prefill (reported beside the headline) ------------------
     xs0, ws_bf16 = gen_inputs(torch, dev, 3000)
-    sets = [xs0, [torch.roll(x, 1, 0) for x in xs0]]            # two rotated input sets
-    wq, wsc = [], []
-    for w in ws_bf16:
-        q, s = fb.weight_block_quant(w)
-        wq.append(q); wsc.append(s)
-    outs = []
-    for _ in sets:
-        o = []
-        for (name, N, K) in PREFILL_SHAPES:
-            o.append((torch.empty((M_PREFILL, K), dtype=torch.uint8, device=dev),
-                      torch.empty((M_PREFILL, K // 128), dtype=torch.float32, device=dev),
-                      torch.empty((M_PREFILL, N), dtype=torch.bfloat16, device=dev)))
-        outs.append(o)
-    del ws_bf16
-    torch.cuda.synchronize()
+    llama = leg_summary(PREFILL_SHAPES, M_PREFILL,
+                        *linear_leg(torch, fb, dev, stream, PREFILL_SHAPES, M_PREFILL, xs0,
+                                    ws_bf16, args.steps, args.warmup))
+    del xs0, ws_bf16
 
-    n_proj = len(PREFILL_SHAPES)
-    gemm_flops = [2.0 * M_PREFILL * N * K for (_, N, K) in PREFILL_SHAPES]
-    act_bytes = [M_PREFILL * K * ACT_BYTES_PER_ELEM for (_, N, K) in PREFILL_SHAPES]
-
-    def launch(i, p, ev):
-        xq, xsc, y = outs[i % 2][p]
-        if ev is not None:
-            ev[0].record(stream)
-        fb.fp8_act_quant_group(sets[i % 2][p], xq, xsc)
-        if ev is not None:
-            ev[1].record(stream)
-        fb.fp8_block_gemm(xq, xsc, wq[p], wsc[p], y)
-        if ev is not None:
-            ev[2].record(stream)
-
-    # --- timed region: whole steps (then the same steps with events) -------
-    wall, act_s, gemm_s = run_leg(torch, stream, launch, n_proj, args.steps, args.warmup)
-    ms_per_step = wall * 1e3
-    act_t = [t * 1e3 for t in act_s]
-    gemm_t = [t * 1e3 for t in gemm_s]
-
-    step_flops = sum(gemm_flops)
-    gemm_ms = sum(gemm_t)
-    act_ms = sum(act_t)
-    gemm_tflops = step_flops / (gemm_ms * 1e-3) / 1e12
-    act_gbs = sum(act_bytes) / (act_ms * 1e-3) / 1e9
-    value = step_flops / (ms_per_step * 1e-3) / 1e12
+    # --- headline: DeepSeek-V3 dense projections at M = 8192 ---------------
+    xs0, ws_bf16 = gen_inputs_dsv3(torch, dev, 4000)
+    wall, act_s, gemm_s, step_flops, act_bytes = linear_leg(
+        torch, fb, dev, stream, DSV3_SHAPES, M_DSV3, xs0, ws_bf16, args.steps, args.warmup)
+    del xs0, ws_bf16
+    torch.cuda.empty_cache()
+    head = leg_summary(DSV3_SHAPES, M_DSV3, wall, act_s, gemm_s, step_flops, act_bytes)
+    gemm_tflops = step_flops / sum(gemm_s) / 1e12
+    act_gbs = act_bytes / sum(act_s) / 1e9
+    value = step_flops / wall / 1e12
 
     out = {
         "metric": "fp8_block_gemm TFLOP/s (% dense-fp8 MFMA peak); act-quant GB/s (% HBM)",
@@ -207,27 +265,29 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": round(wall * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp8_e4m3 x fp8_e4m3 -> fp32 accumulate, bf16 out",
-        "data": "synthetic (seeded; Llama-3-8B projection shapes, x ~ N(0,1) with 1% channels x20, W ~ N(0,0.02))",
-        "config": {"workload": "Llama-3-8B prefill linear layers: act quant + block-scaled FP8 GEMM",
-                   "M": M_PREFILL, "shapes_NxK": [[N, K] for (_, N, K) in PREFILL_SHAPES],
+        "data": "synthetic (seeded; DeepSeek-V3 dense projection shapes, x ~ N(0,1) with 0.5% "
+                "entries 10*t(3), W ~ N(0,0.01))",
+        "config": {"workload": "DeepSeek-V3 dense projections at M=8192: act quant + "
+                               "block-scaled FP8 GEMM per projection",
+                   "M": M_DSV3, "shapes_NxK": [[N, K] for (_, N, K) in DSV3_SHAPES],
                    "block": 128, "parallelism": "single GPU"},
         "roofline": {
             "bound": "mfma",
-            "kernel": "block-scaled GEMM: block_gemm_kernel (q/o, gate/up, down), "
-                      "block_gemm_ks_kernel (kv)",
+            "kernel": "block-scaled GEMM (block_gemm_kernel; kv_a 576 columns: the 128x128 tile)",
             "achieved": round(gemm_tflops, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
             "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4), "traffic": measured_traffic(),
-            "traffic_unit": "HBM bytes per launch (mean over the 4 projections)",
+            "traffic_unit": "HBM bytes per launch (mean over the 6 projections)",
+            "algorithmic": "2*M*N*K FLOP per launch, summed over the six projections",
         },
         "act_quant": {"achieved": round(act_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                       "frac": round(act_gbs / PEAK_HBM_GBS, 4), "bound": "hbm"},
-        "per_projection_us": {name: {"act_quant": round(act_t[p] * 1e3, 2), "gemm": round(gemm_t[p] * 1e3, 2)}
-                              for p, (name, _, _) in enumerate(PREFILL_SHAPES)},
+        "per_projection": head["per_projection"],
+        "llama_prefill": llama,
     }
     out["act_quant"]["standalone"] = act_quant_alone(torch, fb, dev, stream)
     out["ceilings"] = ceilings(torch, stream, gemm_tflops)
@@ -558,25 +618,61 @@ def other_rows(torch, fb, dev, stream):
         "us": round(t1 * 1e6, 2), "GB/s": round(byts / t1 / 1e9, 1),
         "torch_swiglu_then_act_quant_us": round(t2 * 1e6, 2)}
     del gus, xq, xsc, h
-    # DeepSeek-V3 q_a and kv_a at M = 512 (48 and 20 tiles of 128x128 for
-    # 256 CUs): fp8_block_gemm against the K split over workgroups
-    # (fp8_block_gemm_ws, its workspace allocated once before timing)
+    # DeepSeek-V3 dense projections at M = 512: act quant + GEMM per shape;
+    # where the library plans a K split over workgroups (small grids), the
+    # plain GEMM beside the split one (its workspace allocated before timing)
     M = 512
-    for name, N, K in (("q_a", 1536, 7168), ("kv_a", 576, 7168)):
+    for name, N, K in DSV3_SHAPES:
         x = torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16)
         xq, xsc = fb.act_quant_group(x)
         wq, wsc = fb.weight_block_quant(
             (torch.randn((N, K), generator=g, device=dev) * 0.01).to(torch.bfloat16))
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        work = torch.empty(fb.fp8_block_gemm_workspace_bytes(M, N, K), dtype=torch.uint8,
-                           device=dev)
+        need = fb.fp8_block_gemm_workspace_bytes(M, N, K)
+        work = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        ta = _time(torch, stream, lambda: fb.fp8_act_quant_group(x, xq, xsc))
         t0 = _time(torch, stream, lambda: fb.fp8_block_gemm(xq, xsc, wq, wsc, y))
-        t1 = _time(torch, stream, lambda: fb.fp8_block_gemm_ws(xq, xsc, wq, wsc, y, work))
         fl = 2.0 * M * N * K
-        rows[f"dsv3_{name}_M512_split_k"] = {
-            "plain_us": round(t0 * 1e6, 2), "split_us": round(t1 * 1e6, 2),
-            "split_TFLOP/s": round(fl / t1 / 1e12, 1), "workspace_MB": round(work.numel() / 1e6, 2)}
+        r = {"act_quant_us": round(ta * 1e6, 2), "gemm_us": round(t0 * 1e6, 2),
+             "gemm_TFLOP/s": round(fl / t0 / 1e12, 1),
+             "gemm_frac": round(fl / t0 / 1e12 / PEAK_FP8_TFLOPS, 4)}
+        if need:
+            t1 = _time(torch, stream, lambda: fb.fp8_block_gemm_ws(xq, xsc, wq, wsc, y, work))
+            r.update({"split_us": round(t1 * 1e6, 2), "split_TFLOP/s": round(fl / t1 / 1e12, 1),
+                      "split_frac": round(fl / t1 / 1e12 / PEAK_FP8_TFLOPS, 4),
+                      "workspace_MB": round(need / 1e6, 2)})
+        rows[f"dsv3_{name}_M512"] = r
         del x, xq, xsc, wq, wsc, y, work
+    # the tiny configuration (x[16,512], W[512,512]): one linear layer
+    xt = torch.randn((16, 512), generator=g, device=dev).to(torch.bfloat16)
+    wq, wsc = fb.weight_block_quant(torch.randn((512, 512), generator=g, device=dev).to(torch.bfloat16))
+    yt = torch.empty((16, 512), dtype=torch.bfloat16, device=dev)
+    xq = torch.empty((16, 512), dtype=torch.uint8, device=dev)
+    xsc = torch.empty((16, 4), dtype=torch.float32, device=dev)
+    t1 = _time(torch, stream, lambda: fb.fp8_linear(xt, wq, wsc, yt), iters=100)
+
+    def two_tiny():
+        fb.fp8_act_quant_group(xt, xq, xsc)
+        fb.fp8_block_gemm(xq, xsc, wq, wsc, yt)
+    t2 = _time(torch, stream, two_tiny, iters=100)
+    rows["tiny_16x512x512"] = {"fp8_linear_us": round(t1 * 1e6, 2), "two_launch_us": round(t2 * 1e6, 2)}
+    # decode K split (four slabs per workgroup, K over workgroups) against
+    # the unsplit decode GEMM: DeepSeek-V3 o_proj at M = 16 and Llama down
+    # at M = 9, 12, 16; weights rotated through HBM
+    for name, N, K, Ms in (("dsv3_o_proj", 7168, 16384, (16,)), ("llama_down", 4096, 14336, (9, 12, 16))):
+        wq, wsc = fb.weight_block_quant((torch.randn((N, K), generator=g, device=dev) * 0.01).to(torch.bfloat16))
+        copies = _weight_copies(wq, wsc)
+        for Md in Ms:
+            x = torch.randn((Md, K), generator=g, device=dev).to(torch.bfloat16)
+            xq, xsc = fb.act_quant_group(x)
+            y = torch.empty((Md, N), dtype=torch.bfloat16, device=dev)
+            need = fb.fp8_block_gemm_workspace_bytes(Md, N, K)
+            work = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+            tp = _time(torch, stream, _rotating(copies, lambda w, s: fb.fp8_block_gemm(xq, xsc, w, s, y)))
+            ts = _time(torch, stream, _rotating(copies, lambda w, s: fb.fp8_block_gemm_ws(xq, xsc, w, s, y, work)))
+            rows[f"decode_split_{name}_M{Md}"] = {"plain_us": round(tp * 1e6, 2),
+                                                  "split_us": round(ts * 1e6, 2), "planned": bool(need)}
+        del copies
     return rows
 
 
