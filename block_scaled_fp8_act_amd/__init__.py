@@ -56,7 +56,7 @@ __all__ = [
     "Fp8BlkError", "BLOCK", "lib_path", "load_library", "status_string",
     "fp8_weight_block_quant", "fp8_act_quant_group", "fp8_block_gemm",
     "fp8_grouped_block_gemm", "fp8_block_gemm_ws", "fp8_block_gemm_workspace_bytes",
-    "fp8_block_gemm_ue8m0_ws",
+    "fp8_block_gemm_ue8m0_ws", "fp8_block_gemm_noalloc", "SCRATCH_BYTES",
     "fp8_weight_block_quant_ue8m0", "fp8_act_quant_group_ue8m0",
     "fp8_block_gemm_ue8m0", "fp8_grouped_block_gemm_ue8m0", "fp8_act_quant_static",
     "fp8_block_gemm_static", "act_quant_static", "block_gemm_static", "linear_static",
@@ -72,7 +72,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "lib", "libfp8blk.so")
 _lib = None
 
-OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DEVICE, ERR_LAUNCH = range(6)
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DEVICE, ERR_LAUNCH, ERR_SCRATCH = range(7)
+SCRATCH_BYTES = 16 * 1024 * 1024 + 64 * 1024     # FP8BLK_SCRATCH_BYTES
 
 
 class Fp8BlkError(RuntimeError):
@@ -105,6 +106,7 @@ def load_library() -> ctypes.CDLL:
         "fp8_act_quant_group": [vp, i64, i64, vp, vp, vp],
         "fp8_block_gemm": [vp, vp, vp, vp, i64, i64, i64, vp, vp],
         "fp8_block_gemm_ws": [vp, vp, vp, vp, i64, i64, i64, vp, vp, ctypes.c_size_t, vp],
+        "fp8_block_gemm_noalloc": [vp, vp, vp, vp, i64, i64, i64, vp, vp],
         "fp8_grouped_block_gemm": [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp, vp],
         "fp8_linear": [vp, i64, i64, i64, vp, vp, vp, vp, vp, vp],
         "fp8_batched_block_gemm": [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp, vp],
@@ -252,6 +254,12 @@ def fp8_act_quant_group(x, x_q, x_scale):
 
 def fp8_block_gemm(x_q, x_scale, w_q, w_scale, y):
     _gemm("fp8_block_gemm", _F32, x_q, x_scale, w_q, w_scale, y)
+
+
+def fp8_block_gemm_noalloc(x_q, x_scale, w_q, w_scale, y):
+    """fp8_block_gemm_ws with the library's own device scratch: no
+    workspace, no allocation (callers that cannot allocate)."""
+    _gemm("fp8_block_gemm_noalloc", _F32, x_q, x_scale, w_q, w_scale, y)
 
 
 def fp8_block_gemm_workspace_bytes(M, N, K, scale_fmt="float"):

@@ -117,6 +117,7 @@ const char *fp8blk_status_string(int s) {
     case FP8BLK_ERR_ALIGN: return "FP8BLK_ERR_ALIGN: a base pointer is not 16-byte aligned";
     case FP8BLK_ERR_DEVICE: return "FP8BLK_ERR_DEVICE: no usable device, or the current device is not gfx950";
     case FP8BLK_ERR_LAUNCH: return "FP8BLK_ERR_LAUNCH: kernel launch failed";
+    case FP8BLK_ERR_SCRATCH: return "FP8BLK_ERR_SCRATCH: the call needs more device scratch than the library holds (FP8BLK_SCRATCH_BYTES)";
     default: return "FP8BLK_ERR_UNKNOWN";
   }
 }
@@ -200,6 +201,18 @@ fp8blk_status fp8_block_gemm_static(const void *x_q, const float *x_scale, const
   if (M == 0 || N == 0) return FP8BLK_OK;
   return launched(fp8blk::launch_block_gemm_static(x_q, x_scale, w_q, w_scale, M, N, K, y_bf16,
                                                    static_cast<hipStream_t>(stream)));
+}
+
+fp8blk_status fp8_block_gemm_noalloc(const void *x_q, const float *x_scale, const void *w_q,
+                                     const float *w_scale, int64_t M, int64_t N, int64_t K,
+                                     void *y_bf16, void *stream) {
+  static_assert(fp8blk::kScratchBytes == FP8BLK_SCRATCH_BYTES, "scratch size out of step");
+  if (fp8blk_status c = check_gemm(x_q, x_scale, w_q, w_scale, M, N, K, y_bf16, 16, 16)) return c;
+  if (M == 0 || N == 0) return FP8BLK_OK;
+  if (fp8blk::block_gemm_workspace_bytes(M, N, K) > fp8blk::kScratchBytes)
+    return FP8BLK_ERR_SCRATCH;
+  return launched(fp8blk::launch_block_gemm_noalloc(x_q, x_scale, w_q, w_scale, M, N, K, y_bf16,
+                                                    static_cast<hipStream_t>(stream)));
 }
 
 fp8blk_status fp8_linear(const void *x_bf16, int64_t M, int64_t N, int64_t K, const void *w_q,

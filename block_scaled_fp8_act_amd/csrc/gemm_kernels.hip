@@ -26,6 +26,7 @@
 // 32 K values; a 128-block scale is simply the same byte for all four), and
 // adds into the fp32 accumulator -- no per-block partials, no promotion FMAs.
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "fp8blk_device.h"
@@ -1537,6 +1538,46 @@ hipError_t launch_block_gemm_ws(const void *xq, const float *xs, const void *wq,
                                 int64_t M, int64_t N, int64_t K, void *y, void *work,
                                 size_t work_bytes, hipStream_t stream) {
   return launch_splitk<float>(xq, xs, wq, ws, M, N, K, y, work, work_bytes, stream);
+}
+
+// Device scratch for the K split of fp8_block_gemm_noalloc (callers that
+// cannot allocate: graph capture, tight serving loops).  One copy per GPU,
+// held until the process ends.  Its size covers every split plan: a tiled
+// plan has at most 128 tiles of 128x128 and at most 256 / tiles ranges
+// (<= 256 * 128 * 128 fp32 = 16 MiB, plus the rounding of slices to 4
+// elements), a decode plan at most 1 MiB.  In host code `scratch` only
+// names the symbol; its device address comes from hipGetSymbolAddress,
+// taken once per device with that device current.
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+static std::mutex g_scratch_mu;
+static void *g_scratch_addr[kScratchMaxDevices];
+
+hipError_t scratch_address(void **addr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_addr[dev] == nullptr) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_addr[dev] = p;
+  }
+  *addr = g_scratch_addr[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_block_gemm_noalloc(const void *xq, const float *xs, const void *wq,
+                                     const float *ws, int64_t M, int64_t N, int64_t K, void *y,
+                                     hipStream_t stream) {
+  if (block_gemm_workspace_bytes(M, N, K) == 0)
+    return launch_block_gemm(xq, xs, wq, ws, M, N, K, y, stream);
+  void *p = nullptr;
+  hipError_t e = scratch_address(&p);
+  if (e != hipSuccess) return e;
+  return launch_block_gemm_ws(xq, xs, wq, ws, M, N, K, y, p, kScratchBytes, stream);
 }
 
 hipError_t launch_block_gemm_e8m0_ws(const void *xq, const uint8_t *xs, const void *wq,

@@ -73,7 +73,8 @@ typedef enum {
     FP8BLK_ERR_SHAPE = 2,   /* negative size, K % 128 != 0, size over limit  */
     FP8BLK_ERR_ALIGN = 3,   /* a base pointer is not 16-byte aligned         */
     FP8BLK_ERR_DEVICE = 4,  /* no device, or the current device is not gfx950 */
-    FP8BLK_ERR_LAUNCH = 5   /* the kernel launch failed                      */
+    FP8BLK_ERR_LAUNCH = 5,  /* the kernel launch failed                      */
+    FP8BLK_ERR_SCRATCH = 6  /* more device scratch needed than the library holds */
 } fp8blk_status;
 
 #define FP8BLK_BLOCK 128
@@ -148,6 +149,28 @@ FP8BLK_API fp8blk_status fp8_block_gemm_ws(const void *x_q, const float *x_scale
                                            int64_t M, int64_t N, int64_t K, void *y_bf16,
                                            void *workspace, size_t workspace_bytes,
                                            void *stream);
+
+/* fp8_block_gemm_ws without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same operation, plan and kernels as
+ * fp8_block_gemm_ws given a large enough workspace (bit-identical output);
+ * the K split's fp32 partial sums go to a device array inside the library
+ * of FP8BLK_SCRATCH_BYTES bytes, one per GPU, held until the process ends,
+ * whose address is looked up once per device on the first call made with
+ * that device current.  Allocates nothing.
+ *   Arguments and errors as fp8_block_gemm; FP8BLK_ERR_SCRATCH if the split
+ *   would need more than FP8BLK_SCRATCH_BYTES (no valid size does today:
+ *   the largest plan is 16 MiB plus a few bytes).
+ *   All calls on one GPU share its scratch array, which keeps the last
+ *   call's contents (the split writes every partial it reads, so nothing
+ *   needs clearing): calls that may overlap on one GPU (different streams,
+ *   no ordering between them) race on it and must be serialised by the
+ *   caller. */
+#define FP8BLK_SCRATCH_BYTES ((size_t)16 * 1024 * 1024 + (size_t)64 * 1024)
+FP8BLK_API fp8blk_status fp8_block_gemm_noalloc(const void *x_q, const float *x_scale,
+                                                const void *w_q, const float *w_scale,
+                                                int64_t M, int64_t N, int64_t K,
+                                                void *y_bf16, void *stream);
 
 /* Grouped block-scaled FP8 GEMM for mixture-of-experts layers: expert e
  * multiplies rows [off[e], off[e+1]) of x by its own W[e].  "Fine-grained

@@ -47,7 +47,7 @@ def test_internal_symbols_hidden(lib):
 
 def test_status_strings(lib):
     import block_scaled_fp8_act_amd as fb
-    for code in range(6):
+    for code in range(7):
         assert fb.status_string(code).startswith("FP8BLK_")
     assert fb.status_string(99) == "FP8BLK_ERR_UNKNOWN"
     assert lib.fp8blk_abi_version() == 1
@@ -365,3 +365,31 @@ def test_ceiling_library_exports_and_checks_arguments():
     assert f(1, A, None, 8, 0, None) == -1
     assert f(-1, A, None, 8, 8, None) == -1
     assert f(4, A, A, 8, 8, None) == -1
+
+
+def test_noalloc_scratch_covers_every_split_plan(lib):
+    """fp8_block_gemm_noalloc keeps the K split's partial sums in a device
+    array of FP8BLK_SCRATCH_BYTES: no split plan may need more (tiled plans
+    over M > 64 and decode plans over 9 <= M <= 16, scanned over sizes)."""
+    import block_scaled_fp8_act_amd as fb
+    header = open(HEADER).read()
+    m = re.search(r"#define FP8BLK_SCRATCH_BYTES \(\(size_t\)16 \* 1024 \* 1024 \+ \(size_t\)64 \* 1024\)", header)
+    assert m and fb.SCRATCH_BYTES == 16 * 1024 * 1024 + 64 * 1024
+    worst = 0
+    for K in (512, 1024, 2048, 4096, 7168, 14336, 18432, 32768, 65536):
+        for M in list(range(9, 17)) + list(range(65, 2100, 37)):
+            for N in list(range(1, 4200, 97)) + [576, 1536, 7168, 16384]:
+                worst = max(worst, lib.fp8_block_gemm_workspace_bytes(M, N, K))
+    assert 0 < worst <= fb.SCRATCH_BYTES, worst
+
+
+def test_noalloc_validates_before_the_device(lib):
+    st = lib.fp8_block_gemm_noalloc(A, B, C, D, -1, 64, 128, E_, None)
+    assert st == 2
+    st = lib.fp8_block_gemm_noalloc(A, B, C, D, 64, 64, 100, E_, None)
+    assert st == 2
+    st = lib.fp8_block_gemm_noalloc(A + 4, B, C, D, 64, 64, 128, E_, None)
+    assert st == 3
+    st = lib.fp8_block_gemm_noalloc(None, B, C, D, 64, 64, 128, E_, None)
+    assert st == 1
+    assert lib.fp8_block_gemm_noalloc(A, B, C, D, 0, 64, 128, E_, None) in (0, 4)
