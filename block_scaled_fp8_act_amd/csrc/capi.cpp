@@ -209,7 +209,7 @@ fp8blk_status fp8_block_gemm_noalloc(const void *x_q, const float *x_scale, cons
   static_assert(fp8blk::kScratchBytes == FP8BLK_SCRATCH_BYTES, "scratch size out of step");
   if (fp8blk_status c = check_gemm(x_q, x_scale, w_q, w_scale, M, N, K, y_bf16, 16, 16)) return c;
   if (M == 0 || N == 0) return FP8BLK_OK;
-  if (fp8blk::block_gemm_workspace_bytes(M, N, K) > fp8blk::kScratchBytes)
+  if (fp8blk::block_gemm_split_workspace_bytes(M, N, K) > fp8blk::kScratchBytes)
     return FP8BLK_ERR_SCRATCH;
   return launched(fp8blk::launch_block_gemm_noalloc(x_q, x_scale, w_q, w_scale, M, N, K, y_bf16,
                                                     static_cast<hipStream_t>(stream)));

@@ -42,7 +42,9 @@ size_t block_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_block_gemm_ws(const void *xq, const float *xs, const void *wq, const float *ws,
                                 int64_t M, int64_t N, int64_t K, void *y, void *work,
                                 size_t work_bytes, hipStream_t stream);
-// The same split through the library's own device scratch (no caller
+// Workspace of the K splits over workgroups alone (no stream-K tail).
+size_t block_gemm_split_workspace_bytes(int64_t M, int64_t N, int64_t K);
+// The same splits through the library's own device scratch (no caller
 // workspace, no allocation); the plan's workspace must fit kScratchBytes.
 constexpr size_t kScratchBytes = (size_t(16) << 20) + (size_t(64) << 10);
 constexpr int kScratchMaxDevices = 64;

@@ -1131,9 +1131,8 @@ hipError_t launch_linear_decode(const void *x, const void *wq, const float *ws, 
 // round-robin over the 8 XCDs (each with its own L2); consecutive logical
 // tiles are made to land on one XCD, and logical tiles are ordered in
 // groups of 8 tile rows so that neighbours share A rows and B columns.
-__device__ __forceinline__ void tile_coords(int bid, int total, int tiles_m, int tiles_n,
-                                            int &tm, int &tn) {
-  if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
+__device__ __forceinline__ void group_coords(int bid, int tiles_m, int tiles_n, int &tm,
+                                             int &tn) {
   constexpr int GM = 8;
   const int per_group = GM * tiles_n;
   const int group = bid / per_group;
@@ -1142,6 +1141,15 @@ __device__ __forceinline__ void tile_coords(int bid, int total, int tiles_m, int
   const int in_group = bid - group * per_group;
   tm = first_m + in_group % gsz;
   tn = in_group / gsz;
+}
+
+__device__ __forceinline__ int xcd_remap(int bid, int total) {
+  return (total & 7) == 0 ? (bid & 7) * (total >> 3) + (bid >> 3) : bid;
+}
+
+__device__ __forceinline__ void tile_coords(int bid, int total, int tiles_m, int tiles_n,
+                                            int &tm, int &tn) {
+  group_coords(xcd_remap(bid, total), tiles_m, tiles_n, tm, tn);
 }
 
 // One tile with either scale type: S = float -> gemm_tile, S = uint8_t
@@ -1273,6 +1281,88 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
     for (int sp = 1; sp < splits; ++sp) a += part[sp * slice_elems + i];
     y[i] = (uint16_t)bf16_rne(a);
   }
+}
+
+// Stream-K tail of the 256x256 tiled GEMM (fp32 per-token-group scales).
+// With T output tiles on kCUs compute units, T % kCUs tiles would run as a
+// last, partly empty round.  Here the first t_dp = (T / kCUs) * kCUs tiles
+// (in the tiled order: 8-row groups, XCD-aware) run whole as in
+// block_gemm_kernel, and the remaining `rem` tiles' K blocks, rem * KB
+// (tile, K block) steps taken in tile-major order, are cut into nsk equal
+// contiguous ranges of L steps, one per extra workgroup.  A range covers
+// the end of one tile and/or the start of the next (L <= KB): each piece is
+// one gemm_tile over those K blocks, promoting every 128-long partial sum
+// with its scale pair as always, and stores its unrounded fp32 sums to a
+// workspace slot (256x256 fp32, tile-local rows).  The piece of tail tile s
+// run by range w goes to slot w + s.  sk_reduce_kernel then adds each tail
+// tile's pieces in K order and rounds once to bf16.
+constexpr int kCUs = 256;  // MI355X compute units
+
+template <int WM, int WN, int FM>
+__global__ __launch_bounds__(WM * WN * 64) void block_gemm_sk_kernel(
+    const uint8_t *__restrict__ xq, const float *__restrict__ xs, const uint8_t *__restrict__ wq,
+    const float *__restrict__ ws, int64_t M, int64_t N, int64_t K, uint16_t *__restrict__ y,
+    float *__restrict__ part, int tiles_m, int tiles_n, int t_dp, int rem, int L) {
+  using T = Tile<WM, WN, FM>;
+  __shared__ typename T::Smem sm;
+  const int64_t KB = K / 128;
+  const int bid = blockIdx.x;
+  int tm, tn;
+  if (bid < t_dp) {
+    group_coords(xcd_remap(bid, t_dp), tiles_m, tiles_n, tm, tn);
+    const int64_t m0 = (int64_t)tm * T::TM, n0 = (int64_t)tn * T::TN;
+    gemm_tile<WM, WN, FM>(xq + m0 * K, xs + m0 * KB, KB, 1, (int)min<int64_t>(T::TM, M - m0),
+                          wq + n0 * K, ws + (n0 / 128) * KB, (int)min<int64_t>(T::TN, N - n0), K,
+                          y + m0 * N + n0, N, sm);
+    return;
+  }
+  const int w = bid - t_dp;
+  const int64_t i0 = (int64_t)w * L;
+  const int64_t i1 = min<int64_t>(i0 + L, (int64_t)rem * KB);
+  const int s0 = (int)(i0 / KB);
+#pragma unroll 1
+  for (int s = s0; s <= s0 + 1 && s < rem && (int64_t)s * KB < i1; ++s) {
+    const int kb0 = (int)(max<int64_t>(i0, (int64_t)s * KB) - (int64_t)s * KB);
+    const int kb1 = (int)(min<int64_t>(i1, (int64_t)(s + 1) * KB) - (int64_t)s * KB);
+    if (s > s0) __syncthreads();  // the previous piece's last reads of LDS are done
+    group_coords(t_dp + s, tiles_m, tiles_n, tm, tn);
+    const int64_t m0 = (int64_t)tm * T::TM, n0 = (int64_t)tn * T::TN;
+    float *slot = part + (int64_t)(w + s) * (T::TM * T::TN);
+    gemm_tile<WM, WN, FM, 1, true>(
+        xq + m0 * K + kb0 * 128, xs + m0 * KB + kb0, KB, 1, (int)min<int64_t>(T::TM, M - m0),
+        wq + n0 * K + kb0 * 128, ws + (n0 / 128) * KB + kb0, (int)min<int64_t>(T::TN, N - n0), K,
+        reinterpret_cast<uint16_t *>(slot), T::TN, sm, kb1 - kb0);
+  }
+}
+
+// y over tail tile s = sum, in K order, of its pieces' slots (ranges
+// floor(s*KB/L) .. floor(((s+1)*KB-1)/L), slot w + s), rounded once to
+// bf16.  Workgroup (s, c) covers rows 4c .. 4c+3 of the tile: 256 threads,
+// four columns each.
+template <int TM, int TN>
+__global__ __launch_bounds__(256) void sk_reduce_kernel(const float *__restrict__ part,
+                                                        int64_t M, int64_t N, int64_t KB,
+                                                        int tiles_m, int tiles_n, int t_dp,
+                                                        int L, uint16_t *__restrict__ y) {
+  static_assert(TN == 256, "one row of four columns per thread");
+  const int s = blockIdx.x / (TM / 4);
+  const int r = (blockIdx.x % (TM / 4)) * 4 + threadIdx.x / 64;
+  const int c = (threadIdx.x % 64) * 4;
+  int tm, tn;
+  group_coords(t_dp + s, tiles_m, tiles_n, tm, tn);
+  const int64_t row = (int64_t)tm * TM + r, col0 = (int64_t)tn * TN + c;
+  if (row >= M) return;
+  const int w0 = (int)(((int64_t)s * KB) / L), w1 = (int)(((int64_t)(s + 1) * KB - 1) / L);
+  float4 a = reinterpret_cast<const float4 *>(part + (int64_t)(w0 + s) * (TM * TN) + r * TN + c)[0];
+  for (int w = w0 + 1; w <= w1; ++w) {
+    const float4 b =
+        reinterpret_cast<const float4 *>(part + (int64_t)(w + s) * (TM * TN) + r * TN + c)[0];
+    a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+  }
+  const float v[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (col0 + j < N) y[row * N + col0 + j] = (uint16_t)bf16_rne(v[j]);
 }
 
 // Grouped variant.  The logical m-tiles of all experts are numbered
@@ -1473,6 +1563,42 @@ static int any_split_plan(int64_t M, int64_t N, int64_t K, int &kb_per, int64_t 
   return splitk_plan(M, N, K, kb_per, slice_elems, std::is_same<S, uint8_t>::value);
 }
 
+// Stream-K tail plan (fp32 scales, the 256x256 tiled path).  A time model
+// fitted to measurements on MI355X: a K step of the 256x256 tile takes
+// ~1.9 us, so the tail saves (KB - L) steps; the pieces' fp32 sums cost
+// their traffic (written, then read by the reduction) at ~4 TB/s plus ~4 us
+// for the second launch.  Used only when the model gains more than 8 us
+// (DeepSeek-V3 o_proj and MLP down at M = 8192: 3.5 rounds of tiles, the
+// last half-empty; a short-K tail such as Llama gate/up's gains nothing).
+struct SkPlan {
+  int t_dp = 0, rem = 0, L = 0, nsk = 0;
+  size_t bytes = 0;
+};
+
+static bool sk_plan(int64_t M, int64_t N, int64_t K, SkPlan &p) {
+  // (also called before argument validation: sizes past the library's
+  // limits are simply not split)
+  if (M <= kDecMaxM || N <= 0 || K <= 0) return false;
+  if (M > (int64_t(1) << 31) || N > (int64_t(1) << 31) || K > (int64_t(1) << 24)) return false;
+  using T = Tile<2, 4, 8>;
+  const int64_t tiles = ((M + T::TM - 1) / T::TM) * ((N + T::TN - 1) / T::TN);
+  if (tiles < 192 || tiles > (int64_t(1) << 24)) return false;  // not the 256x256 path
+  const int64_t rem = tiles % kCUs, KB = K / 128;
+  if (rem == 0) return false;
+  const int64_t L = (rem * KB + kCUs - 1) / kCUs;
+  const int64_t nsk = (rem * KB + L - 1) / L;
+  const int64_t pieces = nsk + rem;  // upper bound (and the slot count)
+  const double saved = 1.9 * (double)(KB - L);
+  const double cost = 4.0 + 2.0 * (double)pieces * (double)(T::TM * T::TN * 4) / 4.0e6;
+  if (saved - cost <= 8.0) return false;
+  p.t_dp = (int)(tiles - rem);
+  p.rem = (int)rem;
+  p.L = (int)L;
+  p.nsk = (int)nsk;
+  p.bytes = (size_t)pieces * (size_t)(T::TM * T::TN) * sizeof(float);
+  return true;
+}
+
 template <typename S>
 static size_t splitk_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   int kb_per = 0;
@@ -1483,6 +1609,12 @@ static size_t splitk_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 }
 
 size_t block_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  SkPlan sk;
+  if (sk_plan(M, N, K, sk)) return sk.bytes;
+  return splitk_workspace_bytes<float>(M, N, K);
+}
+
+size_t block_gemm_split_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   return splitk_workspace_bytes<float>(M, N, K);
 }
 size_t block_gemm_e8m0_workspace_bytes(int64_t M, int64_t N, int64_t K) {
@@ -1492,7 +1624,27 @@ size_t block_gemm_e8m0_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 template <typename S>
 static hipError_t launch_splitk(const void *xq, const S *xs, const void *wq, const S *ws,
                                 int64_t M, int64_t N, int64_t K, void *y, void *work,
-                                size_t work_bytes, hipStream_t stream) {
+                                size_t work_bytes, hipStream_t stream, bool allow_sk = true) {
+  if constexpr (std::is_same<S, float>::value) {
+    SkPlan sk;
+    if (allow_sk && sk_plan(M, N, K, sk)) {
+      if (work == nullptr || work_bytes < sk.bytes)
+        return launch_block_gemm(xq, xs, wq, ws, M, N, K, y, stream);
+      using T = Tile<2, 4, 8>;
+      const int tm = (int)((M + T::TM - 1) / T::TM), tn = (int)((N + T::TN - 1) / T::TN);
+      float *part = static_cast<float *>(work);
+      hipLaunchKernelGGL((block_gemm_sk_kernel<2, 4, 8>), dim3((unsigned)(sk.t_dp + sk.nsk)),
+                         dim3(T::kThreads), 0, stream, static_cast<const uint8_t *>(xq), xs,
+                         static_cast<const uint8_t *>(wq), ws, M, N, K,
+                         static_cast<uint16_t *>(y), part, tm, tn, sk.t_dp, sk.rem, sk.L);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((sk_reduce_kernel<T::TM, T::TN>), dim3((unsigned)(sk.rem * (T::TM / 4))),
+                         dim3(256), 0, stream, part, M, N, K / 128, tm, tn, sk.t_dp, sk.L,
+                         static_cast<uint16_t *>(y));
+      return hipGetLastError();
+    }
+  }
   int kb_per = 0;
   int64_t slice = 0;
   bool dec = false;
@@ -1572,12 +1724,14 @@ hipError_t scratch_address(void **addr) {
 hipError_t launch_block_gemm_noalloc(const void *xq, const float *xs, const void *wq,
                                      const float *ws, int64_t M, int64_t N, int64_t K, void *y,
                                      hipStream_t stream) {
-  if (block_gemm_workspace_bytes(M, N, K) == 0)
+  // the K splits over workgroups only: a stream-K tail's slots (tens of MB)
+  // are not held in the scratch, and such shapes run unsplit
+  if (block_gemm_split_workspace_bytes(M, N, K) == 0)
     return launch_block_gemm(xq, xs, wq, ws, M, N, K, y, stream);
   void *p = nullptr;
   hipError_t e = scratch_address(&p);
   if (e != hipSuccess) return e;
-  return launch_block_gemm_ws(xq, xs, wq, ws, M, N, K, y, p, kScratchBytes, stream);
+  return launch_splitk<float>(xq, xs, wq, ws, M, N, K, y, p, kScratchBytes, stream, false);
 }
 
 hipError_t launch_block_gemm_e8m0_ws(const void *xq, const uint8_t *xs, const void *wq,

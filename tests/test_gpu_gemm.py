@@ -381,6 +381,52 @@ def test_gemm_ws_misaligned_workspace_raises():
 
 
 # ----------------------------------------------------------------------------
+# stream-K tail (fp8_block_gemm_ws on 3.5 rounds of 256x256 tiles, long K)
+
+def test_stream_k_tail_exact_ragged():
+    """8000 x 7000 x 16384: 32 x 28 tiles of 256x256, the last 128 (8-row
+    group 3, columns 12..27, incl. the ragged last row and column tiles)
+    split over 256 ranges of 64 K blocks.  Integer operands with
+    power-of-two scales keep every partial sum exact, so the rows checked --
+    all in the tail's row range or in the whole tiles -- must equal
+    bf16_RNE(exact) bit for bit; a second call gives the same bits."""
+    M, N, K = 8000, 7000, 16384
+    need = fb.fp8_block_gemm_workspace_bytes(M, N, K)
+    assert need == 384 * 256 * 256 * 4
+    rng = np.random.default_rng(17)
+    xq = oe.encode(rng.integers(-8, 9, (M, K)).astype(np.float32))
+    wq = oe.encode(rng.integers(-8, 9, (N, K)).astype(np.float32))
+    KB, NB = K // 128, -(-N // 128)
+    xs = np.exp2(rng.integers(-1, 2, (M, KB))).astype(np.float32)
+    ws = np.exp2(rng.integers(0, 2, (NB, KB))).astype(np.float32)
+    y, _ = gpu_gemm_ws(xq, xs, wq, ws)
+    y2, _ = gpu_gemm_ws(xq, xs, wq, ws, fill=0x00)
+    assert np.array_equal(y, y2)
+    rows = np.sort(np.concatenate([[0, 255, 6143, 6144, 7935, 7936, M - 1],
+                                   rng.choice(np.arange(6144, M), 40, replace=False),
+                                   rng.choice(np.arange(0, 6144), 16, replace=False)]))
+    want = og.bf16_rne_bits(og.block_gemm(xq[rows], xs[rows], wq, ws))
+    bad = np.argwhere(y[rows] != want)
+    assert bad.size == 0, f"{len(bad)} outputs differ, first {bad[:3].tolist()}"
+
+
+def test_stream_k_tail_without_workspace_is_plain():
+    """Without a large enough workspace the stream-K shape runs
+    fp8_block_gemm (same bits) and leaves the workspace alone."""
+    M, N, K = 8000, 7000, 16384
+    rng = np.random.default_rng(18)
+    xq = oe.encode(rng.integers(-8, 9, (M, K)).astype(np.float32))
+    wq = oe.encode(rng.integers(-8, 9, (N, K)).astype(np.float32))
+    xs = np.ones((M, K // 128), np.float32)
+    ws = np.ones((-(-N // 128), K // 128), np.float32)
+    plain = gpu_gemm_plain(xq, xs, wq, ws)
+    need = fb.fp8_block_gemm_workspace_bytes(M, N, K)
+    y, work = gpu_gemm_ws(xq, xs, wq, ws, work_bytes=need - 16, fill=0x5A)
+    assert np.array_equal(y, plain)
+    assert bool((work == 0x5A).all())
+
+
+# ----------------------------------------------------------------------------
 # grouped GEMM
 
 def _grouped_case(sizes, N, K, seed):

@@ -65,3 +65,24 @@ def test_noalloc_decode_split_and_unsplit():
             fb.fp8_block_gemm(to_dev(xq), to_dev(xs), to_dev(wq), to_dev(ws), y_plain)
             torch.cuda.synchronize()
             assert np.array_equal(bf16_to_host(y_plain), y_na)
+
+
+def test_noalloc_stream_k_shape_runs_unsplit():
+    """A stream-K tail shape (3.5 rounds of 256x256 tiles, long K) needs far
+    more than the scratch: fp8_block_gemm_noalloc runs it as
+    fp8_block_gemm, bit for bit."""
+    M, N, K = 8192, 7168, 16384
+    assert fb.fp8_block_gemm_workspace_bytes(M, N, K) > fb.SCRATCH_BYTES
+    d = dev()
+    g = torch.Generator(device=d)
+    g.manual_seed(5)
+    xq = torch.randint(0, 0x7e, (M, K), generator=g, device=d, dtype=torch.uint8)
+    wq = torch.randint(0, 0x7e, (N, K), generator=g, device=d, dtype=torch.uint8)
+    xs = torch.rand((M, K // 128), generator=g, device=d) + 0.5
+    ws = torch.rand((-(-N // 128), K // 128), generator=g, device=d) + 0.5
+    y_plain = torch.empty((M, N), dtype=torch.bfloat16, device=d)
+    y_na = torch.empty((M, N), dtype=torch.bfloat16, device=d)
+    fb.fp8_block_gemm(xq, xs, wq, ws, y_plain)
+    fb.fp8_block_gemm_noalloc(xq, xs, wq, ws, y_na)
+    torch.cuda.synchronize()
+    assert torch.equal(y_plain.view(torch.int16), y_na.view(torch.int16))
