@@ -164,14 +164,16 @@ __device__ __forceinline__ void store_tile_rows16(const v4f (&acc)[FM][4], uint1
 // one static scale; B: w_q
 // at the tile's first column's row, rows_b valid rows; Bs: w_scale row of
 // that first column's 128-block; Y: y at the tile origin (row stride ldy).
-// Rows past rows_a / rows_b are read from the last valid row (never out of
-// bounds); their outputs are not stored.
+// Operand rows past rows_a / rows_b read as zeros (never out of bounds) and
+// their scales from the last valid row; their outputs are not stored.
 //
-// The loop over a wave's FM A fragments is software-pipelined: each MFMA of
-// fragment mi is followed by the four promotion FMAs of the same column
-// fragment of mi-1 (whose MFMAs finished long ago), and the LDS reads for
-// fragment mi+1 go out right after the first MFMA; scheduling barriers pin
-// this order so the FMAs fill the MFMA shadow without waiting on a result.
+// The loop over a wave's FM A fragments is software-pipelined: each MFMA is
+// followed by the four promotion FMAs of the MFMA issued two before it
+// (whose result is complete), and the LDS reads for fragment mi+2 go out
+// right after fragment mi's first MFMA; scheduling barriers pin this order
+// so the FMAs fill the MFMA shadow without waiting on a result.  Three MFMA
+// results and two sets of scale products are live at a time (the kernel
+// fits in 256 VGPRs with room to spare).
 //
 // KS > 1 splits K inside the workgroup: KS groups of WM x WN waves, each with
 // its own two LDS stages (sm0 is the first of KS consecutive Smem), take K
@@ -206,23 +208,17 @@ __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ A,
 
   // DMA load i of a wave fills LDS rows [8r, 8r+8), r = kDma*w + i; lane l
   // writes bytes [16l, 16l+16) of that 1 KB run = row 8r + l/8, physical
-  // chunk l%8, which holds logical chunk (l%8) ^ swz_f(row).
-  // 32-bit byte offsets from the tile's base (< 256 * K <= 2^32), so each
-  // DMA address is a uniform base plus one VGPR.
-  uint32_t oa[T::kDmaA];
-  uint32_t ob[T::kDmaB];
-#pragma unroll
-  for (int i = 0; i < T::kDmaA; ++i) {
-    const int row = 8 * (T::kDmaA * wave + i) + (lane >> 3);
-    const int lchunk = (lane & 7) ^ swz_f(row);
-    oa[i] = (uint32_t)min(row, rows_a - 1) * (uint32_t)K + lchunk * 16;
-  }
-#pragma unroll
-  for (int i = 0; i < T::kDmaB; ++i) {
-    const int row = 8 * (T::kDmaB * wave + i) + (lane >> 3);
-    const int lchunk = (lane & 7) ^ swz_f(row);
-    ob[i] = (uint32_t)min(row, rows_b - 1) * (uint32_t)K + lchunk * 16;
-  }
+  // chunk l%8, which holds logical chunk (l%8) ^ swz_f(row) (row & 7 = l/8,
+  // so the chunk is the same for every i).  The loads go through a buffer
+  // resource based at the K block, sized to the tile's valid rows: one VGPR
+  // offset per operand, load i adding 8*i*K as a scalar offset (offsets
+  // stay below 256 * K <= 2^32), and rows past rows_a / rows_b read as
+  // zeros (their outputs are not stored).
+  const int drow = lane >> 3;
+  const uint32_t dchunk = (uint32_t)(((lane & 7) ^ swz_f(drow)) * 16);
+  const uint32_t va = (uint32_t)(8 * T::kDmaA * wave + drow) * (uint32_t)K + dchunk;
+  const uint32_t vb = (uint32_t)(8 * T::kDmaB * wave + drow) * (uint32_t)K + dchunk;
+  const uint32_t row8 = 8u * (uint32_t)K;
   // Activation scales of rows 64w + l (waves w < TM/64).
   const float *ps = As + (int64_t)min(64 * wave + lane, rows_a - 1) * xs_rs;
   // Weight-block scales of the tile's column blocks (TN / 128 of them),
@@ -235,14 +231,15 @@ __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ A,
   const int wsel = (wn * 64) / 128;  // this wave's column block within the tile
 
   auto issue = [&](int kb, int st) {
-    const uint8_t *ak = A + (int64_t)kb * 128;
-    const uint8_t *bk = B + (int64_t)kb * 128;
+    const uint64_t ko = (uint64_t)kb * 128u;
+    const __amdgpu_buffer_rsrc_t rA = buffer_rsrc(A + ko, (uint64_t)rows_a * (uint64_t)K - ko);
+    const __amdgpu_buffer_rsrc_t rB = buffer_rsrc(B + ko, (uint64_t)rows_b * (uint64_t)K - ko);
 #pragma unroll
     for (int i = 0; i < T::kDmaA; ++i)
-      lds_dma16(ak + oa[i], sm.a[st] + (T::kDmaA * wave + i) * 1024);
+      buf_dma16(rA, va, (uint32_t)i * row8, sm.a[st] + (T::kDmaA * wave + i) * 1024);
 #pragma unroll
     for (int i = 0; i < T::kDmaB; ++i)
-      lds_dma16(bk + ob[i], sm.b[st] + (T::kDmaB * wave + i) * 1024);
+      buf_dma16(rB, vb, (uint32_t)i * row8, sm.b[st] + (T::kDmaB * wave + i) * 1024);
     if (wave < T::TM / 64) lds_dma4(ps + (int64_t)kb * xs_ks, &sm.as[st][64 * wave]);
     if (wave == T::TM / 64 && lane < kNbTile) lds_dma4(pws + kb, &sm.ws[st][0]);
   };
@@ -267,7 +264,10 @@ __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ A,
   const int arow0 = wm * FM * 16 + r16;
   const int brow0 = wn * 64 + r16;
   const int srow0 = wm * FM * 16 + 4 * (lane >> 4);
-
+  // MFMA results in flight (result j is promoted after MFMA j+2 is issued)
+  // and the scale products of the current and previous A fragment
+  v4f pc[3];
+  float scp[2][4];
 
   for (int it = 0; it < KI; ++it) {
     const int st = it & 1;
@@ -302,25 +302,33 @@ __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ A,
     __builtin_amdgcn_sched_barrier(0);
     v8i afn2 = afn;
     float4 s4n2 = s4n;
-    v4f pp[4];
-    float scp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    // MFMA j = 4*mi + ni; after issuing it, the promotion FMAs of MFMA j-2
+    // (issued two MFMAs = 64 cycles earlier, its result complete) fill the
+    // matrix core's shadow; scheduling barriers pin this order
 #pragma unroll
     for (int mi = 0; mi < FM; ++mi) {
-      v4f pc[4];
 #pragma unroll
       for (int ni = 0; ni < 4; ++ni) {
-        pc[ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+        const int j = mi * 4 + ni;
+        pc[j % 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
             af, bfr[ni], v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
-        if (ni == 0 && mi + 2 < FM) {
-          afn2 = read_a(mi + 2);
-          s4n2 = sas[(mi + 2) * 4];
+        if (ni == 0) {
+          if (mi + 2 < FM) {
+            afn2 = read_a(mi + 2);
+            s4n2 = sas[(mi + 2) * 4];
+          }
+          scp[mi & 1][0] = s4.x * wsc;
+          scp[mi & 1][1] = s4.y * wsc;
+          scp[mi & 1][2] = s4.z * wsc;
+          scp[mi & 1][3] = s4.w * wsc;
           __builtin_amdgcn_sched_barrier(0);
         }
-        if (mi > 0) {
+        if (j >= 2) {
+          const int jj = j - 2, mj = jj / 4, nj = jj % 4;
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            acc[mi - 1][ni][r] = fmaf(pp[ni][r], scp[r], acc[mi - 1][ni][r]);
+            acc[mj][nj][r] = fmaf(pc[jj % 3][r], scp[mj & 1][r], acc[mj][nj][r]);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -330,22 +338,22 @@ __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ A,
         if (it + 1 < KI) issue(min((it + 1) * KS + kg, NKB - 1), st ^ 1);
         __builtin_amdgcn_sched_barrier(0);
       }
-      scp[0] = s4.x * wsc; scp[1] = s4.y * wsc; scp[2] = s4.z * wsc; scp[3] = s4.w * wsc;
-#pragma unroll
-      for (int ni = 0; ni < 4; ++ni) pp[ni] = pc[ni];
       af = afn;
       s4 = s4n;
       afn = afn2;
       s4n = s4n2;
     }
-    // all MFMAs of this step are issued: publish the next stage, start its
-    // fragment reads, then finish this step's last promotion meanwhile
+    // all MFMAs of this step are issued: publish the next stage, then finish
+    // this step's last two promotions
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
+    for (int jj = 4 * FM - 2; jj < 4 * FM; ++jj) {
+      const int mj = jj / 4, nj = jj % 4;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[FM - 1][ni][r] = fmaf(pp[ni][r], scp[r], acc[FM - 1][ni][r]);
+      for (int r = 0; r < 4; ++r)
+        acc[mj][nj][r] = fmaf(pc[jj % 3][r], scp[mj & 1][r], acc[mj][nj][r]);
+    }
   }
 
   if constexpr (KS > 1) {
@@ -1413,10 +1421,25 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(
   const int64_t n0 = (int64_t)tn * T::TN;
   const int64_t KB = K / 128;
   const int64_t NB = (N + 127) / 128;
+  const uint8_t *wt = wq + (int64_t)e * N * K + n0 * K;
+  const S *wst = ws + ((int64_t)e * NB + n0 / 128) * KB;
+  const int rows_b = (int)min<int64_t>(T::TN, N - n0);
+  if constexpr (FM % 2 == 0) {
+    // a row tile with at most half its rows (an expert's ragged last tile)
+    // runs the half-height tile: the same waves, half the A fragments each,
+    // half the MFMA work
+    using H = Tile<WM, WN, FM / 2>;
+    if (r1 - r0 <= H::TM) {
+      auto &smh = *reinterpret_cast<typename TileSmem<WM, WN, FM / 2, S>::type *>(&sm);
+      static_assert(sizeof(typename TileSmem<WM, WN, FM / 2, S>::type) <= sizeof(sm), "LDS");
+      run_tile<WM, WN, FM / 2, S>(xq + r0 * K, xs + r0 * xs_rs, xs_rs, xs_ks, (int)(r1 - r0), wt,
+                                  wst, rows_b, K, y + r0 * N + n0, N, smh);
+      return;
+    }
+  }
   run_tile<WM, WN, FM, S>(xq + r0 * K, xs + r0 * xs_rs, xs_rs, xs_ks,
-                          (int)min<int64_t>(T::TM, r1 - r0), wq + (int64_t)e * N * K + n0 * K,
-                          ws + ((int64_t)e * NB + n0 / 128) * KB,
-                          (int)min<int64_t>(T::TN, N - n0), K, y + r0 * N + n0, N, sm);
+                          (int)min<int64_t>(T::TM, r1 - r0), wt, wst, rows_b, K, y + r0 * N + n0,
+                          N, sm);
 }
 
 template <int WM, int WN, int FM, typename S>
