@@ -113,28 +113,38 @@ FP8BLK_API fp8blk_status fp8_block_gemm(const void *x_q, const float *x_scale,
                                         int64_t M, int64_t N, int64_t K,
                                         void *y_bf16, void *stream);
 
-/* The same GEMM with a caller workspace, for shapes whose grid of 128x128
- * output tiles would leave most compute units idle (small M and N, long K,
- * e.g. the DeepSeek-V3 q_a and kv_a projections at a few hundred tokens),
- * and for decode batches of 9 to 16 rows with long K (e.g. a 4096 x 14336
- * down projection), where a workgroup covering 64 output columns over part
- * of K re-reads less of x than one covering 16 columns over all of it.
- * The same operation and passage as fp8_block_gemm: each workgroup runs one
- * output tile over one contiguous range of K blocks, promoting each
- * 128-long partial sum with its scale pair into fp32 as fp8_block_gemm does,
- * and stores the range's unrounded fp32 sums in the workspace; a second
- * kernel adds the ranges in K order and rounds once to bf16.  The result
- * meets the same tolerance; it is not bit-identical to fp8_block_gemm (the
- * fp32 sums are associated differently).
- *   fp8_block_gemm_workspace_bytes(M, N, K): bytes this split needs, 0 when
+/* The same GEMM with a caller workspace, for shapes whose grid of output
+ * tiles would leave compute units idle: small M and N with long K (e.g.
+ * the DeepSeek-V3 q_a and kv_a projections at a few hundred tokens); large
+ * grids of 256x256 tiles whose last round of 256 compute units is partly
+ * empty (e.g. 8192 x 7168 x 16384: 896 tiles, 3.5 rounds); and decode
+ * batches of 9 to 16 rows with long K (e.g. a 4096 x 14336 down
+ * projection), where a workgroup covering 64 output columns over part of K
+ * re-reads less of x than one covering 16 columns over all of it.  The same
+ * operation and passage as fp8_block_gemm: a workgroup runs one output tile
+ * over one contiguous range of K blocks, promoting each 128-long partial
+ * sum with its scale pair into fp32 as fp8_block_gemm does, and stores the
+ * range's unrounded fp32 sums in the workspace; a second kernel adds a
+ * tile's ranges in K order and rounds once to bf16.  In the partly empty
+ * last round case only that round's tiles are split (their K blocks cut
+ * into 256 equal ranges, "stream-K"); the whole rounds before it run
+ * unsplit in the same launch.  The result meets the same tolerance; split
+ * tiles are not bit-identical to fp8_block_gemm (the fp32 sums are
+ * associated differently), unsplit ones are.
+ *   fp8_block_gemm_workspace_bytes(M, N, K): bytes the split needs, 0 when
  *     it is not used for these sizes.  17 <= M <= 64 never splits.  M > 64:
- *     at most 128 output tiles of 128x128 and K long enough for the split
- *     to gain (a time model measured on MI355X picks the number of K
- *     ranges, 2 to min(256 / tiles, K / 512), or none).  9 <= M <= 16:
- *     ceil(N / 64) column groups times the number of K ranges (at most
- *     256 / groups and K / 2048) must reach 192, where N is too small for
- *     ceil(N / 64) groups alone to fill the chip and K is at most 65536.
- *     Invalid sizes: 0.  Host arithmetic only, no HIP call.
+ *     either at most 128 output tiles of 128x128 and K long enough for the
+ *     split to gain (a time model measured on MI355X picks the number of K
+ *     ranges, 2 to min(256 / tiles, K / 512), or none): ranges x M x N x 4
+ *     bytes; or at least 192 tiles of 256x256, not a whole number of rounds
+ *     of 256, where a time model (1.9 us per K block of a tile against the
+ *     partial sums' traffic) gains more than 8 us: (the ranges, at most
+ *     256, plus the last round's tiles) x 256 KB (100.7 MB for 8192 x 7168
+ *     x 16384).
+ *     9 <= M <= 16: ceil(N / 64) column groups times the number of K ranges
+ *     (at most 256 / groups and K / 2048) must reach 192, where N is too
+ *     small for ceil(N / 64) groups alone to fill the chip and K is at most
+ *     65536.  Invalid sizes: 0.  Host arithmetic only, no HIP call.
  *   fp8_block_gemm_ws: arguments as fp8_block_gemm, plus `workspace`
  *     (device, 16-byte aligned, owned by the caller, overwritten, not
  *     initialised by the caller) of `workspace_bytes` bytes.  When the
@@ -153,8 +163,11 @@ FP8BLK_API fp8blk_status fp8_block_gemm_ws(const void *x_q, const float *x_scale
 /* fp8_block_gemm_ws without a caller workspace, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation).  Same operation, plan and kernels as
- * fp8_block_gemm_ws given a large enough workspace (bit-identical output);
- * the K split's fp32 partial sums go to a device array inside the library
+ * fp8_block_gemm_ws given a large enough workspace (bit-identical output),
+ * except that shapes fp8_block_gemm_ws would give the stream-K split of a
+ * partly empty last round run unsplit, as fp8_block_gemm (bit-identical to
+ * it; those partial sums take up to ~100 MB); the split's fp32 partial sums
+ * go to a device array inside the library
  * of FP8BLK_SCRATCH_BYTES bytes, one per GPU, held until the process ends,
  * whose address is looked up once per device on the first call made with
  * that device current.  Allocates nothing.
