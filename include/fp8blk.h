@@ -218,7 +218,9 @@ FP8BLK_API fp8blk_status fp8_grouped_block_gemm(const void *x_q, const float *x_
  * those of fp8_act_quant_group; y is bit-identical to fp8_act_quant_group
  * followed by fp8_block_gemm except in the fused kernel for 32 < M <= 64
  * (it splits K over fewer waves, so its fp32 partial sums are added in
- * another order).
+ * another order).  It takes no GEMM workspace and so never the K splits of
+ * fp8_block_gemm_ws (small grids, stream-K tail, decode with long K);
+ * callers that want them run fp8_act_quant_group then fp8_block_gemm_ws.
  *   x_bf16 [M,K], w_q [N,K], w_scale [ceil(N/128),K/128] in; y_bf16 [M,N] out. */
 FP8BLK_API fp8blk_status fp8_linear(const void *x_bf16, int64_t M, int64_t N, int64_t K,
                                     const void *w_q, const float *w_scale, void *x_q_ws,
