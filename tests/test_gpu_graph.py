@@ -110,3 +110,33 @@ def test_split_k_gemm_graph(M, N, K):
         jq, js = fb.act_quant_group(junk)
         fb.fp8_block_gemm_ws(jq, js, wq, wsc, torch.empty_like(y), work)
     _replay_and_check(step, [y], ref, other)
+
+
+def test_stream_k_gemm_graph():
+    """The stream-K tail of a partly empty last round (8192 x 7168 x 16384:
+    3.5 rounds of 256x256 tiles; the GEMM kernel with its extra range
+    workgroups, then the reduction) captured and replayed: every replay
+    equals the eager bits."""
+    d = dev()
+    M, N, K = 8192, 7168, 16384
+    need = fb.fp8_block_gemm_workspace_bytes(M, N, K)
+    assert need > 0
+    g = torch.Generator(device=d)
+    g.manual_seed(31)
+    xq = torch.randint(0, 0x7e, (M, K), generator=g, device=d, dtype=torch.uint8)
+    wq = torch.randint(0, 0x7e, (N, K), generator=g, device=d, dtype=torch.uint8)
+    xs = torch.rand((M, K // 128), generator=g, device=d) + 0.5
+    ws = torch.rand((N // 128, K // 128), generator=g, device=d) + 0.5
+    work = torch.empty(need, dtype=torch.uint8, device=d)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=d)
+
+    def step():
+        fb.fp8_block_gemm_ws(xq, xs, wq, ws, y, work)
+    step()
+    torch.cuda.synchronize()
+    ref = [_bits(y)]
+    xq2 = torch.randint(0, 0x7e, (M, K), generator=g, device=d, dtype=torch.uint8)
+
+    def other():
+        fb.fp8_block_gemm_ws(xq2, xs, wq, ws, torch.empty_like(y), work)
+    _replay_and_check(step, [y], ref, other)
