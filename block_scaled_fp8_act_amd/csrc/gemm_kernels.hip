@@ -757,9 +757,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_gemm_kernel(
   static_assert(NS == 1 || NS == 2 || NS == 4, "slabs per workgroup: 1, 2 or 4");
   constexpr int R = MF * 16;                          // staged rows
   // register buffers of U K blocks: two (the next batch's loads go out
-  // before the current batch's MFMAs) unless four row fragments leave no
-  // room (then one, reloaded after its MFMAs)
-  constexpr int NB = MF >= 4 ? 1 : 2;
+  // before the current batch's MFMAs) unless four row fragments, or four
+  // slabs with E8M0 scale operands, leave no room in 128 VGPRs (then one,
+  // reloaded after its MFMAs; for the four E8M0 slabs that still beats two
+  // slabs in two rounds of workgroups: 14336 x 4096 at M = 16 18.2 ->
+  // 14.5 us, M = 4 15.2 -> 13.8 us)
+  constexpr int NB = (MF >= 4 || (MX && NS == 4)) ? 1 : 2;
   constexpr int U = (4 / NB) / (MF * NS) > 0 ? (4 / NB) / (MF * NS) : 1;
   extern __shared__ __align__(16) float dsm[];
   float *s_as = dsm;                                  // [KB][R] (fp32 scales only)
@@ -940,11 +943,9 @@ static hipError_t launch_decode(const void *xq, const S *xs, int64_t xs_rs, int 
                                 const void *wq, const S *ws, int64_t M, int64_t N, int64_t K,
                                 void *y, hipStream_t stream) {
   const int64_t KB = K / 128;
-  // slabs per workgroup for one row fragment (2 at most with E8M0 scales,
-  // for registers)
+  // slabs per workgroup for one row fragment
   const int64_t slabs = (N + 15) / 16;
-  constexpr bool kMx = std::is_same<S, uint8_t>::value;
-  const int NS = MF == 1 ? decode_slabs(N, kMx ? 2 : 4) : 1;
+  const int NS = MF == 1 ? decode_slabs(N, 4) : 1;
   const size_t part = (size_t)kDecWaves * NS * MF * 64 * 16;
   const size_t lds = (std::is_same<S, uint8_t>::value || kRow)
                          ? part
@@ -954,7 +955,7 @@ static hipError_t launch_decode(const void *xq, const S *xs, int64_t xs_rs, int 
   const auto *b = static_cast<const uint8_t *>(wq);
   auto *out = static_cast<uint16_t *>(y);
   if (NS == 4)
-    hipLaunchKernelGGL((decode_gemm_kernel<MF, S, kRow, (MF == 1 && !kMx ? 4 : 1)>), grid,
+    hipLaunchKernelGGL((decode_gemm_kernel<MF, S, kRow, (MF == 1 ? 4 : 1)>), grid,
                        dim3(kDecThreads), lds, stream, a, xs, xs_rs, xs_ks, b, ws, (int)M, N, K,
                        out, nullptr, (int64_t)0, 0);
   else if (NS == 2)
