@@ -495,11 +495,12 @@ def other_rows(torch, fb, dev, stream):
     rows["weight_quant_18432x7168"] = {"us": round(t * 1e6, 2), "GB/s": round(18432 * 7168 * 3 / t / 1e9, 1)}
     del w, q, s
     # decode GEMMs (HBM-bound): M = 1, 4, 16 (the Llama-3-8B decode
-    # configuration), weights rotated through HBM
+    # configuration) and 32, 64 (small batches, still the decode kernel),
+    # weights rotated through HBM
     for name, N, K in PREFILL_SHAPES:
         wq, wsc = fb.weight_block_quant((torch.randn((N, K), generator=g, device=dev) * 0.02).to(torch.bfloat16))
         copies = _weight_copies(wq, wsc)
-        for Md in (1, 4, 16):
+        for Md in (1, 4, 16, 32, 64):
             x = torch.randn((Md, K), generator=g, device=dev).to(torch.bfloat16)
             xq, xsc = fb.act_quant_group(x)
             y = torch.empty((Md, N), dtype=torch.bfloat16, device=dev)

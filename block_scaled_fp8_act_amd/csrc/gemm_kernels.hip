@@ -757,12 +757,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_gemm_kernel(
   static_assert(NS == 1 || NS == 2 || NS == 4, "slabs per workgroup: 1, 2 or 4");
   constexpr int R = MF * 16;                          // staged rows
   // register buffers of U K blocks: two (the next batch's loads go out
-  // before the current batch's MFMAs) unless four row fragments, or four
-  // slabs with E8M0 scale operands, leave no room in 128 VGPRs (then one,
-  // reloaded after its MFMAs; for the four E8M0 slabs that still beats two
-  // slabs in two rounds of workgroups: 14336 x 4096 at M = 16 18.2 ->
-  // 14.5 us, M = 4 15.2 -> 13.8 us)
-  constexpr int NB = (MF >= 4 || (MX && NS == 4)) ? 1 : 2;
+  // before the current batch's MFMAs) unless four row fragments, four slabs
+  // with E8M0 scale operands, or eight (slab, fragment) pairs leave no room
+  // in 128 VGPRs (then one, reloaded after its MFMAs; for the four E8M0
+  // slabs that still beats two slabs in two rounds of workgroups: 14336 x
+  // 4096 at M = 16 18.2 -> 14.5 us, M = 4 15.2 -> 13.8 us)
+  constexpr int NB = (MF >= 4 || (MX && NS == 4) || MF * NS >= 8) ? 1 : 2;
   constexpr int U = (4 / NB) / (MF * NS) > 0 ? (4 / NB) / (MF * NS) : 1;
   extern __shared__ __align__(16) float dsm[];
   float *s_as = dsm;                                  // [KB][R] (fp32 scales only)
@@ -919,11 +919,11 @@ __global__ __launch_bounds__(kDecThreads) void decode_gemm_kernel(
     }
   }
 }
-// 16-column slabs per decode workgroup for one row fragment of x (M <= 16):
-// 1, 2 or up to max_ns.  More slabs make each workgroup stream more weight
-// bytes (and, in the fused layer, amortize its quantization of x); with one
-// workgroup per CU the count is picked for the fullest last round of
-// workgroups (ties: more slabs).
+// 16-column slabs per decode workgroup: 1, 2 or up to max_ns.  More slabs
+// make each workgroup stream more weight bytes per read of x (and, in the
+// fused layer, amortize its quantization of x); with one workgroup per CU
+// the count is picked for the fullest last round of workgroups (ties: more
+// slabs).
 static int decode_slabs(int64_t N, int max_ns) {
   const int64_t slabs = (N + 15) / 16;
   int ns_best = 1;
@@ -943,9 +943,19 @@ static hipError_t launch_decode(const void *xq, const S *xs, int64_t xs_rs, int 
                                 const void *wq, const S *ws, int64_t M, int64_t N, int64_t K,
                                 void *y, hipStream_t stream) {
   const int64_t KB = K / 128;
-  // slabs per workgroup for one row fragment
+  // slabs per workgroup: up to four for one or two row fragments, up to two
+  // for four (their partials fill 128 KB of LDS); with fp32 block scales
+  // only for more than one fragment (E8M0 and row-wise keep one).  Every
+  // workgroup reads all of x (M x K bytes) once per K pass, as many bytes
+  // as its slab of weights at M = 16 and twice or four times as many at
+  // M = 32 or 64, so packing slabs cuts the bytes per output column:
+  // measured (weights streamed from HBM) 14336 x 4096 at M = 17-32
+  // 27.3-31.8 -> 18.7-20.0 us, M = 48-64 44-51 -> 41-44 us; 7168 x 16384
+  // at M = 17-32 42-52 -> 32-36 us, M = 64 85 -> 71 us; shapes that keep
+  // one slab unchanged.
+  constexpr bool kBlk = std::is_same<S, float>::value && !kRow;
   const int64_t slabs = (N + 15) / 16;
-  const int NS = MF == 1 ? decode_slabs(N, 4) : 1;
+  const int NS = MF == 1 ? decode_slabs(N, 4) : (kBlk ? decode_slabs(N, MF == 2 ? 4 : 2) : 1);
   const size_t part = (size_t)kDecWaves * NS * MF * 64 * 16;
   const size_t lds = (std::is_same<S, uint8_t>::value || kRow)
                          ? part
@@ -955,11 +965,11 @@ static hipError_t launch_decode(const void *xq, const S *xs, int64_t xs_rs, int 
   const auto *b = static_cast<const uint8_t *>(wq);
   auto *out = static_cast<uint16_t *>(y);
   if (NS == 4)
-    hipLaunchKernelGGL((decode_gemm_kernel<MF, S, kRow, (MF == 1 ? 4 : 1)>), grid,
-                       dim3(kDecThreads), lds, stream, a, xs, xs_rs, xs_ks, b, ws, (int)M, N, K,
-                       out, nullptr, (int64_t)0, 0);
+    hipLaunchKernelGGL((decode_gemm_kernel<MF, S, kRow, (MF == 1 || (kBlk && MF == 2) ? 4 : 1)>),
+                       grid, dim3(kDecThreads), lds, stream, a, xs, xs_rs, xs_ks, b, ws, (int)M, N,
+                       K, out, nullptr, (int64_t)0, 0);
   else if (NS == 2)
-    hipLaunchKernelGGL((decode_gemm_kernel<MF, S, kRow, (MF == 1 ? 2 : 1)>), grid,
+    hipLaunchKernelGGL((decode_gemm_kernel<MF, S, kRow, (MF == 1 || kBlk ? 2 : 1)>), grid,
                        dim3(kDecThreads), lds, stream, a, xs, xs_rs, xs_ks, b, ws, (int)M, N, K,
                        out, nullptr, (int64_t)0, 0);
   else

@@ -94,13 +94,16 @@ def test_gemm_split_k_tiles_tolerance(M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 14380, 256), (7, 7176, 384), (16, 14380, 512),
-                                   (16, 14336, 1024), (3, 4100, 768)])
+                                   (16, 14336, 1024), (3, 4100, 768),
+                                   (17, 14380, 256), (32, 7176, 384), (24, 14336, 640),
+                                   (33, 14380, 256), (64, 7176, 512), (48, 4100, 768),
+                                   (64, 4096, 1024)])
 def test_gemm_decode_multi_slab_exact(M, N, K):
-    """Decode shapes (M <= 16) for which the launcher packs four (N = 14380,
-    14336) or two (N = 7176) 16-column slabs per workgroup, with a partly
-    empty last workgroup and a ragged last slab, and one unpacked ragged
-    shape: integer operands, power-of-two scales, bit-exact against
-    bf16_RNE(exact)."""
+    """Decode shapes for which the launcher packs four (N = 14380, 14336 at
+    M <= 32) or two (N = 7176 and 4100, and every packed shape at M = 33-64)
+    16-column slabs per workgroup, with a partly empty last workgroup and a
+    ragged last slab, and one unpacked shape (N = 4096 at M = 64): integer
+    operands, power-of-two scales, bit-exact against bf16_RNE(exact)."""
     rng = np.random.default_rng(M * 5 + N + K)
     xi = rng.integers(-8, 9, (M, K)); wi = rng.integers(-8, 9, (N, K))
     xq = oe.encode(xi.astype(np.float32)); wq = oe.encode(wi.astype(np.float32))
@@ -152,7 +155,7 @@ def test_gemm_ragged(M, N, K):
 
 
 @pytest.mark.parametrize("shape_index", range(4))
-@pytest.mark.parametrize("M", [1, 4, 16])
+@pytest.mark.parametrize("M", [1, 4, 16, 32, 64])
 def test_gemm_llama_decode(shape_index, M):
     x, w = synth.llama_inputs(shape_index, M, config=2)
     xq, xs, wq, ws = quantized_operands(x, w)
