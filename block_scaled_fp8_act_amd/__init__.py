@@ -346,9 +346,10 @@ FUSED_MAX_M = 64
 
 def fp8_linear(x, w_q, w_scale, y, x_q_ws=None, x_scale_ws=None):
     """One C call for the linear layer: fused in one kernel for M <= 64 when
-    N * K <= 2^25, when the fused kernel packs several 16-column slabs per
-    workgroup (M <= 16, K <= 8192, wide N), or when no workspaces are given; else
-    quantization into the workspaces (required for M > 64) and the GEMM."""
+    no workspaces are given, and with workspaces where that is faster (M <= 16
+    with N * K <= 2^25 or with several 16-column slabs per workgroup at
+    K <= 8192; 16 < M <= 32 with N * K <= 2^24); else quantization into the
+    workspaces (required for M > 64) and the GEMM."""
     _need(x, "x", (torch.bfloat16,), 2); _need(w_q, "w_q", _CODES, 2)
     _need(w_scale, "w_scale", _F32, 2); _need(y, "y", (torch.bfloat16,), 2)
     M, K = x.shape
@@ -509,11 +510,12 @@ def grouped_block_gemm(x_q, x_scale, w_q, w_scale, offsets):
 def linear(x, w_q, w_scale):
     """The FP8 linear layer: dynamic per-token-group quantization of x, then
     the block-scaled GEMM on the current stream (fp32 scales: one C call,
-    fused into one kernel for M <= 64; the quantizer then the split-K GEMM
-    when the library plans a K split: output grids too small to fill the
-    chip, and 9 <= M <= 16 with long K, where the fused kernel's per-column
-    re-reads of x cost more than the separate quantizer).  E8M0 weight
-    scales select power-of-two activation scales as well."""
+    fused into one kernel where the library finds that faster, M <= 32; the
+    quantizer then the split-K GEMM when the library plans a K split: output
+    grids too small to fill the chip, and 9 <= M <= 16 with long K, where the
+    fused kernel's per-column re-reads of x cost more than the separate
+    quantizer).  E8M0 weight scales select power-of-two activation scales as
+    well."""
     if _is_e8m0(w_scale):
         x_q, x_s = act_quant_group(x, "ue8m0")
         return block_gemm(x_q, x_s, w_q, w_scale)

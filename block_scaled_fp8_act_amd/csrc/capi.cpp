@@ -220,21 +220,33 @@ fp8blk_status fp8_linear(const void *x_bf16, int64_t M, int64_t N, int64_t K, co
                          void *stream) {
   // The fused decode kernel re-quantizes x in every workgroup (each reads
   // all of x in bf16 from L2), once per K block for all the workgroup's
-  // 16-column slabs.  It pays for small weights (the second launch costs
-  // more), and for K <= 8192 when the launcher packs two or more slabs per
-  // workgroup; otherwise the two kernels run when workspaces are at hand.
-  // Measured at M = 16, weights streamed from HBM (fused against two
-  // kernels): 4096x4096 10.1 us / 19.4; 14336x4096 (4 slabs) 15.9 / 19.5;
-  // 24576x1536 (2 slabs) 16.5 / 19.5; 4096x14336 (1 slab) 26.7 / 21.1;
-  // 7168x16384 (2 slabs) 38.4 / 33.5; 18432x7168 (1 slab) 66.4 / 47.2.
+  // 16-column slabs.  With workspaces at hand it runs only where it beats
+  // the two kernels: at M <= 16 for small weights (the second launch costs
+  // more) and for K <= 8192 when the launcher packs two or more slabs per
+  // workgroup; at M = 17-32 for weights of at most 2^24 elements; never
+  // past M = 32.  Measured, weights streamed from HBM (fused against two
+  // kernels), M = 16: 4096x4096 10.1 us / 19.4; 14336x4096 (4 slabs) 15.9 /
+  // 19.5; 24576x1536 (2 slabs) 16.5 / 19.5; 4096x14336 (1 slab) 26.7 /
+  // 21.1; 7168x16384 (2 slabs) 38.4 / 33.5; 18432x7168 (1 slab) 66.4 /
+  // 47.2.  M = 17-32: 4096x4096 13.4-14.4 / 19.3-19.6; 1024x4096 11.4-12.6
+  // / 19.1; 1536x7168 17.6-20.2 / 18.9-19.0; 14336x4096 27-31 / 23-24.
+  // M = 33-64: 4096x4096 24.2-25.1 / 19.6-19.7; 1024x4096 21.1-23.1 /
+  // 19.2-19.3; 1536x7168 35.7-39.1 / 19.3-25.7.
   constexpr int64_t kFusedMaxM = 64;
-  constexpr int64_t kFusedMaxWeight = int64_t(1) << 25;  // N * K elements
+  constexpr int64_t kFusedMaxWeight = int64_t(1) << 25;     // N * K elements, M <= 16
+  constexpr int64_t kFusedMaxWeight32 = int64_t(1) << 24;   // N * K elements, M <= 32
   constexpr int64_t kFusedSlabsMaxK = 8192;
   const bool work = M > 0 && N > 0;
   const bool have_ws = x_q_ws != nullptr && x_scale_ws != nullptr;
-  const bool fused = M <= kFusedMaxM &&
-                     (!have_ws || N * K <= kFusedMaxWeight ||
-                      (K <= kFusedSlabsMaxK && fp8blk::linear_decode_slabs(M, N) >= 2));
+  // (N * K only for sizes within the limits, which keep it below 2^55;
+  // others are refused below)
+  const bool sized = !bad_rows(N) && !bad_k(K);
+  const bool fused =
+      M <= kFusedMaxM &&
+      (!have_ws || !sized ||
+       (M <= 16 && (N * K <= kFusedMaxWeight ||
+                    (K <= kFusedSlabsMaxK && fp8blk::linear_decode_slabs(M, N) >= 2))) ||
+       (M <= 32 && N * K <= kFusedMaxWeight32));
   if (work && (!x_bf16 || !w_q || !w_scale || !y_bf16 || (!fused && (!x_q_ws || !x_scale_ws))))
     return FP8BLK_ERR_NULL;
   if (bad_rows(M) || bad_rows(N) || bad_k(K) || too_big(M, K) || too_big(N, K) || too_big(M, N))

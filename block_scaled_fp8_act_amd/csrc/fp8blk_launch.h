@@ -26,7 +26,8 @@ hipError_t launch_linear_decode(const void *x, const void *wq, const float *ws, 
                                 int64_t N, int64_t K, void *y, hipStream_t stream);
 hipError_t launch_act_quant_e8m0(const void *x, int64_t M, int64_t K, void *q, uint8_t *s,
                                  hipStream_t stream);
-// Column slabs per workgroup of the fused decode layer (1 for M > 16).
+// Column slabs per workgroup of the fused decode layer (up to 4 for
+// M <= 16, up to 2 above).
 int linear_decode_slabs(int64_t M, int64_t N);
 hipError_t launch_swiglu_act_quant(const void *gu, int64_t M, int64_t I, void *q, float *s,
                                    hipStream_t stream);

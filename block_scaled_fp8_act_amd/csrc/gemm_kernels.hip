@@ -936,7 +936,7 @@ static int decode_slabs(int64_t N, int max_ns) {
   return ns_best;
 }
 
-int linear_decode_slabs(int64_t M, int64_t N) { return M <= 16 ? decode_slabs(N, 4) : 1; }
+int linear_decode_slabs(int64_t M, int64_t N) { return decode_slabs(N, M <= 16 ? 4 : 2); }
 
 template <int MF, typename S, bool kRow = false>
 static hipError_t launch_decode(const void *xq, const S *xs, int64_t xs_rs, int xs_ks,
@@ -1118,10 +1118,18 @@ __global__ __launch_bounds__(NW * 64) void decode_linear_kernel(
   }
 }
 
+// Slabs per workgroup: up to four for one row fragment, up to two for two
+// or four (more would spill: the bf16 x fragments take 16 VGPRs each).
+// Every workgroup reads and quantizes all of x (2 M K bytes), twice its
+// slab's weight bytes at M = 16, so packing matters more as M grows:
+// measured with no workspaces (weights streamed from HBM) 14336 x 4096 at
+// M = 17-32 46-49 -> 27-31 us and M = 33-64 85-91 -> 47-49 us, 7168 x 16384
+// at M = 17-32 77-82 -> 48-55 us and M = 33-64 149-154 -> 82-85 us;
+// bit-identical (same waves per K split).
 template <int MF, int NW>
 static hipError_t launch_decode_linear(const void *x, const void *wq, const float *ws, int64_t M,
                                        int64_t N, int64_t K, void *y, hipStream_t stream) {
-  const int NS = MF == 1 ? decode_slabs(N, 4) : 1;
+  const int NS = decode_slabs(N, MF == 1 ? 4 : 2);
   const size_t lds = (size_t)NW * NS * MF * 64 * 16;
   const dim3 grid((unsigned)(((N + 15) / 16 + NS - 1) / NS));
   const auto *xp = static_cast<const uint16_t *>(x);
@@ -1131,7 +1139,7 @@ static hipError_t launch_decode_linear(const void *x, const void *wq, const floa
     hipLaunchKernelGGL((decode_linear_kernel<MF, NW, (MF == 1 ? 4 : 1)>), grid, dim3(NW * 64), lds,
                        stream, xp, wp, ws, (int)M, N, K, yp);
   else if (NS == 2)
-    hipLaunchKernelGGL((decode_linear_kernel<MF, NW, (MF == 1 ? 2 : 1)>), grid, dim3(NW * 64), lds,
+    hipLaunchKernelGGL((decode_linear_kernel<MF, NW, 2>), grid, dim3(NW * 64), lds,
                        stream, xp, wp, ws, (int)M, N, K, yp);
   else
     hipLaunchKernelGGL((decode_linear_kernel<MF, NW, 1>), grid, dim3(NW * 64), lds, stream, xp, wp,

@@ -207,18 +207,19 @@ FP8BLK_API fp8blk_status fp8_grouped_block_gemm(const void *x_q, const float *x_
  * quantization "fused ahead of the GEMM").  For M <= 64 (decode) one kernel
  * can do both: the activation codes and scales are formed in registers
  * inside the weight-streaming GEMM and never reach memory.  It is used when
- * M <= 64 and either N * K <= 2^25, or M <= 16, K <= 8192 and N wide
- * enough for the kernel to pack several 16-column slabs per workgroup, or
- * no workspaces are given (x_q_ws and x_scale_ws may be NULL for M <= 64; they are then
- * not touched).
+ * no workspaces are given (x_q_ws and x_scale_ws may be NULL for M <= 64;
+ * they are then not touched), and with workspaces where it is the faster
+ * path: M <= 16 with N * K <= 2^25, or with K <= 8192 and N wide enough for
+ * the kernel to pack several 16-column slabs per workgroup; 16 < M <= 32
+ * with N * K <= 2^24.
  * Otherwise the two kernels run back to back on `stream` through the
  * caller's workspaces x_q_ws [M,K] and x_scale_ws [M,K/128] (required for
  * M > 64, 16-byte aligned), which then hold the activation codes and
  * scales.  The activation codes and scales are always
  * those of fp8_act_quant_group; y is bit-identical to fp8_act_quant_group
- * followed by fp8_block_gemm except in the fused kernel for 32 < M <= 64
- * (it splits K over fewer waves, so its fp32 partial sums are added in
- * another order).  It takes no GEMM workspace and so never the K splits of
+ * followed by fp8_block_gemm except in the fused kernel for 32 < M <= 64,
+ * which runs only without workspaces (it splits K over fewer waves, so its
+ * fp32 partial sums are added in another order).  It takes no GEMM workspace and so never the K splits of
  * fp8_block_gemm_ws (small grids, stream-K tail, decode with long K);
  * callers that want them run fp8_act_quant_group then fp8_block_gemm_ws.
  *   x_bf16 [M,K], w_q [N,K], w_scale [ceil(N/128),K/128] in; y_bf16 [M,N] out. */

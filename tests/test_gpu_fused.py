@@ -55,8 +55,13 @@ def test_fused_decode_llama(M, shape_index):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 16, 128), (3, 100, 256), (16, 300, 384), (31, 576, 18432),
-                                   (40, 1000, 1280), (64, 24576, 1536), (7, 7168, 16384)])
+                                   (40, 1000, 1280), (64, 24576, 1536), (7, 7168, 16384),
+                                   (20, 7176, 512), (32, 14380, 256), (48, 4100, 384),
+                                   (33, 14336, 640)])
 def test_fused_decode_ragged(M, N, K):
+    """Ragged shapes, including two 16-column slabs per workgroup at
+    M = 17-64 (N = 7176, 14380, 4100, 14336, 24576), some with a last
+    workgroup holding one slab and a last slab of 4-12 columns."""
     x = synth.dsv3_activations(M + K, M, K, N)
     w = synth.normal_bf16(N + K, (N, K), 0.02)
     check(x, w, f"fused {M}x{N}x{K}", bit_identical=M <= 32)
@@ -102,6 +107,35 @@ def test_linear_workspace_path(M):
     assert np.array_equal(bf16_to_host(y), bf16_to_host(y2))
     with pytest.raises(ValueError):
         fb.fp8_linear(xd, wqd, wsd, y)
+
+
+@pytest.mark.parametrize("M,N,K,fused", [(24, 4096, 4096, True), (32, 1536, 7168, True),
+                                         (17, 14336, 4096, False), (48, 4096, 4096, False),
+                                         (64, 1024, 4096, False)])
+def test_linear_with_workspaces_small_batch(M, N, K, fused):
+    """fp8_linear with workspaces at M = 17-64: fused for 16 < M <= 32 with
+    N * K <= 2^24, else the quantizer into the workspaces and the GEMM.
+    Either way y equals the two-launch result bit for bit (the fused kernel
+    sums in the same order up to M = 32); the workspaces hold the oracle's
+    codes and scales exactly when the two kernels ran and are untouched
+    (still NaN-filled) when the fused kernel ran."""
+    x = synth.llama_activations(M + N + K, M, K, 7)
+    w = synth.normal_bf16(N + K, (N, K), 0.02)
+    wq, ws = oq.weight_block_quant(w)
+    xd, wqd, wsd = to_dev_bf16(x), to_dev(wq), to_dev(ws)
+    xq_ws = torch.full((M, K), 0x7F, dtype=torch.uint8, device=dev())
+    xs_ws = torch.full((M, K // 128), float("nan"), dtype=torch.float32, device=dev())
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev())
+    fb.fp8_linear(xd, wqd, wsd, y, xq_ws, xs_ws)
+    y2 = two_launch(xd, wqd, wsd)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_to_host(y), bf16_to_host(y2))
+    if fused:
+        assert bool(torch.all(xq_ws == 0x7F)) and bool(torch.all(torch.isnan(xs_ws)))
+    else:
+        oxq, oxs = oq.act_quant_group(x)
+        assert np.array_equal(host(xq_ws), oxq)
+        assert np.array_equal(host(xs_ws).view(np.uint32), oxs.view(np.uint32))
 
 
 @pytest.mark.parametrize("N,K", [(4096, 4096), (14336, 4096), (4096, 14336), (24576, 1536),
