@@ -1490,13 +1490,22 @@ static hipError_t launch_tiled_ks(const void *xq, const S *xs, int64_t xs_rs, in
 }
 
 // Configuration choice (both scale types): the decode kernel for M <= 64
-// (fp32 scales: while its LDS scale staging fits), 256x256 tiles when they
-// fill the chip (>= 192 tiles), 128x128 otherwise.
+// (fp32 scales: while its LDS scale staging fits, and for 33-64 rows only
+// below kDecWideN columns), 256x256 tiles when they fill the chip (>= 192
+// tiles), 128x128 otherwise.  With four row fragments every decode
+// workgroup reads four times its weight bytes of x, and for wide N the
+// tiled kernel (rows padded to 128) wins: measured at M = 33-64, weights
+// streamed from HBM, decode against tiled: 14336x4096 38.7-43.8 / 31.7-34.7
+// us, 24576x1536 28.2-30.9 / 16.5-18.0, 18432x7168 73.6-101.3 / 52.9-57.3;
+// narrower shapes the other way (4096x4096 11.9-14.1 / 31.2-32.7,
+// 7168x16384 62.0-71.7 / 103-114).
+constexpr int64_t kDecWideN = 8192;
+
 template <typename S>
 static hipError_t dispatch_gemm(const void *xq, const S *xs, int64_t xs_rs, int xs_ks,
                                 const void *wq, const S *ws, int64_t M, int64_t N, int64_t K,
                                 void *y, hipStream_t stream) {
-  if (M <= kDecMaxM) {
+  if (M <= kDecMaxM && (std::is_same<S, uint8_t>::value || M <= 32 || N < kDecWideN)) {
     const int MF = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
     if (std::is_same<S, uint8_t>::value || (K / 128) * MF * 16 * 4 <= kDecMaxScaleBytes) {
       if (MF == 1) return launch_decode<1, S>(xq, xs, xs_rs, xs_ks, wq, ws, M, N, K, y, stream);
@@ -1528,8 +1537,19 @@ static hipError_t dispatch_gemm(const void *xq, const S *xs, int64_t xs_rs, int 
 // 2 us.  Measured: q_a 512x1536x7168 41.2 -> 21.2 us, kv_a 512x576x7168
 // 30.5 -> 18.7 us, 1024x1024x4096 25.3 -> 19.3 us; 256x7168x2048 (12.6 ->
 // 19.6) and 300x576x2048 (12.5 -> 13.2) are slower split and stay whole.
+//
+// fp32 scales with 33-64 rows and K >= kSplitSmallMMinK take this split
+// (one padded row tile) instead of the decode kernel: measured at M =
+// 33-64, weights streamed from HBM, decode against the split: 4096x14336
+// 28.1-39.2 / 23.1-25.0 us, 1536x7168 16.4-21.3 / 14.5-15.8, 576x7168
+// 15.5-20.0 / 12.7-13.8, 7168x16384 60.9-70.5 / 39.8-43.5, 7168x18432
+// (whose scales do not fit the decode kernel: the plain tiled kernel)
+// 118.8-130.3 / 42.0-45.4; at K = 4096 the decode kernel is as fast or
+// faster (4096x4096 11.9-14.1 / 14.9-16.6, 1024x4096 11.4-12.9 /
+// 11.3-12.4).
 constexpr int64_t kSplitMaxTiles = 128;
 constexpr int kSplitMinKb = 4;
+constexpr int64_t kSplitSmallMMinK = 6144;
 
 // even: every range a multiple of 2 K blocks (the E8M0 tile's two wave
 // groups cannot sit a step out), hence K/128 even too.
@@ -1537,7 +1557,8 @@ static int splitk_plan(int64_t M, int64_t N, int64_t K, int &kb_per, int64_t &sl
                        bool even = false) {
   // (also called before argument validation: sizes past the library's
   // limits are simply not split)
-  if (M <= kDecMaxM || N <= 0 || K <= 0) return 0;
+  if (M <= (even ? kDecMaxM : 32) || N <= 0 || K <= 0) return 0;
+  if (!even && M <= kDecMaxM && K < kSplitSmallMMinK) return 0;
   if (M > (int64_t(1) << 31) || N > (int64_t(1) << 31) || K > (int64_t(1) << 24)) return 0;
   const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
   if (tiles > kSplitMaxTiles) return 0;

@@ -120,7 +120,9 @@ FP8BLK_API fp8blk_status fp8_block_gemm(const void *x_q, const float *x_scale,
  * empty (e.g. 8192 x 7168 x 16384: 896 tiles, 3.5 rounds); and decode
  * batches of 9 to 16 rows with long K (e.g. a 4096 x 14336 down
  * projection), where a workgroup covering 64 output columns over part of K
- * re-reads less of x than one covering 16 columns over all of it.  The same
+ * re-reads less of x than one covering 16 columns over all of it, and of
+ * 33 to 64 rows with K >= 6144, where one row tile of 128 split over K
+ * beats the decode kernel's per-workgroup re-reads of x.  The same
  * operation and passage as fp8_block_gemm: a workgroup runs one output tile
  * over one contiguous range of K blocks, promoting each 128-long partial
  * sum with its scale pair into fp32 as fp8_block_gemm does, and stores the
@@ -132,7 +134,8 @@ FP8BLK_API fp8blk_status fp8_block_gemm(const void *x_q, const float *x_scale,
  * tiles are not bit-identical to fp8_block_gemm (the fp32 sums are
  * associated differently), unsplit ones are.
  *   fp8_block_gemm_workspace_bytes(M, N, K): bytes the split needs, 0 when
- *     it is not used for these sizes.  17 <= M <= 64 never splits.  M > 64:
+ *     it is not used for these sizes.  17 <= M <= 32 never splits.  M > 32
+ *     (with K >= 6144 when M <= 64):
  *     either at most 128 output tiles of 128x128 and K long enough for the
  *     split to gain (a time model measured on MI355X picks the number of K
  *     ranges, 2 to min(256 / tiles, K / 512), or none): ranges x M x N x 4

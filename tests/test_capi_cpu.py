@@ -104,7 +104,15 @@ def test_gemm_validation(lib, args, want):
     (65, 1, 5120, 10 * 68 * 4),                 # slices padded to a multiple of 4 floats
     (256, 7168, 2048, 0),                       # the model gains too little (measured slower)
     (300, 576, 2048, 0),
-    (64, 1536, 7168, 0),                        # 17 <= M <= 64: the decode kernel, whole
+    (32, 1536, 7168, 0),                        # 17 <= M <= 32: the decode kernel, whole
+    # 33 <= M <= 64 with K >= 6144: one row tile of 128 (rows padded), K split
+    (64, 1536, 7168, 14 * 64 * 1536 * 4),       # DeepSeek-V3 q_a: 14 ranges of 4 K blocks
+    (33, 4096, 14336, 8 * 33 * 4096 * 4),       # Llama down: 8 ranges of 14
+    (33, 4096, 6144, 8 * 33 * 4096 * 4),        # K = 6144: the smallest K split at this M
+    (33, 4096, 6016, 0),                        # K < 6144: the decode kernel
+    (48, 4096, 4096, 0),
+    (64, 14336, 4096, 0),                       # 112 tiles, K = 4096: the model gains too little
+    (64, 7168, 18432, 7340032),                 # DeepSeek-V3 MLP down
     (4096, 1024, 4096, 0),                      # 256 tiles: the chip is full
     # 9 <= M <= 16: decode with four 16-column slabs per workgroup, K split
     # so that (N/64 column groups) x (splits) fills the chip
@@ -378,7 +386,7 @@ def test_noalloc_scratch_covers_every_split_plan(lib):
     assert m and fb.SCRATCH_BYTES == 16 * 1024 * 1024 + 64 * 1024
     worst = 0
     for K in (512, 1024, 2048, 4096, 7168, 14336, 18432, 32768, 65536):
-        for M in list(range(9, 17)) + list(range(65, 2100, 37)):
+        for M in list(range(9, 17)) + list(range(33, 65, 5)) + list(range(65, 2100, 37)):
             for N in list(range(1, 4200, 97)) + [576, 1536, 7168, 16384]:
                 # at 192 or more output tiles of 256x256 the plan can only be
                 # the stream-K tail, which fp8_block_gemm_noalloc never runs

@@ -111,7 +111,7 @@ def test_linear_workspace_path(M):
 
 @pytest.mark.parametrize("M,N,K,fused", [(24, 4096, 4096, True), (32, 1536, 7168, True),
                                          (17, 14336, 4096, False), (48, 4096, 4096, False),
-                                         (64, 1024, 4096, False)])
+                                         (64, 1024, 4096, False), (40, 14336, 4096, False)])
 def test_linear_with_workspaces_small_batch(M, N, K, fused):
     """fp8_linear with workspaces at M = 17-64: fused for 16 < M <= 32 with
     N * K <= 2^24, else the quantizer into the workspaces and the GEMM.

@@ -44,10 +44,13 @@ def quantized_operands(x_bits, w_bits):
 # ----------------------------------------------------------------------------
 # exact pins
 
-@pytest.mark.parametrize("M,N,K", [(16, 16, 128), (64, 192, 1024), (130, 576, 4096), (1, 300, 512)])
+@pytest.mark.parametrize("M,N,K", [(16, 16, 128), (64, 192, 1024), (130, 576, 4096), (1, 300, 512),
+                                   (40, 9000, 256), (64, 8192, 384)])
 def test_gemm_exact_integer_operands(M, N, K):
     """|codes| <= 8 integers, scales in {1/2, 1, 2}: every partial sum and
-    every promotion is exact in fp32, so y must equal bf16_RNE(exact)."""
+    every promotion is exact in fp32, so y must equal bf16_RNE(exact).
+    (40, 9000) and (64, 8192): 33-64 rows with N >= 8192 take the tiled
+    kernel (one padded row tile) instead of the decode kernel."""
     rng = np.random.default_rng(M + N + K)
     xi = rng.integers(-8, 9, (M, K)); wi = rng.integers(-8, 9, (N, K))
     xq = oe.encode(xi.astype(np.float32)); wq = oe.encode(wi.astype(np.float32))
@@ -245,14 +248,16 @@ def gpu_gemm_plain(xq, xs, wq, ws):
 
 
 @pytest.mark.parametrize("M,N,K", [(65, 1536, 7168), (130, 100, 3072), (77, 333, 5760),
-                                   (1000, 700, 5632), (512, 1536, 7168), (257, 129, 4096)])
+                                   (1000, 700, 5632), (512, 1536, 7168), (257, 129, 4096),
+                                   (40, 1000, 8192), (48, 576, 7168), (33, 300, 6144)])
 def test_gemm_split_over_workgroups_exact(M, N, K):
     """Integer operands with power-of-two scales: every partial sum of every
     K range, and their sum, is exact in fp32, so the split result must equal
     bf16_RNE(exact) bit for bit (ranges, scale offsets and the reduction
     indexing are all checked).  The shapes cover ragged M and N, ranges of
-    an odd number of K blocks (77x333x5760: 9 ranges of 5) and a shorter
-    last range (1000x700x5632: 5 ranges of 9, the last of 8)."""
+    an odd number of K blocks (77x333x5760: 9 ranges of 5), a shorter
+    last range (1000x700x5632: 5 ranges of 9, the last of 8), and 33-64
+    rows with K >= 6144 (one row tile of 128, most of it padding)."""
     assert fb.fp8_block_gemm_workspace_bytes(M, N, K) > 0, "shape must take the split path"
     rng = np.random.default_rng(M * 13 + N + K)
     xi = rng.integers(-8, 9, (M, K)); wi = rng.integers(-8, 9, (N, K))
