@@ -1633,6 +1633,25 @@ static int any_split_plan(int64_t M, int64_t N, int64_t K, int &kb_per, int64_t 
 // for the second launch.  Used only when the model gains more than 8 us
 // (DeepSeek-V3 o_proj and MLP down at M = 8192: 3.5 rounds of tiles, the
 // last half-empty; a short-K tail such as Llama gate/up's gains nothing).
+//
+// Grids of fewer than 192 256x256 tiles run the 128x128 kernels; with long
+// K (at least 56 blocks), at least 32 such tiles and more than
+// kSplitMaxTiles 128x128 tiles (past the split over workgroups), the whole
+// grid runs as stream-K on 256x256 tiles (no data-parallel part) when the
+// same model of it beats an estimate of the 128x128 kernel by 10 %: ~0.9
+// us per K block with one tile per CU (split K inside the workgroup, at
+// most 256 tiles), ~1.46 us per K block and round of 512 tiles (two per
+// CU) beyond.  The estimates fit measurements on MI355X within ~20 %, and
+// the rule took every measured case the faster way but for a few small
+// gains forgone; measured (random codes, one launch at a time) DeepSeek-V3
+// at M = 512 o_proj 7168x16384 116 -> 98 us, MLP up 18432x7168 139 -> 117,
+// MLP down 7168x18432 132 -> 101; at M = 768-1536 o_proj 160-280 ->
+// 124-205, MLP down 175-329 -> 126-263, Llama down 4096x14336 101-134 ->
+// 72-111; short K (K = 4096 and below) and MLP up at M = 384 (one round of
+// 432 128x128 tiles: 82 us against 99) stay on the 128x128 kernels.
+constexpr int64_t kSkSmallMinTiles = 32;
+constexpr int64_t kSkSmallMinKb = 56;
+
 struct SkPlan {
   int t_dp = 0, rem = 0, L = 0, nsk = 0;
   size_t bytes = 0;
@@ -1645,15 +1664,29 @@ static bool sk_plan(int64_t M, int64_t N, int64_t K, SkPlan &p) {
   if (M > (int64_t(1) << 31) || N > (int64_t(1) << 31) || K > (int64_t(1) << 24)) return false;
   using T = Tile<2, 4, 8>;
   const int64_t tiles = ((M + T::TM - 1) / T::TM) * ((N + T::TN - 1) / T::TN);
-  if (tiles < 192 || tiles > (int64_t(1) << 24)) return false;  // not the 256x256 path
-  const int64_t rem = tiles % kCUs, KB = K / 128;
+  if (tiles > (int64_t(1) << 24)) return false;
+  const int64_t KB = K / 128;
+  const bool small = tiles < 192;  // below the 256x256 path's threshold
+  if (small) {
+    const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
+    if (tiles < kSkSmallMinTiles || KB < kSkSmallMinKb || t128 <= kSplitMaxTiles) return false;
+  }
+  const int64_t rem = tiles % kCUs;
   if (rem == 0) return false;
   const int64_t L = (rem * KB + kCUs - 1) / kCUs;
   const int64_t nsk = (rem * KB + L - 1) / L;
   const int64_t pieces = nsk + rem;  // upper bound (and the slot count)
-  const double saved = 1.9 * (double)(KB - L);
   const double cost = 4.0 + 2.0 * (double)pieces * (double)(T::TM * T::TN * 4) / 4.0e6;
-  if (saved - cost <= 8.0) return false;
+  if (small) {
+    const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
+    const double cur = t128 <= kKsMaxTiles
+                           ? 0.9 * (double)KB
+                           : 1.46 * (double)KB * (double)((t128 + 2 * kCUs - 1) / (2 * kCUs));
+    if (1.9 * (double)L + cost > 0.9 * cur) return false;
+  } else {
+    const double saved = 1.9 * (double)(KB - L);
+    if (saved - cost <= 8.0) return false;
+  }
   p.t_dp = (int)(tiles - rem);
   p.rem = (int)rem;
   p.L = (int)L;

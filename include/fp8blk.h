@@ -117,7 +117,8 @@ FP8BLK_API fp8blk_status fp8_block_gemm(const void *x_q, const float *x_scale,
  * tiles would leave compute units idle: small M and N with long K (e.g.
  * the DeepSeek-V3 q_a and kv_a projections at a few hundred tokens); large
  * grids of 256x256 tiles whose last round of 256 compute units is partly
- * empty (e.g. 8192 x 7168 x 16384: 896 tiles, 3.5 rounds); and decode
+ * empty (e.g. 8192 x 7168 x 16384: 896 tiles, 3.5 rounds), or that fill
+ * less than one round with long K (e.g. 512 x 7168 x 16384); and decode
  * batches of 9 to 16 rows with long K (e.g. a 4096 x 14336 down
  * projection), where a workgroup covering 64 output columns over part of K
  * re-reads less of x than one covering 16 columns over all of it, and of
@@ -143,7 +144,11 @@ FP8BLK_API fp8blk_status fp8_block_gemm(const void *x_q, const float *x_scale,
  *     of 256, where a time model (1.9 us per K block of a tile against the
  *     partial sums' traffic) gains more than 8 us: (the ranges, at most
  *     256, plus the last round's tiles) x 256 KB (100.7 MB for 8192 x 7168
- *     x 16384).
+ *     x 16384); or 32 to 191 tiles of 256x256 with K >= 7168 and more than
+ *     128 tiles of 128x128, run wholly as stream-K where the same model
+ *     beats an estimate of the 128x128 kernels by 10 % (e.g. the
+ *     DeepSeek-V3 o_proj, MLP up and MLP down at M = 512): (the ranges plus
+ *     the tiles) x 256 KB (81.8 MB for 512 x 7168 x 16384).
  *     9 <= M <= 16: ceil(N / 64) column groups times the number of K ranges
  *     (at most 256 / groups and K / 2048) must reach 192, where N is too
  *     small for ceil(N / 64) groups alone to fill the chip and K is at most

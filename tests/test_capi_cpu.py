@@ -388,9 +388,9 @@ def test_noalloc_scratch_covers_every_split_plan(lib):
     for K in (512, 1024, 2048, 4096, 7168, 14336, 18432, 32768, 65536):
         for M in list(range(9, 17)) + list(range(33, 65, 5)) + list(range(65, 2100, 37)):
             for N in list(range(1, 4200, 97)) + [576, 1536, 7168, 16384]:
-                # at 192 or more output tiles of 256x256 the plan can only be
-                # the stream-K tail, which fp8_block_gemm_noalloc never runs
-                if M > 64 and -(-M // 256) * -(-N // 256) >= 192:
+                # past 128 output tiles of 128x128 (M > 64) the plan can only
+                # be stream-K, which fp8_block_gemm_noalloc never runs
+                if M > 64 and -(-M // 128) * -(-N // 128) > 128:
                     continue
                 worst = max(worst, lib.fp8_block_gemm_workspace_bytes(M, N, K))
     assert 0 < worst <= fb.SCRATCH_BYTES, worst
@@ -406,6 +406,25 @@ def test_noalloc_validates_before_the_device(lib):
     st = lib.fp8_block_gemm_noalloc(None, B, C, D, 64, 64, 128, E_, None)
     assert st == 1
     assert lib.fp8_block_gemm_noalloc(A, B, C, D, 0, 64, 128, E_, None) in (0, 4)
+
+
+def test_stream_k_small_grid_plan(lib):
+    """Grids of 32-191 256x256 tiles with K >= 7168 and more than 128
+    128x128 tiles run wholly as stream-K when the model beats the 128x128
+    kernels' estimate by 10 %: DeepSeek-V3 o_proj, MLP up and MLP down at
+    M = 512, Llama down at M = 768; not MLP up at M = 384 (one round of
+    128x128 tiles), short K, or the split-over-workgroups regime."""
+    slot = 256 * 256 * 4
+    lib.fp8_block_gemm_workspace_bytes.restype = ctypes.c_size_t
+    lib.fp8_block_gemm_workspace_bytes.argtypes = [ctypes.c_int64] * 3
+    assert lib.fp8_block_gemm_workspace_bytes(512, 7168, 16384) == 312 * slot
+    assert lib.fp8_block_gemm_workspace_bytes(512, 18432, 7168) == 396 * slot
+    assert lib.fp8_block_gemm_workspace_bytes(512, 7168, 18432) == 308 * slot
+    assert lib.fp8_block_gemm_workspace_bytes(768, 4096, 14336) == 304 * slot
+    assert lib.fp8_block_gemm_workspace_bytes(700, 4000, 14336) == 304 * slot
+    for M, N, K in ((384, 18432, 7168), (512, 4096, 4096), (1536, 4096, 4096),
+                    (1024, 4096, 14336), (512, 24576, 1536), (768, 18432, 7168)):
+        assert lib.fp8_block_gemm_workspace_bytes(M, N, K) == 0, (M, N, K)
 
 
 def test_stream_k_tail_plan(lib):

@@ -418,6 +418,49 @@ def test_stream_k_tail_exact_ragged():
     assert bad.size == 0, f"{len(bad)} outputs differ, first {bad[:3].tolist()}"
 
 
+@pytest.mark.parametrize("M,N", [(768, 4096), (700, 4000)])
+def test_stream_k_small_grid_exact(M, N):
+    """A grid of 48 256x256 tiles with K = 14336 (112 blocks) runs entirely
+    as stream-K: 256 ranges of 21 K blocks over the linearized (tile, block)
+    space, every range spanning one or two tiles, no data-parallel part.
+    700 x 4000 makes the last row and column tiles ragged.  Integer
+    operands with power-of-two scales keep every partial sum exact, so the
+    sampled rows (from every row tile) must equal bf16_RNE(exact) in every
+    column; a second call into a zero-filled workspace gives the same
+    bits."""
+    K = 14336
+    need = fb.fp8_block_gemm_workspace_bytes(M, N, K)
+    assert need == 304 * 256 * 256 * 4
+    rng = np.random.default_rng(M + N)
+    xq = oe.encode(rng.integers(-8, 9, (M, K)).astype(np.float32))
+    wq = oe.encode(rng.integers(-8, 9, (N, K)).astype(np.float32))
+    KB, NB = K // 128, -(-N // 128)
+    xs = np.exp2(rng.integers(-1, 2, (M, KB))).astype(np.float32)
+    ws = np.exp2(rng.integers(0, 2, (NB, KB))).astype(np.float32)
+    y, _ = gpu_gemm_ws(xq, xs, wq, ws)
+    y2, _ = gpu_gemm_ws(xq, xs, wq, ws, fill=0x00)
+    assert np.array_equal(y, y2)
+    rows = np.unique(np.concatenate([[0, 255, 256, 511, 512, M - 1],
+                                     rng.choice(M, 26, replace=False)]))
+    want = og.bf16_rne_bits(og.block_gemm(xq[rows], xs[rows], wq, ws))
+    bad = np.argwhere(y[rows] != want)
+    assert bad.size == 0, f"{len(bad)} outputs differ, first {bad[:3].tolist()}"
+
+
+def test_stream_k_small_grid_dsv3_m512_tolerance():
+    """DeepSeek-V3 o_proj at M = 512 (56 tiles of 256x256, K = 16384) on the
+    small-grid stream-K path, data-like operands quantized by the oracle:
+    every row within the GEMM tolerance."""
+    M, N, K = 512, 7168, 16384
+    assert fb.fp8_block_gemm_workspace_bytes(M, N, K) == 312 * 256 * 256 * 4
+    x = synth.dsv3_activations(77, M, K, 78)
+    w = synth.normal_bf16(79, (N, K), 0.01)
+    xq, xs, wq, ws = quantized_operands(x, w)
+    y, _ = gpu_gemm_ws(xq, xs, wq, ws)
+    check_tol(y, og.block_gemm(xq, xs, wq, ws), og.term_magnitude(xq, xs, wq, ws),
+              "stream-K small grid o_proj M=512")
+
+
 def test_stream_k_tail_without_workspace_is_plain():
     """Without a large enough workspace the stream-K shape runs
     fp8_block_gemm (same bits) and leaves the workspace alone."""
