@@ -511,11 +511,12 @@ def linear(x, w_q, w_scale):
     """The FP8 linear layer: dynamic per-token-group quantization of x, then
     the block-scaled GEMM on the current stream (fp32 scales: one C call,
     fused into one kernel where the library finds that faster, M <= 32; the
-    quantizer then the split-K GEMM when the library plans a K split: output
-    grids too small to fill the chip, and 9 <= M <= 16 with long K, where the
-    fused kernel's per-column re-reads of x cost more than the separate
-    quantizer).  E8M0 weight scales select power-of-two activation scales as
-    well."""
+    quantizer then the GEMM with a workspace when the library asks for one:
+    output grids too small to fill the chip (K split over workgroups, or
+    stream-K with long K), a partly empty last round of tiles, and 9 <= M <=
+    16 or 33 <= M <= 64 with long K, where re-reading x per column slab costs
+    more than the separate quantizer and the split).  E8M0 weight scales
+    select power-of-two activation scales as well."""
     if _is_e8m0(w_scale):
         x_q, x_s = act_quant_group(x, "ue8m0")
         return block_gemm(x_q, x_s, w_q, w_scale)
