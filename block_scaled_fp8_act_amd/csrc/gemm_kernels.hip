@@ -944,16 +944,18 @@ static hipError_t launch_decode(const void *xq, const S *xs, int64_t xs_rs, int 
                                 void *y, hipStream_t stream) {
   const int64_t KB = K / 128;
   // slabs per workgroup: up to four for one or two row fragments, up to two
-  // for four (their partials fill 128 KB of LDS); with fp32 block scales
-  // only for more than one fragment (E8M0 and row-wise keep one).  Every
-  // workgroup reads all of x (M x K bytes) once per K pass, as many bytes
-  // as its slab of weights at M = 16 and twice or four times as many at
-  // M = 32 or 64, so packing slabs cuts the bytes per output column:
-  // measured (weights streamed from HBM) 14336 x 4096 at M = 17-32
-  // 27.3-31.8 -> 18.7-20.0 us, M = 48-64 44-51 -> 41-44 us; 7168 x 16384
-  // at M = 17-32 42-52 -> 32-36 us, M = 64 85 -> 71 us; shapes that keep
-  // one slab unchanged.
-  constexpr bool kBlk = std::is_same<S, float>::value && !kRow;
+  // for four (their partials fill 128 KB of LDS); for more than one
+  // fragment with fp32 scales only (block or row-wise; packed E8M0 variants
+  // spill and measured mixed).  Every workgroup reads all of x (M x K
+  // bytes) once per K pass, as many bytes as its slab of weights at M = 16
+  // and twice or four times as many at M = 32 or 64, so packing slabs cuts
+  // the bytes per output column: measured (weights streamed from HBM)
+  // 14336 x 4096 at M = 17-32 27.3-31.8 -> 18.7-20.0 us, M = 48-64 44-51 ->
+  // 41-44 us; 7168 x 16384 at M = 17-32 42-52 -> 32-36 us, M = 64 85 -> 71
+  // us; row-wise 14336 x 4096 at M = 17-64 22.9-42.4 -> 15.3-29.4 us,
+  // 7168 x 16384 37.7-75.5 -> 30.3-48.3 us; shapes that keep one slab
+  // unchanged.
+  constexpr bool kBlk = std::is_same<S, float>::value;
   const int64_t slabs = (N + 15) / 16;
   const int NS = MF == 1 ? decode_slabs(N, 4) : (kBlk ? decode_slabs(N, MF == 2 ? 4 : 2) : 1);
   const size_t part = (size_t)kDecWaves * NS * MF * 64 * 16;

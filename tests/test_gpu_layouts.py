@@ -125,8 +125,12 @@ def gpu_rowwise_gemm(xq, xs, wq, ws):
 @pytest.mark.parametrize("M,N,K", [(16, 16, 128), (1, 300, 512), (64, 192, 1024),
                                    (130, 576, 4096), (2048, 4096, 512), (257, 1000, 640),
                                    (300, 2000, 2048), (1, 14380, 256), (7, 7176, 384),
-                                   (16, 14380, 512)])
+                                   (16, 14380, 512), (32, 14380, 256), (24, 7176, 384),
+                                   (64, 7176, 384), (48, 4100, 768)])
 def test_rowwise_gemm_exact_integer_operands(M, N, K):
+    """Integer codes with power-of-two row scales: exact, bit for bit.
+    M = 24-64 with N = 14380, 7176 and 4100 packs four or two 16-column
+    slabs per decode workgroup (ragged last slabs and groups)."""
     rng = np.random.default_rng(M + N + K)
     xq = oe.encode(rng.integers(-8, 9, (M, K)).astype(np.float32))
     wq = oe.encode(rng.integers(-8, 9, (N, K)).astype(np.float32))
@@ -151,7 +155,7 @@ def test_rowwise_gemm_ragged(M, N, K):
 
 
 @pytest.mark.parametrize("shape_index", range(4))
-@pytest.mark.parametrize("M", [1, 16, 4096])
+@pytest.mark.parametrize("M", [1, 16, 32, 64, 4096])
 def test_linear_rowwise_llama(shape_index, M):
     x, w = synth.llama_inputs(shape_index, M, config=3 if M > 16 else 2)
     wq_d, ws_d = fb.rowwise_quant(to_dev_bf16(w))
@@ -159,7 +163,7 @@ def test_linear_rowwise_llama(shape_index, M):
     torch.cuda.synchronize()
     wq, ws = olay.rowwise_quant(w)
     assert np.array_equal(host(wq_d), wq) and np.array_equal(host(ws_d).view(np.uint32), ws.view(np.uint32))
-    rows = np.arange(M) if M <= 16 else np.sort(np.concatenate(
+    rows = np.arange(M) if M <= 64 else np.sort(np.concatenate(
         [[0, M - 1], np.random.default_rng(shape_index).choice(np.arange(1, M - 1), 62, replace=False)]))
     xq, xs = olay.rowwise_quant(x[rows])
     check_tol(y[rows], olay.rowwise_gemm(xq, xs, wq, ws), olay.rowwise_term_magnitude(xq, xs, wq, ws),
