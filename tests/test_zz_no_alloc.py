@@ -54,8 +54,9 @@ def test_noalloc_matches_workspace_entry_two_calls():
 
 
 def test_noalloc_decode_split_and_unsplit():
-    # decode split (M = 12, long K), then a grid that needs no split
-    for M, N, K, seed in ((12, 4096, 14336, 3), (300, 2048, 1024, 4)):
+    # decode split (M = 12, long K), one padded row tile split over K
+    # (M = 48, long K), then a grid that needs no split
+    for M, N, K, seed in ((12, 4096, 14336, 3), (48, 4096, 14336, 6), (300, 2048, 1024, 4)):
         xq, xs, wq, ws = _operands(M, N, K, seed)
         y_ws, y_na, need = _both(xq, xs, wq, ws)
         say("noalloc", M, N, K, "split workspace", need)
@@ -67,11 +68,11 @@ def test_noalloc_decode_split_and_unsplit():
             assert np.array_equal(bf16_to_host(y_plain), y_na)
 
 
-def test_noalloc_stream_k_shape_runs_unsplit():
-    """A stream-K tail shape (3.5 rounds of 256x256 tiles, long K) needs far
-    more than the scratch: fp8_block_gemm_noalloc runs it as
-    fp8_block_gemm, bit for bit."""
-    M, N, K = 8192, 7168, 16384
+@pytest.mark.parametrize("M,N,K", [(8192, 7168, 16384), (512, 7168, 16384)])
+def test_noalloc_stream_k_shape_runs_unsplit(M, N, K):
+    """Stream-K shapes (a partly empty last round of 256x256 tiles, and a
+    small grid with long K) need far more than the scratch:
+    fp8_block_gemm_noalloc runs them as fp8_block_gemm, bit for bit."""
     assert fb.fp8_block_gemm_workspace_bytes(M, N, K) > fb.SCRATCH_BYTES
     d = dev()
     g = torch.Generator(device=d)
