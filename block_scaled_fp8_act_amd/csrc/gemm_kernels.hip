@@ -1492,22 +1492,25 @@ static hipError_t launch_tiled_ks(const void *xq, const S *xs, int64_t xs_rs, in
 }
 
 // Configuration choice (both scale types): the decode kernel for M <= 64
-// (fp32 scales: while its LDS scale staging fits, and for 33-64 rows only
-// below kDecWideN columns), 256x256 tiles when they fill the chip (>= 192
+// (fp32 scales: while its LDS scale staging fits; for 33-64 rows only below
+// kDecWideN columns), 256x256 tiles when they fill the chip (>= 192
 // tiles), 128x128 otherwise.  With four row fragments every decode
 // workgroup reads four times its weight bytes of x, and for wide N the
 // tiled kernel (rows padded to 128) wins: measured at M = 33-64, weights
 // streamed from HBM, decode against tiled: 14336x4096 38.7-43.8 / 31.7-34.7
-// us, 24576x1536 28.2-30.9 / 16.5-18.0, 18432x7168 73.6-101.3 / 52.9-57.3;
-// narrower shapes the other way (4096x4096 11.9-14.1 / 31.2-32.7,
-// 7168x16384 62.0-71.7 / 103-114).
-constexpr int64_t kDecWideN = 8192;
+// us, 24576x1536 28.2-30.9 / 16.5-18.0, 18432x7168 73.6-101.3 / 52.9-57.3,
+// 12288x4096 29.7-38.9 / 31.6-34.2; narrower shapes the other way
+// (8192x4096 22.6-24.7 / 31.4-32.6, 8192x7168 30.9-36.1 / 49.9-54.4,
+// 4096x4096 11.9-14.1 / 31.2-32.7).  E8M0 scales likewise: 14336x4096
+// 45.2-61.1 / 28.4-30.0 us, 24576x1536 29.8-36.3 / 15.7-17.2, 18432x7168
+// 77.0-101.6 / 46.1-49.3.
+constexpr int64_t kDecWideN = 12288;
 
 template <typename S>
 static hipError_t dispatch_gemm(const void *xq, const S *xs, int64_t xs_rs, int xs_ks,
                                 const void *wq, const S *ws, int64_t M, int64_t N, int64_t K,
                                 void *y, hipStream_t stream) {
-  if (M <= kDecMaxM && (std::is_same<S, uint8_t>::value || M <= 32 || N < kDecWideN)) {
+  if (M <= kDecMaxM && (M <= 32 || N < kDecWideN)) {
     const int MF = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
     if (std::is_same<S, uint8_t>::value || (K / 128) * MF * 16 * 4 <= kDecMaxScaleBytes) {
       if (MF == 1) return launch_decode<1, S>(xq, xs, xs_rs, xs_ks, wq, ws, M, N, K, y, stream);

@@ -108,13 +108,13 @@ def check_tol(y_bits, y_hat, S, what):
 
 @pytest.mark.parametrize("M,N,K", [(16, 16, 128), (64, 192, 1024), (130, 576, 4096),
                                    (1, 300, 512), (300, 520, 768), (2048, 2048, 512),
-                                   (32, 14380, 256), (64, 7176, 384), (40, 9000, 256)])
+                                   (32, 14380, 256), (64, 7176, 384), (40, 12300, 256)])
 def test_static_gemm_exact_integer_operands(M, N, K):
     """Integer codes |c| <= 8, activation scale 0.5, weight scales in
     {1/2, 1, 2}: exact in fp32, so y must equal bf16_RNE(exact).  The last
     three take the decode kernel with four and two column slabs per
     workgroup (M = 32, 64) and the tiled kernel at M = 33-64 with
-    N >= 8192."""
+    N >= 12288."""
     rng = np.random.default_rng(M + N + K)
     xq = oe.encode(rng.integers(-8, 9, (M, K)).astype(np.float32))
     wq = oe.encode(rng.integers(-8, 9, (N, K)).astype(np.float32))

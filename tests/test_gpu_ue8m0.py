@@ -163,15 +163,19 @@ def operands(x_bits, w_bits):
 @pytest.mark.parametrize("M,N,K", [(16, 16, 128), (64, 192, 1024), (130, 576, 4096),
                                    (1, 300, 512), (300, 520, 768), (1024, 1024, 1280),
                                    (257, 1000, 640), (200, 300, 384), (1024, 1024, 1152),
-                                   (1, 14380, 256), (16, 7176, 512), (16, 14336, 1024)])
+                                   (1, 14380, 256), (16, 7176, 512), (16, 14336, 1024),
+                                   (40, 12300, 256), (64, 14336, 384), (48, 8192, 256)])
 def test_gemm_ue8m0_exact_integer_operands(M, N, K):
     """|codes| <= 8 integers, scale bytes 126..128 (x) and 127..128 (W):
     every product and partial sum is exact in fp32, so y must equal
     bf16_RNE(exact).  Grids of at most 256 128x128 tiles split K over two
     wave groups when the K-block count is even (130x576x4096, 300x520x768,
     1024x1024x1280) and run unsplit when it is odd (the next three); the
-    last three are decode shapes wide enough for two 16-column slabs per
-    workgroup (a partly empty last workgroup, a ragged last slab)."""
+    next three are decode shapes wide enough for two 16-column slabs per
+    workgroup (a partly empty last workgroup, a ragged last slab); at
+    M = 33-64, N >= 12288 takes the 128x128 tiles (40x12300x256: two wave
+    groups, 64x14336x384: an odd K-block count, unsplit) and 48x8192 the
+    decode kernel."""
     rng = np.random.default_rng(M + N + K)
     xi = rng.integers(-8, 9, (M, K)); wi = rng.integers(-8, 9, (N, K))
     xq = oe.encode(xi.astype(np.float32)); wq = oe.encode(wi.astype(np.float32))
