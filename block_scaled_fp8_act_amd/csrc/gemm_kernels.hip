@@ -739,6 +739,10 @@ constexpr int kDecThreads = kDecWaves * 64;
 constexpr int kDecMaxM = 64;
 constexpr int kDecMaxScaleBytes = 32 * 1024;  // x_scale staging limit (KB * MF * 16 * 4)
 
+// NW waves per workgroup (kDecWaves by default; 8 for four row fragments
+// with fp32 block scales, whose twice larger register budget per wave holds
+// two load buffers without spilling).
+//
 // S = float: fp32 scales, promoted per K block with FMAs as in gemm_tile;
 // S = uint8_t: E8M0 scale bytes, loaded with the operands and applied by the
 // matrix core (nothing staged in LDS but the final partials).  kRow: fp32
@@ -746,8 +750,9 @@ constexpr int kDecMaxScaleBytes = 32 * 1024;  // x_scale staging limit (KB * MF 
 // the sum is scaled by xs[m] * ws[n] at the end.  kPartial (fp32 block
 // scales only): workgroup (x, s) takes K blocks [s * kb_per, (s + 1) * kb_per)
 // and writes its unrounded fp32 sums to part + s * slice (row stride N).
-template <int MF, typename S, bool kRow = false, int NS = 1, bool kPartial = false>
-__global__ __launch_bounds__(kDecThreads) void decode_gemm_kernel(
+template <int MF, typename S, bool kRow = false, int NS = 1, bool kPartial = false,
+          int NW = kDecWaves>
+__global__ __launch_bounds__(NW * 64) void decode_gemm_kernel(
     const uint8_t *__restrict__ xq, const S *__restrict__ xs, int64_t xs_rs, int xs_ks,
     const uint8_t *__restrict__ wq, const S *__restrict__ ws, int M, int64_t N, int64_t K,
     uint16_t *__restrict__ y, float *__restrict__ part, int64_t slice, int kb_per) {
@@ -759,10 +764,13 @@ __global__ __launch_bounds__(kDecThreads) void decode_gemm_kernel(
   // register buffers of U K blocks: two (the next batch's loads go out
   // before the current batch's MFMAs) unless four row fragments, four slabs
   // with E8M0 scale operands, or eight (slab, fragment) pairs leave no room
-  // in 128 VGPRs (then one, reloaded after its MFMAs; for the four E8M0
-  // slabs that still beats two slabs in two rounds of workgroups: 14336 x
-  // 4096 at M = 16 18.2 -> 14.5 us, M = 4 15.2 -> 13.8 us)
-  constexpr int NB = (MF >= 4 || (MX && NS == 4) || MF * NS >= 8) ? 1 : 2;
+  // in the 128 VGPRs of a 16-wave workgroup (then one, reloaded after its
+  // MFMAs; for the four E8M0 slabs that still beats two slabs in two rounds
+  // of workgroups: 14336 x 4096 at M = 16 18.2 -> 14.5 us, M = 4 15.2 ->
+  // 13.8 us).  With 8 waves (256 VGPRs) only the E8M0 case keeps one.
+  static_assert(NW == kDecWaves || NW == kDecWaves / 2, "16 or 8 waves");
+  constexpr bool kRoomy = NW < kDecWaves;
+  constexpr int NB = ((MX && NS == 4) || (!kRoomy && (MF >= 4 || MF * NS >= 8))) ? 1 : 2;
   constexpr int U = (4 / NB) / (MF * NS) > 0 ? (4 / NB) / (MF * NS) : 1;
   extern __shared__ __align__(16) float dsm[];
   float *s_as = dsm;                                  // [KB][R] (fp32 scales only)
@@ -791,7 +799,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_gemm_kernel(
   // the NS slabs (16 * NS <= 64 columns from a multiple of 16 * NS) share
   // one 128-column weight block
   const S *pws = ws + (n0 / 128) * KB;
-  const int nmine = wave < kbn ? (kbn - wave + kDecWaves - 1) / kDecWaves : 0;
+  const int nmine = wave < kbn ? (kbn - wave + NW - 1) / NW : 0;
 
   uint4 bw[NB][U][NS][2];
   v8i af[NB][U][MF];
@@ -801,7 +809,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_gemm_kernel(
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (j0 + u < nmine) {
-        const int kb = kb0 + wave + kDecWaves * (j0 + u);
+        const int kb = kb0 + wave + NW * (j0 + u);
         const int64_t ko = (int64_t)kb * 128;
 #pragma unroll
         for (int sl = 0; sl < NS; ++sl) {
@@ -823,7 +831,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_gemm_kernel(
   load(std::integral_constant<int, 0>{}, 0);
 
   if constexpr (!MX && !kRow) {
-    for (int i = t; i < kbn * R; i += kDecThreads) {
+    for (int i = t; i < kbn * R; i += NW * 64) {
       const int kb = kb0 + i / R, m = i % R;
       s_as[i] = xs[(int64_t)min(m, M - 1) * xs_rs + (int64_t)kb * xs_ks];
     }
@@ -841,7 +849,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_gemm_kernel(
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (j0 + u < nmine) {
-        const int kb = kb0 + wave + kDecWaves * (j0 + u);
+        const int kb = kb0 + wave + NW * (j0 + u);
         float4 s4[MF];
         float wsc = 1.0f;
         if constexpr (!MX && !kRow) {
@@ -898,7 +906,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_gemm_kernel(
     const int sl = wave / MF, f = wave % MF;
     v4f sum = s_part[(sl * MF + f) * 64 + lane];
 #pragma unroll
-    for (int w = 1; w < kDecWaves; ++w) {
+    for (int w = 1; w < NW; ++w) {
       const v4f v = s_part[((w * NS + sl) * MF + f) * 64 + lane];
       sum[0] += v[0]; sum[1] += v[1]; sum[2] += v[2]; sum[3] += v[3];
     }
@@ -955,10 +963,18 @@ static hipError_t launch_decode(const void *xq, const S *xs, int64_t xs_rs, int 
   // us; row-wise 14336 x 4096 at M = 17-64 22.9-42.4 -> 15.3-29.4 us,
   // 7168 x 16384 37.7-75.5 -> 30.3-48.3 us; shapes that keep one slab
   // unchanged.
+  //
+  // Four row fragments with fp32 block scales run 8 waves per workgroup:
+  // with 16 they had one load buffer and spilled; with 8 (256 VGPRs each)
+  // they keep two and none spills.  Measured (M = 24-64, weights streamed
+  // from HBM, one launch at a time): 7168 x 16384 at M = 48 / 64 71.0 /
+  // 76.6 -> 52.2 / 57.4 us, the other decode shapes within 3 %.  One or
+  // two fragments keep 16 waves (8 measured up to 16 % slower at M = 1-16).
   constexpr bool kBlk = std::is_same<S, float>::value;
+  constexpr int NW = (MF == 4 && kBlk && !kRow) ? kDecWaves / 2 : kDecWaves;
   const int64_t slabs = (N + 15) / 16;
   const int NS = MF == 1 ? decode_slabs(N, 4) : (kBlk ? decode_slabs(N, MF == 2 ? 4 : 2) : 1);
-  const size_t part = (size_t)kDecWaves * NS * MF * 64 * 16;
+  const size_t part = (size_t)NW * NS * MF * 64 * 16;
   const size_t lds = (std::is_same<S, uint8_t>::value || kRow)
                          ? part
                          : std::max((size_t)KB * MF * 16 * 4, part);
@@ -967,15 +983,16 @@ static hipError_t launch_decode(const void *xq, const S *xs, int64_t xs_rs, int 
   const auto *b = static_cast<const uint8_t *>(wq);
   auto *out = static_cast<uint16_t *>(y);
   if (NS == 4)
-    hipLaunchKernelGGL((decode_gemm_kernel<MF, S, kRow, (MF == 1 || (kBlk && MF == 2) ? 4 : 1)>),
-                       grid, dim3(kDecThreads), lds, stream, a, xs, xs_rs, xs_ks, b, ws, (int)M, N,
-                       K, out, nullptr, (int64_t)0, 0);
+    hipLaunchKernelGGL(
+        (decode_gemm_kernel<MF, S, kRow, (MF == 1 || (kBlk && MF == 2) ? 4 : 1), false, NW>),
+        grid, dim3(NW * 64), lds, stream, a, xs, xs_rs, xs_ks, b, ws, (int)M, N, K, out, nullptr,
+        (int64_t)0, 0);
   else if (NS == 2)
-    hipLaunchKernelGGL((decode_gemm_kernel<MF, S, kRow, (MF == 1 || kBlk ? 2 : 1)>), grid,
-                       dim3(kDecThreads), lds, stream, a, xs, xs_rs, xs_ks, b, ws, (int)M, N, K,
-                       out, nullptr, (int64_t)0, 0);
+    hipLaunchKernelGGL((decode_gemm_kernel<MF, S, kRow, (MF == 1 || kBlk ? 2 : 1), false, NW>),
+                       grid, dim3(NW * 64), lds, stream, a, xs, xs_rs, xs_ks, b, ws, (int)M, N,
+                       K, out, nullptr, (int64_t)0, 0);
   else
-    hipLaunchKernelGGL((decode_gemm_kernel<MF, S, kRow, 1>), grid, dim3(kDecThreads), lds,
+    hipLaunchKernelGGL((decode_gemm_kernel<MF, S, kRow, 1, false, NW>), grid, dim3(NW * 64), lds,
                        stream, a, xs, xs_rs, xs_ks, b, ws, (int)M, N, K, out, nullptr,
                        (int64_t)0, 0);
   return hipGetLastError();

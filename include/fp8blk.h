@@ -225,9 +225,12 @@ FP8BLK_API fp8blk_status fp8_grouped_block_gemm(const void *x_q, const float *x_
  * M > 64, 16-byte aligned), which then hold the activation codes and
  * scales.  The activation codes and scales are always
  * those of fp8_act_quant_group; y is bit-identical to fp8_act_quant_group
- * followed by fp8_block_gemm except in the fused kernel for 32 < M <= 64,
- * which runs only without workspaces (it splits K over fewer waves, so its
- * fp32 partial sums are added in another order).  It takes no GEMM workspace and so never the K splits of
+ * followed by fp8_block_gemm wherever that GEMM runs its decode kernel
+ * (M <= 32, and 32 < M <= 64 with N < 12288 and K <= 16384: the same K
+ * split over the same waves); where it runs a tiled kernel instead
+ * (32 < M <= 64 with N >= 12288 or K > 16384, reached by the fused kernel
+ * only without workspaces) the fp32 partial sums are added in another
+ * order.  It takes no GEMM workspace and so never the K splits of
  * fp8_block_gemm_ws (small grids, stream-K tail, decode with long K);
  * callers that want them run fp8_act_quant_group then fp8_block_gemm_ws.
  *   x_bf16 [M,K], w_q [N,K], w_scale [ceil(N/128),K/128] in; y_bf16 [M,N] out. */
