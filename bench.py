@@ -69,6 +69,12 @@ GEMM_SOURCE = os.path.join(ROOT, "block_scaled_fp8_act_amd", "csrc", "gemm_kerne
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "block_gemm_dsv3_m8192_traffic.md")
 
 
+def progress(msg):
+    """One line on stderr per finished part of the run (stdout carries only
+    the result line)."""
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
+
+
 def source_digest(path):
     import hashlib
     with open(path, "rb") as f:
@@ -250,6 +256,7 @@ def main():
                         *linear_leg(torch, fb, dev, stream, PREFILL_SHAPES, M_PREFILL, xs0,
                                     ws_bf16, args.steps, args.warmup))
     del xs0, ws_bf16
+    progress("Llama-3-8B prefill leg done")
 
     # --- headline: DeepSeek-V3 dense projections at M = 8192 ---------------
     xs0, ws_bf16 = gen_inputs_dsv3(torch, dev, 4000)
@@ -258,6 +265,7 @@ def main():
     del xs0, ws_bf16
     torch.cuda.empty_cache()
     head = leg_summary(DSV3_SHAPES, M_DSV3, wall, act_s, gemm_s, step_flops, act_bytes)
+    progress("DeepSeek-V3 M = 8192 leg done")
     gemm_tflops = step_flops / sum(gemm_s) / 1e12
     act_gbs = act_bytes / sum(act_s) / 1e9
     value = step_flops / wall / 1e12
@@ -297,10 +305,12 @@ def main():
     }
     out["act_quant"]["standalone"] = act_quant_alone(torch, fb, dev, stream)
     out["ceilings"] = ceilings(torch, stream, gemm_tflops)
+    progress("quantizer alone and matrix-core ceilings done")
     if args.rows:
         out["rows"] = other_rows(torch, fb, dev, stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
+        progress("CPU baseline done")
     if args.calibrate_copy:
         src = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -518,9 +528,11 @@ def other_rows(torch, fb, dev, stream):
                     {"split_k_us": round(t * 1e6, 2), "split_k_GB/s": round(byts / t / 1e9, 1)})
                 del work
         del copies
+    progress("rows: weight quant and decode GEMMs done")
     rows.update(ue8m0_rows(torch, fb, dev, stream, g))
     rows.update(static_rows(torch, fb, dev, stream))
     rows.update(rowwise_rows(torch, fb, dev, stream))
+    progress("rows: UE8M0, static and row-wise legs done")
     # the whole decode linear layer from bf16 x (M = 16): one fused kernel
     # against the two launches (act quant + GEMM); weights rotated
     for name, N, K in PREFILL_SHAPES:
@@ -567,6 +579,7 @@ def other_rows(torch, fb, dev, stream):
     t_graph = _time(torch, stream, graph.replay)
     rows["decode_step_M16"] = {"eager_us": round(t_eager * 1e6, 2), "graph_us": round(t_graph * 1e6, 2)}
     del lin, graph
+    progress("rows: decode linear layers done")
     # grouped MoE (32 experts, Zipf top-8 routing of 4096 tokens)
     _, off = synth.moe_routing()
     total = int(off[-1])
@@ -650,6 +663,7 @@ def other_rows(torch, fb, dev, stream):
                       "workspace_MB": round(need / 1e6, 2)})
         rows[f"dsv3_{name}_M512"] = r
         del x, xq, xsc, wq, wsc, y, work
+    progress("rows: MoE, SwiGLU and DeepSeek-V3 M = 512 done")
     # the tiny configuration (x[16,512], W[512,512]): one linear layer
     xt = torch.randn((16, 512), generator=g, device=dev).to(torch.bfloat16)
     wq, wsc = fb.weight_block_quant(torch.randn((512, 512), generator=g, device=dev).to(torch.bfloat16))
