@@ -767,10 +767,10 @@ __global__ __launch_bounds__(NW * 64) void decode_gemm_kernel(
   // in the 128 VGPRs of a 16-wave workgroup (then one, reloaded after its
   // MFMAs; for the four E8M0 slabs that still beats two slabs in two rounds
   // of workgroups: 14336 x 4096 at M = 16 18.2 -> 14.5 us, M = 4 15.2 ->
-  // 13.8 us).  With 8 waves (256 VGPRs) only the E8M0 case keeps one.
+  // 13.8 us).  With 8 waves (256 VGPRs) every variant keeps two.
   static_assert(NW == kDecWaves || NW == kDecWaves / 2, "16 or 8 waves");
   constexpr bool kRoomy = NW < kDecWaves;
-  constexpr int NB = ((MX && NS == 4) || (!kRoomy && (MF >= 4 || MF * NS >= 8))) ? 1 : 2;
+  constexpr int NB = (!kRoomy && (MF >= 4 || (MX && NS == 4) || MF * NS >= 8)) ? 1 : 2;
   constexpr int U = (4 / NB) / (MF * NS) > 0 ? (4 / NB) / (MF * NS) : 1;
   extern __shared__ __align__(16) float dsm[];
   float *s_as = dsm;                                  // [KB][R] (fp32 scales only)
@@ -970,10 +970,19 @@ static hipError_t launch_decode(const void *xq, const S *xs, int64_t xs_rs, int 
   // from HBM, one launch at a time): 7168 x 16384 at M = 48 / 64 71.0 /
   // 76.6 -> 52.2 / 57.4 us, the other decode shapes within 3 %.  One or
   // two fragments keep 16 waves (8 measured up to 16 % slower at M = 1-16).
+  //
+  // E8M0 scales past 16 rows (two or four fragments) likewise run 8 waves,
+  // which leaves room to pack slabs as the fp32 kernel does (with 16 waves
+  // the packed variants spilled, so they kept one slab).  Measured, one
+  // slab on 16 waves against packed slabs on 8: 14336 x 4096 at M = 17-32
+  // 33.8-42.1 -> 21.8-23.8 us, 7168 x 16384 at M = 17-64 51-112 -> 40-72
+  // us, the other Llama and DeepSeek-V3 decode shapes within 3 %.
   constexpr bool kBlk = std::is_same<S, float>::value;
-  constexpr int NW = (MF == 4 && kBlk && !kRow) ? kDecWaves / 2 : kDecWaves;
+  constexpr bool kMx8 = !kBlk && MF >= 2;
+  constexpr int NW = ((MF == 4 && kBlk && !kRow) || kMx8) ? kDecWaves / 2 : kDecWaves;
   const int64_t slabs = (N + 15) / 16;
-  const int NS = MF == 1 ? decode_slabs(N, 4) : (kBlk ? decode_slabs(N, MF == 2 ? 4 : 2) : 1);
+  const int NS = MF == 1 ? decode_slabs(N, 4)
+                         : ((kBlk || kMx8) ? decode_slabs(N, MF == 2 ? 4 : 2) : 1);
   const size_t part = (size_t)NW * NS * MF * 64 * 16;
   const size_t lds = (std::is_same<S, uint8_t>::value || kRow)
                          ? part
@@ -984,11 +993,12 @@ static hipError_t launch_decode(const void *xq, const S *xs, int64_t xs_rs, int 
   auto *out = static_cast<uint16_t *>(y);
   if (NS == 4)
     hipLaunchKernelGGL(
-        (decode_gemm_kernel<MF, S, kRow, (MF == 1 || (kBlk && MF == 2) ? 4 : 1), false, NW>),
+        (decode_gemm_kernel<MF, S, kRow, (MF == 1 || ((kBlk || kMx8) && MF == 2) ? 4 : 1), false,
+                            NW>),
         grid, dim3(NW * 64), lds, stream, a, xs, xs_rs, xs_ks, b, ws, (int)M, N, K, out, nullptr,
         (int64_t)0, 0);
   else if (NS == 2)
-    hipLaunchKernelGGL((decode_gemm_kernel<MF, S, kRow, (MF == 1 || kBlk ? 2 : 1), false, NW>),
+    hipLaunchKernelGGL((decode_gemm_kernel<MF, S, kRow, (MF == 1 || kBlk || kMx8 ? 2 : 1), false, NW>),
                        grid, dim3(NW * 64), lds, stream, a, xs, xs_rs, xs_ks, b, ws, (int)M, N,
                        K, out, nullptr, (int64_t)0, 0);
   else

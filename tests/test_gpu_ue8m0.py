@@ -164,7 +164,9 @@ def operands(x_bits, w_bits):
                                    (1, 300, 512), (300, 520, 768), (1024, 1024, 1280),
                                    (257, 1000, 640), (200, 300, 384), (1024, 1024, 1152),
                                    (1, 14380, 256), (16, 7176, 512), (16, 14336, 1024),
-                                   (40, 12300, 256), (64, 14336, 384), (48, 8192, 256)])
+                                   (40, 12300, 256), (64, 14336, 384), (48, 8192, 256),
+                                   (24, 14336, 256), (32, 7176, 384), (20, 4100, 512),
+                                   (40, 4100, 384), (64, 8200, 256)])
 def test_gemm_ue8m0_exact_integer_operands(M, N, K):
     """|codes| <= 8 integers, scale bytes 126..128 (x) and 127..128 (W):
     every product and partial sum is exact in fp32, so y must equal
@@ -175,7 +177,9 @@ def test_gemm_ue8m0_exact_integer_operands(M, N, K):
     workgroup (a partly empty last workgroup, a ragged last slab); at
     M = 33-64, N >= 12288 takes the 128x128 tiles (40x12300x256: two wave
     groups, 64x14336x384: an odd K-block count, unsplit) and 48x8192 the
-    decode kernel."""
+    decode kernel.  The last five run the decode kernel past 16 rows (8
+    waves): four slabs per workgroup at 24 rows, two at 32, 20 and 40 rows
+    (ragged last slabs, partly empty last workgroups), one at 64 rows."""
     rng = np.random.default_rng(M + N + K)
     xi = rng.integers(-8, 9, (M, K)); wi = rng.integers(-8, 9, (N, K))
     xq = oe.encode(xi.astype(np.float32)); wq = oe.encode(wi.astype(np.float32))
@@ -226,7 +230,8 @@ def test_gemm_ue8m0_extreme_scales():
                                    (130, 300, 1024), (257, 1000, 512), (16, 4096, 4096),
                                    (200, 129, 7168), (129, 257, 128), (33, 4096, 4096),
                                    (40, 300, 512), (64, 1024, 2048), (65, 256, 256),
-                                   (2, 24576, 1536), (3, 576, 18432), (520, 3000, 1280)])
+                                   (2, 24576, 1536), (3, 576, 18432), (520, 3000, 1280),
+                                   (32, 14336, 4096), (48, 7168, 16384)])
 def test_gemm_ue8m0_ragged(M, N, K):
     x = synth.dsv3_activations(M + 11 * K, M, K, N)
     w = synth.normal_bf16(N + 13 * K, (N, K), 0.02)
