@@ -736,6 +736,15 @@ __device__ __forceinline__ void gemm_tile_mx(const uint8_t *__restrict__ A,
 // once in LDS, transposed to [kb][row], while the first weight loads fly.
 constexpr int kDecWaves = 16;
 constexpr int kDecThreads = kDecWaves * 64;
+// Two row fragments (17-32 rows, fp32 block scales) run 8 waves from this
+// many columns on, in the decode GEMM and the fused layer alike (the same K
+// split over the same waves, so the two stay bit-identical).  Measured
+// against 16 waves, weights streamed from HBM, M = 17-32: the GEMM 14336 x
+// 4096 25.2-26.1 -> 22.5-22.7 us; the fused layer 14336 x 4096 33.3-37.5 ->
+// 33.1-33.9 us and 7168 x 16384 52.8-61.8 -> 52.0-53.9 us; on narrower
+// shapes the fused layer lost up to 12 % (4096 x 14336, 1536 x 7168 at
+// M = 17), hence the bound.
+constexpr int64_t kDecWide8N = 8192;
 constexpr int kDecMaxM = 64;
 constexpr int kDecMaxScaleBytes = 32 * 1024;  // x_scale staging limit (KB * MF * 16 * 4)
 
@@ -946,10 +955,10 @@ static int decode_slabs(int64_t N, int max_ns) {
 
 int linear_decode_slabs(int64_t M, int64_t N) { return decode_slabs(N, M <= 16 ? 4 : 2); }
 
-template <int MF, typename S, bool kRow = false>
-static hipError_t launch_decode(const void *xq, const S *xs, int64_t xs_rs, int xs_ks,
-                                const void *wq, const S *ws, int64_t M, int64_t N, int64_t K,
-                                void *y, hipStream_t stream) {
+template <int MF, typename S, bool kRow, int NW>
+static hipError_t launch_decode_nw(const void *xq, const S *xs, int64_t xs_rs, int xs_ks,
+                                   const void *wq, const S *ws, int64_t M, int64_t N, int64_t K,
+                                   void *y, hipStream_t stream) {
   const int64_t KB = K / 128;
   // slabs per workgroup: up to four for one or two row fragments, up to two
   // for four (their partials fill 128 KB of LDS); for more than one
@@ -977,9 +986,11 @@ static hipError_t launch_decode(const void *xq, const S *xs, int64_t xs_rs, int 
   // slab on 16 waves against packed slabs on 8: 14336 x 4096 at M = 17-32
   // 33.8-42.1 -> 21.8-23.8 us, 7168 x 16384 at M = 17-64 51-112 -> 40-72
   // us, the other Llama and DeepSeek-V3 decode shapes within 3 %.
+  //
+  // Two fragments with fp32 block scales take 8 waves from kDecWide8N
+  // columns on (launch_decode).
   constexpr bool kBlk = std::is_same<S, float>::value;
   constexpr bool kMx8 = !kBlk && MF >= 2;
-  constexpr int NW = ((MF == 4 && kBlk && !kRow) || kMx8) ? kDecWaves / 2 : kDecWaves;
   const int64_t slabs = (N + 15) / 16;
   const int NS = MF == 1 ? decode_slabs(N, 4)
                          : ((kBlk || kMx8) ? decode_slabs(N, MF == 2 ? 4 : 2) : 1);
@@ -1006,6 +1017,24 @@ static hipError_t launch_decode(const void *xq, const S *xs, int64_t xs_rs, int 
                        stream, a, xs, xs_rs, xs_ks, b, ws, (int)M, N, K, out, nullptr,
                        (int64_t)0, 0);
   return hipGetLastError();
+}
+
+template <int MF, typename S, bool kRow = false>
+static hipError_t launch_decode(const void *xq, const S *xs, int64_t xs_rs, int xs_ks,
+                                const void *wq, const S *ws, int64_t M, int64_t N, int64_t K,
+                                void *y, hipStream_t stream) {
+  constexpr bool kBlk = std::is_same<S, float>::value;
+  if constexpr (MF == 2 && kBlk && !kRow) {
+    if (N >= kDecWide8N)
+      return launch_decode_nw<MF, S, kRow, kDecWaves / 2>(xq, xs, xs_rs, xs_ks, wq, ws, M, N, K,
+                                                           y, stream);
+    return launch_decode_nw<MF, S, kRow, kDecWaves>(xq, xs, xs_rs, xs_ks, wq, ws, M, N, K, y,
+                                                    stream);
+  } else {
+    constexpr int NW = ((MF == 4 && kBlk && !kRow) || (!kBlk && MF >= 2)) ? kDecWaves / 2
+                                                                             : kDecWaves;
+    return launch_decode_nw<MF, S, kRow, NW>(xq, xs, xs_rs, xs_ks, wq, ws, M, N, K, y, stream);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1179,7 +1208,9 @@ static hipError_t launch_decode_linear(const void *x, const void *wq, const floa
 hipError_t launch_linear_decode(const void *x, const void *wq, const float *ws, int64_t M,
                                 int64_t N, int64_t K, void *y, hipStream_t stream) {
   if (M <= 16) return launch_decode_linear<1, 16>(x, wq, ws, M, N, K, y, stream);
-  if (M <= 32) return launch_decode_linear<2, 16>(x, wq, ws, M, N, K, y, stream);
+  if (M <= 32)
+    return N >= kDecWide8N ? launch_decode_linear<2, 8>(x, wq, ws, M, N, K, y, stream)
+                           : launch_decode_linear<2, 16>(x, wq, ws, M, N, K, y, stream);
   return launch_decode_linear<4, 8>(x, wq, ws, M, N, K, y, stream);
 }
 

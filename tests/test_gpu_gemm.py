@@ -100,13 +100,15 @@ def test_gemm_split_k_tiles_tolerance(M, N, K):
                                    (16, 14336, 1024), (3, 4100, 768),
                                    (17, 14380, 256), (32, 7176, 384), (24, 14336, 640),
                                    (33, 14380, 256), (64, 7176, 512), (48, 4100, 768),
-                                   (64, 4096, 1024)])
+                                   (64, 4096, 1024), (20, 8192, 384), (32, 8191, 256)])
 def test_gemm_decode_multi_slab_exact(M, N, K):
     """Decode shapes for which the launcher packs four (N = 14380, 14336 at
     M <= 32) or two (N = 7176 and 4100, and every packed shape at M = 33-64)
     16-column slabs per workgroup, with a partly empty last workgroup and a
     ragged last slab, and one unpacked shape (N = 4096 at M = 64): integer
-    operands, power-of-two scales, bit-exact against bf16_RNE(exact)."""
+    operands, power-of-two scales, bit-exact against bf16_RNE(exact).  At
+    17-32 rows N >= 8192 runs 8 waves per workgroup (14380, 14336, and
+    8192 against 8191 at the boundary), narrower N 16."""
     rng = np.random.default_rng(M * 5 + N + K)
     xi = rng.integers(-8, 9, (M, K)); wi = rng.integers(-8, 9, (N, K))
     xq = oe.encode(xi.astype(np.float32)); wq = oe.encode(wi.astype(np.float32))
