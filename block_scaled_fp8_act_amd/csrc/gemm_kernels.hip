@@ -16,8 +16,9 @@
 // chip; 128x128 tiles otherwise (with K split over two wave groups inside
 // the workgroup when there is at most one workgroup per CU, and, given a
 // caller workspace, over several workgroups when the grid would leave most
-// CUs idle); and a weight-streaming kernel with K split over its waves for
-// M <= 64 (decode).
+// CUs idle, or stream-K over 256x256 tiles for a partly empty last round
+// and for small grids with long K); and a weight-streaming kernel with K
+// split over its waves for M <= 64 (decode).
 //
 // With power-of-two scales stored as E8M0 bytes (the "UE8M0 scale format"
 // section of the same page) the scale pair is applied by the matrix core
@@ -726,8 +727,9 @@ __device__ __forceinline__ void gemm_tile_mx(const uint8_t *__restrict__ A,
 // ---------------------------------------------------------------------------
 // Small-M ("decode") configuration, M <= 64: the GEMM is a stream of W from
 // HBM (arithmetic intensity 2..32 flop/byte).  One workgroup owns a slab of
-// 16 output columns; its kDecWaves waves split the K blocks round-robin
-// (wave w takes kb = w, w + S, ...), so the slab's weight rows are read once,
+// 16 output columns; its waves (16, or 8 where the register budget calls
+// for it) split the K blocks round-robin (wave w of S takes kb = w, w + S,
+// ...), so the slab's weight rows are read once,
 // straight from global memory into MFMA operand registers (no LDS staging),
 // U blocks per wave at a time so that many loads are in flight.  Each wave
 // keeps 16x16 partial tiles for up to four 16-row fragments of x; the
@@ -749,8 +751,9 @@ constexpr int kDecMaxM = 64;
 constexpr int kDecMaxScaleBytes = 32 * 1024;  // x_scale staging limit (KB * MF * 16 * 4)
 
 // NW waves per workgroup (kDecWaves by default; 8 for four row fragments
-// with fp32 block scales, whose twice larger register budget per wave holds
-// two load buffers without spilling).
+// with fp32 block scales, for two from kDecWide8N columns on, and for E8M0
+// scales past 16 rows: the twice larger register budget per wave holds two
+// load buffers, and packed slabs, without spilling).
 //
 // S = float: fp32 scales, promoted per K block with FMAs as in gemm_tile;
 // S = uint8_t: E8M0 scale bytes, loaded with the operands and applied by the
@@ -961,9 +964,9 @@ static hipError_t launch_decode_nw(const void *xq, const S *xs, int64_t xs_rs, i
                                    void *y, hipStream_t stream) {
   const int64_t KB = K / 128;
   // slabs per workgroup: up to four for one or two row fragments, up to two
-  // for four (their partials fill 128 KB of LDS); for more than one
-  // fragment with fp32 scales only (block or row-wise; packed E8M0 variants
-  // spill and measured mixed).  Every workgroup reads all of x (M x K
+  // for four; for more than one fragment with fp32 scales (block or
+  // row-wise) and with E8M0 scales on 8 waves (below).  Every workgroup
+  // reads all of x (M x K
   // bytes) once per K pass, as many bytes as its slab of weights at M = 16
   // and twice or four times as many at M = 32 or 64, so packing slabs cuts
   // the bytes per output column: measured (weights streamed from HBM)
