@@ -39,10 +39,11 @@ def _replay_and_check(step, outs, ref, other):
         torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("M", [16, 300])
+@pytest.mark.parametrize("M", [16, 24, 48, 300])
 def test_linear_layer_graph(M):
-    """fp8_act_quant_group + fp8_block_gemm (prefill) or the fused decode
-    kernel (M = 16) for two projections, captured and replayed."""
+    """fp8_act_quant_group + fp8_block_gemm (prefill, and M = 48: the
+    quantizer and the 8-wave decode GEMM) or the fused decode kernel
+    (M = 16, 24) for two projections, captured and replayed."""
     d = dev()
     shapes = [(1024, 2048), (576, 4096)]
     xs = [to_dev_bf16(synth.dsv3_activations(7 + K, M, K, 3)) for (_, K) in shapes]
