@@ -1354,9 +1354,21 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
                                                             int64_t MN, uint16_t *__restrict__ y) {
   const int64_t stride = (int64_t)gridDim.x * 256;
   const int64_t n4 = MN / 4;
+  // the first kBatch partials are loaded together (their latencies
+  // overlap), then added in split order like any later ones
+  constexpr int kBatch = 8;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride) {
-    float4 a = reinterpret_cast<const float4 *>(part)[i];
-    for (int sp = 1; sp < splits; ++sp) {
+    float4 p[kBatch];
+#pragma unroll
+    for (int sp = 0; sp < kBatch; ++sp)
+      if (sp < splits) p[sp] = reinterpret_cast<const float4 *>(part + sp * slice_elems)[i];
+    float4 a = p[0];
+#pragma unroll
+    for (int sp = 1; sp < kBatch; ++sp)
+      if (sp < splits) {
+        a.x += p[sp].x; a.y += p[sp].y; a.z += p[sp].z; a.w += p[sp].w;
+      }
+    for (int sp = kBatch; sp < splits; ++sp) {
       const float4 b = reinterpret_cast<const float4 *>(part + sp * slice_elems)[i];
       a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
     }
@@ -1443,11 +1455,36 @@ __global__ __launch_bounds__(256) void sk_reduce_kernel(const float *__restrict_
   const int64_t row = (int64_t)tm * TM + r, col0 = (int64_t)tn * TN + c;
   if (row >= M) return;
   const int w0 = (int)(((int64_t)s * KB) / L), w1 = (int)(((int64_t)(s + 1) * KB - 1) / L);
-  float4 a = reinterpret_cast<const float4 *>(part + (int64_t)(w0 + s) * (TM * TN) + r * TN + c)[0];
-  for (int w = w0 + 1; w <= w1; ++w) {
-    const float4 b =
-        reinterpret_cast<const float4 *>(part + (int64_t)(w + s) * (TM * TN) + r * TN + c)[0];
+  auto piece = [&](int w) {
+    return reinterpret_cast<const float4 *>(part + (int64_t)(w + s) * (TM * TN) + r * TN + c)[0];
+  };
+  // the first kBatch pieces are loaded together (their latencies overlap),
+  // then added in K order like any later ones
+  constexpr int kBatch = 8;
+  const int np = w1 - w0 + 1;
+  float4 p[kBatch];
+#pragma unroll
+  for (int i = 0; i < kBatch; ++i)
+    if (i < np) p[i] = piece(w0 + i);
+  float4 a = p[0];
+#pragma unroll
+  for (int i = 1; i < kBatch; ++i)
+    if (i < np) {
+      a.x += p[i].x; a.y += p[i].y; a.z += p[i].z; a.w += p[i].w;
+    }
+  for (int w = w0 + kBatch; w <= w1; ++w) {
+    const float4 b = piece(w);
     a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+  }
+  if ((N & 3) == 0 && col0 + 3 < N) {
+    // four whole columns of a row starting at a multiple of 4: one 8-byte
+    // store (non-temporal, as the GEMM epilogue)
+    typedef unsigned v2u __attribute__((ext_vector_type(2)));
+    v2u o;
+    o.x = bf16_rne(a.x) | (bf16_rne(a.y) << 16);
+    o.y = bf16_rne(a.z) | (bf16_rne(a.w) << 16);
+    __builtin_nontemporal_store(o, reinterpret_cast<v2u *>(y + row * N + col0));
+    return;
   }
   const float v[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
