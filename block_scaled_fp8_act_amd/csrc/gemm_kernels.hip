@@ -772,6 +772,7 @@ __global__ __launch_bounds__(NW * 64) void decode_gemm_kernel(
   static_assert(!(kRow && MX), "row-wise scales are fp32");
   static_assert(!kPartial || (!MX && !kRow), "partial sums: fp32 block scales only");
   static_assert(NS == 1 || NS == 2 || NS == 4, "slabs per workgroup: 1, 2 or 4");
+  static_assert(NS * MF <= NW, "one wave per (slab, fragment) sums the partials");
   constexpr int R = MF * 16;                          // staged rows
   // register buffers of U K blocks: two (the next batch's loads go out
   // before the current batch's MFMAs) unless four row fragments, four slabs
@@ -1058,6 +1059,7 @@ __global__ __launch_bounds__(NW * 64) void decode_linear_kernel(
     const uint16_t *__restrict__ x, const uint8_t *__restrict__ wq, const float *__restrict__ ws,
     int M, int64_t N, int64_t K, uint16_t *__restrict__ y) {
   static_assert(NS == 1 || NS == 2 || NS == 4, "slabs per workgroup: 1, 2 or 4");
+  static_assert(NS * MF <= NW, "one wave per (slab, fragment) sums the partials");
   // K blocks in flight (bf16 x takes 16 VGPRs per fragment)
   constexpr int U = (MF == 1 && NS < 4) ? 2 : 1;
   extern __shared__ __align__(16) float dsm[];
