@@ -27,6 +27,7 @@
 // 32 K values; a 128-block scale is simply the same byte for all four), and
 // adds into the fp32 accumulator -- no per-block partials, no promotion FMAs.
 #include <algorithm>
+#include <cstdint>
 #include <mutex>
 #include <type_traits>
 
@@ -72,6 +73,7 @@ struct Tile {
     uint8_t b[2][TN * 128];
     float as[2][TM];
     float ws[2][64];  // weight-block scales of the tile's (<= 2) column blocks
+    float asc[2][TM * 4];  // activation scales four K blocks at a time, [row][4]
   };
   struct SmemMx {  // E8M0 scale bytes, one zero-extended dword per slot
     uint8_t a[2][TM * 128];
@@ -188,7 +190,21 @@ __device__ __forceinline__ void store_tile_rows16(const v4f (&acc)[FM][4], uint1
 // row stride of A and B, K/128 that of the weight scales); with kPartial
 // the tile's fp32 sums go unrounded to Y reinterpreted as float (row
 // stride ldy floats), one K range of a split over workgroups.
-template <int WM, int WN, int FM, int KS = 1, bool kPartial = false>
+//
+// kChunk (256x256 tiles over all of K; the caller guarantees xs_ks == 1,
+// xs_rs and K/128 multiples of 4 and As 16-byte aligned): the activation
+// scales travel four K blocks at a time, one 16-byte DMA per row into an
+// LDS ring [row][4], a quarter of the rows per step (wave it & 3 loads the
+// next chunk's rows 64(it & 3)..+63 during step it).  Per K step the tile
+// then asks for 64 scale lines instead of one line per row (256): rows
+// [M, K/128] apart are all in different lines, and those requests share the
+// per-CU L1 miss slots with the 512 operand lines of the step.  Same
+// values, so the same bits.  Measured (same inputs streamed from HBM, one
+// launch at a time): 1.4-5.2 % faster on K >= 4096 shapes (q_a
+// 8192x1536x7168 120.5 -> 114.2 us, Llama down 243.0 -> 236.6, gate/up
+// 280.6 -> 274.8); all rows reading one address instead (a timing bound,
+// not the method) measured 3-10 %.  Where it is used: chunked_scales_ok.
+template <int WM, int WN, int FM, int KS = 1, bool kPartial = false, bool kChunk = false>
 __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ A,
                                           const float *__restrict__ As, int64_t xs_rs, int xs_ks,
                                           int rows_a, const uint8_t *__restrict__ B,
@@ -241,9 +257,25 @@ __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ A,
 #pragma unroll
     for (int i = 0; i < T::kDmaB; ++i)
       buf_dma16(rB, vb, (uint32_t)i * row8, sm.b[st] + (T::kDmaB * wave + i) * 1024);
-    if (wave < T::TM / 64) lds_dma4(ps + (int64_t)kb * xs_ks, &sm.as[st][64 * wave]);
+    if constexpr (kChunk) {
+      // during step kb - 1: rows 64q..64q+63 (q = (kb - 1) & 3) of the next
+      // chunk; past the last chunk the last one is loaded again (its buffer
+      // is not the one being read)
+      if (kb > 0) {
+        const int itc = kb - 1;
+        const int q = itc & 3;
+        const int ch = min((itc >> 2) + 1, NKB / 4 - 1);
+        if (wave == q)
+          lds_dma16(As + (int64_t)min(64 * q + lane, rows_a - 1) * xs_rs + 4 * ch,
+                    &sm.asc[((itc >> 2) + 1) & 1][64 * q * 4]);
+      }
+    } else {
+      if (wave < T::TM / 64) lds_dma4(ps + (int64_t)kb * xs_ks, &sm.as[st][64 * wave]);
+    }
     if (wave == T::TM / 64 && lane < kNbTile) lds_dma4(pws + kb, &sm.ws[st][0]);
   };
+  static_assert(!kChunk || (T::TM == 256 && KS == 1 && !kPartial),
+                "chunked scales: 256-row tiles over all of K");
 
   v4f acc[FM][4];
 #pragma unroll
@@ -252,6 +284,11 @@ __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ A,
     for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
   issue(min(kg, NKB - 1), 0);
+  if constexpr (kChunk) {
+    // chunk 0 (K blocks 0..3) of every row
+    if (wave < 4)
+      lds_dma16(As + (int64_t)min(64 * wave + lane, rows_a - 1) * xs_rs, &sm.asc[0][64 * wave * 4]);
+  }
   // Y (a kernel argument) is first used by the epilogue; consuming it here
   // makes its scalar load complete before the loop.  With no scalar load in
   // flight the LDS reads of the loop can be waited on partially (LDS
@@ -276,6 +313,16 @@ __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ A,
     __builtin_amdgcn_sched_barrier(0);
     const uint8_t *sa = sm.a[st];
     const float4 *sas = reinterpret_cast<const float4 *>(&sm.as[st][srow0]);
+    const float *sch = &sm.asc[(it >> 2) & 1][srow0 * 4 + (it & 3)];
+    // the activation scales of rows srow0 + 16 mi + 0..3 at this K block
+    auto rs = [&](int mi) {
+      if constexpr (kChunk) {
+        const float *p = sch + mi * 64;
+        return float4{p[0], p[4], p[8], p[12]};
+      } else {
+        return sas[mi * 4];
+      }
+    };
     // Reads in first-use order (B0, A0, B1, B2, B3, scales, then fragment 1),
     // so the first MFMA waits only for the first four; LDS returns in order.
     // A fragments are then fetched two fragments ahead of their MFMAs.
@@ -297,9 +344,9 @@ __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ A,
                           *reinterpret_cast<const uint4 *>(sb + swz(row, c0 + 1)));
       __builtin_amdgcn_sched_barrier(0);
     }
-    float4 s4 = sas[0];
+    float4 s4 = rs(0);
     v8i afn = read_a(1);
-    float4 s4n = sas[4];
+    float4 s4n = rs(1);
     __builtin_amdgcn_sched_barrier(0);
     v8i afn2 = afn;
     float4 s4n2 = s4n;
@@ -317,7 +364,7 @@ __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ A,
         if (ni == 0) {
           if (mi + 2 < FM) {
             afn2 = read_a(mi + 2);
-            s4n2 = sas[(mi + 2) * 4];
+            s4n2 = rs(mi + 2);
           }
           scp[mi & 1][0] = s4.x * wsc;
           scp[mi & 1][1] = s4.y * wsc;
@@ -1255,7 +1302,7 @@ struct TileSmem {
 
 // xs_rs / xs_ks address the fp32 activation scales (E8M0 bytes always use
 // the per-token-group layout).
-template <int WM, int WN, int FM, typename S>
+template <int WM, int WN, int FM, typename S, bool kChunk = false>
 __device__ __forceinline__ void run_tile(const uint8_t *A, const S *As, int64_t xs_rs, int xs_ks,
                                          int rows_a, const uint8_t *B, const S *Bs, int rows_b,
                                          int64_t K, uint16_t *Y, int64_t ldy,
@@ -1263,10 +1310,11 @@ __device__ __forceinline__ void run_tile(const uint8_t *A, const S *As, int64_t 
   if constexpr (std::is_same<S, uint8_t>::value)
     gemm_tile_mx<WM, WN, FM, (FM <= 4)>(A, As, rows_a, B, Bs, rows_b, K, Y, ldy, sm);
   else
-    gemm_tile<WM, WN, FM>(A, As, xs_rs, xs_ks, rows_a, B, Bs, rows_b, K, Y, ldy, sm);
+    gemm_tile<WM, WN, FM, 1, false, kChunk>(A, As, xs_rs, xs_ks, rows_a, B, Bs, rows_b, K, Y,
+                                            ldy, sm);
 }
 
-template <int WM, int WN, int FM, typename S>
+template <int WM, int WN, int FM, typename S, bool kChunk = false>
 __global__ __launch_bounds__(WM * WN * 64) void block_gemm_kernel(
     const uint8_t *__restrict__ xq, const S *__restrict__ xs, int64_t xs_rs, int xs_ks,
     const uint8_t *__restrict__ wq, const S *__restrict__ ws, int64_t M, int64_t N, int64_t K,
@@ -1277,9 +1325,10 @@ __global__ __launch_bounds__(WM * WN * 64) void block_gemm_kernel(
   tile_coords(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * T::TM, n0 = (int64_t)tn * T::TN;
   const int64_t KB = K / 128;
-  run_tile<WM, WN, FM, S>(xq + m0 * K, xs + m0 * xs_rs, xs_rs, xs_ks,
-                          (int)min<int64_t>(T::TM, M - m0), wq + n0 * K, ws + (n0 / 128) * KB,
-                          (int)min<int64_t>(T::TN, N - n0), K, y + m0 * N + n0, N, sm);
+  run_tile<WM, WN, FM, S, kChunk>(xq + m0 * K, xs + m0 * xs_rs, xs_rs, xs_ks,
+                                  (int)min<int64_t>(T::TM, M - m0), wq + n0 * K,
+                                  ws + (n0 / 128) * KB, (int)min<int64_t>(T::TN, N - n0), K,
+                                  y + m0 * N + n0, N, sm);
 }
 
 // Split-K inside the workgroup: KS groups of WM x WN waves on one tile, for
@@ -1402,7 +1451,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
 // tile's pieces in K order and rounds once to bf16.
 constexpr int kCUs = 256;  // MI355X compute units
 
-template <int WM, int WN, int FM>
+template <int WM, int WN, int FM, bool kChunk = false>
 __global__ __launch_bounds__(WM * WN * 64) void block_gemm_sk_kernel(
     const uint8_t *__restrict__ xq, const float *__restrict__ xs, const uint8_t *__restrict__ wq,
     const float *__restrict__ ws, int64_t M, int64_t N, int64_t K, uint16_t *__restrict__ y,
@@ -1415,9 +1464,11 @@ __global__ __launch_bounds__(WM * WN * 64) void block_gemm_sk_kernel(
   if (bid < t_dp) {
     group_coords(xcd_remap(bid, t_dp), tiles_m, tiles_n, tm, tn);
     const int64_t m0 = (int64_t)tm * T::TM, n0 = (int64_t)tn * T::TN;
-    gemm_tile<WM, WN, FM>(xq + m0 * K, xs + m0 * KB, KB, 1, (int)min<int64_t>(T::TM, M - m0),
-                          wq + n0 * K, ws + (n0 / 128) * KB, (int)min<int64_t>(T::TN, N - n0), K,
-                          y + m0 * N + n0, N, sm);
+    gemm_tile<WM, WN, FM, 1, false, kChunk>(xq + m0 * K, xs + m0 * KB, KB, 1,
+                                            (int)min<int64_t>(T::TM, M - m0), wq + n0 * K,
+                                            ws + (n0 / 128) * KB,
+                                            (int)min<int64_t>(T::TN, N - n0), K, y + m0 * N + n0,
+                                            N, sm);
     return;
   }
   const int w = bid - t_dp;
@@ -1563,12 +1614,34 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(
                           N, sm);
 }
 
+// The chunked activation-scale loads of gemm_tile apply: per-token-group
+// scales (K-block stride 1) whose rows and K-block count are multiples of 4
+// floats from a 16-byte aligned base, with K >= 4096.  In the bench step
+// (same box, runs alternated): the six DeepSeek-V3 GEMMs 3398-3419 ->
+// 3351-3381 us (q_a -4 %, MLP down -2.6 %, MLP up -1.7 %), the Llama four
+// 577-578 -> 570 us; q_b (K = 1536, three chunks) ~1 % slower, hence the
+// bound.
+template <typename S>
+static bool chunked_scales_ok(const S *xs, int64_t xs_rs, int xs_ks, int64_t K) {
+  return std::is_same<S, float>::value && xs_ks == 1 && xs_rs % 4 == 0 && (K / 128) % 4 == 0 &&
+         K / 128 >= 32 && (reinterpret_cast<uintptr_t>(xs) & 15) == 0;
+}
+
 template <int WM, int WN, int FM, typename S>
 static hipError_t launch_tiled(const void *xq, const S *xs, int64_t xs_rs, int xs_ks,
                                const void *wq, const S *ws, int64_t M, int64_t N, int64_t K,
                                void *y, hipStream_t stream) {
   using T = Tile<WM, WN, FM>;
   const int tm = (int)((M + T::TM - 1) / T::TM), tn = (int)((N + T::TN - 1) / T::TN);
+  if constexpr (T::TM == 256 && std::is_same<S, float>::value) {
+    if (chunked_scales_ok(xs, xs_rs, xs_ks, K)) {
+      hipLaunchKernelGGL((block_gemm_kernel<WM, WN, FM, S, true>), dim3((unsigned)(tm * tn)),
+                         dim3(T::kThreads), 0, stream, static_cast<const uint8_t *>(xq), xs, xs_rs,
+                         xs_ks, static_cast<const uint8_t *>(wq), ws, M, N, K,
+                         static_cast<uint16_t *>(y), tm, tn);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((block_gemm_kernel<WM, WN, FM, S>), dim3((unsigned)(tm * tn)),
                      dim3(T::kThreads), 0, stream, static_cast<const uint8_t *>(xq), xs, xs_rs,
                      xs_ks, static_cast<const uint8_t *>(wq), ws, M, N, K,
@@ -1834,10 +1907,17 @@ static hipError_t launch_splitk(const void *xq, const S *xs, const void *wq, con
       using T = Tile<2, 4, 8>;
       const int tm = (int)((M + T::TM - 1) / T::TM), tn = (int)((N + T::TN - 1) / T::TN);
       float *part = static_cast<float *>(work);
-      hipLaunchKernelGGL((block_gemm_sk_kernel<2, 4, 8>), dim3((unsigned)(sk.t_dp + sk.nsk)),
-                         dim3(T::kThreads), 0, stream, static_cast<const uint8_t *>(xq), xs,
-                         static_cast<const uint8_t *>(wq), ws, M, N, K,
-                         static_cast<uint16_t *>(y), part, tm, tn, sk.t_dp, sk.rem, sk.L);
+      if (chunked_scales_ok(xs, K / 128, 1, K))
+        hipLaunchKernelGGL((block_gemm_sk_kernel<2, 4, 8, true>),
+                           dim3((unsigned)(sk.t_dp + sk.nsk)), dim3(T::kThreads), 0, stream,
+                           static_cast<const uint8_t *>(xq), xs, static_cast<const uint8_t *>(wq),
+                           ws, M, N, K, static_cast<uint16_t *>(y), part, tm, tn, sk.t_dp,
+                           sk.rem, sk.L);
+      else
+        hipLaunchKernelGGL((block_gemm_sk_kernel<2, 4, 8>), dim3((unsigned)(sk.t_dp + sk.nsk)),
+                           dim3(T::kThreads), 0, stream, static_cast<const uint8_t *>(xq), xs,
+                           static_cast<const uint8_t *>(wq), ws, M, N, K,
+                           static_cast<uint16_t *>(y), part, tm, tn, sk.t_dp, sk.rem, sk.L);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL((sk_reduce_kernel<T::TM, T::TN>), dim3((unsigned)(sk.rem * (T::TM / 4))),

@@ -45,12 +45,16 @@ def quantized_operands(x_bits, w_bits):
 # exact pins
 
 @pytest.mark.parametrize("M,N,K", [(16, 16, 128), (64, 192, 1024), (130, 576, 4096), (1, 300, 512),
-                                   (40, 12300, 256), (64, 12288, 384)])
+                                   (40, 12300, 256), (64, 12288, 384), (3900, 3300, 4096),
+                                   (4000, 3200, 640)])
 def test_gemm_exact_integer_operands(M, N, K):
     """|codes| <= 8 integers, scales in {1/2, 1, 2}: every partial sum and
     every promotion is exact in fp32, so y must equal bf16_RNE(exact).
     (40, 12300) and (64, 12288): 33-64 rows with N >= 12288 take the tiled
-    kernel (one padded row tile) instead of the decode kernel."""
+    kernel (one padded row tile) instead of the decode kernel.  The last
+    two run 256x256 tiles with ragged last row and column tiles: at
+    K = 4096 the activation scales load four K blocks at a time, at
+    K = 640 one block per step."""
     rng = np.random.default_rng(M + N + K)
     xi = rng.integers(-8, 9, (M, K)); wi = rng.integers(-8, 9, (N, K))
     xq = oe.encode(xi.astype(np.float32)); wq = oe.encode(wi.astype(np.float32))
