@@ -1553,7 +1553,7 @@ __global__ __launch_bounds__(256) void sk_reduce_kernel(const float *__restrict_
 // [e*capacity, e*capacity + count[e]) with count[e] = offsets[e] clamped to
 // [0, capacity]; its tiles are numbered directly (ceil(capacity/TM) per
 // expert) and tiles past the count exit.
-template <int WM, int WN, int FM, typename S>
+template <int WM, int WN, int FM, typename S, bool kChunk = false>
 __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(
     const uint8_t *__restrict__ xq, const S *__restrict__ xs, int64_t xs_rs, int xs_ks,
     const uint8_t *__restrict__ wq, const S *__restrict__ ws,
@@ -1609,9 +1609,9 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(
       return;
     }
   }
-  run_tile<WM, WN, FM, S>(xq + r0 * K, xs + r0 * xs_rs, xs_rs, xs_ks,
-                          (int)min<int64_t>(T::TM, r1 - r0), wt, wst, rows_b, K, y + r0 * N + n0,
-                          N, sm);
+  run_tile<WM, WN, FM, S, kChunk>(xq + r0 * K, xs + r0 * xs_rs, xs_rs, xs_ks,
+                                  (int)min<int64_t>(T::TM, r1 - r0), wt, wst, rows_b, K,
+                                  y + r0 * N + n0, N, sm);
 }
 
 // The chunked activation-scale loads of gemm_tile apply: per-token-group
@@ -2029,6 +2029,19 @@ static hipError_t dispatch_grouped(const void *xq, const S *xs, const void *wq, 
   const int64_t tiles_n = (N + T::TN - 1) / T::TN;
   const int64_t tiles_m = capacity > 0 ? (int64_t)E * ((capacity + T::TM - 1) / T::TM)
                                        : (total_M + T::TM - 1) / T::TM + E;
+  // full row tiles load the activation scales four K blocks at a time where
+  // that applies (any row offset keeps the 16-byte alignment when K / 128
+  // is a multiple of 4)
+  if constexpr (std::is_same<S, float>::value) {
+    if (chunked_scales_ok(xs, K / 128, 1, K)) {
+      hipLaunchKernelGGL((grouped_gemm_kernel<2, 4, 8, S, true>),
+                         dim3((unsigned)(tiles_m * tiles_n)), dim3(T::kThreads), 0, stream,
+                         static_cast<const uint8_t *>(xq), xs, K / 128, 1,
+                         static_cast<const uint8_t *>(wq), ws, offsets, (int)E, total_M, N, K,
+                         static_cast<uint16_t *>(y), (int)tiles_n, capacity);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((grouped_gemm_kernel<2, 4, 8, S>), dim3((unsigned)(tiles_m * tiles_n)),
                      dim3(T::kThreads), 0, stream, static_cast<const uint8_t *>(xq), xs, K / 128,
                      1, static_cast<const uint8_t *>(wq), ws, offsets, (int)E, total_M, N, K,
